@@ -1,0 +1,179 @@
+"""Benchmark of the KDA forward hot path on one MI355X.
+
+One step = one kda_chunk_fwd call over the K3-shaped layer workload
+(B1, T65536, H96, d128, bf16 inputs, fp32 state, output gate, y and S_T
+outputs), inputs already resident in HBM.  Prints ONE JSON line.
+
+Per-kernel durations come from HIP events recorded by the library around each
+of its launches on the launch stream (kda_chunk_fwd_traced); the dominant
+kernel's roofline uses its algorithmic bytes:
+  intra-chunk : q, k, z (3 * 2d B) + beta (2 B) per token-head
+  state scan  : v (2d B) per token-head + initial / final state
+  gate        : gate logits in, y out (2 * 2d B) per token-head
+which add up to the path's 1,538 B per token-head (2d = 256 B at d = 128).
+The CPU baseline is the fp64 C oracle timed on a bounded sample of heads.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA fwd tokens·heads/s at T=64K,H=96,d=128 bf16; % MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def kernel_bytes(name: str, token_heads: int, d: int, BH: int, T: int) -> float:
+    if name == "intra":
+        return token_heads * (3 * 2 * d + 2)
+    if name == "scan":
+        return token_heads * (2 * d) + 2 * BH * d * d * 4
+    if name == "gate":
+        return token_heads * (2 * 2 * d)
+    raise KeyError(name)
+
+
+def path_flops_per_token_head(d: int, C: int = 64) -> float:
+    # 6 d^2 (state products) + 5 (C + 16) d (sub-tile products) + C^2 / 3 (UT inverse)
+    return 6 * d * d + 5 * (C + 16) * d + C * C / 3
+
+
+def cpu_baseline(wl, heads: int, threads: int) -> dict:
+    import oracle
+    from synth.workloads import gen_inputs
+
+    x = gen_inputs(wl, heads=(0, heads))
+    t0 = time.perf_counter()
+    oracle.forward_c(x["q"], x["k"], x["v"], x["beta"], x["z"], x["A"], gate=x["gate"], nthreads=threads)
+    dt = time.perf_counter() - t0
+    th = wl.B * wl.T * heads
+    return {"value": th / dt, "unit": "tokens·heads/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 C oracle (sequential recurrence + gate, OpenMP over heads) on heads 0..{heads - 1} "
+                      f"of the {wl.name} workload, all {wl.T} tokens ({th} token-heads, {dt:.1f} s)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="k3_layer")
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-baseline sample (0: all heads)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every box here has a single MI355X). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_84_amd as kda
+    from synth.workloads import WORKLOADS, gen_inputs
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kda.lib()
+
+    t_gen = time.perf_counter()
+    x = gen_inputs(wl)
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    t = {k: to_dev(v) for k, v in x.items()}
+    del x
+    t_gen = time.perf_counter() - t_gen
+    B, T, H, D = wl.B, wl.T, wl.H, wl.D
+    token_heads = B * T * H
+    odt = torch.bfloat16
+    out = {"y": torch.empty((B, T, H, D), dtype=odt, device=dev),
+           "S_T": torch.empty((B, H, D, D), dtype=torch.float32, device=dev)}
+    desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16)
+    ws = torch.empty(kda.workspace_size(desc), dtype=torch.uint8, device=dev)
+    n_seg = 1  # whole sequence in one segment at this size
+    names = ["intra", "scan", "gate"] * n_seg
+
+    def step(events=None):
+        kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t.get("S0"), gate=t["gate"],
+                      want_o=False, out=out, workspace=ws, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-step kernel events (created by a first record, then re-recorded by the library)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))] for _ in range(args.steps)]
+    for row in ev:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    handles = [[e.cuda_event for e in row] for row in ev]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        step(events=handles[k])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / args.steps
+
+    per = {n: [] for n in set(names)}
+    for row in ev:
+        for i, n in enumerate(names):
+            per[n].append(row[2 * i].elapsed_time(row[2 * i + 1]))
+    kern_ms = {n: float(np.mean(v)) for n, v in per.items()}
+    dom = max(kern_ms, key=kern_ms.get)
+    dom_bytes = kernel_bytes(dom, token_heads, D, B * H, T)
+    achieved = dom_bytes / (kern_ms[dom] * 1e-3) / 1e9
+    path_bytes = token_heads * (1538 if D == 128 else (6 * D + 2 + 4 * D)) + 2 * B * H * D * D * 4
+    path_gbs = path_bytes / (ms * 1e-3) / 1e9
+    path_tflops = token_heads * path_flops_per_token_head(D) / (ms * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": token_heads / (ms * 1e-3),
+        "unit": "tokens·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; K3 layer shapes, no trained weights)",
+        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "d_k": D, "d_v": D, "chunk": 64,
+                   "inputs": "bf16", "state": "fp32", "outputs": "y (bf16) + S_T (fp32)", "gate": True},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "path_roofline": {"achieved_GBs": path_gbs, "frac_hbm": path_gbs / HBM_PEAK_GBS,
+                          "achieved_TFLOPs": path_tflops, "frac_bf16_mfma": path_tflops / BF16_PEAK_TFLOPS,
+                          "algorithmic_bytes": path_bytes},
+        "kernel_ms": kern_ms,
+        "input_setup_s": t_gen,
+    }
+    if not args.no_cpu_baseline:
+        threads = min(16, os.cpu_count() or 1)
+        heads = args.cpu_heads or H
+        result["cpu_baseline"] = cpu_baseline(wl, min(heads, H), threads)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,201 @@
+"""Python binding of libkda (MI355X / gfx950 Kimi Delta Attention).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/kda.h``.  PyTorch provides device memory
+and the current HIP stream.  There is no fallback path: if ``libkda.so`` has
+not been built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "kda.h")
+
+KDA_F32, KDA_BF16 = 0, 1
+STATE_ZERO, STATE_IMPORT, STATE_EXPORT = 0, 1, 2
+LAYOUT_KV, LAYOUT_VK = 0, 1
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL_ARG", 2: "KDA_ERR_BAD_SHAPE", 3: "KDA_ERR_BAD_DTYPE",
+          4: "KDA_ERR_MISALIGNED", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_HIP"}
+
+
+class KdaDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("g_min", ctypes.c_float), ("q_scale", ctypes.c_float), ("l2_eps", ctypes.c_float),
+                ("rms_eps", ctypes.c_float), ("qk_l2norm", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int)]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python __graft_entry__.py` "
+                               "(no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+        dp = ctypes.POINTER(KdaDesc)
+        L.kda_abi_version.restype = ctypes.c_int
+        L.kda_status_str.restype = ctypes.c_char_p
+        L.kda_status_str.argtypes = [ctypes.c_int]
+        L.kda_desc_init.restype = ctypes.c_int
+        L.kda_desc_init.argtypes = [dp, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int]
+        L.kda_chunk_fwd_workspace_size.restype = sz
+        L.kda_chunk_fwd_workspace_size.argtypes = [dp]
+        L.kda_chunk_fwd_workspace_size_for.restype = sz
+        L.kda_chunk_fwd_workspace_size_for.argtypes = [dp, i32]
+        L.kda_chunk_fwd.restype = ctypes.c_int
+        L.kda_chunk_fwd.argtypes = [dp] + [vp] * 13 + [sz, vp]
+        L.kda_chunk_fwd_traced.restype = ctypes.c_int
+        L.kda_chunk_fwd_traced.argtypes = [dp] + [vp] * 13 + [sz, vp, ctypes.POINTER(vp), i32]
+        L.kda_recurrent_step.restype = ctypes.c_int
+        L.kda_recurrent_step.argtypes = [dp] + [vp] * 12
+        L.kda_state_io.restype = ctypes.c_int
+        L.kda_state_io.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.c_int, vp, vp, vp, vp]
+        L.kda_prepass.restype = ctypes.c_int
+        L.kda_prepass.argtypes = [dp] + [vp] * 7 + [vp]
+        _lib = L
+    return _lib
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def make_desc(B, T, H, D, in_dtype, out_dtype, g_min=-5.0, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6,
+              qk_l2norm=True) -> KdaDesc:
+    d = KdaDesc()
+    rc = lib().kda_desc_init(ctypes.byref(d), B, T, H, D, in_dtype, out_dtype)
+    if rc != 0:
+        raise KdaError("kda_desc_init", rc)
+    d.g_min, d.q_scale, d.l2_eps, d.rms_eps, d.qk_l2norm = g_min, q_scale, l2_eps, rms_eps, int(bool(qk_l2norm))
+    return d
+
+
+def workspace_size(desc: KdaDesc, segment_tokens: int | None = None) -> int:
+    if segment_tokens is None:
+        return int(lib().kda_chunk_fwd_workspace_size(ctypes.byref(desc)))
+    return int(lib().kda_chunk_fwd_workspace_size_for(ctypes.byref(desc), int(segment_tokens)))
+
+
+def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=None, want_o=True,
+              want_y=None, want_state=True, workspace=None, segment_tokens=None, out=None, events=None,
+              **opts):
+    """KDA forward over whole sequences.  q, k, z: [B, T, H, D]; v (and gate):
+    [B, T, H, D]; beta: [B, T, H]; A: [H] fp32; S0: [B, H, D, D] fp32 or None.
+    Returns a dict with 'o' / 'y' (out_dtype, default the input dtype) and
+    'S_T' (fp32).  ``out`` may supply preallocated output tensors; ``events``
+    (raw hipEvent_t handles) selects the traced entry point."""
+    B, T, H, D = q.shape
+    in_dt = _dt(q)
+    odt = q.dtype if out_dtype is None else out_dtype
+    desc = make_desc(B, T, H, D, in_dt, _dt(torch.empty(0, dtype=odt)), **opts)
+    want_y = (gate is not None) if want_y is None else want_y
+    res = dict(out or {})
+    dev = q.device
+    if want_o and "o" not in res:
+        res["o"] = torch.empty((B, T, H, D), dtype=odt, device=dev)
+    if want_y and "y" not in res:
+        res["y"] = torch.empty((B, T, H, D), dtype=odt, device=dev)
+    if want_state and "S_T" not in res:
+        res["S_T"] = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    if workspace is None:
+        nbytes = workspace_size(desc, segment_tokens)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), _ptr(S0), _ptr(gate),
+            _ptr(rms_w), _ptr(res.get("o")), _ptr(res.get("y")), _ptr(res.get("S_T")), _ptr(workspace),
+            workspace.numel(), _stream(dev))
+    if events is None:
+        rc = lib().kda_chunk_fwd(*args)
+    else:
+        arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e) for e in events])
+        rc = lib().kda_chunk_fwd_traced(*args, arr, len(events))
+    if rc != 0:
+        raise KdaError("kda_chunk_fwd", rc)
+    return res
+
+
+def recurrent_step(q, k, v, beta, z, A, S_pool, slot=None, gate=None, rms_w=None, *, out_dtype=None,
+                   want_o=True, want_y=None, out=None, **opts):
+    """One decode token for n sequences.  q, k, v, z (and gate): [n, H, D];
+    beta [n, H]; S_pool [n_slots, H, D, D] fp32 updated in place; slot: int32
+    [n] or None."""
+    n, H, D = q.shape
+    odt = q.dtype if out_dtype is None else out_dtype
+    desc = make_desc(n, 1, H, D, _dt(q), _dt(torch.empty(0, dtype=odt)), **opts)
+    want_y = (gate is not None) if want_y is None else want_y
+    res = dict(out or {})
+    if want_o and "o" not in res:
+        res["o"] = torch.empty((n, H, D), dtype=odt, device=q.device)
+    if want_y and "y" not in res:
+        res["y"] = torch.empty((n, H, D), dtype=odt, device=q.device)
+    rc = lib().kda_recurrent_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A),
+                                  _ptr(S_pool), _ptr(slot), _ptr(gate), _ptr(rms_w), _ptr(res.get("o")),
+                                  _ptr(res.get("y")), _stream(q.device))
+    if rc != 0:
+        raise KdaError("kda_recurrent_step", rc)
+    return res
+
+
+def state_io(op: int, pool, user=None, slot=None, n=None, layout: int = LAYOUT_KV):
+    """ZERO / IMPORT / EXPORT states between ``pool`` [n_slots, H, D, D] and
+    ``user`` [n, H, D, D] (layout KV) or its transpose (layout VK)."""
+    _, H, Dk, Dv = pool.shape
+    if n is None:
+        n = user.shape[0] if user is not None else (slot.numel() if slot is not None else pool.shape[0])
+    rc = lib().kda_state_io(op, n, H, Dk, Dv, layout, _ptr(pool), _ptr(slot), _ptr(user), _stream(pool.device))
+    if rc != 0:
+        raise KdaError("kda_state_io", rc)
+
+
+def prepass(q, k, z, A, **opts):
+    """Chunk-local cumulative log-decay G [B, T, H, D] and inverse norms rq, rk
+    [B, T, H] (diagnostic view of the first step of chunk_fwd)."""
+    B, T, H, D = q.shape
+    desc = make_desc(B, T, H, D, _dt(q), KDA_F32, **opts)
+    G = torch.empty((B, T, H, D), dtype=torch.float32, device=q.device)
+    rq = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    rk = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    rc = lib().kda_prepass(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(z), _ptr(A), _ptr(G), _ptr(rq), _ptr(rk),
+                           _stream(q.device))
+    if rc != 0:
+        raise KdaError("kda_prepass", rc)
+    return G, rq, rk
+
+
+def build():
+    from . import _build
+    return _build.build()

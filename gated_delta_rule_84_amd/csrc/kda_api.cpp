@@ -1,0 +1,406 @@
+// Host side of the C ABI declared in include/kda.h: argument validation,
+// workspace carving, the segment loop and kernel launches.  No device memory
+// is allocated here and no host synchronisation happens (unless KDA_DEBUG=1,
+// which synchronises after every launch to localise failures).
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+
+#include "kda_params.hpp"
+
+namespace {
+
+using kda::kChunk;
+
+constexpr int32_t kDefaultSegmentTokens = 65536;
+
+bool debug_sync() {
+  const char* e = std::getenv("KDA_DEBUG");
+  return e != nullptr && e[0] == '1';
+}
+
+kda_status check_launch(hipError_t e, hipStream_t s) {
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return KDA_ERR_HIP;
+  }
+  if (debug_sync()) {
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return KDA_ERR_HIP;
+    }
+  }
+  return KDA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_size(kda_dtype t) { return t == KDA_F32 ? 4 : 2; }
+
+kda_status validate_desc(const kda_desc* d) {
+  if (d == nullptr) return KDA_ERR_NULL_ARG;
+  if (d->B < 1 || d->H < 1 || d->T < 0 || d->d_k < 1 || d->d_v < 1 || d->chunk < 1) return KDA_ERR_BAD_SHAPE;
+  if ((d->in_dtype != KDA_F32 && d->in_dtype != KDA_BF16) || (d->out_dtype != KDA_F32 && d->out_dtype != KDA_BF16))
+    return KDA_ERR_BAD_DTYPE;
+  if (d->d_k != d->d_v || (d->d_k != 64 && d->d_k != 128)) return KDA_ERR_UNSUPPORTED;
+  if (d->chunk != kChunk) return KDA_ERR_UNSUPPORTED;
+  if (!(d->g_min < 0.0f) || d->g_min < -5.5f) return KDA_ERR_UNSUPPORTED;
+  if (!(d->l2_eps >= 0.0f) || !(d->rms_eps >= 0.0f)) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct WsLayout {
+  size_t off_qg, off_kg, off_kdt, off_tb, off_aqh, off_aql, off_gam, off_o32, off_carry, total;
+};
+
+// Workspace for a segment of seg_nc chunks.
+WsLayout layout_for(const kda_desc* d, int64_t seg_nc, bool gated) {
+  const size_t es = elem_size(d->in_dtype);
+  const int64_t D = d->d_k;
+  const int64_t R = (int64_t)d->B * d->H * seg_nc;
+  WsLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  L.off_qg = take(R * kChunk * D * es);
+  L.off_kg = take(R * kChunk * D * es);
+  L.off_kdt = take(R * kChunk * D * es);
+  L.off_tb = take(R * kChunk * kChunk * es);
+  L.off_aqh = take(R * kChunk * kChunk * es);
+  L.off_aql = (d->in_dtype == KDA_BF16) ? take(R * kChunk * kChunk * es) : 0;
+  L.off_gam = take(R * D * 4);
+  L.off_o32 = gated ? take((size_t)d->B * seg_nc * kChunk * d->H * D * 4) : 0;
+  L.off_carry = take((size_t)d->B * d->H * D * D * 4);
+  L.total = o;
+  return L;
+}
+
+int64_t num_chunks(const kda_desc* d) { return ((int64_t)d->T + kChunk - 1) / kChunk; }
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_str(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL_ARG: return "required pointer is NULL";
+    case KDA_ERR_BAD_SHAPE: return "invalid size";
+    case KDA_ERR_BAD_DTYPE: return "invalid dtype";
+    case KDA_ERR_MISALIGNED: return "misaligned pointer";
+    case KDA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+kda_status kda_desc_init(kda_desc* d, int32_t B, int32_t T, int32_t H, int32_t head_dim, kda_dtype in_dtype,
+                         kda_dtype out_dtype) {
+  if (d == nullptr) return KDA_ERR_NULL_ARG;
+  std::memset(d, 0, sizeof(*d));
+  d->B = B;
+  d->T = T;
+  d->H = H;
+  d->d_k = head_dim;
+  d->d_v = head_dim;
+  d->chunk = kChunk;
+  d->g_min = -5.0f;
+  d->q_scale = 1.0f;
+  d->l2_eps = 1e-6f;
+  d->rms_eps = 1e-6f;
+  d->qk_l2norm = 1;
+  d->in_dtype = in_dtype;
+  d->out_dtype = out_dtype;
+  return validate_desc(d);
+}
+
+size_t kda_chunk_fwd_workspace_size_for(const kda_desc* d, int32_t segment_tokens) {
+  if (validate_desc(d) != KDA_OK || segment_tokens < 1) return 0;
+  const int64_t seg_nc = ((int64_t)segment_tokens + kChunk - 1) / kChunk;
+  return layout_for(d, seg_nc, true).total;
+}
+
+size_t kda_chunk_fwd_workspace_size(const kda_desc* d) {
+  if (validate_desc(d) != KDA_OK) return 0;
+  const int32_t toks = d->T < kDefaultSegmentTokens ? (d->T > 0 ? d->T : 1) : kDefaultSegmentTokens;
+  return kda_chunk_fwd_workspace_size_for(d, toks);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Records events[2i] / events[2i+1] around the i-th launch while they last.
+struct Tracer {
+  void* const* ev;
+  int32_t n;
+  int32_t i = 0;
+  void before(hipStream_t s) {
+    if (ev && 2 * i + 1 < n) (void)hipEventRecord(static_cast<hipEvent_t>(ev[2 * i]), s);
+  }
+  void after(hipStream_t s) {
+    if (ev && 2 * i + 1 < n) (void)hipEventRecord(static_cast<hipEvent_t>(ev[2 * i + 1]), s);
+    ++i;
+  }
+};
+
+kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
+                          const void* z, const float* A, const float* S0, const void* gate, const float* rms_w,
+                          void* o, void* y, float* S_T, void* ws, size_t ws_bytes, void* stream, Tracer tr) {
+  kda_status st = validate_desc(d);
+  if (st != KDA_OK) return st;
+  if (!o && !y && !S_T) return KDA_ERR_NULL_ARG;
+  if (d->T == 0) {  // nothing to read: S_T = S0 (or zero); inputs may be NULL
+    if ((S0 && !aligned(S0, 4)) || (S_T && !aligned(S_T, 4))) return KDA_ERR_MISALIGNED;
+    if (S_T && S_T != S0)
+      return check_launch(kda::launch_copy_state(S0, S_T, (int64_t)d->B * d->H * d->d_k * d->d_v,
+                                                 static_cast<hipStream_t>(stream)),
+                          static_cast<hipStream_t>(stream));
+    return KDA_OK;
+  }
+  if (!q || !k || !v || !beta || !z || !A) return KDA_ERR_NULL_ARG;
+  if (y && !gate) return KDA_ERR_NULL_ARG;
+  const size_t es = elem_size(d->in_dtype);
+  for (const void* p : {q, k, v, z, (const void*)o, (const void*)y, gate, (const void*)ws})
+    if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
+  if (!aligned(beta, es) || !aligned(A, 4) || (S0 && !aligned(S0, 4)) || (S_T && !aligned(S_T, 4)) ||
+      (rms_w && !aligned(rms_w, 4)))
+    return KDA_ERR_MISALIGNED;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = d->d_k;
+  const int in_f32 = d->in_dtype == KDA_F32;
+  const int out_f32 = d->out_dtype == KDA_F32;
+  const int64_t nc_total = num_chunks(d);
+
+  const bool gated = (y != nullptr);
+  // largest segment whose workspace fits
+  const WsLayout one = layout_for(d, 1, gated);
+  if (!ws || ws_bytes < one.total) return KDA_ERR_WORKSPACE;
+  int64_t seg_nc = 1;
+  {
+    int64_t lo = 1, hi = nc_total;
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo + 1) / 2;
+      if (layout_for(d, mid, gated).total <= ws_bytes)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    seg_nc = lo;
+  }
+  const WsLayout L = layout_for(d, seg_nc, gated);
+  char* base = static_cast<char*>(ws);
+  kda::ChunkWs cw{};
+  cw.qg = base + L.off_qg;
+  cw.kg = base + L.off_kg;
+  cw.kdt = base + L.off_kdt;
+  cw.tb = base + L.off_tb;
+  cw.aqh = base + L.off_aqh;
+  cw.aql = (d->in_dtype == KDA_BF16) ? base + L.off_aql : nullptr;
+  cw.gam = reinterpret_cast<float*>(base + L.off_gam);
+  cw.rec_elems_qk = (int64_t)kChunk * D;
+  cw.rec_elems_t = (int64_t)kChunk * kChunk;
+  float* o32 = gated ? reinterpret_cast<float*>(base + L.off_o32) : nullptr;
+  float* carry = reinterpret_cast<float*>(base + L.off_carry);
+  float* S_run = S_T ? S_T : carry;
+
+  const float* S_in = S0;
+  for (int64_t c0 = 0; c0 < nc_total; c0 += seg_nc) {
+    const int nc = (int)((nc_total - c0) < seg_nc ? (nc_total - c0) : seg_nc);
+    const int t0 = (int)(c0 * kChunk);
+
+    kda::IntraParams ip{};
+    ip.q = q;
+    ip.k = k;
+    ip.z = z;
+    ip.beta = beta;
+    ip.A = A;
+    ip.B = d->B;
+    ip.T = d->T;
+    ip.H = d->H;
+    ip.t0 = t0;
+    ip.nc = nc;
+    ip.g_min = d->g_min;
+    ip.q_scale = d->q_scale;
+    ip.l2_eps = d->l2_eps;
+    ip.l2norm = d->qk_l2norm;
+    ip.ws = cw;
+    tr.before(s);
+    st = check_launch(kda::launch_intra(ip, D, in_f32, s), s);
+    tr.after(s);
+    if (st != KDA_OK) return st;
+
+    kda::ScanParams sp{};
+    sp.v = v;
+    sp.S_in = S_in;
+    sp.S_out = S_run;
+    sp.B = d->B;
+    sp.T = d->T;
+    sp.H = d->H;
+    sp.t0 = t0;
+    sp.nc = nc;
+    sp.ws = cw;
+    if (gated) {
+      sp.o = o32;
+      sp.o_f32 = 1;
+      sp.o_tok_stride = (int64_t)d->H * D;
+      sp.o_b_stride = (int64_t)seg_nc * kChunk * d->H * D;
+      sp.o_t0 = t0;
+    } else {
+      sp.o = o;  // NULL when only S_T is requested: the scan then skips o
+      sp.o_f32 = out_f32;
+      sp.o_tok_stride = (int64_t)d->H * D;
+      sp.o_b_stride = (int64_t)d->T * d->H * D;
+      sp.o_t0 = 0;
+    }
+    tr.before(s);
+    st = check_launch(kda::launch_scan(sp, D, in_f32, s), s);
+    tr.after(s);
+    if (st != KDA_OK) return st;
+
+    if (gated) {
+      kda::GateParams gp{};
+      gp.o32 = o32;
+      gp.o32_b_stride = (int64_t)seg_nc * kChunk * d->H * D;
+      gp.gate = gate;
+      gp.rms_w = rms_w;
+      gp.y = y;
+      gp.o = o;
+      gp.B = d->B;
+      gp.T = d->T;
+      gp.H = d->H;
+      gp.t0 = t0;
+      gp.nt = (d->T - t0) < nc * kChunk ? (d->T - t0) : nc * kChunk;
+      gp.rms_eps = d->rms_eps;
+      tr.before(s);
+      st = check_launch(kda::launch_gate(gp, D, in_f32, out_f32, s), s);
+      tr.after(s);
+      if (st != KDA_OK) return st;
+    }
+    S_in = S_run;
+  }
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
+                         const void* z, const float* A, const float* S0, const void* gate, const float* rms_w,
+                         void* o, void* y, float* S_T, void* ws, size_t ws_bytes, void* stream) {
+  return chunk_fwd_impl(d, q, k, v, beta, z, A, S0, gate, rms_w, o, y, S_T, ws, ws_bytes, stream,
+                        Tracer{nullptr, 0});
+}
+
+kda_status kda_chunk_fwd_traced(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
+                                const void* z, const float* A, const float* S0, const void* gate,
+                                const float* rms_w, void* o, void* y, float* S_T, void* ws, size_t ws_bytes,
+                                void* stream, void* const* events, int32_t n_events) {
+  return chunk_fwd_impl(d, q, k, v, beta, z, A, S0, gate, rms_w, o, y, S_T, ws, ws_bytes, stream,
+                        Tracer{events, n_events < 0 ? 0 : n_events});
+}
+
+kda_status kda_recurrent_step(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
+                              const void* z, const float* A, float* S_pool, const int32_t* slot,
+                              const void* gate, const float* rms_w, void* o, void* y, void* stream) {
+  kda_status st = validate_desc(d);
+  if (st != KDA_OK) return st;
+  if (d->T != 1) return KDA_ERR_BAD_SHAPE;
+  if (!q || !k || !v || !beta || !z || !A || !S_pool) return KDA_ERR_NULL_ARG;
+  if (!o && !y) return KDA_ERR_NULL_ARG;
+  if (y && !gate) return KDA_ERR_NULL_ARG;
+  const size_t es = elem_size(d->in_dtype);
+  for (const void* p : {q, k, v, z, (const void*)o, (const void*)y, gate})
+    if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
+  if (!aligned(beta, es) || !aligned(A, 4) || !aligned(S_pool, 4) || (slot && !aligned(slot, 4)) ||
+      (rms_w && !aligned(rms_w, 4)))
+    return KDA_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  kda::DecodeParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.beta = beta;
+  p.z = z;
+  p.A = A;
+  p.S_pool = S_pool;
+  p.slot = slot;
+  p.gate = y ? gate : nullptr;
+  p.rms_w = rms_w;
+  p.o = o;
+  p.y = y;
+  p.n = d->B;
+  p.H = d->H;
+  p.g_min = d->g_min;
+  p.q_scale = d->q_scale;
+  p.l2_eps = d->l2_eps;
+  p.rms_eps = d->rms_eps;
+  p.l2norm = d->qk_l2norm;
+  p.out_f32 = d->out_dtype == KDA_F32;
+  return check_launch(kda::launch_decode(p, d->d_k, d->in_dtype == KDA_F32, s), s);
+}
+
+kda_status kda_state_io(kda_state_op op, int32_t n, int32_t H, int32_t d_k, int32_t d_v, kda_state_layout layout,
+                        float* pool, const int32_t* slot, float* user, void* stream) {
+  if (op != KDA_STATE_ZERO && op != KDA_STATE_IMPORT && op != KDA_STATE_EXPORT) return KDA_ERR_UNSUPPORTED;
+  if (layout != KDA_LAYOUT_KV && layout != KDA_LAYOUT_VK) return KDA_ERR_UNSUPPORTED;
+  if (n < 0 || H < 1 || d_k < 1 || d_v < 1) return KDA_ERR_BAD_SHAPE;
+  if (d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_ERR_UNSUPPORTED;
+  if (!pool) return KDA_ERR_NULL_ARG;
+  if (op != KDA_STATE_ZERO && !user) return KDA_ERR_NULL_ARG;
+  if (!aligned(pool, 4) || (user && !aligned(user, 4)) || (slot && !aligned(slot, 4))) return KDA_ERR_MISALIGNED;
+  if (n == 0) return KDA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  kda::StateIoParams p{};
+  p.op = static_cast<int>(op);
+  p.transpose = layout == KDA_LAYOUT_VK;
+  p.n = n;
+  p.H = H;
+  p.pool = pool;
+  p.slot = slot;
+  p.user = user;
+  return check_launch(kda::launch_state_io(p, d_k, s), s);
+}
+
+kda_status kda_prepass(const kda_desc* d, const void* q, const void* k, const void* z, const float* A, float* G,
+                       float* rq, float* rk, void* stream) {
+  kda_status st = validate_desc(d);
+  if (st != KDA_OK) return st;
+  if (!q || !k || !z || !A || !G || !rq || !rk) return KDA_ERR_NULL_ARG;
+  for (const void* p : {q, k, z})
+    if (!aligned(p, 16)) return KDA_ERR_MISALIGNED;
+  if (!aligned(A, 4) || !aligned(G, 4) || !aligned(rq, 4) || !aligned(rk, 4)) return KDA_ERR_MISALIGNED;
+  if (d->T == 0) return KDA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  kda::PrepassParams p{};
+  p.q = q;
+  p.k = k;
+  p.z = z;
+  p.A = A;
+  p.B = d->B;
+  p.T = d->T;
+  p.H = d->H;
+  p.g_min = d->g_min;
+  p.l2_eps = d->l2_eps;
+  p.l2norm = d->qk_l2norm;
+  p.G = G;
+  p.rq = rq;
+  p.rk = rk;
+  return check_launch(kda::launch_prepass(p, d->d_k, d->in_dtype == KDA_F32, s), s);
+}
+
+}  // extern "C"

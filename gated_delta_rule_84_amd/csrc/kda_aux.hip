@@ -1,0 +1,151 @@
+// Output gate epilogue, state import/export and the pre-pass diagnostic.
+//
+// Source: "Kimi K3: KDA, Attention Residuals and Stable LatentMoE"
+// (hs-black.github.io/posts/kimi-k3), section 2.3 (y = Sigmoid(W_g x) .
+// RMSNorm(o), here with the gate logits W_g x given as an input and RMSNorm
+// over the d_v channels of one head) and section 2.2 (decay map, used by the
+// pre-pass).
+#include "kda_chunk_prologue.hpp"
+
+namespace kda {
+
+__device__ __forceinline__ float wave_sum64(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// ---- gate: one wave per (b, t, h) row ------------------------------------
+template <typename T, typename TO, int D>
+__global__ __launch_bounds__(256) void kda_gate_kernel(const GateParams p) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t rid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t rows = (int64_t)p.B * p.nt * p.H;
+  if (rid >= rows) return;
+  const int h = (int)(rid % p.H);
+  const int64_t bt = rid / p.H;
+  const int t = (int)(bt % p.nt), b = (int)(bt / p.nt);
+  const float* o = p.o32 + (int64_t)b * p.o32_b_stride + ((int64_t)t * p.H + h) * D;
+  const int64_t grow = (((int64_t)b * p.T + p.t0 + t) * p.H + h) * D;
+  float x[EPL];
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    x[e] = o[lane * EPL + e];
+    ss += x[e] * x[e];
+  }
+  ss = wave_sum64(ss);
+  const float rr = 1.0f / sqrtf(ss / D + p.rms_eps);
+  const T* g = static_cast<const T*>(p.gate) + grow;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int c = lane * EPL + e;
+    const float w = (p.rms_w != nullptr) ? p.rms_w[h * D + c] : 1.0f;
+    const float yv = sigmoid_fast(Elem<T>::to_f32(g[c])) * x[e] * rr * w;
+    static_cast<TO*>(p.y)[grow + c] = Elem<TO>::from_f32(yv);
+    if (p.o != nullptr) static_cast<TO*>(p.o)[grow + c] = Elem<TO>::from_f32(x[e]);
+  }
+}
+
+hipError_t launch_gate(const GateParams& p, int D, int in_f32, int out_f32, hipStream_t s) {
+  const int64_t rows = (int64_t)p.B * p.nt * p.H;
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+#define KDA_GATE(TI, TO, DD) hipLaunchKernelGGL((kda_gate_kernel<TI, TO, DD>), grid, block, 0, s, p)
+  if (in_f32) {
+    if (out_f32) { if (D == 64) KDA_GATE(float, float, 64); else KDA_GATE(float, float, 128); }
+    else { if (D == 64) KDA_GATE(float, uint16_t, 64); else KDA_GATE(float, uint16_t, 128); }
+  } else {
+    if (out_f32) { if (D == 64) KDA_GATE(uint16_t, float, 64); else KDA_GATE(uint16_t, float, 128); }
+    else { if (D == 64) KDA_GATE(uint16_t, uint16_t, 64); else KDA_GATE(uint16_t, uint16_t, 128); }
+  }
+#undef KDA_GATE
+  return hipGetLastError();
+}
+
+// ---- state import / export / zero: one workgroup per (n, h) ----------------
+template <int D>
+__global__ __launch_bounds__(256) void kda_state_io_kernel(const StateIoParams p) {
+  __shared__ float tile[32][33];
+  const int h = blockIdx.x, n = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t slot = (p.slot != nullptr) ? (int64_t)p.slot[n] : (int64_t)n;
+  float* pool = p.pool + (slot * p.H + h) * D * D;
+  float* user = (p.user != nullptr) ? p.user + ((int64_t)n * p.H + h) * D * D : nullptr;
+  if (p.op == 0) {
+    for (int i = tid; i < D * D; i += 256) pool[i] = 0.f;
+    return;
+  }
+  if (!p.transpose) {
+    if (p.op == 1)
+      for (int i = tid; i < D * D; i += 256) pool[i] = user[i];
+    else
+      for (int i = tid; i < D * D; i += 256) user[i] = pool[i];
+    return;
+  }
+  // transposed user layout [d_v][d_k]: 32x32 tiles through LDS
+  const float* src = (p.op == 1) ? user : pool;
+  float* dst = (p.op == 1) ? pool : user;
+  const int tx = tid & 31, ty = tid >> 5;  // 32 x 8
+  for (int bi = 0; bi < D; bi += 32)
+    for (int bj = 0; bj < D; bj += 32) {
+      for (int r = ty; r < 32; r += 8) tile[r][tx] = src[(bi + r) * D + bj + tx];
+      __syncthreads();
+      for (int r = ty; r < 32; r += 8) dst[(bj + r) * D + bi + tx] = tile[tx][r];
+      __syncthreads();
+    }
+}
+
+hipError_t launch_state_io(const StateIoParams& p, int D, hipStream_t s) {
+  const dim3 grid(p.H, p.n), block(256);
+  if (D == 64) hipLaunchKernelGGL((kda_state_io_kernel<64>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((kda_state_io_kernel<128>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void kda_copy_state_kernel(const float* src, float* dst, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = (src != nullptr) ? src[i] : 0.f;
+}
+
+hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kda_copy_state_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+// ---- pre-pass diagnostic: chunk-local cumulative log-decay and norms -------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void kda_prepass_kernel(const PrepassParams p) {
+  __shared__ ChunkSmem<T, D> sm;
+  constexpr int GP = ChunkSmem<T, D>::GP;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tok0 = c * kChunk;
+  const int nvalid = min(kChunk, p.T - tok0);
+  chunk_prologue<T, D>(sm, static_cast<const T*>(p.q), static_cast<const T*>(p.k),
+                       static_cast<const T*>(p.z), nullptr, p.A[h], b, h, p.T, p.H,
+                       tok0, nvalid, p.g_min, p.l2_eps, p.l2norm);
+  for (int idx = threadIdx.x; idx < nvalid * D; idx += 256) {
+    const int r = idx / D, ch = idx % D;
+    p.G[(((int64_t)b * p.T + tok0 + r) * p.H + h) * D + ch] = sm.u0.G[r * GP + ch];
+  }
+  if (threadIdx.x < nvalid) {
+    const int64_t ri = ((int64_t)b * p.T + tok0 + threadIdx.x) * p.H + h;
+    p.rq[ri] = sm.rq[threadIdx.x];
+    p.rk[ri] = sm.rk[threadIdx.x];
+  }
+}
+
+hipError_t launch_prepass(const PrepassParams& p, int D, int in_f32, hipStream_t s) {
+  const dim3 grid((p.T + kChunk - 1) / kChunk, p.H, p.B), block(256);
+  if (in_f32) {
+    if (D == 64) hipLaunchKernelGGL((kda_prepass_kernel<float, 64>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((kda_prepass_kernel<float, 128>), grid, block, 0, s, p);
+  } else {
+    if (D == 64) hipLaunchKernelGGL((kda_prepass_kernel<uint16_t, 64>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((kda_prepass_kernel<uint16_t, 128>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kda

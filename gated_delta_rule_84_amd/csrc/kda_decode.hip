@@ -1,0 +1,140 @@
+// Single-token KDA step for many sequences (decode).  One workgroup of 256
+// threads per (sequence, head) streams that head's fp32 state through
+// registers once: read, update, write back.
+//
+// Source: "Kimi K3: KDA, Attention Residuals and Stable LatentMoE"
+// (hs-black.github.io/posts/kimi-k3), section 2.1 (one step of
+// S_t = (I - beta k k^T) Diag(alpha) S_{t-1} + beta k v^T, o = S^T q, applied as
+// S <- Diag(alpha) S; S <- S + k (beta (v - S^T k))^T), section 2.2 (alpha from
+// the bounded decay map) and section 2.3 (gate Sigmoid(G) . RMSNorm(o)).
+#include "kda_common.hpp"
+#include "kda_params.hpp"
+
+namespace kda {
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void kda_decode_kernel(const DecodeParams p) {
+  constexpr int RG = 256 / D;     // row groups
+  constexpr int RPT = D / RG;     // rows per thread
+  __shared__ float ks[D], qs[D], as[D];
+  __shared__ float part[RG][D];
+  __shared__ float wred[4][2];
+
+  const int h = blockIdx.x, n = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = tid % D, rg = tid / D;
+  const int64_t row = (int64_t)n * p.H + h;  // [n, H] token row
+  const T* q = static_cast<const T*>(p.q) + row * D;
+  const T* k = static_cast<const T*>(p.k) + row * D;
+  const T* z = static_cast<const T*>(p.z) + row * D;
+  const T* v = static_cast<const T*>(p.v) + row * D;
+
+  // key / query rows, their squared norms and the decay
+  float kx = 0.f, qx = 0.f;
+  if (tid < D) {
+    kx = Elem<T>::to_f32(k[tid]);
+    qx = Elem<T>::to_f32(q[tid]);
+    const float eA = exp2f(p.A[h] * kLog2e);
+    const float g = p.g_min * sigmoid_fast(eA * Elem<T>::to_f32(z[tid]));
+    as[tid] = exp2f(g * kLog2e);
+  }
+  {
+    const float sk = wave_sum(kx * kx), sq = wave_sum(qx * qx);
+    if (lane == 0) {
+      wred[wave][0] = sk;
+      wred[wave][1] = sq;
+    }
+  }
+  __syncthreads();
+  if (tid < D) {
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) {
+      sk += wred[w][0];
+      sq += wred[w][1];
+    }
+    const float rk = p.l2norm ? 1.0f / sqrtf(sk + p.l2_eps) : 1.0f;
+    const float rq = p.l2norm ? 1.0f / sqrtf(sq + p.l2_eps) : 1.0f;
+    ks[tid] = kx * rk;
+    qs[tid] = qx * rq * p.q_scale;
+  }
+  __syncthreads();
+
+  const int64_t slot = (p.slot != nullptr) ? (int64_t)p.slot[n] : (int64_t)n;
+  float* S = p.S_pool + (slot * p.H + h) * D * D;
+  float s[RPT];
+  float w = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rg * RPT + i;
+    s[i] = S[r * D + col] * as[r];
+    w += s[i] * ks[r];
+  }
+  part[rg][col] = w;
+  __syncthreads();
+  float wt = 0.f;
+#pragma unroll
+  for (int j = 0; j < RG; ++j) wt += part[j][col];
+  const float bt = Elem<T>::to_f32(static_cast<const T*>(p.beta)[row]);
+  const float u = bt * (Elem<T>::to_f32(v[col]) - wt);
+  float ov = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rg * RPT + i;
+    s[i] += ks[r] * u;
+    ov += s[i] * qs[r];
+    S[r * D + col] = s[i];
+  }
+  __syncthreads();  // everyone has read part[] for w
+  part[rg][col] = ov;
+  __syncthreads();
+  float o = 0.f;
+#pragma unroll
+  for (int j = 0; j < RG; ++j) o += part[j][col];
+
+  if (p.o != nullptr && rg == 0) {
+    if (p.out_f32)
+      static_cast<float*>(p.o)[row * D + col] = o;
+    else
+      static_cast<uint16_t*>(p.o)[row * D + col] = f32_to_bf16(o);
+  }
+  if (p.y != nullptr) {
+    const float sq = wave_sum(rg == 0 ? o * o : 0.f);
+    __syncthreads();
+    if (lane == 0) wred[wave][0] = sq;
+    __syncthreads();
+    float ms = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) ms += wred[wv][0];
+    if (rg == 0) {
+      const float rr = 1.0f / sqrtf(ms / D + p.rms_eps);
+      const float gl = Elem<T>::to_f32(static_cast<const T*>(p.gate)[row * D + col]);
+      const float wv = (p.rms_w != nullptr) ? p.rms_w[h * D + col] : 1.0f;
+      const float yv = sigmoid_fast(gl) * o * rr * wv;
+      if (p.out_f32)
+        static_cast<float*>(p.y)[row * D + col] = yv;
+      else
+        static_cast<uint16_t*>(p.y)[row * D + col] = f32_to_bf16(yv);
+    }
+  }
+}
+
+hipError_t launch_decode(const DecodeParams& p, int D, int in_f32, hipStream_t s) {
+  const dim3 grid(p.H, p.n), block(256);
+  if (in_f32) {
+    if (D == 64) hipLaunchKernelGGL((kda_decode_kernel<float, 64>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((kda_decode_kernel<float, 128>), grid, block, 0, s, p);
+  } else {
+    if (D == 64) hipLaunchKernelGGL((kda_decode_kernel<uint16_t, 64>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((kda_decode_kernel<uint16_t, 128>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kda

@@ -1,0 +1,124 @@
+// Kernel parameter blocks and host launchers shared between the HIP kernel
+// files and the C-ABI layer.  Internal; not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kChunk = 64;   // tokens per chunk
+constexpr int kSub = 16;     // tokens per sub-tile
+
+// Per-chunk intermediates written by the intra-chunk kernel and read by the
+// state scan.  One record per (b, h, chunk of the current segment); W is the
+// operand element type (bf16 bits or fp32).  Layout of one record, D = head dim:
+//   qg  [64][D]   (q^ * Gamma), columns in slot order per 32-group
+//   kg  [64][D]   (k^ * Gamma), columns in slot order
+//   kdt [D][64]   (k^ * Gamma_last / Gamma)^T, token columns in slot order
+//   tb  [64][64]  (I + StrictTril(Diag(beta) A_kk))^{-1} Diag(beta), slot order
+//   aqh [64][64]  Tril(A_qk) high part (bf16) or value (fp32), slot order
+//   aql [64][64]  Tril(A_qk) low part (bf16 path only)
+//   gam [D]       Gamma_last (fp32)
+struct ChunkWs {
+  void* qg;
+  void* kg;
+  void* kdt;
+  void* tb;
+  void* aqh;
+  void* aql;
+  float* gam;
+  int64_t rec_elems_qk;   // elements per record of qg / kg / kdt (64*D)
+  int64_t rec_elems_t;    // elements per record of tb / aqh / aql (64*64)
+};
+
+struct IntraParams {
+  const void* q;
+  const void* k;
+  const void* z;
+  const void* beta;
+  const float* A;
+  int B, T, H;
+  int t0;          // first token of the segment
+  int nc;          // chunks in the segment
+  float g_min, q_scale, l2_eps;
+  int l2norm;
+  ChunkWs ws;
+};
+
+struct ScanParams {
+  const void* v;
+  const float* S_in;    // [B, H, D, D] or nullptr (zero state)
+  float* S_out;         // [B, H, D, D] (may equal S_in)
+  void* o;              // [B, T, H, D] output, element type by o_f32
+  int o_f32;            // 1: o is fp32, 0: bf16
+  int64_t o_tok_stride; // elements between consecutive tokens of o (H*D)
+  int64_t o_b_stride;   // elements between batches of o
+  int o_t0;             // token offset subtracted before indexing o
+  int B, T, H;
+  int t0, nc;
+  ChunkWs ws;
+};
+
+struct GateParams {
+  const float* o32;     // fp32, segment-local tokens: o32[b * o32_b_stride + (t*H + h)*D]
+  int64_t o32_b_stride;
+  const void* gate;     // [B, T, H, D] input dtype
+  const float* rms_w;   // [H, D] or nullptr
+  void* y;              // [B, T, H, D] out dtype
+  void* o;              // [B, T, H, D] out dtype or nullptr
+  int B, T, H, t0, nt;
+  float rms_eps;
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* beta;
+  const void* z;
+  const float* A;
+  float* S_pool;          // [*, H, D, D]
+  const int32_t* slot;    // [n] or nullptr
+  const void* gate;       // [n, H, D] or nullptr
+  const float* rms_w;     // [H, D] or nullptr
+  void* o;                // [n, H, D] or nullptr
+  void* y;                // [n, H, D] or nullptr
+  int n, H;
+  float g_min, q_scale, l2_eps, rms_eps;
+  int l2norm;
+  int out_f32;
+};
+
+struct StateIoParams {
+  int op;          // 0 zero, 1 import (user -> pool), 2 export (pool -> user)
+  int transpose;   // user layout [D_v][D_k] when 1
+  int n, H;
+  float* pool;
+  const int32_t* slot;
+  float* user;
+};
+
+struct PrepassParams {
+  const void* q;
+  const void* k;
+  const void* z;
+  const float* A;
+  int B, T, H;
+  float g_min, l2_eps;
+  int l2norm;
+  float* G;    // [B, T, H, D] chunk-local inclusive cumulative log-decay
+  float* rq;   // [B, T, H]
+  float* rk;   // [B, T, H]
+};
+
+// Host launchers (one per kernel family).  in_f32: inputs are fp32 (else bf16).
+hipError_t launch_intra(const IntraParams& p, int D, int in_f32, hipStream_t s);
+hipError_t launch_scan(const ScanParams& p, int D, int in_f32, hipStream_t s);
+hipError_t launch_gate(const GateParams& p, int D, int in_f32, int out_f32, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int D, int in_f32, hipStream_t s);
+hipError_t launch_state_io(const StateIoParams& p, int D, hipStream_t s);
+hipError_t launch_prepass(const PrepassParams& p, int D, int in_f32, hipStream_t s);
+hipError_t launch_copy_state(const float* src, float* dst, int64_t n_floats, hipStream_t s);
+
+}  // namespace kda

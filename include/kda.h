@@ -1,0 +1,172 @@
+/*
+ * kda.h - C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) library.
+ *
+ * KDA is the per-head gated delta rule of "Kimi K3: KDA, Attention Residuals
+ * and Stable LatentMoE" (hs-black.github.io/posts/kimi-k3):
+ *   section 2.1  S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *                o_t = S_t^T q_t, q and k L2-normalised, computed in chunked form;
+ *   section 2.2  alpha_t = e^{g_t},  g_t = g_min * Sigmoid(e^{A_h} z_t),  g_min = -5;
+ *   section 2.3  y_t = Sigmoid(G_t) . RMSNorm(o_t)   (G_t = W_g x_t supplied by the caller;
+ *                the W_g and W_o projections themselves are not part of this library).
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are dense, row-major, caller-owned DEVICE pointers (HIP device
+ *    memory).  The library never allocates or frees device memory and keeps no
+ *    global state; it is safe to call from several host threads.
+ *  - Layouts: q, k, z: [B, T, H, d_k]; v, o, gate, y: [B, T, H, d_v];
+ *    beta: [B, T, H]; A: [H] fp32; states S0, S_T, S_pool: [.., H, d_k, d_v]
+ *    fp32 with the key channel as row index (o = S^T q).
+ *  - Element types: q, k, v, beta, z and gate are all `in_dtype`; o and y are
+ *    `out_dtype`; A, states and rms_w are fp32.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on it and returns without waiting for the GPU.
+ *  - Errors: arguments are validated on the host before anything is enqueued.
+ *    On any error nothing is enqueued and no output is touched.  A failed
+ *    kernel launch returns KDA_ERR_HIP.  No C++ exception crosses the ABI.
+ *  - Pointers to q, k, v, z, gate, o, y and to the workspace must be 16-byte
+ *    aligned; beta 2-byte (bf16) or 4-byte (fp32); A, rms_w, S0, S_T, S_pool
+ *    4-byte.
+ *  - Supported shapes: d_k == d_v in {64, 128}, chunk == 64, B, H >= 1, T >= 0,
+ *    any T (a short last chunk is handled), -5.5 <= g_min < 0 (so a 16-token
+ *    sub-tile's cumulative log-decay stays above -88, keeping its reciprocal
+ *    within bf16 / fp32 range, section 2.2).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL_ARG = 1,     /* a required pointer is NULL                         */
+  KDA_ERR_BAD_SHAPE = 2,    /* a size is negative / zero where it must not be      */
+  KDA_ERR_BAD_DTYPE = 3,    /* unknown dtype enum                                  */
+  KDA_ERR_MISALIGNED = 4,   /* a pointer breaks the alignment rules above          */
+  KDA_ERR_UNSUPPORTED = 5,  /* valid request outside what the kernels implement    */
+  KDA_ERR_WORKSPACE = 6,    /* workspace missing or smaller than one chunk needs   */
+  KDA_ERR_HIP = 7           /* a kernel launch failed (HIP error read and cleared)  */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef enum { KDA_STATE_ZERO = 0, KDA_STATE_IMPORT = 1, KDA_STATE_EXPORT = 2 } kda_state_op;
+
+typedef enum {
+  KDA_LAYOUT_KV = 0, /* user state is [d_k][d_v], same as the pool               */
+  KDA_LAYOUT_VK = 1  /* user state is [d_v][d_k] (transposed)                      */
+} kda_state_layout;
+
+/* Problem descriptor.  kda_desc_init fills the defaults shown. */
+typedef struct {
+  int32_t B, T, H;       /* batch, tokens per sequence, heads                      */
+  int32_t d_k, d_v;      /* head dims (equal; 64 or 128)                           */
+  int32_t chunk;         /* tokens per chunk: 64                                   */
+  float g_min;           /* lower bound of the log-decay: -5                       */
+  float q_scale;         /* multiplier of q after L2Norm: 1 (the pages show none)  */
+  float l2_eps;          /* q / sqrt(|q|^2 + l2_eps): 1e-6                          */
+  float rms_eps;         /* o / sqrt(mean(o^2) + rms_eps): 1e-6                     */
+  int32_t qk_l2norm;     /* 1: L2-normalise q and k inside the kernel               */
+  kda_dtype in_dtype;    /* q, k, v, beta, z, gate                                 */
+  kda_dtype out_dtype;   /* o, y                                                   */
+} kda_desc;
+
+/* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
+int kda_abi_version(void);
+
+/* Static description of a status code. */
+const char* kda_status_str(kda_status s);
+
+/* Fill *d with the defaults above for the given sizes and dtypes. */
+kda_status kda_desc_init(kda_desc* d, int32_t B, int32_t T, int32_t H, int32_t head_dim, kda_dtype in_dtype,
+                         kda_dtype out_dtype);
+
+/* Workspace bytes that let kda_chunk_fwd run the whole sequence (at most
+ * 65536 tokens per internal segment) in one pass; 0 if *d is invalid.  A
+ * smaller workspace also works as long as it holds one chunk: the sequence is
+ * then processed in more, shorter segments. */
+size_t kda_chunk_fwd_workspace_size(const kda_desc* d);
+
+/* Bytes needed for a segment of `segment_tokens` tokens (rounded up to whole
+ * chunks); 0 if *d is invalid. */
+size_t kda_chunk_fwd_workspace_size_for(const kda_desc* d, int32_t segment_tokens);
+
+/*
+ * Chunked KDA forward over whole sequences (prefill / training forward),
+ * section 2.1's chunk form with section 2.2's 16-token dense sub-tiles.
+ *
+ *  q, k, v, beta, z, A   inputs (see layouts above); beta in (0, 1).
+ *  S0     [B, H, d_k, d_v] fp32 initial state, or NULL for zero.
+ *  gate   [B, T, H, d_v] gate logits W_g x, or NULL (no gate).
+ *  rms_w  [H, d_v] fp32 RMSNorm weight, or NULL (weight 1).
+ *  o      [B, T, H, d_v] output o_t = S_t^T q_t, or NULL.
+ *  y      [B, T, H, d_v] gated output (requires gate), or NULL.
+ *  S_T    [B, H, d_k, d_v] fp32 final state, or NULL.  May alias S0.
+ *  ws     device workspace of ws_bytes bytes (see the size queries), owned by
+ *         the caller; its contents are scratch.  May be NULL when T == 0.
+ * At least one of o, y, S_T must be non-NULL.  When d->T == 0 nothing is read:
+ * S_T receives S0 (or zeros) and q, k, v, beta, z, A and ws may be NULL.
+ */
+kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
+                         const void* z, const float* A, const float* S0, const void* gate, const float* rms_w,
+                         void* o, void* y, float* S_T, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kda_chunk_fwd with per-kernel timing: identical work and results, and in
+ * addition, for the i-th kernel launch of the call (launch order per segment:
+ * intra-chunk, state scan, then the gate epilogue when y is requested),
+ * hipEventRecord(events[2i]) right before it and hipEventRecord(events[2i+1])
+ * right after it on `stream`, while 2i+1 < n_events.  `events` are caller-owned
+ * hipEvent_t handles.  Used to measure kernel durations on the launch stream.
+ */
+kda_status kda_chunk_fwd_traced(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
+                                const void* z, const float* A, const float* S0, const void* gate,
+                                const float* rms_w, void* o, void* y, float* S_T, void* ws, size_t ws_bytes,
+                                void* stream, void* const* events, int32_t n_events);
+
+/*
+ * One decode step (single token) for d->B sequences: the same recurrence,
+ * section 2.1, applied to one token.  d->T must be 1.  Each sequence n reads
+ * and updates its state in place at S_pool[slot[n]] (slot == NULL: slot n):
+ *  q, k, v, z, gate, o, y  are [B, 1, H, d], beta is [B, 1, H];
+ *  S_pool  [n_slots, H, d_k, d_v] fp32 state pool, updated in place;
+ *  slot    [B] int32 device array of distinct pool rows, or NULL;
+ *  o, y    outputs as in kda_chunk_fwd (y requires gate).
+ * Slots must be distinct within one call (two sequences writing one slot race).
+ */
+kda_status kda_recurrent_step(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
+                              const void* z, const float* A, float* S_pool, const int32_t* slot,
+                              const void* gate, const float* rms_w, void* o, void* y, void* stream);
+
+/*
+ * State hand-off between a state pool and caller buffers (prefill -> decode,
+ * prefix-cache snapshots): ZERO clears pool rows, IMPORT copies user -> pool,
+ * EXPORT copies pool -> user.
+ *  n      number of states moved; slot [n] int32 device array or NULL (0..n-1);
+ *  pool   [n_slots, H, d_k, d_v] fp32;  user [n, H, ...] fp32 in `layout`
+ *         (NULL for ZERO).  d_k == d_v in {64, 128}.
+ */
+kda_status kda_state_io(kda_state_op op, int32_t n, int32_t H, int32_t d_k, int32_t d_v, kda_state_layout layout,
+                        float* pool, const int32_t* slot, float* user, void* stream);
+
+/*
+ * Pre-pass diagnostic (the first step of kda_chunk_fwd, exposed for tests):
+ *  G      [B, T, H, d_k] fp32, chunk-local inclusive cumulative sum of
+ *         g = g_min * Sigmoid(e^{A_h} z) over each 64-token chunk (section 2.2);
+ *  rq, rk [B, T, H] fp32 inverse L2 norms 1 / sqrt(|x|^2 + l2_eps) (1 when
+ *         d->qk_l2norm == 0).
+ */
+kda_status kda_prepass(const kda_desc* d, const void* q, const void* k, const void* z, const float* A, float* G,
+                       float* rq, float* rk, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

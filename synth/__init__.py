@@ -71,6 +71,8 @@ def fill(kind: int, dtype: int, seed: int, stream: int, shape, block=None,
         out = np.empty((nb, nt, nh, D), dtype=_NP[dtype])
     if out.shape != (nb, nt, nh, D) or out.dtype != _NP[dtype]:
         raise ValueError(f"out has shape {out.shape} / {out.dtype}, need {(nb, nt, nh, D)} / {_NP[dtype]}")
+    if out.size == 0:
+        return out
     if out.strides[3] != out.itemsize:
         raise ValueError("last axis of out must be contiguous")
     osb, ost, osh = (s // out.itemsize for s in out.strides[:3])
