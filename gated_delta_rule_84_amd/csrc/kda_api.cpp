@@ -56,12 +56,12 @@ kda_status validate_desc(const kda_desc* d) {
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct WsLayout {
-  size_t off_qg, off_kg, off_kdt, off_tb, off_aqh, off_aql, off_gam, off_o32, off_carry, total;
+  size_t off_rec, rec_bytes, off_o32, off_carry, total;
 };
 
 // Workspace for a segment of seg_nc chunks.
 WsLayout layout_for(const kda_desc* d, int64_t seg_nc, bool gated) {
-  const size_t es = elem_size(d->in_dtype);
+  const int es = (int)elem_size(d->in_dtype);
   const int64_t D = d->d_k;
   const int64_t R = (int64_t)d->B * d->H * seg_nc;
   WsLayout L{};
@@ -71,13 +71,8 @@ WsLayout layout_for(const kda_desc* d, int64_t seg_nc, bool gated) {
     o = align256(o + bytes);
     return at;
   };
-  L.off_qg = take(R * kChunk * D * es);
-  L.off_kg = take(R * kChunk * D * es);
-  L.off_kdt = take(R * kChunk * D * es);
-  L.off_tb = take(R * kChunk * kChunk * es);
-  L.off_aqh = take(R * kChunk * kChunk * es);
-  L.off_aql = (d->in_dtype == KDA_BF16) ? take(R * kChunk * kChunk * es) : 0;
-  L.off_gam = take(R * D * 4);
+  L.rec_bytes = (size_t)kda::rec_layout(es, (int)D).bytes;
+  L.off_rec = take(R * L.rec_bytes);
   L.off_o32 = gated ? take((size_t)d->B * seg_nc * kChunk * d->H * D * 4) : 0;
   L.off_carry = take((size_t)d->B * d->H * D * D * 4);
   L.total = o;
@@ -204,15 +199,8 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   const WsLayout L = layout_for(d, seg_nc, gated);
   char* base = static_cast<char*>(ws);
   kda::ChunkWs cw{};
-  cw.qg = base + L.off_qg;
-  cw.kg = base + L.off_kg;
-  cw.kdt = base + L.off_kdt;
-  cw.tb = base + L.off_tb;
-  cw.aqh = base + L.off_aqh;
-  cw.aql = (d->in_dtype == KDA_BF16) ? base + L.off_aql : nullptr;
-  cw.gam = reinterpret_cast<float*>(base + L.off_gam);
-  cw.rec_elems_qk = (int64_t)kChunk * D;
-  cw.rec_elems_t = (int64_t)kChunk * kChunk;
+  cw.base = base + L.off_rec;
+  cw.rec_bytes = (int64_t)L.rec_bytes;
   float* o32 = gated ? reinterpret_cast<float*>(base + L.off_o32) : nullptr;
   float* carry = reinterpret_cast<float*>(base + L.off_carry);
   float* S_run = S_T ? S_T : carry;

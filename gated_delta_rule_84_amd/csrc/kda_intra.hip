@@ -77,12 +77,15 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) 
                        static_cast<const T*>(p.z), static_cast<const T*>(p.beta), p.A[h], b, h, p.T,
                        p.H, tok0, nvalid, p.g_min, p.l2_eps, p.l2norm);
 
-  T* qg = static_cast<T*>(p.ws.qg) + rec * p.ws.rec_elems_qk;
-  T* kg = static_cast<T*>(p.ws.kg) + rec * p.ws.rec_elems_qk;
-  T* kdt = static_cast<T*>(p.ws.kdt) + rec * p.ws.rec_elems_qk;
-  T* tb = static_cast<T*>(p.ws.tb) + rec * p.ws.rec_elems_t;
-  T* aqh = static_cast<T*>(p.ws.aqh) + rec * p.ws.rec_elems_t;
-  T* aql = (p.ws.aql != nullptr) ? static_cast<T*>(p.ws.aql) + rec * p.ws.rec_elems_t : nullptr;
+  constexpr RecLayout RL = rec_layout((int)sizeof(T), D);
+  char* recp = p.ws.base + rec * p.ws.rec_bytes;
+  T* qg = reinterpret_cast<T*>(recp + RL.qg);
+  T* kg = reinterpret_cast<T*>(recp + RL.kg);
+  T* kdt = reinterpret_cast<T*>(recp + RL.kdt);
+  T* tb = reinterpret_cast<T*>(recp + RL.tb);
+  T* aqh = reinterpret_cast<T*>(recp + RL.aqh);
+  T* aql = reinterpret_cast<T*>(recp + RL.aql);
+  float* gam = reinterpret_cast<float*>(recp + RL.gam);
   const float* G = sm.u0.G;
 
   // ---- factor tensors for the state scan (columns in slot order) ----------
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) 
     store8<T>(kg + r * D + 8 * pg, xk);
   }
   for (int idx = tid; idx < D * 8; idx += 256) {
-    const int ch = idx % D, pg = idx / D;
+    const int ch = idx >> 3, pg = idx & 7;  // 8 neighbouring threads fill one kdt row
     const float glast = G[(kChunk - 1) * GP + ch];
     float x[8];
 #pragma unroll
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) 
     }
     store8<T>(kdt + ch * kChunk + 8 * pg, x);
   }
-  if (tid < D) p.ws.gam[rec * D + tid] = exp2f(G[(kChunk - 1) * GP + tid] * kLog2e);
+  if (tid < D) gam[tid] = exp2f(G[(kChunk - 1) * GP + tid] * kLog2e);
 
   // ---- sub-tile products A_kk(i, j), A_qk(i, j), j <= i; wave i = row tile --
   const int n = lane & 15, g4 = lane >> 4;
@@ -158,7 +161,9 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) 
   }
   __syncthreads();  // q, k, G no longer read: their LDS becomes L and Tm
 
-  // L = Diag(beta) StrictTril(A_kk) into LDS; Tril(A_qk) to the workspace.
+  // L = Diag(beta) StrictTril(A_kk) into LDS; Tril(A_qk) staged in LDS (slot
+  // order) for coalesced stores of its hi / lo parts.
+  float* Aq = sm.u0.Tm;
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) {
 #pragma unroll
@@ -168,11 +173,21 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) 
       const float vkk = (jt <= ti && s < rr) ? sm.beta[rr] * akk[jt][ii] : 0.0f;
       const float vqk = (jt <= ti && s <= rr) ? aqk[jt][ii] : 0.0f;
       sm.u1.L[rr * LP + s] = vkk;
-      const int pos = rr * kChunk + slot_pos64(s);
-      const T hi = Elem<T>::from_f32(vqk);
-      aqh[pos] = hi;
-      if (aql != nullptr) aql[pos] = Elem<T>::from_f32(vqk - Elem<T>::to_f32(hi));
+      Aq[rr * LP + slot_pos64(s)] = vqk;
     }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < kChunk * 8; idx += 256) {
+    const int rr = idx >> 3, pg = idx & 7;
+    float x[8], lo[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = Aq[rr * LP + 8 * pg + j];
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lo[j] = x[j] - bf16_to_f32(f32_to_bf16(x[j]));
+      store8<T>(aql + rr * kChunk + 8 * pg, lo);
+    }
+    store8<T>(aqh + rr * kChunk + 8 * pg, x);
   }
   __syncthreads();
 

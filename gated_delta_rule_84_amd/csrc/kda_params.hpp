@@ -11,25 +11,35 @@ constexpr int kChunk = 64;   // tokens per chunk
 constexpr int kSub = 16;     // tokens per sub-tile
 
 // Per-chunk intermediates written by the intra-chunk kernel and read by the
-// state scan.  One record per (b, h, chunk of the current segment); W is the
-// operand element type (bf16 bits or fp32).  Layout of one record, D = head dim:
-//   qg  [64][D]   (q^ * Gamma), columns in slot order per 32-group
-//   kg  [64][D]   (k^ * Gamma), columns in slot order
-//   kdt [D][64]   (k^ * Gamma_last / Gamma)^T, token columns in slot order
-//   tb  [64][64]  (I + StrictTril(Diag(beta) A_kk))^{-1} Diag(beta), slot order
-//   aqh [64][64]  Tril(A_qk) high part (bf16) or value (fp32), slot order
-//   aql [64][64]  Tril(A_qk) low part (bf16 path only)
-//   gam [D]       Gamma_last (fp32)
+// state scan: one contiguous record per (b, h, chunk of the current segment),
+// record index ((b * H + h) * nc + c).  Element type T = the input type (bf16
+// bits or fp32).  Byte layout of one record (D = head dim, ES = sizeof(T)):
+//   qg  [64][D]   q^ . Gamma, columns in slot order per 32-group
+//   kg  [64][D]   k^ . Gamma, columns in slot order
+//   kdt [D][64]   (k^ . Gamma_last / Gamma)^T, token columns in slot order
+//   tb  [64][64]  (I + Diag(beta) StrictTril(A_kk))^{-1} Diag(beta), slot order
+//   aqh [64][64]  Tril(A_qk): high bf16 part (bf16 path) or value (fp32 path)
+//   aql [64][64]  Tril(A_qk) - aqh (bf16 path only)
+//   gam [D]       Gamma_last, fp32
+// padded to a multiple of 256 bytes.
+struct RecLayout {
+  int qg, kg, kdt, tb, aqh, aql, gam, bytes;
+};
+__host__ __device__ constexpr int round256(int x) { return (x + 255) & ~255; }
+__host__ __device__ constexpr RecLayout rec_layout(int es, int D) {
+  return RecLayout{0,
+                   64 * D * es,
+                   2 * 64 * D * es,
+                   3 * 64 * D * es,
+                   3 * 64 * D * es + 64 * 64 * es,
+                   3 * 64 * D * es + 2 * 64 * 64 * es,
+                   3 * 64 * D * es + (es == 2 ? 3 : 2) * 64 * 64 * es,
+                   round256(3 * 64 * D * es + (es == 2 ? 3 : 2) * 64 * 64 * es + 4 * D)};
+}
+
 struct ChunkWs {
-  void* qg;
-  void* kg;
-  void* kdt;
-  void* tb;
-  void* aqh;
-  void* aql;
-  float* gam;
-  int64_t rec_elems_qk;   // elements per record of qg / kg / kdt (64*D)
-  int64_t rec_elems_t;    // elements per record of tb / aqh / aql (64*64)
+  char* base;       // record 0
+  int64_t rec_bytes;
 };
 
 struct IntraParams {

@@ -1,7 +1,11 @@
-// Inter-chunk state scan.  Each wave owns 16 value columns of one head's
-// state S (d_k x 16, fp32, kept in MFMA accumulators for the whole sequence)
-// and walks the chunks in order.  The columns of S evolve independently, so
-// the waves of one head never communicate.
+// Inter-chunk state scan.  A workgroup of 4 waves owns 64 value columns of
+// one head (16 per wave); each wave keeps its d_k x 16 slice of the fp32 state
+// S in MFMA accumulators for the whole sequence and walks the chunks in order.
+// The columns of S evolve independently, so waves never exchange state.  The
+// chunk record written by the intra-chunk kernel, and the workgroup's 64x64
+// slab of V, are copied into LDS by the whole workgroup: the loads for chunk
+// c + 1 are in flight in registers while chunk c is computed from LDS, and
+// are committed to LDS after it.
 //
 // Source: "Kimi K3: KDA, Attention Residuals and Stable LatentMoE"
 // (hs-black.github.io/posts/kimi-k3), section 2.1: per chunk with entry
@@ -27,7 +31,7 @@ struct ScanOps<uint16_t> {
   struct Prec {  // operand of the split product
     bf16x8 hi, lo;
   };
-  static __device__ __forceinline__ V8 ld(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  static __device__ __forceinline__ V8 ld(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
   static __device__ __forceinline__ V8 from_acc(const f32x4& a, const f32x4& b) { return acc_pair_to_bf16(a, b); }
   static __device__ __forceinline__ Prec prec_from_acc(const f32x4& a, const f32x4& b) {
     Prec r;
@@ -35,8 +39,7 @@ struct ScanOps<uint16_t> {
     return r;
   }
   static __device__ __forceinline__ V8 prec_main(const Prec& p) { return p.hi; }
-  static __device__ __forceinline__ f32x4 mma_prec(const uint16_t* ah, const uint16_t* al, const Prec& b,
-                                                   f32x4 acc) {
+  static __device__ __forceinline__ f32x4 mma_prec(const char* ah, const char* al, const Prec& b, f32x4 acc) {
     return mma32_x3(ld(ah), ld(al), b.hi, b.lo, acc);
   }
   // a (bf16) times a split operand: a * hi + a * lo
@@ -53,9 +56,9 @@ struct ScanOps<float> {
   struct Prec {
     f32x8 v;
   };
-  static __device__ __forceinline__ V8 ld(const float* p) {
+  static __device__ __forceinline__ V8 ld(const char* p) {
     const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    const float4 b = *reinterpret_cast<const float4*>(p + 16);
     return f32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   }
   static __device__ __forceinline__ V8 from_acc(const f32x4& a, const f32x4& b) { return acc_pair_to_f32(a, b); }
@@ -63,7 +66,7 @@ struct ScanOps<float> {
     return Prec{acc_pair_to_f32(a, b)};
   }
   static __device__ __forceinline__ V8 prec_main(const Prec& p) { return p.v; }
-  static __device__ __forceinline__ f32x4 mma_prec(const float* ah, const float*, const Prec& b, f32x4 acc) {
+  static __device__ __forceinline__ f32x4 mma_prec(const char* ah, const char*, const Prec& b, f32x4 acc) {
     return mma32(ld(ah), b.v, acc);
   }
   static __device__ __forceinline__ f32x4 mma_split_b(const V8& a, const Prec& b, f32x4 acc) {
@@ -72,43 +75,136 @@ struct ScanOps<float> {
   static __device__ __forceinline__ float in_f32(float x) { return x; }
 };
 
-template <typename T, int D, int WPB>
-__global__ __launch_bounds__(64 * WPB) void kda_scan_kernel(const ScanParams p) {
+// LDS image of one chunk record: the record's arrays with each row padded by
+// 16 bytes so that the 16 rows read by one MFMA operand load hit distinct banks.
+template <typename T, int D>
+struct ScanLds {
+  static constexpr int ES = sizeof(T);
+  static constexpr int PQ = D * ES + 16;    // row pitch of qg / kg
+  static constexpr int PK = 64 * ES + 16;   // row pitch of kdt / tb / aqh / aql
+  static constexpr int QG = 0;
+  static constexpr int KG = QG + 64 * PQ;
+  static constexpr int KDT = KG + 64 * PQ;
+  static constexpr int TB = KDT + D * PK;
+  static constexpr int AQH = TB + 64 * PK;
+  static constexpr int AQL = AQH + 64 * PK;
+  static constexpr int GAM = AQL + (ES == 2 ? 64 * PK : 0);
+  static constexpr int PV = 64 * ES + 16;   // row pitch of the V slab (64 columns)
+  static constexpr int VS = GAM + 4 * D;
+  static constexpr int BYTES = VS + 64 * PV;
+  // the record, in 16-byte units, then the V slab (64 tokens x 64 columns)
+  static constexpr RecLayout RL = rec_layout(ES, D);
+  static constexpr int REC_UNITS = (RL.gam + 4 * D) / 16;
+  static constexpr int V_UNITS = 64 * 64 * ES / 16;
+  static constexpr int PER_THREAD = (REC_UNITS + V_UNITS + 255) / 256;
+};
+
+// Record byte offset of 16-byte unit u -> byte offset in the padded LDS image.
+template <typename T, int D>
+__device__ __forceinline__ int lds_offset_of_unit(int u) {
+  using L = ScanLds<T, D>;
+  constexpr RecLayout RL = L::RL;
+  constexpr int RQ = D * L::ES;   // bytes per row of qg / kg
+  constexpr int RK = 64 * L::ES;  // bytes per row of the 64-wide arrays
+  const int b = u * 16;
+  if (b < RL.kg) return L::QG + (b / RQ) * L::PQ + b % RQ;
+  if (b < RL.kdt) { const int o = b - RL.kg; return L::KG + (o / RQ) * L::PQ + o % RQ; }
+  if (b < RL.tb) { const int o = b - RL.kdt; return L::KDT + (o / RK) * L::PK + o % RK; }
+  if (b < RL.aqh) { const int o = b - RL.tb; return L::TB + (o / RK) * L::PK + o % RK; }
+  if (b < RL.aql) { const int o = b - RL.aqh; return L::AQH + (o / RK) * L::PK + o % RK; }
+  if (b < RL.gam) { const int o = b - RL.aql; return L::AQL + (o / RK) * L::PK + o % RK; }
+  return L::GAM + (b - RL.gam);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 1) void kda_scan_kernel(const ScanParams p) {
   using Ops = ScanOps<T>;
   using V8 = typename Ops::V8;
+  using L = ScanLds<T, D>;
   constexpr int MT = D / 16;  // 16-row tiles of the state (key channels)
   constexpr int KS = D / 32;  // K-steps over key channels
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g4 = lane >> 4;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int v0 = 16 * (blockIdx.x * WPB + wave);
-  const int col = v0 + n;
+  const int col = 64 * blockIdx.x + 16 * wave + n;
   const int64_t bh = (int64_t)b * p.H + h;
+  const bool col_ok = col < D;  // D = 64: one workgroup per head, all columns valid
+
+  // Per-thread 16-byte units (the same for every chunk): record units first,
+  // then V-slab units (VPR units per token row of the slab's 64 columns).
+  constexpr int UNITS = L::REC_UNITS + L::V_UNITS;
+  constexpr int VPR = 64 * L::ES / 16;
+  int lofs[L::PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < L::PER_THREAD; ++i) {
+    const int u = tid + 256 * i;
+    if (u < L::REC_UNITS) {
+      lofs[i] = lds_offset_of_unit<T, D>(u);
+    } else {
+      const int vu = u - L::REC_UNITS;
+      lofs[i] = L::VS + (vu / VPR) * L::PV + (vu % VPR) * 16;
+    }
+  }
+  constexpr int FULL = UNITS / 256;  // slots that are always inside
+  const bool tail_ok = tid + 256 * FULL < UNITS;
+  const T* vin = static_cast<const T*>(p.v);
+  u32x4 stg[L::PER_THREAD];
+  auto fetch = [&](int c) {
+    const char* rec = p.ws.base + (bh * p.nc + c) * p.ws.rec_bytes;
+    const int tok0 = p.t0 + c * kChunk;
+    const int last = min(kChunk, p.T - tok0) - 1;
+#pragma unroll
+    for (int i = 0; i < L::PER_THREAD; ++i) {
+      const int u = tid + 256 * i;
+      if (i < FULL || tail_ok) {
+        const u32x4* src;
+        if (u < L::REC_UNITS) {
+          src = reinterpret_cast<const u32x4*>(rec) + u;
+        } else {  // V rows past the end are clamped (zeroed when used)
+          const int vu = u - L::REC_UNITS;
+          const int r = min(vu / VPR, last);
+          src = reinterpret_cast<const u32x4*>(vin + ((int64_t)(b * (int64_t)p.T + tok0 + r) * p.H + h) * D +
+                                               64 * blockIdx.x + (vu % VPR) * (16 / L::ES));
+        }
+        stg[i] = *src;
+      }
+    }
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int i = 0; i < L::PER_THREAD; ++i)
+      if (i < FULL || tail_ok) *reinterpret_cast<u32x4*>(lds + lofs[i]) = stg[i];
+  };
 
   // state: lane holds S[16 mt + 4 g4 + i][col]
   f32x4 S[MT];
-  if (p.S_in != nullptr) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) S[mt] = zero4();
+  if (p.S_in != nullptr && col_ok) {
     const float* s0 = p.S_in + bh * D * D;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[mt][i] = s0[(16 * mt + 4 * g4 + i) * D + col];
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) S[mt] = zero4();
   }
 
-  const T* vin = static_cast<const T*>(p.v);
+  fetch(0);
+  commit();
+  __syncthreads();
+
   for (int c = 0; c < p.nc; ++c) {
-    const int64_t rec = bh * p.nc + c;
-    const T* qg = static_cast<const T*>(p.ws.qg) + rec * p.ws.rec_elems_qk;
-    const T* kg = static_cast<const T*>(p.ws.kg) + rec * p.ws.rec_elems_qk;
-    const T* kdt = static_cast<const T*>(p.ws.kdt) + rec * p.ws.rec_elems_qk;
-    const T* tb = static_cast<const T*>(p.ws.tb) + rec * p.ws.rec_elems_t;
-    const T* aqh = static_cast<const T*>(p.ws.aqh) + rec * p.ws.rec_elems_t;
-    const T* aql = (p.ws.aql != nullptr) ? static_cast<const T*>(p.ws.aql) + rec * p.ws.rec_elems_t : aqh;
-    const float* gam = p.ws.gam + rec * D;
+    const bool more = c + 1 < p.nc;
+    if (more) fetch(c + 1);
+    const char* base = lds;
+    const char* qg = base + L::QG;
+    const char* kg = base + L::KG;
+    const char* kdt = base + L::KDT;
+    const char* tb = base + L::TB;
+    const char* aqh = base + L::AQH;
+    const char* aql = base + L::AQL;
+    const float* gam = reinterpret_cast<const float*>(base + L::GAM);
     const int tok0 = p.t0 + c * kChunk;
     const int nvalid = min(kChunk, p.T - tok0);
 
@@ -125,21 +221,21 @@ __global__ __launch_bounds__(64 * WPB) void kda_scan_kernel(const ScanParams p) 
       O[mt] = zero4();
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        const int off = (16 * mt + n) * D + 32 * kk + 8 * g4;
+        const int off = (16 * mt + n) * L::PQ + (32 * kk + 8 * g4) * L::ES;
         X[mt] = mma32(Ops::ld(kg + off), Sb[kk], X[mt]);
         O[mt] = mma32(Ops::ld(qg + off), Sb[kk], O[mt]);
       }
     }
 
-    // R = V - X at the accumulator positions (rows past the end read as 0)
+    // R = V - X at the accumulator positions (rows past the end: V = 0)
     f32x4 R[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mt + 4 * g4 + i;
-        float vv = 0.f;
-        if (r < nvalid) vv = Ops::in_f32(vin[((int64_t)(b * (int64_t)p.T + tok0 + r) * p.H + h) * D + col]);
+        const T vraw = *reinterpret_cast<const T*>(base + L::VS + r * L::PV + (16 * wave + n) * L::ES);
+        const float vv = (r < nvalid && col_ok) ? Ops::in_f32(vraw) : 0.f;
         R[mt][i] = vv - X[mt][i];
       }
     typename Ops::Prec Rp[2];
@@ -153,7 +249,7 @@ __global__ __launch_bounds__(64 * WPB) void kda_scan_kernel(const ScanParams p) 
       U[mt] = zero4();
 #pragma unroll
       for (int kk = 0; kk <= (mt >> 1); ++kk)
-        U[mt] = Ops::mma_split_b(Ops::ld(tb + (16 * mt + n) * kChunk + 32 * kk + 8 * g4), Rp[kk], U[mt]);
+        U[mt] = Ops::mma_split_b(Ops::ld(tb + (16 * mt + n) * L::PK + (32 * kk + 8 * g4) * L::ES), Rp[kk], U[mt]);
     }
     typename Ops::Prec Up[2];
     Up[0] = Ops::prec_from_acc(U[0], U[1]);
@@ -164,55 +260,66 @@ __global__ __launch_bounds__(64 * WPB) void kda_scan_kernel(const ScanParams p) 
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int kk = 0; kk <= (mt >> 1); ++kk) {
-        const int off = (16 * mt + n) * kChunk + 32 * kk + 8 * g4;
+        const int off = (16 * mt + n) * L::PK + (32 * kk + 8 * g4) * L::ES;
         O[mt] = Ops::mma_prec(aqh + off, aql + off, Up[kk], O[mt]);
       }
 
-    // outputs
-    if (p.o != nullptr)
+    // outputs (a full chunk stores without per-row guards)
+    if (p.o != nullptr && col_ok) {
+      const int64_t o0 = (int64_t)b * p.o_b_stride + (int64_t)(tok0 - p.o_t0) * p.o_tok_stride + h * D + col;
+      const bool full = nvalid == kChunk;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * mt + 4 * g4 + i;
-        if (r < nvalid) {
-          const int64_t oi = (int64_t)b * p.o_b_stride + (int64_t)(tok0 + r - p.o_t0) * p.o_tok_stride + h * D + col;
-          if (p.o_f32)
-            static_cast<float*>(p.o)[oi] = O[mt][i];
-          else
-            static_cast<uint16_t*>(p.o)[oi] = f32_to_bf16(O[mt][i]);
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * mt + 4 * g4 + i;
+          if (full || r < nvalid) {
+            const int64_t oi = o0 + (int64_t)r * p.o_tok_stride;
+            if (p.o_f32)
+              static_cast<float*>(p.o)[oi] = O[mt][i];
+            else
+              static_cast<uint16_t*>(p.o)[oi] = f32_to_bf16(O[mt][i]);
+          }
         }
-      }
+    }
 
     // S <- Diag(Gamma_last) S + Kd^T U'
     const V8 Ub0 = Ops::prec_main(Up[0]);
     const V8 Ub1 = Ops::prec_main(Up[1]);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
+      const f32x4 gm = *reinterpret_cast<const f32x4*>(gam + 16 * mt + 4 * g4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S[mt][i] *= gam[16 * mt + 4 * g4 + i];
-      const int off = (16 * mt + n) * kChunk + 8 * g4;
+      for (int i = 0; i < 4; ++i) S[mt][i] *= gm[i];
+      const int off = (16 * mt + n) * L::PK + 8 * g4 * L::ES;
       S[mt] = mma32(Ops::ld(kdt + off), Ub0, S[mt]);
-      S[mt] = mma32(Ops::ld(kdt + off + 32), Ub1, S[mt]);
+      S[mt] = mma32(Ops::ld(kdt + off + 32 * L::ES), Ub1, S[mt]);
+    }
+
+    if (more) {
+      __syncthreads();  // every wave is done reading chunk c from LDS
+      commit();
+      __syncthreads();
     }
   }
 
-  float* so = p.S_out + bh * D * D;
+  if (col_ok) {
+    float* so = p.S_out + bh * D * D;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) so[(16 * mt + 4 * g4 + i) * D + col] = S[mt][i];
+      for (int i = 0; i < 4; ++i) so[(16 * mt + 4 * g4 + i) * D + col] = S[mt][i];
+  }
 }
 
 hipError_t launch_scan(const ScanParams& p, int D, int in_f32, hipStream_t s) {
-  constexpr int WPB = 2;
-  const dim3 grid(D / (16 * WPB), p.H, p.B), block(64 * WPB);
+  const dim3 grid((D + 63) / 64, p.H, p.B), block(256);
   if (in_f32) {
-    if (D == 64) hipLaunchKernelGGL((kda_scan_kernel<float, 64, WPB>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((kda_scan_kernel<float, 128, WPB>), grid, block, 0, s, p);
+    if (D == 64) hipLaunchKernelGGL((kda_scan_kernel<float, 64>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((kda_scan_kernel<float, 128>), grid, block, 0, s, p);
   } else {
-    if (D == 64) hipLaunchKernelGGL((kda_scan_kernel<uint16_t, 64, WPB>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((kda_scan_kernel<uint16_t, 128, WPB>), grid, block, 0, s, p);
+    if (D == 64) hipLaunchKernelGGL((kda_scan_kernel<uint16_t, 64>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((kda_scan_kernel<uint16_t, 128>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
