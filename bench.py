@@ -8,8 +8,7 @@ Per-kernel durations come from HIP events recorded by the library around each
 of its launches on the launch stream (kda_chunk_fwd_traced); the dominant
 kernel's roofline uses its algorithmic bytes:
   intra-chunk : q, k, z (3 * 2d B) + beta (2 B) per token-head
-  state scan  : v (2d B) per token-head + initial / final state
-  gate        : gate logits in, y out (2 * 2d B) per token-head
+  state scan  : v, gate logits in, y out (3 * 2d B) per token-head + final state
 which add up to the path's 1,538 B per token-head (2d = 256 B at d = 128).
 The CPU baseline is the fp64 C oracle timed on a bounded sample of heads.
 """
@@ -30,12 +29,12 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 
 
 def kernel_bytes(name: str, token_heads: int, d: int, BH: int, T: int) -> float:
+    """Algorithmic HBM bytes of one launch (its share of the path's inputs and
+    outputs; intermediates between the two kernels are not algorithmic)."""
     if name == "intra":
-        return token_heads * (3 * 2 * d + 2)
+        return token_heads * (3 * 2 * d + 2)          # q, k, z, beta
     if name == "scan":
-        return token_heads * (2 * d) + 2 * BH * d * d * 4
-    if name == "gate":
-        return token_heads * (2 * 2 * d)
+        return token_heads * (3 * 2 * d) + BH * d * d * 4  # v, gate in, y out; final state
     raise KeyError(name)
 
 
@@ -66,6 +65,10 @@ def main() -> int:
     ap.add_argument("--workload", default="k3_layer")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-baseline sample (0: all heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--segment-tokens", type=int, default=0,
+                    help="tokens per internal segment (workspace size); 0: whole sequence")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="only run a plain device copy of GIB GiB (reference for HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -82,6 +85,16 @@ def main() -> int:
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration > 0:
+        nbytes = int(args.copy_calibration * (1 << 30))
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b_ = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b_.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "reads_per_copy": nbytes, "writes_per_copy": nbytes}))
+        return 0
     kda.lib()
 
     t_gen = time.perf_counter()
@@ -102,9 +115,10 @@ def main() -> int:
     out = {"y": torch.empty((B, T, H, D), dtype=odt, device=dev),
            "S_T": torch.empty((B, H, D, D), dtype=torch.float32, device=dev)}
     desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16)
-    ws = torch.empty(kda.workspace_size(desc), dtype=torch.uint8, device=dev)
-    n_seg = 1  # whole sequence in one segment at this size
-    names = ["intra", "scan", "gate"] * n_seg
+    seg = args.segment_tokens or min(T, 65536)
+    ws = torch.empty(kda.workspace_size(desc, seg), dtype=torch.uint8, device=dev)
+    n_seg = -(-T // seg)
+    names = ["intra", "scan"] * n_seg
 
     def step(events=None):
         kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t.get("S0"), gate=t["gate"],
@@ -134,9 +148,12 @@ def main() -> int:
 
     per = {n: [] for n in set(names)}
     for row in ev:
+        tot = {n: 0.0 for n in per}
         for i, n in enumerate(names):
-            per[n].append(row[2 * i].elapsed_time(row[2 * i + 1]))
-    kern_ms = {n: float(np.mean(v)) for n, v in per.items()}
+            tot[n] += row[2 * i].elapsed_time(row[2 * i + 1])
+        for n in per:
+            per[n].append(tot[n])
+    kern_ms = {n: float(np.mean(v)) for n, v in per.items()}  # per step, summed over segments
     dom = max(kern_ms, key=kern_ms.get)
     dom_bytes = kernel_bytes(dom, token_heads, D, B * H, T)
     achieved = dom_bytes / (kern_ms[dom] * 1e-3) / 1e9
@@ -158,7 +175,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded; K3 layer shapes, no trained weights)",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "d_k": D, "d_v": D, "chunk": 64,
-                   "inputs": "bf16", "state": "fp32", "outputs": "y (bf16) + S_T (fp32)", "gate": True},
+                   "inputs": "bf16", "state": "fp32", "outputs": "y (bf16) + S_T (fp32)", "gate": True,
+                   "segment_tokens": seg},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None},
         "path_roofline": {"achieved_GBs": path_gbs, "frac_hbm": path_gbs / HBM_PEAK_GBS,

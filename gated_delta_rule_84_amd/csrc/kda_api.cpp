@@ -56,11 +56,12 @@ kda_status validate_desc(const kda_desc* d) {
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct WsLayout {
-  size_t off_rec, rec_bytes, off_o32, off_carry, total;
+  size_t off_rec, rec_bytes, off_carry, total;
 };
 
-// Workspace for a segment of seg_nc chunks.
-WsLayout layout_for(const kda_desc* d, int64_t seg_nc, bool gated) {
+// Workspace for a segment of seg_nc chunks: one record per (b, h, chunk) and
+// the fp32 state carried between segments.
+WsLayout layout_for(const kda_desc* d, int64_t seg_nc) {
   const int es = (int)elem_size(d->in_dtype);
   const int64_t D = d->d_k;
   const int64_t R = (int64_t)d->B * d->H * seg_nc;
@@ -73,7 +74,6 @@ WsLayout layout_for(const kda_desc* d, int64_t seg_nc, bool gated) {
   };
   L.rec_bytes = (size_t)kda::rec_layout(es, (int)D).bytes;
   L.off_rec = take(R * L.rec_bytes);
-  L.off_o32 = gated ? take((size_t)d->B * seg_nc * kChunk * d->H * D * 4) : 0;
   L.off_carry = take((size_t)d->B * d->H * D * D * 4);
   L.total = o;
   return L;
@@ -124,7 +124,7 @@ kda_status kda_desc_init(kda_desc* d, int32_t B, int32_t T, int32_t H, int32_t h
 size_t kda_chunk_fwd_workspace_size_for(const kda_desc* d, int32_t segment_tokens) {
   if (validate_desc(d) != KDA_OK || segment_tokens < 1) return 0;
   const int64_t seg_nc = ((int64_t)segment_tokens + kChunk - 1) / kChunk;
-  return layout_for(d, seg_nc, true).total;
+  return layout_for(d, seg_nc).total;
 }
 
 size_t kda_chunk_fwd_workspace_size(const kda_desc* d) {
@@ -180,28 +180,26 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   const int out_f32 = d->out_dtype == KDA_F32;
   const int64_t nc_total = num_chunks(d);
 
-  const bool gated = (y != nullptr);
   // largest segment whose workspace fits
-  const WsLayout one = layout_for(d, 1, gated);
+  const WsLayout one = layout_for(d, 1);
   if (!ws || ws_bytes < one.total) return KDA_ERR_WORKSPACE;
   int64_t seg_nc = 1;
   {
     int64_t lo = 1, hi = nc_total;
     while (lo < hi) {
       const int64_t mid = lo + (hi - lo + 1) / 2;
-      if (layout_for(d, mid, gated).total <= ws_bytes)
+      if (layout_for(d, mid).total <= ws_bytes)
         lo = mid;
       else
         hi = mid - 1;
     }
     seg_nc = lo;
   }
-  const WsLayout L = layout_for(d, seg_nc, gated);
+  const WsLayout L = layout_for(d, seg_nc);
   char* base = static_cast<char*>(ws);
   kda::ChunkWs cw{};
   cw.base = base + L.off_rec;
   cw.rec_bytes = (int64_t)L.rec_bytes;
-  float* o32 = gated ? reinterpret_cast<float*>(base + L.off_o32) : nullptr;
   float* carry = reinterpret_cast<float*>(base + L.off_carry);
   float* S_run = S_T ? S_T : carry;
 
@@ -233,51 +231,24 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
 
     kda::ScanParams sp{};
     sp.v = v;
+    sp.gate = y ? gate : nullptr;
+    sp.rms_w = rms_w;
     sp.S_in = S_in;
     sp.S_out = S_run;
+    sp.o = o;  // NULL when only S_T (or only y) is requested
+    sp.y = y;
+    sp.out_f32 = out_f32;
+    sp.rms_eps = d->rms_eps;
     sp.B = d->B;
     sp.T = d->T;
     sp.H = d->H;
     sp.t0 = t0;
     sp.nc = nc;
     sp.ws = cw;
-    if (gated) {
-      sp.o = o32;
-      sp.o_f32 = 1;
-      sp.o_tok_stride = (int64_t)d->H * D;
-      sp.o_b_stride = (int64_t)seg_nc * kChunk * d->H * D;
-      sp.o_t0 = t0;
-    } else {
-      sp.o = o;  // NULL when only S_T is requested: the scan then skips o
-      sp.o_f32 = out_f32;
-      sp.o_tok_stride = (int64_t)d->H * D;
-      sp.o_b_stride = (int64_t)d->T * d->H * D;
-      sp.o_t0 = 0;
-    }
     tr.before(s);
     st = check_launch(kda::launch_scan(sp, D, in_f32, s), s);
     tr.after(s);
     if (st != KDA_OK) return st;
-
-    if (gated) {
-      kda::GateParams gp{};
-      gp.o32 = o32;
-      gp.o32_b_stride = (int64_t)seg_nc * kChunk * d->H * D;
-      gp.gate = gate;
-      gp.rms_w = rms_w;
-      gp.y = y;
-      gp.o = o;
-      gp.B = d->B;
-      gp.T = d->T;
-      gp.H = d->H;
-      gp.t0 = t0;
-      gp.nt = (d->T - t0) < nc * kChunk ? (d->T - t0) : nc * kChunk;
-      gp.rms_eps = d->rms_eps;
-      tr.before(s);
-      st = check_launch(kda::launch_gate(gp, D, in_f32, out_f32, s), s);
-      tr.after(s);
-      if (st != KDA_OK) return st;
-    }
     S_in = S_run;
   }
   return KDA_OK;

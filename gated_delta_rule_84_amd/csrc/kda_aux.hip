@@ -1,67 +1,11 @@
-// Output gate epilogue, state import/export and the pre-pass diagnostic.
+// State import / export and the pre-pass diagnostic.
 //
 // Source: "Kimi K3: KDA, Attention Residuals and Stable LatentMoE"
-// (hs-black.github.io/posts/kimi-k3), section 2.3 (y = Sigmoid(W_g x) .
-// RMSNorm(o), here with the gate logits W_g x given as an input and RMSNorm
-// over the d_v channels of one head) and section 2.2 (decay map, used by the
+// (hs-black.github.io/posts/kimi-k3), section 2.2 (decay map, used by the
 // pre-pass).
 #include "kda_chunk_prologue.hpp"
 
 namespace kda {
-
-__device__ __forceinline__ float wave_sum64(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  return x;
-}
-
-// ---- gate: one wave per (b, t, h) row ------------------------------------
-template <typename T, typename TO, int D>
-__global__ __launch_bounds__(256) void kda_gate_kernel(const GateParams p) {
-  constexpr int EPL = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t rid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t rows = (int64_t)p.B * p.nt * p.H;
-  if (rid >= rows) return;
-  const int h = (int)(rid % p.H);
-  const int64_t bt = rid / p.H;
-  const int t = (int)(bt % p.nt), b = (int)(bt / p.nt);
-  const float* o = p.o32 + (int64_t)b * p.o32_b_stride + ((int64_t)t * p.H + h) * D;
-  const int64_t grow = (((int64_t)b * p.T + p.t0 + t) * p.H + h) * D;
-  float x[EPL];
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    x[e] = o[lane * EPL + e];
-    ss += x[e] * x[e];
-  }
-  ss = wave_sum64(ss);
-  const float rr = 1.0f / sqrtf(ss / D + p.rms_eps);
-  const T* g = static_cast<const T*>(p.gate) + grow;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const int c = lane * EPL + e;
-    const float w = (p.rms_w != nullptr) ? p.rms_w[h * D + c] : 1.0f;
-    const float yv = sigmoid_fast(Elem<T>::to_f32(g[c])) * x[e] * rr * w;
-    static_cast<TO*>(p.y)[grow + c] = Elem<TO>::from_f32(yv);
-    if (p.o != nullptr) static_cast<TO*>(p.o)[grow + c] = Elem<TO>::from_f32(x[e]);
-  }
-}
-
-hipError_t launch_gate(const GateParams& p, int D, int in_f32, int out_f32, hipStream_t s) {
-  const int64_t rows = (int64_t)p.B * p.nt * p.H;
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-#define KDA_GATE(TI, TO, DD) hipLaunchKernelGGL((kda_gate_kernel<TI, TO, DD>), grid, block, 0, s, p)
-  if (in_f32) {
-    if (out_f32) { if (D == 64) KDA_GATE(float, float, 64); else KDA_GATE(float, float, 128); }
-    else { if (D == 64) KDA_GATE(float, uint16_t, 64); else KDA_GATE(float, uint16_t, 128); }
-  } else {
-    if (out_f32) { if (D == 64) KDA_GATE(uint16_t, float, 64); else KDA_GATE(uint16_t, float, 128); }
-    else { if (D == 64) KDA_GATE(uint16_t, uint16_t, 64); else KDA_GATE(uint16_t, uint16_t, 128); }
-  }
-#undef KDA_GATE
-  return hipGetLastError();
-}
 
 // ---- state import / export / zero: one workgroup per (n, h) ----------------
 template <int D>

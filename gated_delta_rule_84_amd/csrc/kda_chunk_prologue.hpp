@@ -88,7 +88,7 @@ __device__ __forceinline__ void chunk_prologue(ChunkSmem<T, D>& sm, const T* __r
   constexpr int GP = ChunkSmem<T, D>::GP;
   constexpr int XP = ChunkSmem<T, D>::XP;
   const int tid = threadIdx.x;
-  const float eA = exp2f(A_h * kLog2e);
+  const float eA = hw_exp2(A_h * kLog2e);
   for (int idx = tid; idx < kChunk * VPR; idx += 256) {
     const int r = idx / VPR;
     const int cv = (idx % VPR) * VEC;
@@ -133,7 +133,7 @@ __device__ __forceinline__ void chunk_prologue(ChunkSmem<T, D>& sm, const T* __r
 #pragma unroll
       for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
     }
-    const float rn = l2norm ? 1.0f / sqrtf(ss + l2_eps) : 1.0f;
+    const float rn = l2norm ? hw_rsqrt(ss + l2_eps) : 1.0f;
     if (tid - D < kChunk)
       sm.rq[r] = rn;
     else

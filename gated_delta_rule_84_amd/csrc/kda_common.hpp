@@ -126,9 +126,16 @@ __device__ __forceinline__ f32x8 acc_pair_to_f32(const f32x4& t0, const f32x4& t
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// Logistic function for moderate arguments via exp2 (v_exp_f32) and v_rcp_f32.
-__device__ __forceinline__ float sigmoid_fast(float x) {
-  return __frcp_rn(1.0f + exp2f(-x * kLog2e));
-}
+// Hardware transcendental approximations (about 1 ulp): 2^x, 1/x and
+// 1/sqrt(x).  2^x flushes results below the normal range to 0, which is the
+// right limit everywhere they are used here (decay factors and gates whose
+// true values are negligibly small).
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float hw_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
+__device__ __forceinline__ float hw_exp(float x) { return hw_exp2(x * kLog2e); }
+
+// Logistic function: 1 / (1 + e^{-x}); saturates to 0 and 1 at the extremes.
+__device__ __forceinline__ float sigmoid_fast(float x) { return hw_rcp(1.0f + hw_exp2(-x * kLog2e)); }
 
 }  // namespace kda

@@ -40,9 +40,9 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const DecodeParams p) {
   if (tid < D) {
     kx = Elem<T>::to_f32(k[tid]);
     qx = Elem<T>::to_f32(q[tid]);
-    const float eA = exp2f(p.A[h] * kLog2e);
+    const float eA = hw_exp2(p.A[h] * kLog2e);
     const float g = p.g_min * sigmoid_fast(eA * Elem<T>::to_f32(z[tid]));
-    as[tid] = exp2f(g * kLog2e);
+    as[tid] = hw_exp2(g * kLog2e);
   }
   {
     const float sk = wave_sum(kx * kx), sq = wave_sum(qx * qx);
@@ -59,8 +59,8 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const DecodeParams p) {
       sk += wred[w][0];
       sq += wred[w][1];
     }
-    const float rk = p.l2norm ? 1.0f / sqrtf(sk + p.l2_eps) : 1.0f;
-    const float rq = p.l2norm ? 1.0f / sqrtf(sq + p.l2_eps) : 1.0f;
+    const float rk = p.l2norm ? hw_rsqrt(sk + p.l2_eps) : 1.0f;
+    const float rq = p.l2norm ? hw_rsqrt(sq + p.l2_eps) : 1.0f;
     ks[tid] = kx * rk;
     qs[tid] = qx * rq * p.q_scale;
   }
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int wv = 0; wv < 4; ++wv) ms += wred[wv][0];
     if (rg == 0) {
-      const float rr = 1.0f / sqrtf(ms / D + p.rms_eps);
+      const float rr = hw_rsqrt(ms / D + p.rms_eps);
       const float gl = Elem<T>::to_f32(static_cast<const T*>(p.gate)[row * D + col]);
       const float wv = (p.rms_w != nullptr) ? p.rms_w[h * D + col] : 1.0f;
       const float yv = sigmoid_fast(gl) * o * rr * wv;

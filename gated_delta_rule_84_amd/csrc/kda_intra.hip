@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int ch = cb + slot_row(8 * (pg & 3) + j);
-      const float e = exp2f(G[r * GP + ch] * kLog2e);
+      const float e = hw_exp2(G[r * GP + ch] * kLog2e);
       xq[j] = Elem<T>::to_f32(sm.u1.x.q[r * XP + ch]) * sq * e;
       xk[j] = Elem<T>::to_f32(sm.u1.x.k[r * XP + ch]) * sk * e;
     }
@@ -111,11 +111,11 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int r = slot_row64(8 * pg + j);
-      x[j] = Elem<T>::to_f32(sm.u1.x.k[r * XP + ch]) * sm.rk[r] * exp2f((glast - G[r * GP + ch]) * kLog2e);
+      x[j] = Elem<T>::to_f32(sm.u1.x.k[r * XP + ch]) * sm.rk[r] * hw_exp2((glast - G[r * GP + ch]) * kLog2e);
     }
     store8<T>(kdt + ch * kChunk + 8 * pg, x);
   }
-  if (tid < D) gam[tid] = exp2f(G[(kChunk - 1) * GP + tid] * kLog2e);
+  if (tid < D) gam[tid] = hw_exp2(G[(kChunk - 1) * GP + tid] * kLog2e);
 
   // ---- sub-tile products A_kk(i, j), A_qk(i, j), j <= i; wave i = row tile --
   const int n = lane & 15, g4 = lane >> 4;
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) 
       load8_lds<T>(&sm.u1.x.k[r * XP + c0], xk);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float e = exp2f((gr[j] - ga[j]) * kLog2e);
+        const float e = hw_exp2((gr[j] - ga[j]) * kLog2e);
         xq[j] *= sq * e;
         xk[j] *= sk * e;
       }
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) 
           load8_lds<T>(&sm.u1.x.k[s * XP + c0], y);
           const float ss = sm.rk[s];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) y[j] *= ss * exp2f((ga[j] - gs[j]) * kLog2e);
+          for (int j = 0; j < 8; ++j) y[j] *= ss * hw_exp2((ga[j] - gs[j]) * kLog2e);
           const typename AP::Op oy = AP::make(y);
           akk[jt] = AP::mma(ok, oy, akk[jt]);
           aqk[jt] = AP::mma(oq, oy, aqk[jt]);

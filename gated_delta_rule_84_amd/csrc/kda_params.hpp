@@ -58,27 +58,17 @@ struct IntraParams {
 
 struct ScanParams {
   const void* v;
+  const void* gate;     // [B, T, H, D] gate logits (input dtype) or nullptr
+  const float* rms_w;   // [H, D] or nullptr (weight 1)
   const float* S_in;    // [B, H, D, D] or nullptr (zero state)
   float* S_out;         // [B, H, D, D] (may equal S_in)
-  void* o;              // [B, T, H, D] output, element type by o_f32
-  int o_f32;            // 1: o is fp32, 0: bf16
-  int64_t o_tok_stride; // elements between consecutive tokens of o (H*D)
-  int64_t o_b_stride;   // elements between batches of o
-  int o_t0;             // token offset subtracted before indexing o
-  int B, T, H;
-  int t0, nc;
-  ChunkWs ws;
-};
-
-struct GateParams {
-  const float* o32;     // fp32, segment-local tokens: o32[b * o32_b_stride + (t*H + h)*D]
-  int64_t o32_b_stride;
-  const void* gate;     // [B, T, H, D] input dtype
-  const float* rms_w;   // [H, D] or nullptr
-  void* y;              // [B, T, H, D] out dtype
-  void* o;              // [B, T, H, D] out dtype or nullptr
-  int B, T, H, t0, nt;
+  void* o;              // [B, T, H, D] or nullptr
+  void* y;              // [B, T, H, D] or nullptr (requires gate)
+  int out_f32;          // element type of o and y: 1 fp32, 0 bf16
   float rms_eps;
+  int B, T, H;
+  int t0, nc;           // first token and number of chunks of the segment
+  ChunkWs ws;
 };
 
 struct DecodeParams {
@@ -125,7 +115,6 @@ struct PrepassParams {
 // Host launchers (one per kernel family).  in_f32: inputs are fp32 (else bf16).
 hipError_t launch_intra(const IntraParams& p, int D, int in_f32, hipStream_t s);
 hipError_t launch_scan(const ScanParams& p, int D, int in_f32, hipStream_t s);
-hipError_t launch_gate(const GateParams& p, int D, int in_f32, int out_f32, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int D, int in_f32, hipStream_t s);
 hipError_t launch_state_io(const StateIoParams& p, int D, hipStream_t s);
 hipError_t launch_prepass(const PrepassParams& p, int D, int in_f32, hipStream_t s);

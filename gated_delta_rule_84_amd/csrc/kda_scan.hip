@@ -1,22 +1,24 @@
-// Inter-chunk state scan.  A workgroup of 4 waves owns 64 value columns of
-// one head (16 per wave); each wave keeps its d_k x 16 slice of the fp32 state
-// S in MFMA accumulators for the whole sequence and walks the chunks in order.
-// The columns of S evolve independently, so waves never exchange state.  The
-// chunk record written by the intra-chunk kernel, and the workgroup's 64x64
-// slab of V, are copied into LDS by the whole workgroup: the loads for chunk
-// c + 1 are in flight in registers while chunk c is computed from LDS, and
-// are committed to LDS after it.
+// Inter-chunk state scan with the fused output gate.  One workgroup per
+// (batch, head) with D / 16 waves; wave w owns value columns 16 w .. 16 w + 15
+// and keeps its d_k x 16 slice of the fp32 state S in MFMA accumulators for
+// the whole sequence.  The columns of S evolve independently, so waves never
+// exchange state.  Per chunk, the chunk record written by the intra-chunk
+// kernel and the head's 64 x D slab of V are loaded into registers while the
+// previous chunk is computed, then committed to LDS.  The chunk's outputs go
+// through an LDS tile so that the RMSNorm over a row and the stores of o / y
+// are done row by row with contiguous 16-byte stores.
 //
 // Source: "Kimi K3: KDA, Attention Residuals and Stable LatentMoE"
-// (hs-black.github.io/posts/kimi-k3), section 2.1: per chunk with entry
+// (hs-black.github.io/posts/kimi-k3).  Section 2.1: per chunk with entry
 // state S and the UT pair of the intra-chunk kernel,
 //     U'     = T Diag(beta) (V - (K . Gamma) S)      (= U - W S)
 //     O      = (Q . Gamma) S + Tril(A_qk) U'
 //     S_next = Diag(Gamma_last) S + (K . Gamma_last / Gamma)^T U'
-// Rounding plan (bf16 path): S, K . Gamma, Q . Gamma and U' enter bf16 MFMAs
-// with fp32 accumulation; the residual V - (K . Gamma) S is split into hi/lo
-// bf16 parts (two products); Tril(A_qk) U' uses hi/lo split operands on both
-// sides; S itself stays fp32.  The fp32 path uses fp32 MFMA.
+// Section 2.3: y = Sigmoid(gate) . RMSNorm(o) over the d_v channels of a head.
+// Rounding plan (bf16 path): S, K . Gamma and Q . Gamma enter bf16 MFMAs with
+// fp32 accumulation; the residual V - (K . Gamma) S and U' are split into
+// hi/lo bf16 parts where they are multiplied (T R, Kd^T U'); Tril(A_qk) U'
+// uses hi/lo parts on both sides; S stays fp32.  The fp32 path uses fp32 MFMA.
 #include "kda_common.hpp"
 #include "kda_params.hpp"
 
@@ -28,7 +30,7 @@ struct ScanOps;
 template <>
 struct ScanOps<uint16_t> {
   using V8 = bf16x8;
-  struct Prec {  // operand of the split product
+  struct Prec {  // operand of a split product
     bf16x8 hi, lo;
   };
   static __device__ __forceinline__ V8 ld(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
@@ -38,7 +40,6 @@ struct ScanOps<uint16_t> {
     acc_pair_split(a, b, r.hi, r.lo);
     return r;
   }
-  static __device__ __forceinline__ V8 prec_main(const Prec& p) { return p.hi; }
   static __device__ __forceinline__ f32x4 mma_prec(const char* ah, const char* al, const Prec& b, f32x4 acc) {
     return mma32_x3(ld(ah), ld(al), b.hi, b.lo, acc);
   }
@@ -65,7 +66,6 @@ struct ScanOps<float> {
   static __device__ __forceinline__ Prec prec_from_acc(const f32x4& a, const f32x4& b) {
     return Prec{acc_pair_to_f32(a, b)};
   }
-  static __device__ __forceinline__ V8 prec_main(const Prec& p) { return p.v; }
   static __device__ __forceinline__ f32x4 mma_prec(const char* ah, const char*, const Prec& b, f32x4 acc) {
     return mma32(ld(ah), b.v, acc);
   }
@@ -75,12 +75,14 @@ struct ScanOps<float> {
   static __device__ __forceinline__ float in_f32(float x) { return x; }
 };
 
-// LDS image of one chunk record: the record's arrays with each row padded by
-// 16 bytes so that the 16 rows read by one MFMA operand load hit distinct banks.
+// LDS image of one chunk record (rows padded by 16 bytes so that the 16 rows
+// read by one MFMA operand load hit distinct banks), the V slab and the output
+// tile.
 template <typename T, int D>
 struct ScanLds {
   static constexpr int ES = sizeof(T);
-  static constexpr int PQ = D * ES + 16;    // row pitch of qg / kg
+  static constexpr int NT = 4 * D;          // threads (D / 16 waves)
+  static constexpr int PQ = D * ES + 16;    // row pitch of qg / kg / V slab
   static constexpr int PK = 64 * ES + 16;   // row pitch of kdt / tb / aqh / aql
   static constexpr int QG = 0;
   static constexpr int KG = QG + 64 * PQ;
@@ -89,14 +91,28 @@ struct ScanLds {
   static constexpr int AQH = TB + 64 * PK;
   static constexpr int AQL = AQH + 64 * PK;
   static constexpr int GAM = AQL + (ES == 2 ? 64 * PK : 0);
-  static constexpr int PV = 64 * ES + 16;   // row pitch of the V slab (64 columns)
-  static constexpr int VS = GAM + 4 * D;
-  static constexpr int BYTES = VS + 64 * PV;
-  // the record, in 16-byte units, then the V slab (64 tokens x 64 columns)
+  static constexpr int REC = GAM + 4 * D;   // end of the record image
+  static constexpr int PO = D + 4;          // fp32 output tile [64][D + 4]
+  static constexpr int LIMIT = 160 * 1024;
+  // The V slab goes through LDS when it fits (else straight to registers),
+  // and the output tile shares the record's space when a separate one does not.
+  static constexpr bool V_LDS = REC + 64 * PQ <= LIMIT;
+  static constexpr int VS = REC;
+  static constexpr int AFTER_V = REC + (V_LDS ? 64 * PQ : 0);
+  static constexpr bool O_ALIAS = AFTER_V + 64 * PO * 4 > LIMIT;
+  static constexpr int OT = O_ALIAS ? QG : AFTER_V;
+  static constexpr int BYTES = O_ALIAS ? AFTER_V : AFTER_V + 64 * PO * 4;
+  static_assert(BYTES <= LIMIT, "scan LDS image too large");
+  static_assert(!O_ALIAS || 64 * PO * 4 <= KDT, "aliased output tile must fit in qg / kg");
   static constexpr RecLayout RL = rec_layout(ES, D);
-  static constexpr int REC_UNITS = (RL.gam + 4 * D) / 16;
-  static constexpr int V_UNITS = 64 * 64 * ES / 16;
-  static constexpr int PER_THREAD = (REC_UNITS + V_UNITS + 255) / 256;
+  static constexpr int REC_UNITS = (RL.gam + 4 * D) / 16;   // 16-byte units
+  static constexpr int V_UNITS = V_LDS ? 64 * D * ES / 16 : 0;
+  static constexpr int UNITS = REC_UNITS + V_UNITS;
+  static constexpr int PER_THREAD = (UNITS + NT - 1) / NT;
+  static constexpr int FULL = UNITS / NT;  // unit slots that are always in range
+  // epilogue: TPR threads per token row, 16 columns each
+  static constexpr int TPR = NT / 64;
+  static constexpr int GV = 16 * ES / 16;  // 16-byte vectors of gate logits per thread
 };
 
 // Record byte offset of 16-byte unit u -> byte offset in the padded LDS image.
@@ -116,39 +132,56 @@ __device__ __forceinline__ int lds_offset_of_unit(int u) {
   return L::GAM + (b - RL.gam);
 }
 
+// 16 consecutive fp32 values -> 16 outputs (fp32 or bf16) at dst.
+__device__ __forceinline__ void store16(void* dst, const float* x, int out_f32) {
+  if (out_f32) {
+    float4* d = static_cast<float4*>(dst);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d[q] = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+  } else {
+    u32x4 w[2];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      w[q >> 2][q & 3] = static_cast<uint32_t>(f32_to_bf16(x[2 * q])) |
+                         (static_cast<uint32_t>(f32_to_bf16(x[2 * q + 1])) << 16);
+    u32x4* d = static_cast<u32x4*>(dst);
+    d[0] = w[0];
+    d[1] = w[1];
+  }
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void kda_scan_kernel(const ScanParams p) {
+__global__ __launch_bounds__(4 * D, 1) void kda_scan_kernel(const ScanParams p) {
   using Ops = ScanOps<T>;
   using V8 = typename Ops::V8;
   using L = ScanLds<T, D>;
   constexpr int MT = D / 16;  // 16-row tiles of the state (key channels)
   constexpr int KS = D / 32;  // K-steps over key channels
+  constexpr int NT = L::NT;
   __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g4 = lane >> 4;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int col = 64 * blockIdx.x + 16 * wave + n;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int col = 16 * wave + n;
   const int64_t bh = (int64_t)b * p.H + h;
-  const bool col_ok = col < D;  // D = 64: one workgroup per head, all columns valid
+  const int64_t tok_stride = (int64_t)p.H * D;  // elements between tokens of one head
+  const int64_t head_base = ((int64_t)b * p.T * p.H + h) * D;
 
-  // Per-thread 16-byte units (the same for every chunk): record units first,
-  // then V-slab units (VPR units per token row of the slab's 64 columns).
-  constexpr int UNITS = L::REC_UNITS + L::V_UNITS;
-  constexpr int VPR = 64 * L::ES / 16;
+  // ---- per-thread copy units: record units, then V-slab units -------------
+  constexpr int VPR = D * L::ES / 16;  // 16-byte units per V row
   int lofs[L::PER_THREAD];
 #pragma unroll
   for (int i = 0; i < L::PER_THREAD; ++i) {
-    const int u = tid + 256 * i;
+    const int u = tid + NT * i;
     if (u < L::REC_UNITS) {
       lofs[i] = lds_offset_of_unit<T, D>(u);
     } else {
       const int vu = u - L::REC_UNITS;
-      lofs[i] = L::VS + (vu / VPR) * L::PV + (vu % VPR) * 16;
+      lofs[i] = L::VS + (vu / VPR) * L::PQ + (vu % VPR) * 16;
     }
   }
-  constexpr int FULL = UNITS / 256;  // slots that are always inside
-  const bool tail_ok = tid + 256 * FULL < UNITS;
+  const bool tail_ok = tid + NT * L::FULL < L::UNITS;
   const T* vin = static_cast<const T*>(p.v);
   u32x4 stg[L::PER_THREAD];
   auto fetch = [&](int c) {
@@ -157,16 +190,15 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(const ScanParams p) {
     const int last = min(kChunk, p.T - tok0) - 1;
 #pragma unroll
     for (int i = 0; i < L::PER_THREAD; ++i) {
-      const int u = tid + 256 * i;
-      if (i < FULL || tail_ok) {
+      const int u = tid + NT * i;
+      if (i < L::FULL || tail_ok) {
         const u32x4* src;
         if (u < L::REC_UNITS) {
           src = reinterpret_cast<const u32x4*>(rec) + u;
-        } else {  // V rows past the end are clamped (zeroed when used)
+        } else {  // V rows past the end are clamped (and zeroed where used)
           const int vu = u - L::REC_UNITS;
           const int r = min(vu / VPR, last);
-          src = reinterpret_cast<const u32x4*>(vin + ((int64_t)(b * (int64_t)p.T + tok0 + r) * p.H + h) * D +
-                                               64 * blockIdx.x + (vu % VPR) * (16 / L::ES));
+          src = reinterpret_cast<const u32x4*>(vin + head_base + (tok0 + r) * tok_stride) + (vu % VPR);
         }
         stg[i] = *src;
       }
@@ -175,14 +207,22 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(const ScanParams p) {
   auto commit = [&]() {
 #pragma unroll
     for (int i = 0; i < L::PER_THREAD; ++i)
-      if (i < FULL || tail_ok) *reinterpret_cast<u32x4*>(lds + lofs[i]) = stg[i];
+      if (i < L::FULL || tail_ok) *reinterpret_cast<u32x4*>(lds + lofs[i]) = stg[i];
   };
 
-  // state: lane holds S[16 mt + 4 g4 + i][col]
+  // ---- epilogue role: token row er, columns ec .. ec + 15 -----------------
+  const int er = tid / L::TPR, ec = (tid % L::TPR) * 16;
+  const bool gated = p.y != nullptr;
+  float wv[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) wv[j] = (gated && p.rms_w != nullptr) ? p.rms_w[h * D + ec + j] : 1.0f;
+  const T* gin = static_cast<const T*>(p.gate);
+
+  // ---- state: lane holds S[16 mt + 4 g4 + i][col] ---------------------------
   f32x4 S[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) S[mt] = zero4();
-  if (p.S_in != nullptr && col_ok) {
+  if (p.S_in != nullptr) {
     const float* s0 = p.S_in + bh * D * D;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -194,19 +234,38 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(const ScanParams p) {
   commit();
   __syncthreads();
 
+  const char* qg = lds + L::QG;
+  const char* kg = lds + L::KG;
+  const char* kdt = lds + L::KDT;
+  const char* tb = lds + L::TB;
+  const char* aqh = lds + L::AQH;
+  const char* aql = lds + L::AQL;
+  const float* gam = reinterpret_cast<const float*>(lds + L::GAM);
+  float* otile = reinterpret_cast<float*>(lds + L::OT);
+
   for (int c = 0; c < p.nc; ++c) {
     const bool more = c + 1 < p.nc;
-    if (more) fetch(c + 1);
-    const char* base = lds;
-    const char* qg = base + L::QG;
-    const char* kg = base + L::KG;
-    const char* kdt = base + L::KDT;
-    const char* tb = base + L::TB;
-    const char* aqh = base + L::AQH;
-    const char* aql = base + L::AQL;
-    const float* gam = reinterpret_cast<const float*>(base + L::GAM);
     const int tok0 = p.t0 + c * kChunk;
     const int nvalid = min(kChunk, p.T - tok0);
+
+    // gate logits of this chunk for the epilogue (issued before the prefetch
+    // so that waiting for them does not wait for the prefetch)
+    u32x4 gvec[L::GV];
+    if (gated) {
+      const u32x4* src =
+          reinterpret_cast<const u32x4*>(gin + head_base + (tok0 + min(er, nvalid - 1)) * tok_stride + ec);
+#pragma unroll
+      for (int q = 0; q < L::GV; ++q) gvec[q] = src[q];
+    }
+    T vreg[16];  // V at the accumulator positions when it does not go through LDS
+    if constexpr (!L::V_LDS) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          vreg[4 * mt + i] = vin[head_base + (tok0 + min(16 * mt + 4 * g4 + i, nvalid - 1)) * tok_stride + col];
+    }
+    if (more) fetch(c + 1);
 
     // B operands from the state, K-slots in slot order
     V8 Sb[KS];
@@ -234,9 +293,12 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(const ScanParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mt + 4 * g4 + i;
-        const T vraw = *reinterpret_cast<const T*>(base + L::VS + r * L::PV + (16 * wave + n) * L::ES);
-        const float vv = (r < nvalid && col_ok) ? Ops::in_f32(vraw) : 0.f;
-        R[mt][i] = vv - X[mt][i];
+        T vraw;
+        if constexpr (L::V_LDS)
+          vraw = *reinterpret_cast<const T*>(lds + L::VS + r * L::PQ + col * L::ES);
+        else
+          vraw = vreg[4 * mt + i];
+        R[mt][i] = (r < nvalid ? Ops::in_f32(vraw) : 0.f) - X[mt][i];
       }
     typename Ops::Prec Rp[2];
     Rp[0] = Ops::prec_from_acc(R[0], R[1]);
@@ -264,56 +326,79 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(const ScanParams p) {
         O[mt] = Ops::mma_prec(aqh + off, aql + off, Up[kk], O[mt]);
       }
 
-    // outputs (a full chunk stores without per-row guards)
-    if (p.o != nullptr && col_ok) {
-      const int64_t o0 = (int64_t)b * p.o_b_stride + (int64_t)(tok0 - p.o_t0) * p.o_tok_stride + h * D + col;
-      const bool full = nvalid == kChunk;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * mt + 4 * g4 + i;
-          if (full || r < nvalid) {
-            const int64_t oi = o0 + (int64_t)r * p.o_tok_stride;
-            if (p.o_f32)
-              static_cast<float*>(p.o)[oi] = O[mt][i];
-            else
-              static_cast<uint16_t*>(p.o)[oi] = f32_to_bf16(O[mt][i]);
-          }
-        }
-    }
-
     // S <- Diag(Gamma_last) S + Kd^T U'
-    const V8 Ub0 = Ops::prec_main(Up[0]);
-    const V8 Ub1 = Ops::prec_main(Up[1]);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const f32x4 gm = *reinterpret_cast<const f32x4*>(gam + 16 * mt + 4 * g4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[mt][i] *= gm[i];
       const int off = (16 * mt + n) * L::PK + 8 * g4 * L::ES;
-      S[mt] = mma32(Ops::ld(kdt + off), Ub0, S[mt]);
-      S[mt] = mma32(Ops::ld(kdt + off + 32 * L::ES), Ub1, S[mt]);
+      S[mt] = Ops::mma_split_b(Ops::ld(kdt + off), Up[0], S[mt]);
+      S[mt] = Ops::mma_split_b(Ops::ld(kdt + off + 32 * L::ES), Up[1], S[mt]);
+    }
+
+    // O tile to LDS (when it shares the record's space, wait until no wave
+    // reads the record any more)
+    if constexpr (L::O_ALIAS) __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) otile[(16 * mt + 4 * g4 + i) * L::PO + col] = O[mt][i];
+    __syncthreads();  // O tile complete; chunk c's record and V are no longer read
+
+    // epilogue: row er, columns ec .. ec + 15
+    {
+      float ov[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(otile + er * L::PO + ec + 4 * q);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ov[4 * q + j] = t[j];
+      }
+      const bool row_ok = er < nvalid;
+      const int64_t orow = head_base + (tok0 + er) * tok_stride + ec;
+      if (p.o != nullptr && row_ok) {
+        if (p.out_f32)
+          store16(static_cast<float*>(p.o) + orow, ov, 1);
+        else
+          store16(static_cast<uint16_t*>(p.o) + orow, ov, 0);
+      }
+      if (gated) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) ss += ov[j] * ov[j];
+#pragma unroll
+        for (int m = 1; m < L::TPR; m <<= 1) ss += __shfl_xor(ss, m);
+        const float rinv = hw_rsqrt(ss / D + p.rms_eps);
+        const T* gt = reinterpret_cast<const T*>(gvec);
+        float yv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) yv[j] = sigmoid_fast(Ops::in_f32(gt[j])) * ov[j] * rinv * wv[j];
+        if (row_ok) {
+          if (p.out_f32)
+            store16(static_cast<float*>(p.y) + orow, yv, 1);
+          else
+            store16(static_cast<uint16_t*>(p.y) + orow, yv, 0);
+        }
+      }
     }
 
     if (more) {
-      __syncthreads();  // every wave is done reading chunk c from LDS
-      commit();
+      if constexpr (L::O_ALIAS) __syncthreads();  // the O tile lives in the record's space
+      commit();  // nobody reads chunk c's record or V any more
       __syncthreads();
     }
   }
 
-  if (col_ok) {
-    float* so = p.S_out + bh * D * D;
+  float* so = p.S_out + bh * D * D;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) so[(16 * mt + 4 * g4 + i) * D + col] = S[mt][i];
-  }
+    for (int i = 0; i < 4; ++i) so[(16 * mt + 4 * g4 + i) * D + col] = S[mt][i];
 }
 
 hipError_t launch_scan(const ScanParams& p, int D, int in_f32, hipStream_t s) {
-  const dim3 grid((D + 63) / 64, p.H, p.B), block(256);
+  const dim3 grid(p.H, p.B), block(4 * D);
   if (in_f32) {
     if (D == 64) hipLaunchKernelGGL((kda_scan_kernel<float, 64>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((kda_scan_kernel<float, 128>), grid, block, 0, s, p);

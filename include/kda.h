@@ -120,7 +120,7 @@ kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const 
 /*
  * kda_chunk_fwd with per-kernel timing: identical work and results, and in
  * addition, for the i-th kernel launch of the call (launch order per segment:
- * intra-chunk, state scan, then the gate epilogue when y is requested),
+ * the intra-chunk kernel, then the state scan with the fused gate),
  * hipEventRecord(events[2i]) right before it and hipEventRecord(events[2i+1])
  * right after it on `stream`, while 2i+1 < n_events.  `events` are caller-owned
  * hipEvent_t handles.  Used to measure kernel durations on the launch stream.
