@@ -59,24 +59,42 @@ hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_
 }
 
 // ---- pre-pass diagnostic: chunk-local cumulative log-decay and norms -------
+// Runs the same device routines as the intra-chunk kernel's prologue.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void kda_prepass_kernel(const PrepassParams p) {
-  __shared__ ChunkSmem<T, D> sm;
-  constexpr int GP = ChunkSmem<T, D>::GP;
+  constexpr int GP = D + 4;
+  constexpr int KS = D / 32;
+  __shared__ __attribute__((aligned(16))) float G[64 * GP];
+  __shared__ float tot[256];
+  using R8 = Run8<T>;
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g4 = lane >> 4;
   const int tok0 = c * kChunk;
   const int nvalid = min(kChunk, p.T - tok0);
-  chunk_prologue<T, D>(sm, static_cast<const T*>(p.q), static_cast<const T*>(p.k),
-                       static_cast<const T*>(p.z), nullptr, p.A[h], b, h, p.T, p.H,
-                       tok0, nvalid, p.g_min, p.l2_eps, p.l2norm);
-  for (int idx = threadIdx.x; idx < nvalid * D; idx += 256) {
+  const int64_t tok_stride = (int64_t)p.H * D;
+  const int64_t row0 = ((int64_t)b * p.T + tok0) * p.H * D + (int64_t)h * D;
+  decay_cumsum<T, D>(G, tot, static_cast<const T*>(p.z) + row0, tok_stride, nvalid, p.A[h], p.g_min);
+  for (int idx = tid; idx < nvalid * D; idx += 256) {
     const int r = idx / D, ch = idx % D;
-    p.G[(((int64_t)b * p.T + tok0 + r) * p.H + h) * D + ch] = sm.u0.G[r * GP + ch];
+    p.G[row0 + r * tok_stride + ch] = G[r * GP + ch];
   }
-  if (threadIdx.x < nvalid) {
-    const int64_t ri = ((int64_t)b * p.T + tok0 + threadIdx.x) * p.H + h;
-    p.rq[ri] = sm.rq[threadIdx.x];
-    p.rk[ri] = sm.rk[threadIdx.x];
+  // norms of sub-tile `wave` (every lane takes part in the products)
+  const int r = 16 * wave + n;
+  typename R8::Raw qraw[KS], kraw[KS];
+  const T* qrow = static_cast<const T*>(p.q) + row0 + min(r, nvalid - 1) * tok_stride;
+  const T* krow = static_cast<const T*>(p.k) + row0 + min(r, nvalid - 1) * tok_stride;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    qraw[kk] = R8::load(qrow, kk, g4);
+    kraw[kk] = R8::load(krow, kk, g4);
+  }
+  const float rq = row_inv_norm<T, KS>(qraw, p.l2norm, p.l2_eps);
+  const float rk = row_inv_norm<T, KS>(kraw, p.l2norm, p.l2_eps);
+  if (g4 == 0 && r < nvalid) {
+    const int64_t ri = ((int64_t)b * p.T + tok0 + r) * p.H + h;
+    p.rq[ri] = rq;
+    p.rk[ri] = rk;
   }
 }
 

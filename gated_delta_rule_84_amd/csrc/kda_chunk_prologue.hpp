@@ -1,7 +1,6 @@
 // Chunk prologue shared by the intra-chunk kernel and the pre-pass kernel:
-// loads one 64-token chunk of one head into LDS and computes the K3 bounded
-// log-decay, its chunk-local inclusive cumulative sum and the q / k inverse
-// L2 norms.
+// the K3 bounded log-decay of a 64-token chunk, its chunk-local inclusive
+// cumulative sum, and the q / k inverse L2 norms of one 16-token sub-tile.
 //
 // Source: "Kimi K3: KDA, Attention Residuals and Stable LatentMoE"
 // (hs-black.github.io/posts/kimi-k3), section 2.1 (L2Norm on q and k) and
@@ -14,45 +13,42 @@
 
 namespace kda {
 
-template <typename T, int D>
-struct ChunkSmem {
-  static constexpr int GP = D + 4;                  // fp32 row pitch of G (bank spread)
-  static constexpr int XP = D + 16 / (int)sizeof(T);  // row pitch of q / k (+16 bytes)
-  static constexpr int LP = 64 + 4;                 // fp32 row pitch of 64x64 matrices
-  union {
-    float G[kChunk * GP];   // cumulative log-decay, later the UT inverse (pitch LP)
-    float Tm[kChunk * LP];
-  } u0;
-  union {
-    struct {
-      T q[kChunk * XP];
-      T k[kChunk * XP];
-    } x;
-    float L[kChunk * LP];   // Diag(beta) StrictTril(A_kk), after the products
-  } u1;
-  float rq[kChunk];
-  float rk[kChunk];
-  float beta[kChunk];
-  float P[3][16 * 17];      // scratch for the block inverse
+// Channel set of a lane in one 32-wide K-step: lane group g owns positions
+// 8 g .. 8 g + 7 of the step, which hold channels 32 kk + slot_row(8 g + j),
+// i.e. the two runs 32 kk + 4 g + 0..3 and 32 kk + 16 + 4 g + 0..3.
+__device__ __forceinline__ int lane_ch(int kk, int g, int j) { return 32 * kk + 16 * (j >> 2) + 4 * g + (j & 3); }
+
+// 8 elements of a row in a lane's channel set, as a raw MFMA operand.
+template <typename T>
+struct Run8;
+template <>
+struct Run8<uint16_t> {
+  using Raw = bf16x8;
+  static __device__ __forceinline__ Raw load(const uint16_t* row, int kk, int g) {
+    const uint2 a = *reinterpret_cast<const uint2*>(row + 32 * kk + 4 * g);
+    const uint2 b = *reinterpret_cast<const uint2*>(row + 32 * kk + 16 + 4 * g);
+    const u32x4 w = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(bf16x8, w);
+  }
+  static __device__ __forceinline__ float get(const Raw& r, int j) { return static_cast<float>(r[j]); }
+};
+template <>
+struct Run8<float> {
+  using Raw = f32x8;
+  static __device__ __forceinline__ Raw load(const float* row, int kk, int g) {
+    const float4 a = *reinterpret_cast<const float4*>(row + 32 * kk + 4 * g);
+    const float4 b = *reinterpret_cast<const float4*>(row + 32 * kk + 16 + 4 * g);
+    return f32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  }
+  static __device__ __forceinline__ float get(const Raw& r, int j) { return r[j]; }
 };
 
-template <typename T>
-__device__ __forceinline__ void load8_lds(const T* p, float* out);
-template <>
-__device__ __forceinline__ void load8_lds<uint16_t>(const uint16_t* p, float* out) {
-  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[2 * i] = __uint_as_float(w[i] << 16);
-    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-template <>
-__device__ __forceinline__ void load8_lds<float>(const float* p, float* out) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+// 8 fp32 of a row in a lane's channel set, from an LDS row (two float4 reads).
+__device__ __forceinline__ void lds_run8(const float* row, int kk, int g, float* x) {
+  const float4 a = *reinterpret_cast<const float4*>(row + 32 * kk + 4 * g);
+  const float4 b = *reinterpret_cast<const float4*>(row + 32 * kk + 16 + 4 * g);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
 // Store 8 fp32 values as 8 elements of T (16 or 32 bytes, aligned).
@@ -72,74 +68,73 @@ __device__ __forceinline__ void store8<float>(float* p, const float* x) {
   *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
 }
 
-// 256 threads.  After return (and its trailing barrier) the LDS holds, for the
-// chunk's rows r < nvalid (zeros / flat decay beyond):
-//   x.q, x.k : raw q, k;   rq, rk : inverse L2 norms (1 when l2norm == 0)
-//   G        : inclusive cumulative sum of g over the chunk, per channel
-//   beta     : beta (0 beyond nvalid, or everywhere when beta is null)
+// 256 threads.  G[64][D + 4] (LDS, fp32) receives, per channel, the
+// inclusive cumulative sum over the chunk's tokens of
+//     g = g_min * Sigmoid(e^{A_h} z)      (0 for rows r >= nvalid),
+// summed as per-segment prefixes plus the totals of the earlier segments
+// (256 / D segments per channel).  tot needs 256 floats.  Ends after a
+// barrier with G complete.  zrow0 points at (token 0 of the chunk, head h,
+// channel 0); tokens are tok_stride elements apart.
 template <typename T, int D>
-__device__ __forceinline__ void chunk_prologue(ChunkSmem<T, D>& sm, const T* __restrict__ q,
-                                               const T* __restrict__ k, const T* __restrict__ z,
-                                               const T* __restrict__ beta, float A_h, int b, int h,
-                                               int T_total, int H, int tok0, int nvalid, float g_min,
-                                               float l2_eps, int l2norm) {
+__device__ __forceinline__ void decay_cumsum(float* G, float* tot, const T* __restrict__ zrow0, int64_t tok_stride,
+                                             int nvalid, float A_h, float g_min) {
+  constexpr int GP = D + 4;
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int VPR = D / VEC;
-  constexpr int GP = ChunkSmem<T, D>::GP;
-  constexpr int XP = ChunkSmem<T, D>::XP;
+  constexpr int TPC = 256 / D;   // threads per channel
+  constexpr int RPS = 64 / TPC;  // rows per segment
   const int tid = threadIdx.x;
-  const float eA = hw_exp2(A_h * kLog2e);
-  for (int idx = tid; idx < kChunk * VPR; idx += 256) {
+  const float eA = hw_exp(A_h);
+#pragma unroll
+  for (int it = 0; it < (64 * VPR) / 256; ++it) {
+    const int idx = tid + 256 * it;
     const int r = idx / VPR;
     const int cv = (idx % VPR) * VEC;
-    u32x4 vq = {0u, 0u, 0u, 0u}, vk = {0u, 0u, 0u, 0u}, vz = {0u, 0u, 0u, 0u};
-    if (r < nvalid) {
-      const int64_t off = ((int64_t)(b * (int64_t)T_total + tok0 + r) * H + h) * D + cv;
-      vq = *reinterpret_cast<const u32x4*>(q + off);
-      vk = *reinterpret_cast<const u32x4*>(k + off);
-      vz = *reinterpret_cast<const u32x4*>(z + off);
-    }
-    *reinterpret_cast<u32x4*>(&sm.u1.x.q[r * XP + cv]) = vq;
-    *reinterpret_cast<u32x4*>(&sm.u1.x.k[r * XP + cv]) = vk;
-    float zf[VEC];
-    const T* zt = reinterpret_cast<const T*>(&vz);
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(zrow0 + min(r, nvalid - 1) * tok_stride + cv);
+    const T* zt = reinterpret_cast<const T*>(&raw);
+    float gv[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) zf[e] = Elem<T>::to_f32(zt[e]);
+    for (int e = 0; e < VEC; ++e) gv[e] = (r < nvalid) ? g_min * sigmoid_fast(eA * Elem<T>::to_f32(zt[e])) : 0.0f;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e)
-      sm.u0.G[r * GP + cv + e] = (r < nvalid) ? g_min * sigmoid_fast(eA * zf[e]) : 0.0f;
-  }
-  if (tid < kChunk) {
-    float bv = 0.f;
-    if (tid < nvalid && beta != nullptr) bv = Elem<T>::to_f32(beta[(int64_t)(b * (int64_t)T_total + tok0 + tid) * H + h]);
-    sm.beta[tid] = bv;
+    for (int e = 0; e < VEC; e += 4)
+      *reinterpret_cast<float4*>(&G[r * GP + cv + e]) = make_float4(gv[e], gv[e + 1], gv[e + 2], gv[e + 3]);
   }
   __syncthreads();
-  if (tid < D) {
-    float s = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < kChunk; ++r) {
-      s += sm.u0.G[r * GP + tid];
-      sm.u0.G[r * GP + tid] = s;
-    }
-  } else if (tid < D + 2 * kChunk) {
-    const int r = (tid - D) & (kChunk - 1);
-    const T* row = (tid - D < kChunk) ? &sm.u1.x.q[r * XP] : &sm.u1.x.k[r * XP];
-    float ss = 0.f;
+  const int ch = tid % D, seg = tid / D;
+  float acc[RPS];
+  float s = 0.f;
 #pragma unroll
-    for (int c = 0; c < D; c += 8) {
-      float x[8];
-      load8_lds<T>(row + c, x);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
-    }
-    const float rn = l2norm ? hw_rsqrt(ss + l2_eps) : 1.0f;
-    if (tid - D < kChunk)
-      sm.rq[r] = rn;
-    else
-      sm.rk[r] = rn;
+  for (int i = 0; i < RPS; ++i) {
+    s += G[(seg * RPS + i) * GP + ch];
+    acc[i] = s;
   }
+  tot[seg * D + ch] = s;
   __syncthreads();
+  float off = 0.f;
+#pragma unroll
+  for (int s2 = 0; s2 < TPC - 1; ++s2)
+    if (s2 < seg) off += tot[s2 * D + ch];
+#pragma unroll
+  for (int i = 0; i < RPS; ++i) G[(seg * RPS + i) * GP + ch] = acc[i] + off;
+  __syncthreads();
+}
+
+// Inverse L2 norm of the lane's row (row n of a 16-row sub-tile) from the
+// diagonal of X X^T on MFMA (bf16 products are exact in fp32; sums in fp32).
+// x[kk] is the lane's raw operand of K-step kk; every lane of the row gets
+// 1 / sqrt(|x|^2 + eps) (1 when l2norm == 0).
+template <typename T, int KS>
+__device__ __forceinline__ float row_inv_norm(const typename Run8<T>::Raw* x, int l2norm, float eps) {
+  const int lane = threadIdx.x & 63, n = lane & 15;
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) acc = mma32(x[kk], x[kk], acc);
+  // lane (n, g) holds rows 4 g .. 4 g + 3 of column n: the diagonal entry of
+  // row n sits in lane (n, n / 4) at index n % 4
+  const int i = n & 3;
+  const float d = (i == 0) ? acc[0] : (i == 1) ? acc[1] : (i == 2) ? acc[2] : acc[3];
+  const float dn = __shfl(d, n + 16 * (n >> 2));
+  return l2norm ? hw_rsqrt(dn + eps) : 1.0f;
 }
 
 }  // namespace kda

@@ -1,5 +1,6 @@
 // Intra-chunk kernel: everything of a 64-token chunk that does not depend on
-// the recurrent state.  One workgroup (4 waves) per (chunk, head, batch).
+// the recurrent state.  One workgroup (4 waves) per (chunk, head, batch);
+// wave i owns the chunk's 16-token sub-tile i.
 //
 // Source: "Kimi K3: KDA, Attention Residuals and Stable LatentMoE"
 // (hs-black.github.io/posts/kimi-k3).  Section 2.1 gives the chunked output
@@ -9,14 +10,15 @@
 // cut into 16-token sub-tiles and, because the K3 decay keeps a sub-tile's
 // cumulative log-decay within (-80, 0), every causal sub-tile block --
 // diagonal blocks included -- is a dense matrix product of decay-scaled
-// factors.  Here each row sub-tile i is anchored at its 8th token,
-// Bi = G[16 i + 7], so both factors of every block stay within e^{+-40}:
-//     A(i, j) = (K_i . e^{G_i - Bi}) (K_j . e^{Bi - G_j})^T.
-// The A products use bf16 MFMA on hi/lo split operands (three products per
-// step) because a plain bf16 product misses the output tolerance; the fp32
-// path uses fp32 MFMA.
+// factors.  Sub-tile i is anchored at its 8th token, B_i = G[16 i + 7], so
+// the factors of every block stay within e^{+-40}:
+//     A(i, i) = (K_i . e^{G_i - B_i}) (K_i . e^{B_i - G_i})^T
+//     A(i, j) = (K_i . e^{G_i - B_i} . e^{B_i - B_j}) (K_j . e^{B_j - G_j})^T,  j < i.
+// Diagonal blocks multiply hi/lo bf16 splits of both factors (three MFMAs per
+// step); off-diagonal blocks, whose entries carry at least one sub-tile of
+// decay, use plain bf16 products.  The fp32 path uses fp32 MFMA throughout.
 //
-// Outputs (one ChunkWs record per chunk):
+// Outputs (one record per chunk, layout in kda_params.hpp):
 //   qg = q^ . Gamma, kg = k^ . Gamma, kdt = (k^ . Gamma_last / Gamma)^T,
 //   tb = T Diag(beta) with T = (I + Diag(beta) StrictTril(A_kk))^{-1},
 //   aq = Tril(A_qk) (diagonal included), gam = Gamma_last.
@@ -27,56 +29,96 @@ namespace kda {
 template <typename T>
 struct APolicy;
 template <>
-struct APolicy<uint16_t> {  // bf16 path: split operands, three MFMAs per step
-  struct Op {
+struct APolicy<uint16_t> {  // bf16 path
+  struct Split {
     bf16x8 hi, lo;
   };
-  static __device__ __forceinline__ Op make(const float* x) {
-    Op o;
+  using Plain = bf16x8;
+  static __device__ __forceinline__ Split split(const float* x) {
+    Split o;
     split8_bf16(x, o.hi, o.lo);
     return o;
   }
-  static __device__ __forceinline__ f32x4 mma(const Op& a, const Op& b, f32x4 acc) {
+  static __device__ __forceinline__ Plain plain(const float* x) { return pack8_bf16(x); }
+  static __device__ __forceinline__ f32x4 mma(const Split& a, const Split& b, f32x4 acc) {
     return mma32_x3(a.hi, a.lo, b.hi, b.lo, acc);
   }
+  static __device__ __forceinline__ f32x4 mma(const Plain& a, const Plain& b, f32x4 acc) { return mma32(a, b, acc); }
+  static __device__ __forceinline__ Plain ld(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 };
 template <>
-struct APolicy<float> {
-  struct Op {
-    f32x8 v;
-  };
-  static __device__ __forceinline__ Op make(const float* x) {
-    Op o;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o.v[j] = x[j];
-    return o;
+struct APolicy<float> {  // fp32 path
+  using Split = f32x8;
+  using Plain = f32x8;
+  static __device__ __forceinline__ f32x8 split(const float* x) {
+    return f32x8{x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
   }
-  static __device__ __forceinline__ f32x4 mma(const Op& a, const Op& b, f32x4 acc) {
-    return mma32(a.v, b.v, acc);
+  static __device__ __forceinline__ f32x8 plain(const float* x) { return split(x); }
+  static __device__ __forceinline__ f32x4 mma(const f32x8& a, const f32x8& b, f32x4 acc) { return mma32(a, b, acc); }
+  static __device__ __forceinline__ f32x8 ld(const float* p) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    return f32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   }
 };
 
 __device__ __forceinline__ int slot_pos64(int s) { return (s & 32) + slot_pos(s & 31); }
 __device__ __forceinline__ int slot_row64(int p) { return (p & 32) + slot_row(p & 31); }
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// LDS regions, reused across phases:
+//   R0: G [64][D+4] fp32             -> later L = Diag(beta) StrictTril(A_kk) [64][68]
+//   R1: KC [64][D+pad] (col factors) -> later Tril(A_qk) staging [64][68] fp32, then scratch
+//   R2: Kd^T staging [D][64+pad]     -> later the UT inverse [64][68] fp32
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) {
-  __shared__ ChunkSmem<T, D> sm;
-  constexpr int GP = ChunkSmem<T, D>::GP;
-  constexpr int XP = ChunkSmem<T, D>::XP;
-  constexpr int LP = ChunkSmem<T, D>::LP;
+struct IntraLds {
+  static constexpr int ES = sizeof(T);
+  static constexpr int GP = D + 4;
+  static constexpr int KP = D + 16 / ES;
+  static constexpr int TP = 64 + 16 / ES;
+  static constexpr int LP = 68;
+  static constexpr int R0 = cmax(64 * GP * 4, 64 * LP * 4);
+  static constexpr int R1 = cmax(64 * KP * ES, 64 * LP * 4);
+  static constexpr int R2 = cmax(D * TP * ES, 64 * LP * 4);
+  static constexpr int O1 = R0;
+  static constexpr int O2 = O1 + R1;
+  static constexpr int OE = O2 + R2;            // e^{B_i - B_j}, 6 pairs i > j  [6][D]
+  static constexpr int OEB = OE + 6 * D * 4;    // e^{B_i}                      [4][D]
+  static constexpr int OEL = OEB + 4 * D * 4;   // e^{G_last - B_i}             [4][D]
+  static constexpr int OTOT = OEL + 4 * D * 4;  // cumsum segment totals        [256]
+  static constexpr int OBETA = OTOT + 256 * 4;  // beta                         [64]
+  static constexpr int BYTES = OBETA + 64 * 4;
+};
+
+// index of the pair (i, j), i > j, in 0..5
+__device__ __forceinline__ int pair_index(int i, int j) { return (i * (i - 1)) / 2 + j; }
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void kda_intra_kernel(const IntraParams p) {
+  using L = IntraLds<T, D>;
   using AP = APolicy<T>;
+  using R8 = Run8<T>;
+  constexpr int KS = D / 32;
+  constexpr int GP = L::GP, KP = L::KP, TP = L::TP, LP = L::LP;
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  float* G = reinterpret_cast<float*>(lds);
+  T* KC = reinterpret_cast<T*>(lds + L::O1);
+  T* KdT = reinterpret_cast<T*>(lds + L::O2);
+  float* Et = reinterpret_cast<float*>(lds + L::OE);
+  float* eB = reinterpret_cast<float*>(lds + L::OEB);
+  float* eL = reinterpret_cast<float*>(lds + L::OEL);
+  float* tot = reinterpret_cast<float*>(lds + L::OTOT);
+  float* betas = reinterpret_cast<float*>(lds + L::OBETA);
 
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g4 = lane >> 4;
   const int tok0 = p.t0 + c * kChunk;
   const int nvalid = min(kChunk, p.T - tok0);
+  const int64_t tok_stride = (int64_t)p.H * D;
+  const int64_t row0 = ((int64_t)b * p.T + tok0) * p.H * D + (int64_t)h * D;  // (token 0 of chunk, h)
   const int64_t rec = ((int64_t)b * p.H + h) * p.nc + c;
-
-  chunk_prologue<T, D>(sm, static_cast<const T*>(p.q), static_cast<const T*>(p.k),
-                       static_cast<const T*>(p.z), static_cast<const T*>(p.beta), p.A[h], b, h, p.T,
-                       p.H, tok0, nvalid, p.g_min, p.l2_eps, p.l2norm);
-
   constexpr RecLayout RL = rec_layout((int)sizeof(T), D);
   char* recp = p.ws.base + rec * p.ws.rec_bytes;
   T* qg = reinterpret_cast<T*>(recp + RL.qg);
@@ -86,97 +128,138 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) 
   T* aqh = reinterpret_cast<T*>(recp + RL.aqh);
   T* aql = reinterpret_cast<T*>(recp + RL.aql);
   float* gam = reinterpret_cast<float*>(recp + RL.gam);
-  const float* G = sm.u0.G;
 
-  // ---- factor tensors for the state scan (columns in slot order) ----------
-  for (int idx = tid; idx < kChunk * (D / 8); idx += 256) {
-    const int r = idx / (D / 8), pg = idx % (D / 8);
-    const int cb = 32 * (pg >> 2);
-    float xq[8], xk[8];
-    const float sq = sm.rq[r] * p.q_scale, sk = sm.rk[r];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int ch = cb + slot_row(8 * (pg & 3) + j);
-      const float e = hw_exp2(G[r * GP + ch] * kLog2e);
-      xq[j] = Elem<T>::to_f32(sm.u1.x.q[r * XP + ch]) * sq * e;
-      xk[j] = Elem<T>::to_f32(sm.u1.x.k[r * XP + ch]) * sk * e;
-    }
-    store8<T>(qg + r * D + 8 * pg, xq);
-    store8<T>(kg + r * D + 8 * pg, xk);
-  }
-  for (int idx = tid; idx < D * 8; idx += 256) {
-    const int ch = idx >> 3, pg = idx & 7;  // 8 neighbouring threads fill one kdt row
-    const float glast = G[(kChunk - 1) * GP + ch];
-    float x[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = slot_row64(8 * pg + j);
-      x[j] = Elem<T>::to_f32(sm.u1.x.k[r * XP + ch]) * sm.rk[r] * hw_exp2((glast - G[r * GP + ch]) * kLog2e);
-    }
-    store8<T>(kdt + ch * kChunk + 8 * pg, x);
-  }
-  if (tid < D) gam[tid] = hw_exp2(G[(kChunk - 1) * GP + tid] * kLog2e);
-
-  // ---- sub-tile products A_kk(i, j), A_qk(i, j), j <= i; wave i = row tile --
-  const int n = lane & 15, g4 = lane >> 4;
+  // ---- this wave's sub-tile rows of q and k, as MFMA operands (issued first) --
   const int ti = wave;
-  const int r = 16 * ti + n;
-  const int ra = 16 * ti + 7;  // anchor row of this row tile
-  f32x4 akk[4], aqk[4];
-#pragma unroll
-  for (int jt = 0; jt < 4; ++jt) akk[jt] = aqk[jt] = zero4();
+  const int r = 16 * ti + n;  // row of this lane in the chunk
+  const bool rvalid = r < nvalid;
+  typename R8::Raw qraw[KS], kraw[KS];
   {
-    const float sq = sm.rq[r] * p.q_scale, sk = sm.rk[r];
+    const T* qrow = static_cast<const T*>(p.q) + row0 + min(r, nvalid - 1) * tok_stride;
+    const T* krow = static_cast<const T*>(p.k) + row0 + min(r, nvalid - 1) * tok_stride;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      const int c0 = 32 * kk + 8 * g4;
-      float gr[8], ga[8], xq[8], xk[8];
-      load8_lds<float>(&G[r * GP + c0], gr);
-      load8_lds<float>(&G[ra * GP + c0], ga);
-      load8_lds<T>(&sm.u1.x.q[r * XP + c0], xq);
-      load8_lds<T>(&sm.u1.x.k[r * XP + c0], xk);
+    for (int kk = 0; kk < KS; ++kk) {
+      qraw[kk] = R8::load(qrow, kk, g4);
+      kraw[kk] = R8::load(krow, kk, g4);
+    }
+  }
+  if (tid < kChunk)
+    betas[tid] = (tid < nvalid) ? Elem<T>::to_f32(static_cast<const T*>(p.beta)[((int64_t)b * p.T + tok0 + tid) * p.H + h])
+                                : 0.0f;
+
+  // ---- decay and its chunk-local cumulative sum G ----------------------------
+  decay_cumsum<T, D>(G, tot, static_cast<const T*>(p.z) + row0, tok_stride, nvalid, p.A[h], p.g_min);
+
+  // ---- per-chunk tables: e^{B_i}, e^{G_last - B_i}, e^{B_i - B_j}, Gamma_last --
+  for (int idx = tid; idx < 15 * D; idx += 256) {
+    const int item = idx / D, ch = idx % D;
+    const float gl = G[63 * GP + ch];
+    if (item < 4) {
+      eB[item * D + ch] = hw_exp(G[(16 * item + 7) * GP + ch]);
+    } else if (item < 8) {
+      const int i = item - 4;
+      eL[i * D + ch] = hw_exp(gl - G[(16 * i + 7) * GP + ch]);
+    } else if (item < 14) {
+      const int pi = item - 8;  // pair index -> (i, j)
+      const int i = (pi < 1) ? 1 : (pi < 3) ? 2 : 3;
+      const int j = pi - pair_index(i, 0);
+      Et[pi * D + ch] = hw_exp(G[(16 * i + 7) * GP + ch] - G[(16 * j + 7) * GP + ch]);
+    } else {
+      gam[ch] = hw_exp(gl);
+    }
+  }
+
+  // ---- own sub-tile: norms, factors, record rows, diagonal blocks -------------
+  // (all lanes take part in the norm products; rows past the end get 0)
+  const float nq = row_inv_norm<T, KS>(qraw, p.l2norm, p.l2_eps);
+  const float nk = row_inv_norm<T, KS>(kraw, p.l2norm, p.l2_eps);
+  const float rq = rvalid ? nq * p.q_scale : 0.0f;
+  const float rk = rvalid ? nk : 0.0f;
+  __syncthreads();  // tables ready
+  float KR[KS][8], QR[KS][8];  // row factors (kept for the off-diagonal blocks)
+  f32x4 akk_d = zero4(), aqk_d = zero4();
+  const int ra = 16 * ti + 7;
+  const int rpos = slot_pos64(r);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float e = hw_exp2((gr[j] - ga[j]) * kLog2e);
-        xq[j] *= sq * e;
-        xk[j] *= sk * e;
-      }
-      const typename AP::Op oq = AP::make(xq), ok = AP::make(xk);
+  for (int kk = 0; kk < KS; ++kk) {
+    float gr[8], ga[8], eb[8], el[8];
+    lds_run8(G + r * GP, kk, g4, gr);
+    lds_run8(G + ra * GP, kk, g4, ga);
+    lds_run8(eB + ti * D, kk, g4, eb);
+    lds_run8(eL + ti * D, kk, g4, el);
+    float kc[8], xq[8], xk[8], xd[8];
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        if (jt <= ti) {
-          const int s = 16 * jt + n;
-          float gs[8], y[8];
-          load8_lds<float>(&G[s * GP + c0], gs);
-          load8_lds<T>(&sm.u1.x.k[s * XP + c0], y);
-          const float ss = sm.rk[s];
+    for (int j = 0; j < 8; ++j) {
+      const float d = (gr[j] - ga[j]) * kLog2e;
+      const float rf = hw_exp2(d);   // e^{G_r - B_i}
+      const float cf = hw_exp2(-d);  // e^{B_i - G_r}
+      const float qh = R8::get(qraw[kk], j) * rq;
+      const float kh = R8::get(kraw[kk], j) * rk;
+      KR[kk][j] = kh * rf;
+      QR[kk][j] = qh * rf;
+      kc[j] = kh * cf;
+      xq[j] = qh * (rf * eb[j]);  // q^ . Gamma
+      xk[j] = kh * (rf * eb[j]);  // k^ . Gamma
+      xd[j] = kc[j] * el[j];      // k^ . Gamma_last / Gamma
+    }
+    store8<T>(qg + r * D + 32 * kk + 8 * g4, xq);
+    store8<T>(kg + r * D + 32 * kk + 8 * g4, xk);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) y[j] *= ss * hw_exp2((ga[j] - gs[j]) * kLog2e);
-          const typename AP::Op oy = AP::make(y);
-          akk[jt] = AP::mma(ok, oy, akk[jt]);
-          aqk[jt] = AP::mma(oq, oy, aqk[jt]);
+    for (int j = 0; j < 8; ++j) KdT[lane_ch(kk, g4, j) * TP + rpos] = Elem<T>::from_f32(xd[j]);
+    store8<T>(KC + r * KP + 32 * kk + 8 * g4, kc);  // column factors for later sub-tiles
+    const typename AP::Split sk = AP::split(KR[kk]), sq = AP::split(QR[kk]), sc = AP::split(kc);
+    akk_d = AP::mma(sk, sc, akk_d);
+    aqk_d = AP::mma(sq, sc, aqk_d);
+  }
+  __syncthreads();  // KC of every sub-tile ready
+
+  // ---- off-diagonal blocks (ti, jt), jt < ti: plain products -----------------
+  f32x4 akk[3], aqk[3];
+#pragma unroll
+  for (int jt = 0; jt < 3; ++jt) {
+    akk[jt] = aqk[jt] = zero4();
+    if (jt < ti) {
+      const int pi = pair_index(ti, jt);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        float e8[8], xk[8], xq[8];
+        lds_run8(Et + pi * D, kk, g4, e8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          xk[j] = KR[kk][j] * e8[j];
+          xq[j] = QR[kk][j] * e8[j];
         }
+        const typename AP::Plain bop = AP::ld(KC + (16 * jt + n) * KP + 32 * kk + 8 * g4);
+        akk[jt] = AP::mma(AP::plain(xk), bop, akk[jt]);
+        aqk[jt] = AP::mma(AP::plain(xq), bop, aqk[jt]);
       }
     }
   }
-  __syncthreads();  // q, k, G no longer read: their LDS becomes L and Tm
+  __syncthreads();  // G and KC no longer read
 
-  // L = Diag(beta) StrictTril(A_kk) into LDS; Tril(A_qk) staged in LDS (slot
-  // order) for coalesced stores of its hi / lo parts.
-  float* Aq = sm.u0.Tm;
+  // ---- L = Diag(beta) StrictTril(A_kk) (over G), Tril(A_qk) staging (over KC) --
+  float* Lm = reinterpret_cast<float*>(lds);
+  float* Aq = reinterpret_cast<float*>(lds + L::O1);
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int rr = 16 * ti + 4 * g4 + ii;
       const int s = 16 * jt + n;
-      const float vkk = (jt <= ti && s < rr) ? sm.beta[rr] * akk[jt][ii] : 0.0f;
-      const float vqk = (jt <= ti && s <= rr) ? aqk[jt][ii] : 0.0f;
-      sm.u1.L[rr * LP + s] = vkk;
+      float vkk = 0.f, vqk = 0.f;
+      if (jt == ti) {
+        vkk = (s < rr) ? akk_d[ii] : 0.f;
+        vqk = (s <= rr) ? aqk_d[ii] : 0.f;
+      } else if (jt < ti) {
+        vkk = akk[jt < 3 ? jt : 0][ii];
+        vqk = aqk[jt < 3 ? jt : 0][ii];
+      }
+      Lm[rr * LP + s] = betas[rr] * vkk;
       Aq[rr * LP + slot_pos64(s)] = vqk;
     }
   }
   __syncthreads();
+  // Tril(A_qk) hi / lo and Kd^T to the record, 16-byte stores
   for (int idx = tid; idx < kChunk * 8; idx += 256) {
     const int rr = idx >> 3, pg = idx & 7;
     float x[8], lo[8];
@@ -189,11 +272,19 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) 
     }
     store8<T>(aqh + rr * kChunk + 8 * pg, x);
   }
-  __syncthreads();
+  {
+    constexpr int UPR = 64 * (int)sizeof(T) / 16;  // 16-byte units per Kd^T row
+    for (int u = tid; u < D * UPR; u += 256) {
+      const int rr = u / UPR, cu = u % UPR;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(kdt) + rr * 64 * sizeof(T) + cu * 16) =
+          *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(KdT) + rr * TP * sizeof(T) + cu * 16);
+    }
+  }
+  __syncthreads();  // R1 and R2 free: UT inverse in R2, scratch in R1
 
   // ---- T = (I + L)^{-1}: diagonal 16x16 blocks by forward substitution ------
-  float* Tm = sm.u0.Tm;
-  const float* L = sm.u1.L;
+  float* Tm = reinterpret_cast<float*>(lds + L::O2);
+  float* P = reinterpret_cast<float*>(lds + L::O1);  // [3][16 * 17]
   if (wave == 0) {
     const int ib = lane >> 4, col = lane & 15;
     float x[16];
@@ -201,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) 
     for (int rr = 0; rr < 16; ++rr) {
       float acc = (rr == col) ? 1.0f : 0.0f;
 #pragma unroll
-      for (int ss = 0; ss < rr; ++ss) acc -= L[(16 * ib + rr) * LP + 16 * ib + ss] * x[ss];
+      for (int ss = 0; ss < rr; ++ss) acc -= Lm[(16 * ib + rr) * LP + 16 * ib + ss] * x[ss];
       x[rr] = acc;
     }
 #pragma unroll
@@ -228,13 +319,13 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) 
         for (int bm = bj; bm < bi; ++bm) {
 #pragma unroll
           for (int m = 0; m < 16; ++m) {
-            const float l = L[(16 * bi + pr) * LP + 16 * bm + m];
+            const float l = Lm[(16 * bi + pr) * LP + 16 * bm + m];
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] += l * Tm[(16 * bm + m) * LP + 16 * bj + pc + e];
           }
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.P[wave][pr * 17 + pc + e] = acc[e];
+        for (int e = 0; e < 4; ++e) P[wave * (16 * 17) + pr * 17 + pc + e] = acc[e];
       }
       __syncthreads();
       if (active) {
@@ -243,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) 
         for (int m = 0; m < 16; ++m) {
           const float t = Tm[(16 * bi + pr) * LP + 16 * bi + m];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] += t * sm.P[wave][m * 17 + pc + e];
+          for (int e = 0; e < 4; ++e) acc[e] += t * P[wave * (16 * 17) + m * 17 + pc + e];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) Tm[(16 * bi + pr) * LP + 16 * bj + pc + e] = -acc[e];
@@ -259,7 +350,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(const IntraParams p) 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int s = slot_row64(8 * pg + j);
-      x[j] = Tm[rr * LP + s] * sm.beta[s];
+      x[j] = Tm[rr * LP + s] * betas[s];
     }
     store8<T>(tb + rr * kChunk + 8 * pg, x);
   }
