@@ -59,13 +59,13 @@ hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_
 }
 
 // ---- pre-pass diagnostic: chunk-local cumulative log-decay and norms -------
-// Runs the same device routines as the intra-chunk kernel's prologue.
+// Runs the same device routines as the intra-chunk kernel's prologue: wave i
+// forms sub-tile i's decay prefix in registers; the sub-tile totals are then
+// added up across the chunk through LDS.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void kda_prepass_kernel(const PrepassParams p) {
-  constexpr int GP = D + 4;
   constexpr int KS = D / 32;
-  __shared__ __attribute__((aligned(16))) float G[64 * GP];
-  __shared__ float tot[256];
+  __shared__ __attribute__((aligned(16))) float tot[4 * D];
   using R8 = Run8<T>;
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -74,27 +74,44 @@ __global__ __launch_bounds__(256) void kda_prepass_kernel(const PrepassParams p)
   const int nvalid = min(kChunk, p.T - tok0);
   const int64_t tok_stride = (int64_t)p.H * D;
   const int64_t row0 = ((int64_t)b * p.T + tok0) * p.H * D + (int64_t)h * D;
-  decay_cumsum<T, D>(G, tot, static_cast<const T*>(p.z) + row0, tok_stride, nvalid, p.A[h], p.g_min);
-  for (int idx = tid; idx < nvalid * D; idx += 256) {
-    const int r = idx / D, ch = idx % D;
-    p.G[row0 + r * tok_stride + ch] = G[r * GP + ch];
-  }
-  // norms of sub-tile `wave` (every lane takes part in the products)
   const int r = 16 * wave + n;
-  typename R8::Raw qraw[KS], kraw[KS];
-  const T* qrow = static_cast<const T*>(p.q) + row0 + min(r, nvalid - 1) * tok_stride;
-  const T* krow = static_cast<const T*>(p.k) + row0 + min(r, nvalid - 1) * tok_stride;
+  const bool rvalid = r < nvalid;
+  const int64_t rowp = row0 + min(r, nvalid - 1) * tok_stride;
+  typename R8::Raw qraw[KS], kraw[KS], zraw[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
-    qraw[kk] = R8::load(qrow, kk, g4);
-    kraw[kk] = R8::load(krow, kk, g4);
+    qraw[kk] = R8::load(static_cast<const T*>(p.q) + rowp, kk, g4);
+    kraw[kk] = R8::load(static_cast<const T*>(p.k) + rowp, kk, g4);
+    zraw[kk] = R8::load(static_cast<const T*>(p.z) + rowp, kk, g4);
   }
+  float P[KS][8];
+  subtile_decay_prefix<T, KS>(zraw, p.A[h], p.g_min, rvalid, P);
+  if (n == 15)
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) put_run8(tot + wave * D, kk, g4, P[kk]);
   const float rq = row_inv_norm<T, KS>(qraw, p.l2norm, p.l2_eps);
   const float rk = row_inv_norm<T, KS>(kraw, p.l2norm, p.l2_eps);
-  if (g4 == 0 && r < nvalid) {
-    const int64_t ri = ((int64_t)b * p.T + tok0 + r) * p.H + h;
-    p.rq[ri] = rq;
-    p.rk[ri] = rk;
+  __syncthreads();
+  if (rvalid) {
+    float* Grow = p.G + row0 + r * tok_stride;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      float off[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int w = 0; w < wave; ++w) {
+        float t[8];
+        lds_run8(tot + w * D, kk, g4, t);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) off[j] += t[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) off[j] += P[kk][j];
+      put_run8(Grow, kk, g4, off);
+    }
+    if (g4 == 0) {
+      const int64_t ri = ((int64_t)b * p.T + tok0 + r) * p.H + h;
+      p.rq[ri] = rq;
+      p.rk[ri] = rk;
+    }
   }
 }
 

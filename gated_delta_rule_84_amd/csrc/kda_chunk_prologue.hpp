@@ -1,6 +1,9 @@
-// Chunk prologue shared by the intra-chunk kernel and the pre-pass kernel:
-// the K3 bounded log-decay of a 64-token chunk, its chunk-local inclusive
-// cumulative sum, and the q / k inverse L2 norms of one 16-token sub-tile.
+// Chunk prologue shared by the intra-chunk kernel and the pre-pass kernel.
+// One wave owns one 16-token sub-tile; lane (n, g) holds row n of the
+// sub-tile at the channels of its MFMA operand slots.  From those rows it
+// forms the K3 bounded log-decay, its inclusive prefix within the sub-tile
+// (across the 16 lanes of a row group, in registers) and the q / k inverse
+// L2 norms.
 //
 // Source: "Kimi K3: KDA, Attention Residuals and Stable LatentMoE"
 // (hs-black.github.io/posts/kimi-k3), section 2.1 (L2Norm on q and k) and
@@ -43,12 +46,17 @@ struct Run8<float> {
   static __device__ __forceinline__ float get(const Raw& r, int j) { return r[j]; }
 };
 
-// 8 fp32 of a row in a lane's channel set, from an LDS row (two float4 reads).
+// 8 fp32 of a channel-indexed row in a lane's channel set (two float4 reads).
 __device__ __forceinline__ void lds_run8(const float* row, int kk, int g, float* x) {
   const float4 a = *reinterpret_cast<const float4*>(row + 32 * kk + 4 * g);
   const float4 b = *reinterpret_cast<const float4*>(row + 32 * kk + 16 + 4 * g);
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+// ... and the inverse: write a lane's 8 channel values into a channel-indexed row.
+__device__ __forceinline__ void put_run8(float* row, int kk, int g, const float* x) {
+  *reinterpret_cast<float4*>(row + 32 * kk + 4 * g) = make_float4(x[0], x[1], x[2], x[3]);
+  *reinterpret_cast<float4*>(row + 32 * kk + 16 + 4 * g) = make_float4(x[4], x[5], x[6], x[7]);
 }
 
 // Store 8 fp32 values as 8 elements of T (16 or 32 bytes, aligned).
@@ -68,55 +76,49 @@ __device__ __forceinline__ void store8<float>(float* p, const float* x) {
   *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
 }
 
-// 256 threads.  G[64][D + 4] (LDS, fp32) receives, per channel, the
-// inclusive cumulative sum over the chunk's tokens of
-//     g = g_min * Sigmoid(e^{A_h} z)      (0 for rows r >= nvalid),
-// summed as per-segment prefixes plus the totals of the earlier segments
-// (256 / D segments per channel).  tot needs 256 floats.  Ends after a
-// barrier with G complete.  zrow0 points at (token 0 of the chunk, head h,
-// channel 0); tokens are tok_stride elements apart.
-template <typename T, int D>
-__device__ __forceinline__ void decay_cumsum(float* G, float* tot, const T* __restrict__ zrow0, int64_t tok_stride,
-                                             int nvalid, float A_h, float g_min) {
-  constexpr int GP = D + 4;
-  constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int VPR = D / VEC;
-  constexpr int TPC = 256 / D;   // threads per channel
-  constexpr int RPS = 64 / TPC;  // rows per segment
-  const int tid = threadIdx.x;
-  const float eA = hw_exp(A_h);
+// Store 4 fp32 values as 4 elements of T (8 or 16 bytes, aligned).
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const f32x4& x);
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const f32x4& x) {
+  uint2 w;
+  w.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
+  w.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+  *reinterpret_cast<uint2*>(p) = w;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const f32x4& x) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+// x + (value of the lane S places below in the same 16-lane row; 0 past the
+// row's start): one step of an inclusive prefix sum across a row group.
+template <int S>
+__device__ __forceinline__ float add_row_shr(float x) {
+  const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + S, 0xf, 0xf, true);
+  return x + __builtin_bit_cast(float, y);
+}
+
+// Decay of this lane's row and channels, and its inclusive prefix over the
+// sub-tile's rows 0..n (lanes n of the lane's row group):
+//     P[kk][j] = sum_{m <= n} g(m, lane_ch(kk, g, j)),  g = g_min Sigmoid(e^{A_h} z)
+// Rows past the end of the sequence (valid == false) contribute g = 0.
+template <typename T, int KS>
+__device__ __forceinline__ void subtile_decay_prefix(const typename Run8<T>::Raw* z, float A_h, float g_min,
+                                                     bool valid, float (&P)[KS][8]) {
+  const float c1 = -hw_exp(A_h) * kLog2e;  // Sigmoid(e^A z) = 1 / (1 + 2^{c1 z})
+  const float gm = valid ? g_min : 0.0f;
 #pragma unroll
-  for (int it = 0; it < (64 * VPR) / 256; ++it) {
-    const int idx = tid + 256 * it;
-    const int r = idx / VPR;
-    const int cv = (idx % VPR) * VEC;
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(zrow0 + min(r, nvalid - 1) * tok_stride + cv);
-    const T* zt = reinterpret_cast<const T*>(&raw);
-    float gv[VEC];
+  for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) gv[e] = (r < nvalid) ? g_min * sigmoid_fast(eA * Elem<T>::to_f32(zt[e])) : 0.0f;
-#pragma unroll
-    for (int e = 0; e < VEC; e += 4)
-      *reinterpret_cast<float4*>(&G[r * GP + cv + e]) = make_float4(gv[e], gv[e + 1], gv[e + 2], gv[e + 3]);
-  }
-  __syncthreads();
-  const int ch = tid % D, seg = tid / D;
-  float acc[RPS];
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < RPS; ++i) {
-    s += G[(seg * RPS + i) * GP + ch];
-    acc[i] = s;
-  }
-  tot[seg * D + ch] = s;
-  __syncthreads();
-  float off = 0.f;
-#pragma unroll
-  for (int s2 = 0; s2 < TPC - 1; ++s2)
-    if (s2 < seg) off += tot[s2 * D + ch];
-#pragma unroll
-  for (int i = 0; i < RPS; ++i) G[(seg * RPS + i) * GP + ch] = acc[i] + off;
-  __syncthreads();
+    for (int j = 0; j < 8; ++j) {
+      float x = gm * hw_rcp(1.0f + hw_exp2(c1 * Run8<T>::get(z[kk], j)));
+      x = add_row_shr<1>(x);
+      x = add_row_shr<2>(x);
+      x = add_row_shr<4>(x);
+      x = add_row_shr<8>(x);
+      P[kk][j] = x;
+    }
 }
 
 // Inverse L2 norm of the lane's row (row n of a 16-row sub-tile) from the
