@@ -1,12 +1,20 @@
 // Inter-chunk state scan with the fused output gate.  One workgroup per
-// (batch, head) with D / 16 waves; wave w owns value columns 16 w .. 16 w + 15
-// and keeps its d_k x 16 slice of the fp32 state S in MFMA accumulators for
-// the whole sequence.  The columns of S evolve independently, so waves never
-// exchange state.  Per chunk, the chunk record written by the intra-chunk
-// kernel and the head's 64 x D slab of V are loaded into registers while the
-// previous chunk is computed, then committed to LDS.  The chunk's outputs go
-// through an LDS tile so that the RMSNorm over a row and the stores of o / y
-// are done row by row with contiguous 16-byte stores.
+// (batch, head).  Each compute wave owns a set of value columns and keeps its
+// d_k x columns slice of the fp32 state S in MFMA accumulators for the whole
+// sequence; the columns of S evolve independently, so waves never exchange
+// state.  The chunk record written by the intra-chunk kernel and the head's
+// 64 x D slab of V are staged into LDS (padded rows) one chunk ahead; the
+// chunk's outputs go through an LDS tile so that the RMSNorm over a row and
+// the stores of o / y are done row by row with contiguous 16-byte stores.
+//
+// Two organisations of the workgroup:
+//  * specialised (whenever the LDS image fits): D / 32 compute waves with 32
+//    columns each run only the MFMA chain, while as many helper waves load
+//    the next chunk's record, V and this chunk's gate logits into registers,
+//    turn the previous chunk's output tile into o / y, and commit the loads to
+//    LDS between two barriers;
+//  * serial (fp32 at d = 128): D / 16 waves with 16 columns each do all of it
+//    in turn.
 //
 // Source: "Kimi K3: KDA, Attention Residuals and Stable LatentMoE"
 // (hs-black.github.io/posts/kimi-k3).  Section 2.1: per chunk with entry
@@ -21,6 +29,8 @@
 // uses hi/lo parts on both sides; S stays fp32.  The fp32 path uses fp32 MFMA.
 #include "kda_common.hpp"
 #include "kda_params.hpp"
+
+#include <type_traits>
 
 namespace kda {
 
@@ -40,8 +50,8 @@ struct ScanOps<uint16_t> {
     acc_pair_split(a, b, r.hi, r.lo);
     return r;
   }
-  static __device__ __forceinline__ f32x4 mma_prec(const char* ah, const char* al, const Prec& b, f32x4 acc) {
-    return mma32_x3(ld(ah), ld(al), b.hi, b.lo, acc);
+  static __device__ __forceinline__ f32x4 mma_prec(const V8& ah, const V8& al, const Prec& b, f32x4 acc) {
+    return mma32_x3(ah, al, b.hi, b.lo, acc);
   }
   // a (bf16) times a split operand: a * hi + a * lo
   static __device__ __forceinline__ f32x4 mma_split_b(const V8& a, const Prec& b, f32x4 acc) {
@@ -66,8 +76,8 @@ struct ScanOps<float> {
   static __device__ __forceinline__ Prec prec_from_acc(const f32x4& a, const f32x4& b) {
     return Prec{acc_pair_to_f32(a, b)};
   }
-  static __device__ __forceinline__ f32x4 mma_prec(const char* ah, const char*, const Prec& b, f32x4 acc) {
-    return mma32(ld(ah), b.v, acc);
+  static __device__ __forceinline__ f32x4 mma_prec(const V8& ah, const V8&, const Prec& b, f32x4 acc) {
+    return mma32(ah, b.v, acc);
   }
   static __device__ __forceinline__ f32x4 mma_split_b(const V8& a, const Prec& b, f32x4 acc) {
     return mma32(a, b.v, acc);
@@ -116,9 +126,8 @@ struct ScanLds {
 };
 
 // Record byte offset of 16-byte unit u -> byte offset in the padded LDS image.
-template <typename T, int D>
+template <typename L, int D>
 __device__ __forceinline__ int lds_offset_of_unit(int u) {
-  using L = ScanLds<T, D>;
   constexpr RecLayout RL = L::RL;
   constexpr int RQ = D * L::ES;   // bytes per row of qg / kg
   constexpr int RK = 64 * L::ES;  // bytes per row of the 64-wide arrays
@@ -151,7 +160,7 @@ __device__ __forceinline__ void store16(void* dst, const float* x, int out_f32) 
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(4 * D, 1) void kda_scan_kernel(const ScanParams p) {
+__global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanParams p) {
   using Ops = ScanOps<T>;
   using V8 = typename Ops::V8;
   using L = ScanLds<T, D>;
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_kernel(const ScanParams p) 
   for (int i = 0; i < L::PER_THREAD; ++i) {
     const int u = tid + NT * i;
     if (u < L::REC_UNITS) {
-      lofs[i] = lds_offset_of_unit<T, D>(u);
+      lofs[i] = lds_offset_of_unit<ScanLds<T, D>, D>(u);
     } else {
       const int vu = u - L::REC_UNITS;
       lofs[i] = L::VS + (vu / VPR) * L::PQ + (vu % VPR) * 16;
@@ -323,7 +332,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_kernel(const ScanParams p) 
 #pragma unroll
       for (int kk = 0; kk <= (mt >> 1); ++kk) {
         const int off = (16 * mt + n) * L::PK + (32 * kk + 8 * g4) * L::ES;
-        O[mt] = Ops::mma_prec(aqh + off, aql + off, Up[kk], O[mt]);
+        O[mt] = Ops::mma_prec(Ops::ld(aqh + off), Ops::ld(aql + off), Up[kk], O[mt]);
       }
 
     // S <- Diag(Gamma_last) S + Kd^T U'
@@ -397,14 +406,357 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_kernel(const ScanParams p) 
     for (int i = 0; i < 4; ++i) so[(16 * mt + 4 * g4 + i) * D + col] = S[mt][i];
 }
 
-hipError_t launch_scan(const ScanParams& p, int D, int in_f32, hipStream_t s) {
-  const dim3 grid(p.H, p.B), block(4 * D);
-  if (in_f32) {
-    if (D == 64) hipLaunchKernelGGL((kda_scan_kernel<float, 64>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((kda_scan_kernel<float, 128>), grid, block, 0, s, p);
+
+// ---- specialised workgroup: compute waves + helper waves -------------------
+// LDS: the padded record image (as above), the V slab of the current chunk,
+// the gate-logit slab of the previous chunk, the previous chunk's fp32 output
+// tile.  NCW compute waves (32 columns each) and as many helper waves.
+template <typename T, int D>
+struct WsLds {
+  static constexpr int ES = sizeof(T);
+  static constexpr int NCW = D / 32;           // compute waves
+  static constexpr int NHW = NCW;              // helper waves
+  static constexpr int NT = 64 * (NCW + NHW);  // threads
+  static constexpr int NH = 64 * NHW;          // helper threads
+  static constexpr int PQ = D * ES + 16;
+  static constexpr int PK = 64 * ES + 16;
+  static constexpr int QG = 0;
+  static constexpr int KG = QG + 64 * PQ;
+  static constexpr int KDT = KG + 64 * PQ;
+  static constexpr int TB = KDT + D * PK;
+  static constexpr int AQH = TB + 64 * PK;
+  static constexpr int AQL = AQH + 64 * PK;
+  static constexpr int GAM = AQL + (ES == 2 ? 64 * PK : 0);
+  static constexpr int REC = GAM + 4 * D;
+  static constexpr int VS = REC;               // V slab   [64][PQ]
+  static constexpr int GS = VS + 64 * PQ;      // gate slab [64][PQ]
+  static constexpr int PO = D + 4;
+  static constexpr int OT = GS + 64 * PQ;      // output tile [64][PO] fp32
+  static constexpr int BYTES = OT + 64 * PO * 4;
+  static constexpr RecLayout RL = rec_layout(ES, D);
+  static constexpr int REC_UNITS = (RL.gam + 4 * D) / 16;
+  static constexpr int SLAB_UNITS = 64 * D * ES / 16;
+  static constexpr int UNITS = REC_UNITS + 2 * SLAB_UNITS;
+  static constexpr int PER_THREAD = (UNITS + NH - 1) / NH;
+  static constexpr int FULL = UNITS / NH;
+  static constexpr int TPR = NH / 64;          // helper threads per output row
+  static constexpr int EC = D / TPR;           // columns per helper thread
+  // the specialised organisation is used when its image fits in LDS and the
+  // staging registers of a helper thread stay modest
+  static constexpr bool FITS = BYTES <= 160 * 1024 && PER_THREAD <= 40;
+};
+
+template <typename T, int D, bool OUT_F32>
+__global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const ScanParams p) {
+  using Ops = ScanOps<T>;
+  using V8 = typename Ops::V8;
+  using L = WsLds<T, D>;
+  using OutT = typename std::conditional<OUT_F32, float, uint16_t>::type;
+  constexpr int MT = D / 16;
+  constexpr int KS = D / 32;
+  constexpr int NCT = 2;  // 16-column tiles per compute wave
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g4 = lane >> 4;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int64_t bh = (int64_t)b * p.H + h;
+  const int64_t tok_stride = (int64_t)p.H * D;
+  const int64_t head_base = ((int64_t)b * p.T * p.H + h) * D;
+  float* otile = reinterpret_cast<float*>(lds + L::OT);
+
+  if (wave < L::NCW) {
+    // ======================= compute waves =======================
+    const int col0 = 32 * wave + n;  // column of tile nt: col0 + 16 nt
+    f32x4 S[MT][NCT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NCT; ++nt) S[mt][nt] = zero4();
+    if (p.S_in != nullptr) {
+      const float* s0 = p.S_in + bh * D * D;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NCT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[mt][nt][i] = s0[(16 * mt + 4 * g4 + i) * D + col0 + 16 * nt];
+    }
+    const char* qg = lds + L::QG;
+    const char* kg = lds + L::KG;
+    const char* kdt = lds + L::KDT;
+    const char* tb = lds + L::TB;
+    const char* aqh = lds + L::AQH;
+    const char* aql = lds + L::AQL;
+    const float* gam = reinterpret_cast<const float*>(lds + L::GAM);
+    __syncthreads();  // chunk 0 staged
+
+    for (int c = 0; c < p.nc; ++c) {
+      const int nvalid = min(kChunk, p.T - (p.t0 + c * kChunk));
+      V8 Sb[KS][NCT];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int nt = 0; nt < NCT; ++nt) Sb[kk][nt] = Ops::from_acc(S[2 * kk][nt], S[2 * kk + 1][nt]);
+
+      // X = (K . Gamma) S and O = (Q . Gamma) S; tokens on M
+      f32x4 X[4][NCT], O[4][NCT];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int nt = 0; nt < NCT; ++nt) X[mt][nt] = O[mt][nt] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const int off = (16 * mt + n) * L::PQ + (32 * kk + 8 * g4) * L::ES;
+          const V8 ak = Ops::ld(kg + off), aq = Ops::ld(qg + off);
+#pragma unroll
+          for (int nt = 0; nt < NCT; ++nt) {
+            X[mt][nt] = mma32(ak, Sb[kk][nt], X[mt][nt]);
+            O[mt][nt] = mma32(aq, Sb[kk][nt], O[mt][nt]);
+          }
+        }
+      }
+
+      // R = V - X at the accumulator positions (rows past the end: V = 0)
+      typename Ops::Prec Rp[2][NCT];
+#pragma unroll
+      for (int nt = 0; nt < NCT; ++nt) {
+        f32x4 R[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * mt + 4 * g4 + i;
+            const T vraw = *reinterpret_cast<const T*>(lds + L::VS + r * L::PQ + (col0 + 16 * nt) * L::ES);
+            R[mt][i] = (r < nvalid ? Ops::in_f32(vraw) : 0.f) - X[mt][nt][i];
+          }
+        Rp[0][nt] = Ops::prec_from_acc(R[0], R[1]);
+        Rp[1][nt] = Ops::prec_from_acc(R[2], R[3]);
+      }
+
+      // U' = (T Diag(beta)) R   (block lower triangular: tile mt needs steps <= mt/2)
+      typename Ops::Prec Up[2][NCT];
+      {
+        f32x4 U[4][NCT];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+          for (int nt = 0; nt < NCT; ++nt) U[mt][nt] = zero4();
+#pragma unroll
+          for (int kk = 0; kk <= (mt >> 1); ++kk) {
+            const V8 a = Ops::ld(tb + (16 * mt + n) * L::PK + (32 * kk + 8 * g4) * L::ES);
+#pragma unroll
+            for (int nt = 0; nt < NCT; ++nt) U[mt][nt] = Ops::mma_split_b(a, Rp[kk][nt], U[mt][nt]);
+          }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NCT; ++nt) {
+          Up[0][nt] = Ops::prec_from_acc(U[0][nt], U[1][nt]);
+          Up[1][nt] = Ops::prec_from_acc(U[2][nt], U[3][nt]);
+        }
+      }
+
+      // O += Tril(A_qk) U'
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int kk = 0; kk <= (mt >> 1); ++kk) {
+          const int off = (16 * mt + n) * L::PK + (32 * kk + 8 * g4) * L::ES;
+          const V8 ah = Ops::ld(aqh + off), al = Ops::ld(aql + off);
+#pragma unroll
+          for (int nt = 0; nt < NCT; ++nt) O[mt][nt] = Ops::mma_prec(ah, al, Up[kk][nt], O[mt][nt]);
+        }
+
+      // S <- Diag(Gamma_last) S + Kd^T U'
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(gam + 16 * mt + 4 * g4);
+        const int off = (16 * mt + n) * L::PK + 8 * g4 * L::ES;
+        const V8 a0 = Ops::ld(kdt + off), a1 = Ops::ld(kdt + off + 32 * L::ES);
+#pragma unroll
+        for (int nt = 0; nt < NCT; ++nt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[mt][nt][i] *= gm[i];
+          S[mt][nt] = Ops::mma_split_b(a0, Up[0][nt], S[mt][nt]);
+          S[mt][nt] = Ops::mma_split_b(a1, Up[1][nt], S[mt][nt]);
+        }
+      }
+
+      __syncthreads();  // record and V of chunk c consumed; the helpers are done with tile c - 1
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NCT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) otile[(16 * mt + 4 * g4 + i) * L::PO + col0 + 16 * nt] = O[mt][nt][i];
+      __syncthreads();  // tile c and chunk c + 1's staging visible
+    }
+
+    float* so = p.S_out + bh * D * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NCT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) so[(16 * mt + 4 * g4 + i) * D + col0 + 16 * nt] = S[mt][nt][i];
   } else {
-    if (D == 64) hipLaunchKernelGGL((kda_scan_kernel<uint16_t, 64>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((kda_scan_kernel<uint16_t, 128>), grid, block, 0, s, p);
+    // ======================= helper waves =======================
+    constexpr int NH = L::NH;
+    const int hid = tid - 64 * L::NCW;
+    const bool gated = p.y != nullptr;
+    const T* vin = static_cast<const T*>(p.v);
+    const T* gin = gated ? static_cast<const T*>(p.gate) : vin;  // never read when ungated
+    constexpr int VPR = D * L::ES / 16;  // 16-byte units per slab row
+
+    // copy units: record (chunk c + 1), V slab (chunk c + 1), gate slab (chunk c)
+    int lofs[L::PER_THREAD];
+#pragma unroll
+    for (int i = 0; i < L::PER_THREAD; ++i) {
+      const int u = hid + NH * i;
+      if (u < L::REC_UNITS) {
+        lofs[i] = lds_offset_of_unit<L, D>(u);
+      } else if (u < L::REC_UNITS + L::SLAB_UNITS) {
+        const int vu = u - L::REC_UNITS;
+        lofs[i] = L::VS + (vu / VPR) * L::PQ + (vu % VPR) * 16;
+      } else {
+        const int gu = u - L::REC_UNITS - L::SLAB_UNITS;
+        lofs[i] = L::GS + (gu / VPR) * L::PQ + (gu % VPR) * 16;
+      }
+    }
+    const bool tail_ok = hid + NH * L::FULL < L::UNITS;
+    u32x4 stg[L::PER_THREAD];
+    // record and V of chunk cr (when rec), gate logits of chunk cg (when cg >= 0)
+    auto fetch = [&](int cr, bool rec, int cg) {
+      const char* rp = p.ws.base + (bh * p.nc + cr) * p.ws.rec_bytes;
+      const int tr = p.t0 + cr * kChunk, tg = p.t0 + cg * kChunk;
+      const int lastr = min(kChunk, p.T - tr) - 1, lastg = min(kChunk, p.T - tg) - 1;
+#pragma unroll
+      for (int i = 0; i < L::PER_THREAD; ++i) {
+        const int u = hid + NH * i;
+        if (i < L::FULL || tail_ok) {
+          if (u < L::REC_UNITS) {
+            if (rec) stg[i] = reinterpret_cast<const u32x4*>(rp)[u];
+          } else if (u < L::REC_UNITS + L::SLAB_UNITS) {  // rows past the end are clamped
+            const int vu = u - L::REC_UNITS;
+            if (rec)
+              stg[i] = reinterpret_cast<const u32x4*>(vin + head_base + (tr + min(vu / VPR, lastr)) * tok_stride)[vu % VPR];
+          } else {
+            const int gu = u - L::REC_UNITS - L::SLAB_UNITS;
+            if (cg >= 0)
+              stg[i] = reinterpret_cast<const u32x4*>(gin + head_base + (tg + min(gu / VPR, lastg)) * tok_stride)[gu % VPR];
+          }
+        }
+      }
+    };
+    auto commit = [&](bool rec, bool gate) {
+#pragma unroll
+      for (int i = 0; i < L::PER_THREAD; ++i) {
+        const int u = hid + NH * i;
+        const bool is_gate = u >= L::REC_UNITS + L::SLAB_UNITS;
+        if ((i < L::FULL || tail_ok) && (is_gate ? gate : rec)) *reinterpret_cast<u32x4*>(lds + lofs[i]) = stg[i];
+      }
+    };
+
+    // epilogue role: row er, columns ec .. ec + EC - 1
+    constexpr int EC = L::EC;
+    const int er = hid / L::TPR, ec = (hid % L::TPR) * EC;
+    float wv[EC];
+#pragma unroll
+    for (int j = 0; j < EC; ++j) wv[j] = (p.rms_w != nullptr) ? p.rms_w[h * D + ec + j] : 1.0f;
+    auto pack_store = [&](OutT* dst, const float* x) {
+      if constexpr (OUT_F32) {
+#pragma unroll
+        for (int q = 0; q < EC / 4; ++q)
+          reinterpret_cast<float4*>(dst)[q] = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < EC / 8; ++q) {
+          u32x4 w;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            w[k] = static_cast<uint32_t>(f32_to_bf16(x[8 * q + 2 * k])) |
+                   (static_cast<uint32_t>(f32_to_bf16(x[8 * q + 2 * k + 1])) << 16);
+          reinterpret_cast<u32x4*>(dst)[q] = w;
+        }
+      }
+    };
+    // o / y of chunk c from the output tile and the gate slab
+    auto epilogue = [&](int c) {
+      const int tok0 = p.t0 + c * kChunk;
+      float ov[EC];
+#pragma unroll
+      for (int q = 0; q < EC / 4; ++q) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(otile + er * L::PO + ec + 4 * q);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ov[4 * q + j] = t[j];
+      }
+      if (er < p.T - tok0) {
+        const int64_t orow = head_base + (tok0 + er) * tok_stride + ec;
+        if (p.o != nullptr) pack_store(static_cast<OutT*>(p.o) + orow, ov);
+        if (gated) {
+          float ss = 0.f;
+#pragma unroll
+          for (int j = 0; j < EC; ++j) ss += ov[j] * ov[j];
+#pragma unroll
+          for (int m = 1; m < L::TPR; m <<= 1) ss += __shfl_xor(ss, m);
+          const float rinv = hw_rsqrt(ss / D + p.rms_eps);
+          float yv[EC];
+#pragma unroll
+          for (int q = 0; q < EC * L::ES / 16; ++q) {
+            const u32x4 graw = *reinterpret_cast<const u32x4*>(lds + L::GS + er * L::PQ + ec * L::ES + 16 * q);
+            constexpr int PER = 16 / L::ES;  // logits per 16-byte vector
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+              float gl;
+              if constexpr (sizeof(T) == 2)
+                gl = __uint_as_float((graw[j >> 1] >> (16 * (j & 1))) << 16);
+              else
+                gl = __uint_as_float(graw[j]);
+              const int e = PER * q + j;
+              yv[e] = sigmoid_fast(gl) * ov[e] * rinv * wv[e];
+            }
+          }
+          pack_store(static_cast<OutT*>(p.y) + orow, yv);
+        }
+      }
+    };
+
+    fetch(0, true, -1);
+    commit(true, false);
+    __syncthreads();  // chunk 0 staged
+    for (int c = 0; c < p.nc; ++c) {
+      const bool more = c + 1 < p.nc;
+      fetch(c + 1, more, c);       // next record and V; this chunk's gate logits
+      if (c > 0) epilogue(c - 1);  // tile c - 1 (its row sums need no other chunk)
+      __syncthreads();             // compute waves are done with chunk c's staging
+      commit(more, true);
+      __syncthreads();
+    }
+    if (p.nc > 0) epilogue(p.nc - 1);
+  }
+}
+
+template <typename T, int D>
+static void launch_scan_t(const ScanParams& p, hipStream_t s) {
+  using W = WsLds<T, D>;
+  if constexpr (W::FITS) {
+    if (p.out_f32)
+      hipLaunchKernelGGL((kda_scan_ws_kernel<T, D, true>), dim3(p.H, p.B), dim3(W::NT), 0, s, p);
+    else
+      hipLaunchKernelGGL((kda_scan_ws_kernel<T, D, false>), dim3(p.H, p.B), dim3(W::NT), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((kda_scan_serial_kernel<T, D>), dim3(p.H, p.B), dim3(4 * D), 0, s, p);
+  }
+}
+
+hipError_t launch_scan(const ScanParams& p, int D, int in_f32, hipStream_t s) {
+  if (in_f32) {
+    if (D == 64) launch_scan_t<float, 64>(p, s);
+    else launch_scan_t<float, 128>(p, s);
+  } else {
+    if (D == 64) launch_scan_t<uint16_t, 64>(p, s);
+    else launch_scan_t<uint16_t, 128>(p, s);
   }
   return hipGetLastError();
 }
