@@ -27,7 +27,7 @@
 // selection matrix on MFMA (exact).
 //
 // Outputs (one record per chunk, layout in kda_params.hpp):
-//   qg = q^ . Gamma, kg = k^ . Gamma, kdt = (k^ . Gamma_last / Gamma)^T,
+//   qg = q^ . Gamma, kg = -(k^ . Gamma), kdt = (k^ . Gamma_last / Gamma)^T,
 //   tb = T Diag(beta) with T = (I + Diag(beta) StrictTril(A_kk))^{-1},
 //   aq = Tril(A_qk) (diagonal included), gam = Gamma_last.
 #include "kda_chunk_prologue.hpp"
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 3 : 2)) void kda_intra_kerne
       QR[kk][j] = qf * (rq * rf);
       kc[j] = kf * (rk * cf);
       xq[j] = QR[kk][j] * eb[j];  // q^ . Gamma
-      xk[j] = KR[kk][j] * eb[j];  // k^ . Gamma
+      xk[j] = -KR[kk][j] * eb[j];  // -(k^ . Gamma)
       xd[j] = kc[j] * el[j];      // k^ . Gamma_last / Gamma
     }
     store8<T>(qg + r * D + 32 * kk + 8 * g4, xq);

@@ -15,7 +15,8 @@ constexpr int kSub = 16;     // tokens per sub-tile
 // record index ((b * H + h) * nc + c).  Element type T = the input type (bf16
 // bits or fp32).  Byte layout of one record (D = head dim, ES = sizeof(T)):
 //   qg  [64][D]   q^ . Gamma, columns in slot order per 32-group
-//   kg  [64][D]   k^ . Gamma, columns in slot order
+//   kg  [64][D]   -(k^ . Gamma), columns in slot order (negated, so that the
+//                 scan forms V - (K . Gamma) S in one accumulator chain)
 //   kdt [D][64]   (k^ . Gamma_last / Gamma)^T, token columns in slot order
 //   tb  [64][64]  (I + Diag(beta) StrictTril(A_kk))^{-1} Diag(beta), slot order
 //   aqh [64][64]  Tril(A_qk): high bf16 part (bf16 path) or value (fp32 path)

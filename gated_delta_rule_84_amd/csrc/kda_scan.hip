@@ -281,7 +281,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) Sb[kk] = Ops::from_acc(S[2 * kk], S[2 * kk + 1]);
 
-    // X = (K . Gamma) S and O = (Q . Gamma) S; tokens on M
+    // X = -(K . Gamma) S (the record holds kg negated) and O = (Q . Gamma) S
     f32x4 X[4], O[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
           vraw = *reinterpret_cast<const T*>(lds + L::VS + r * L::PQ + col * L::ES);
         else
           vraw = vreg[4 * mt + i];
-        R[mt][i] = (r < nvalid ? Ops::in_f32(vraw) : 0.f) - X[mt][i];
+        R[mt][i] = (r < nvalid ? Ops::in_f32(vraw) : 0.f) + X[mt][i];
       }
     typename Ops::Prec Rp[2];
     Rp[0] = Ops::prec_from_acc(R[0], R[1]);
@@ -411,6 +411,15 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
 // LDS: the padded record image (as above), the V slab of the current chunk,
 // the gate-logit slab of the previous chunk, the previous chunk's fp32 output
 // tile.  NCW compute waves (32 columns each) and as many helper waves.
+//
+// The staging is split in two parts so that it never stalls the compute waves:
+// part A (qg, kg of the record and the V slab) is read in the first half of a
+// chunk step, part B (kdt, tb, aq, Gamma_last) in the second half.  Helpers
+// commit part B of chunk c during the first half of step c, and part A of
+// chunk c + 1 with chunk c's gate logits during the second half; each part is
+// loaded into registers one step before it is committed.  The helpers turn
+// chunk c - 1's output tile into o / y during the first half of step c, while
+// the compute waves run the long independent product chains of chunk c.
 template <typename T, int D>
 struct WsLds {
   static constexpr int ES = sizeof(T);
@@ -434,17 +443,30 @@ struct WsLds {
   static constexpr int OT = GS + 64 * PQ;      // output tile [64][PO] fp32
   static constexpr int BYTES = OT + 64 * PO * 4;
   static constexpr RecLayout RL = rec_layout(ES, D);
-  static constexpr int REC_UNITS = (RL.gam + 4 * D) / 16;
-  static constexpr int SLAB_UNITS = 64 * D * ES / 16;
-  static constexpr int UNITS = REC_UNITS + 2 * SLAB_UNITS;
-  static constexpr int PER_THREAD = (UNITS + NH - 1) / NH;
-  static constexpr int FULL = UNITS / NH;
+  static constexpr int VPR = D * ES / 16;      // 16-byte units per slab row
+  static constexpr int SLAB_UNITS = 64 * VPR;
+  static constexpr int A_REC = RL.kdt / 16;    // record units of part A (qg, kg)
+  static constexpr int A_UNITS = A_REC + SLAB_UNITS;
+  static constexpr int B_UNITS = (RL.gam + 4 * D - RL.kdt) / 16;
+  static constexpr int PA = (A_UNITS + NH - 1) / NH;
+  static constexpr int PB = (B_UNITS + NH - 1) / NH;
+  static constexpr int PG = (SLAB_UNITS + NH - 1) / NH;
   static constexpr int TPR = NH / 64;          // helper threads per output row
   static constexpr int EC = D / TPR;           // columns per helper thread
-  // the specialised organisation is used when its image fits in LDS and the
-  // staging registers of a helper thread stay modest
-  static constexpr bool FITS = BYTES <= 160 * 1024 && PER_THREAD <= 40;
+  // used when the image fits in LDS and a helper's staging registers stay modest
+  static constexpr bool FITS = BYTES <= 160 * 1024 && PA + PB + PG <= 40;
 };
+
+// 0/1 selection operand for the V product: K-slot j of lane group g is column
+// 8 g + j of the wave's 32 columns; output column n of tile nt is column
+// 16 nt + n.
+template <typename V8>
+__device__ __forceinline__ V8 v_select(int n, int g, int nt) {
+  V8 s;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s[j] = (8 * g + j == 16 * nt + n) ? 1.0f : 0.0f;
+  return s;
+}
 
 template <typename T, int D, bool OUT_F32>
 __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const ScanParams p) {
@@ -483,6 +505,7 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
 #pragma unroll
           for (int i = 0; i < 4; ++i) S[mt][nt][i] = s0[(16 * mt + 4 * g4 + i) * D + col0 + 16 * nt];
     }
+    const V8 vsel0 = v_select<V8>(n, g4, 0), vsel1 = v_select<V8>(n, g4, 1);
     const char* qg = lds + L::QG;
     const char* kg = lds + L::KG;
     const char* kdt = lds + L::KDT;
@@ -490,50 +513,51 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
     const char* aqh = lds + L::AQH;
     const char* aql = lds + L::AQL;
     const float* gam = reinterpret_cast<const float*>(lds + L::GAM);
-    __syncthreads();  // chunk 0 staged
+    __syncthreads();  // part A of chunk 0 staged
 
+    f32x4 O[4][NCT];  // outputs of the chunk
+    auto write_tile = [&]() {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NCT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) otile[(16 * mt + 4 * g4 + i) * L::PO + col0 + 16 * nt] = O[mt][nt][i];
+    };
     for (int c = 0; c < p.nc; ++c) {
-      const int nvalid = min(kChunk, p.T - (p.t0 + c * kChunk));
       V8 Sb[KS][NCT];
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
         for (int nt = 0; nt < NCT; ++nt) Sb[kk][nt] = Ops::from_acc(S[2 * kk][nt], S[2 * kk + 1][nt]);
 
-      // X = (K . Gamma) S and O = (Q . Gamma) S; tokens on M
-      f32x4 X[4][NCT], O[4][NCT];
+      // R = V - (K . Gamma) S (the record holds kg negated; V enters through a
+      // 0/1 selection product, rows past the end are zero) and O = (Q . Gamma) S
+      f32x4 R[4][NCT];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int nt = 0; nt < NCT; ++nt) X[mt][nt] = O[mt][nt] = zero4();
+        const V8 vrow = Ops::ld(lds + L::VS + (16 * mt + n) * L::PQ + (32 * wave + 8 * g4) * L::ES);
+        R[mt][0] = mma32(vrow, vsel0, zero4());
+        R[mt][1] = mma32(vrow, vsel1, zero4());
+        O[mt][0] = O[mt][1] = zero4();
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
           const int off = (16 * mt + n) * L::PQ + (32 * kk + 8 * g4) * L::ES;
           const V8 ak = Ops::ld(kg + off), aq = Ops::ld(qg + off);
 #pragma unroll
           for (int nt = 0; nt < NCT; ++nt) {
-            X[mt][nt] = mma32(ak, Sb[kk][nt], X[mt][nt]);
+            R[mt][nt] = mma32(ak, Sb[kk][nt], R[mt][nt]);
             O[mt][nt] = mma32(aq, Sb[kk][nt], O[mt][nt]);
           }
         }
       }
-
-      // R = V - X at the accumulator positions (rows past the end: V = 0)
       typename Ops::Prec Rp[2][NCT];
 #pragma unroll
       for (int nt = 0; nt < NCT; ++nt) {
-        f32x4 R[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * mt + 4 * g4 + i;
-            const T vraw = *reinterpret_cast<const T*>(lds + L::VS + r * L::PQ + (col0 + 16 * nt) * L::ES);
-            R[mt][i] = (r < nvalid ? Ops::in_f32(vraw) : 0.f) - X[mt][nt][i];
-          }
-        Rp[0][nt] = Ops::prec_from_acc(R[0], R[1]);
-        Rp[1][nt] = Ops::prec_from_acc(R[2], R[3]);
+        Rp[0][nt] = Ops::prec_from_acc(R[0][nt], R[1][nt]);
+        Rp[1][nt] = Ops::prec_from_acc(R[2][nt], R[3][nt]);
       }
+      __syncthreads();  // part A of chunk c consumed; part B of chunk c staged; tile c - 1 done
 
       // U' = (T Diag(beta)) R   (block lower triangular: tile mt needs steps <= mt/2)
       typename Ops::Prec Up[2][NCT];
@@ -583,14 +607,8 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
         }
       }
 
-      __syncthreads();  // record and V of chunk c consumed; the helpers are done with tile c - 1
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NCT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) otile[(16 * mt + 4 * g4 + i) * L::PO + col0 + 16 * nt] = O[mt][nt][i];
-      __syncthreads();  // tile c and chunk c + 1's staging visible
+      write_tile();     // the helpers finished tile c - 1 before the barrier above
+      __syncthreads();  // part B of chunk c consumed; tile c and part A of chunk c + 1 staged
     }
 
     float* so = p.S_out + bh * D * D;
@@ -602,60 +620,85 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
         for (int i = 0; i < 4; ++i) so[(16 * mt + 4 * g4 + i) * D + col0 + 16 * nt] = S[mt][nt][i];
   } else {
     // ======================= helper waves =======================
-    constexpr int NH = L::NH;
+    constexpr int NH = L::NH, VPR = L::VPR;
     const int hid = tid - 64 * L::NCW;
     const bool gated = p.y != nullptr;
     const T* vin = static_cast<const T*>(p.v);
     const T* gin = gated ? static_cast<const T*>(p.gate) : vin;  // never read when ungated
-    constexpr int VPR = D * L::ES / 16;  // 16-byte units per slab row
 
-    // copy units: record (chunk c + 1), V slab (chunk c + 1), gate slab (chunk c)
-    int lofs[L::PER_THREAD];
+    // LDS offsets of this thread's units (loop invariant).  Part A and the gate
+    // slab split evenly over the helper threads; part B's last units are
+    // clamped (a few threads load and store the last unit twice, harmlessly),
+    // so that every load and store below is unconditional.
+    static_assert(L::A_REC % NH == 0 && L::SLAB_UNITS % NH == 0, "part A and slabs must split evenly");
+    constexpr int AR = L::A_REC / NH;  // record steps of part A; the rest is V
+    int lofA[L::PA], lofB[L::PB], lofG[L::PG];
 #pragma unroll
-    for (int i = 0; i < L::PER_THREAD; ++i) {
+    for (int i = 0; i < L::PA; ++i) {
       const int u = hid + NH * i;
-      if (u < L::REC_UNITS) {
-        lofs[i] = lds_offset_of_unit<L, D>(u);
-      } else if (u < L::REC_UNITS + L::SLAB_UNITS) {
-        const int vu = u - L::REC_UNITS;
-        lofs[i] = L::VS + (vu / VPR) * L::PQ + (vu % VPR) * 16;
-      } else {
-        const int gu = u - L::REC_UNITS - L::SLAB_UNITS;
-        lofs[i] = L::GS + (gu / VPR) * L::PQ + (gu % VPR) * 16;
-      }
+      lofA[i] = (i < AR) ? lds_offset_of_unit<L, D>(u)
+                         : L::VS + ((u - L::A_REC) / VPR) * L::PQ + ((u - L::A_REC) % VPR) * 16;
     }
-    const bool tail_ok = hid + NH * L::FULL < L::UNITS;
-    u32x4 stg[L::PER_THREAD];
-    // record and V of chunk cr (when rec), gate logits of chunk cg (when cg >= 0)
-    auto fetch = [&](int cr, bool rec, int cg) {
-      const char* rp = p.ws.base + (bh * p.nc + cr) * p.ws.rec_bytes;
-      const int tr = p.t0 + cr * kChunk, tg = p.t0 + cg * kChunk;
-      const int lastr = min(kChunk, p.T - tr) - 1, lastg = min(kChunk, p.T - tg) - 1;
 #pragma unroll
-      for (int i = 0; i < L::PER_THREAD; ++i) {
+    for (int i = 0; i < L::PB; ++i) lofB[i] = lds_offset_of_unit<L, D>(L::A_REC + min(hid + NH * i, L::B_UNITS - 1));
+#pragma unroll
+    for (int i = 0; i < L::PG; ++i) {
+      const int u = hid + NH * i;
+      lofG[i] = L::GS + (u / VPR) * L::PQ + (u % VPR) * 16;
+    }
+    u32x4 stA[L::PA], stB[L::PB], stG[L::PG];
+    auto rec_ptr = [&](int c) { return p.ws.base + (bh * p.nc + c) * p.ws.rec_bytes; };
+    auto last_row = [&](int c) { return min(kChunk, p.T - (p.t0 + c * kChunk)) - 1; };
+    // part A of chunk c: qg, kg and the V slab (rows past the end are clamped)
+    auto load_A = [&](int c) {
+      const u32x4* rp = reinterpret_cast<const u32x4*>(rec_ptr(c));
+      const T* v0 = vin + head_base + (int64_t)(p.t0 + c * kChunk) * tok_stride;
+      const int last = last_row(c);
+#pragma unroll
+      for (int i = 0; i < L::PA; ++i) {
         const int u = hid + NH * i;
-        if (i < L::FULL || tail_ok) {
-          if (u < L::REC_UNITS) {
-            if (rec) stg[i] = reinterpret_cast<const u32x4*>(rp)[u];
-          } else if (u < L::REC_UNITS + L::SLAB_UNITS) {  // rows past the end are clamped
-            const int vu = u - L::REC_UNITS;
-            if (rec)
-              stg[i] = reinterpret_cast<const u32x4*>(vin + head_base + (tr + min(vu / VPR, lastr)) * tok_stride)[vu % VPR];
-          } else {
-            const int gu = u - L::REC_UNITS - L::SLAB_UNITS;
-            if (cg >= 0)
-              stg[i] = reinterpret_cast<const u32x4*>(gin + head_base + (tg + min(gu / VPR, lastg)) * tok_stride)[gu % VPR];
-          }
+        if (i < AR) {
+          stA[i] = rp[u];
+        } else {
+          const int vu = u - L::A_REC;
+          stA[i] = reinterpret_cast<const u32x4*>(v0 + min(vu / VPR, last) * tok_stride)[vu % VPR];
         }
       }
     };
-    auto commit = [&](bool rec, bool gate) {
+    auto commit_A = [&](int c) {
+      const int last = last_row(c);
 #pragma unroll
-      for (int i = 0; i < L::PER_THREAD; ++i) {
-        const int u = hid + NH * i;
-        const bool is_gate = u >= L::REC_UNITS + L::SLAB_UNITS;
-        if ((i < L::FULL || tail_ok) && (is_gate ? gate : rec)) *reinterpret_cast<u32x4*>(lds + lofs[i]) = stg[i];
+      for (int i = 0; i < L::PA; ++i) {
+        u32x4 x = stA[i];
+        if (i >= AR) {  // V rows past the end are written as zeros
+          const bool zero = (hid + NH * i - L::A_REC) / VPR > last;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) x[w] = zero ? 0u : x[w];
+        }
+        *reinterpret_cast<u32x4*>(lds + lofA[i]) = x;
       }
+    };
+    auto load_B = [&](int c) {
+      const u32x4* rp = reinterpret_cast<const u32x4*>(rec_ptr(c)) + L::A_REC;
+#pragma unroll
+      for (int i = 0; i < L::PB; ++i) stB[i] = rp[min(hid + NH * i, L::B_UNITS - 1)];
+    };
+    auto commit_B = [&]() {
+#pragma unroll
+      for (int i = 0; i < L::PB; ++i) *reinterpret_cast<u32x4*>(lds + lofB[i]) = stB[i];
+    };
+    auto load_G = [&](int c) {
+      const T* g0 = gin + head_base + (int64_t)(p.t0 + c * kChunk) * tok_stride;
+      const int last = last_row(c);
+#pragma unroll
+      for (int i = 0; i < L::PG; ++i) {
+        const int u = hid + NH * i;
+        stG[i] = reinterpret_cast<const u32x4*>(g0 + min(u / VPR, last) * tok_stride)[u % VPR];
+      }
+    };
+    auto commit_G = [&]() {
+#pragma unroll
+      for (int i = 0; i < L::PG; ++i) *reinterpret_cast<u32x4*>(lds + lofG[i]) = stG[i];
     };
 
     // epilogue role: row er, columns ec .. ec + EC - 1
@@ -681,8 +724,9 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
         }
       }
     };
-    // o / y of chunk c from the output tile and the gate slab
-    auto epilogue = [&](int c) {
+    // o / y of chunk c from the output tile and the gate slab; only the last
+    // chunk can have rows past the end
+    auto epilogue = [&](int c, auto check_rows) {
       const int tok0 = p.t0 + c * kChunk;
       float ov[EC];
 #pragma unroll
@@ -691,7 +735,7 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
 #pragma unroll
         for (int j = 0; j < 4; ++j) ov[4 * q + j] = t[j];
       }
-      if (er < p.T - tok0) {
+      if (!decltype(check_rows)::value || er < p.T - tok0) {
         const int64_t orow = head_base + (tok0 + er) * tok_stride + ec;
         if (p.o != nullptr) pack_store(static_cast<OutT*>(p.o) + orow, ov);
         if (gated) {
@@ -714,7 +758,7 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
               else
                 gl = __uint_as_float(graw[j]);
               const int e = PER * q + j;
-              yv[e] = sigmoid_fast(gl) * ov[e] * rinv * wv[e];
+              yv[e] = sigmoid_fast(gl) * ov[e] * (rinv * wv[e]);
             }
           }
           pack_store(static_cast<OutT*>(p.y) + orow, yv);
@@ -722,18 +766,31 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
       }
     };
 
-    fetch(0, true, -1);
-    commit(true, false);
-    __syncthreads();  // chunk 0 staged
+    // Loads past the last chunk are clamped to it (their commits land where
+    // nobody reads any more), so the steady state has no branches.
+    const int cl = p.nc - 1;
+    // prologue: part A of chunk 0 into LDS; part B of chunk 0, part A of
+    // chunk 1 and the gate logits of chunk 0 into registers
+    load_A(0);
+    load_B(0);
+    commit_A(0);
+    load_A(min(1, cl));
+    load_G(0);
+    __syncthreads();
     for (int c = 0; c < p.nc; ++c) {
-      const bool more = c + 1 < p.nc;
-      fetch(c + 1, more, c);       // next record and V; this chunk's gate logits
-      if (c > 0) epilogue(c - 1);  // tile c - 1 (its row sums need no other chunk)
-      __syncthreads();             // compute waves are done with chunk c's staging
-      commit(more, true);
+      // first half of step c: the compute waves read part A of chunk c
+      commit_B();                                        // part B of chunk c
+      load_B(min(c + 1, cl));
+      if (c > 0) epilogue(c - 1, std::false_type{});     // tile and gate logits of chunk c - 1
+      __syncthreads();
+      // second half: the compute waves read part B of chunk c and write tile c
+      commit_A(min(c + 1, cl));
+      commit_G();                                        // gate logits of chunk c
+      load_A(min(c + 2, cl));
+      load_G(min(c + 1, cl));
       __syncthreads();
     }
-    if (p.nc > 0) epilogue(p.nc - 1);
+    epilogue(cl, std::true_type{});
   }
 }
 
