@@ -66,7 +66,9 @@ def main() -> int:
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-baseline sample (0: all heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--segment-tokens", type=int, default=0,
-                    help="tokens per internal segment (workspace size); 0: whole sequence")
+                    help="tokens per segment of the overlapped schedule; 0: library default")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="one stream, segments in turn (the whole sequence per segment by default)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of GIB GiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -114,15 +116,20 @@ def main() -> int:
     odt = torch.bfloat16
     out = {"y": torch.empty((B, T, H, D), dtype=odt, device=dev),
            "S_T": torch.empty((B, H, D, D), dtype=torch.float32, device=dev)}
-    desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16)
-    seg = args.segment_tokens or min(T, 65536)
-    ws = torch.empty(kda.workspace_size(desc, seg), dtype=torch.uint8, device=dev)
+    overlap = not args.no_overlap
+    seg_arg = args.segment_tokens or None
+    desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg_arg if overlap else 0,
+                         overlap=overlap)
+    ws_bytes = kda.workspace_size(desc) if (overlap or not seg_arg) else kda.workspace_size(desc, seg_arg)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    seg, overlapped = kda.schedule(desc, ws_bytes)
     n_seg = -(-T // seg)
-    names = ["intra", "scan"] * n_seg
+    names = ["intra", "scan"] * n_seg  # launch order: per segment, intra then scan
 
     def step(events=None):
         kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t.get("S0"), gate=t["gate"],
-                      want_o=False, out=out, workspace=ws, events=events)
+                      want_o=False, out=out, workspace=ws, events=events, segment_tokens=seg_arg,
+                      overlap=overlap)
 
     for _ in range(args.warmup):
         step()
@@ -153,8 +160,11 @@ def main() -> int:
             tot[n] += row[2 * i].elapsed_time(row[2 * i + 1])
         for n in per:
             per[n].append(tot[n])
-    kern_ms = {n: float(np.mean(v)) for n, v in per.items()}  # per step, summed over segments
-    dom = max(kern_ms, key=kern_ms.get)
+    kern_ms = {n: float(np.mean(v)) for n, v in per.items()}  # per step, summed over its launches
+    launches = {n: names.count(n) for n in per}
+    dom = max(kern_ms, key=lambda n: kern_ms[n] / launches[n])  # longest average launch
+    # algorithmic bytes of all of the kernel's launches in a step over their summed duration
+    # (= bytes per launch / average launch duration for equal segments)
     dom_bytes = kernel_bytes(dom, token_heads, D, B * H, T)
     achieved = dom_bytes / (kern_ms[dom] * 1e-3) / 1e9
     path_bytes = token_heads * (1538 if D == 128 else (6 * D + 2 + 4 * D)) + 2 * B * H * D * D * 4
@@ -176,9 +186,10 @@ def main() -> int:
         "data": "synthetic (seeded; K3 layer shapes, no trained weights)",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "d_k": D, "d_v": D, "chunk": 64,
                    "inputs": "bf16", "state": "fp32", "outputs": "y (bf16) + S_T (fp32)", "gate": True,
-                   "segment_tokens": seg},
+                   "segment_tokens": seg, "overlapped": overlapped},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "launches_per_step": launches[dom], "avg_launch_ms": kern_ms[dom] / launches[dom]},
         "path_roofline": {"achieved_GBs": path_gbs, "frac_hbm": path_gbs / HBM_PEAK_GBS,
                           "achieved_TFLOPs": path_tflops, "frac_bf16_mfma": path_tflops / BF16_PEAK_TFLOPS,
                           "algorithmic_bytes": path_bytes},

@@ -28,7 +28,8 @@ class KdaDesc(ctypes.Structure):
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("g_min", ctypes.c_float), ("q_scale", ctypes.c_float), ("l2_eps", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("qk_l2norm", ctypes.c_int32),
-                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int)]
+                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("segment_tokens", ctypes.c_int32), ("overlap", ctypes.c_int32)]
 
 
 class KdaError(RuntimeError):
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_workspace_size.argtypes = [dp]
         L.kda_chunk_fwd_workspace_size_for.restype = sz
         L.kda_chunk_fwd_workspace_size_for.argtypes = [dp, i32]
+        L.kda_chunk_fwd_schedule.restype = ctypes.c_int
+        L.kda_chunk_fwd_schedule.argtypes = [dp, sz, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.kda_chunk_fwd.restype = ctypes.c_int
         L.kda_chunk_fwd.argtypes = [dp] + [vp] * 13 + [sz, vp]
         L.kda_chunk_fwd_traced.restype = ctypes.c_int
@@ -96,33 +99,50 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 def make_desc(B, T, H, D, in_dtype, out_dtype, g_min=-5.0, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6,
-              qk_l2norm=True) -> KdaDesc:
+              qk_l2norm=True, segment_tokens=0, overlap=True) -> KdaDesc:
     d = KdaDesc()
     rc = lib().kda_desc_init(ctypes.byref(d), B, T, H, D, in_dtype, out_dtype)
     if rc != 0:
         raise KdaError("kda_desc_init", rc)
     d.g_min, d.q_scale, d.l2_eps, d.rms_eps, d.qk_l2norm = g_min, q_scale, l2_eps, rms_eps, int(bool(qk_l2norm))
+    d.segment_tokens, d.overlap = int(segment_tokens or 0), int(bool(overlap))
     return d
 
 
 def workspace_size(desc: KdaDesc, segment_tokens: int | None = None) -> int:
+    """Workspace bytes: the descriptor's preferred schedule (None), or one
+    segment of ``segment_tokens`` tokens processed in turn."""
     if segment_tokens is None:
         return int(lib().kda_chunk_fwd_workspace_size(ctypes.byref(desc)))
     return int(lib().kda_chunk_fwd_workspace_size_for(ctypes.byref(desc), int(segment_tokens)))
 
 
+def schedule(desc: KdaDesc, ws_bytes: int) -> tuple[int, bool]:
+    """(tokens per segment, overlapped) that kda_chunk_fwd uses on the current
+    device for this descriptor and workspace size."""
+    seg, ovl = ctypes.c_int32(0), ctypes.c_int32(0)
+    rc = lib().kda_chunk_fwd_schedule(ctypes.byref(desc), int(ws_bytes), ctypes.byref(seg), ctypes.byref(ovl))
+    if rc != 0:
+        raise KdaError("kda_chunk_fwd_schedule", rc)
+    return int(seg.value), bool(ovl.value)
+
+
 def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=None, want_o=True,
-              want_y=None, want_state=True, workspace=None, segment_tokens=None, out=None, events=None,
-              **opts):
+              want_y=None, want_state=True, workspace=None, segment_tokens=None, overlap=True, out=None,
+              events=None, **opts):
     """KDA forward over whole sequences.  q, k, z: [B, T, H, D]; v (and gate):
     [B, T, H, D]; beta: [B, T, H]; A: [H] fp32; S0: [B, H, D, D] fp32 or None.
     Returns a dict with 'o' / 'y' (out_dtype, default the input dtype) and
     'S_T' (fp32).  ``out`` may supply preallocated output tensors; ``events``
-    (raw hipEvent_t handles) selects the traced entry point."""
+    (raw hipEvent_t handles) selects the traced entry point.  With
+    ``overlap`` the library may run the overlapped schedule in segments of
+    ``segment_tokens`` tokens; without it, ``segment_tokens`` sizes the
+    segments processed in turn (default: the whole sequence)."""
     B, T, H, D = q.shape
     in_dt = _dt(q)
     odt = q.dtype if out_dtype is None else out_dtype
-    desc = make_desc(B, T, H, D, in_dt, _dt(torch.empty(0, dtype=odt)), **opts)
+    desc = make_desc(B, T, H, D, in_dt, _dt(torch.empty(0, dtype=odt)),
+                     segment_tokens=(segment_tokens or 0) if overlap else 0, overlap=overlap, **opts)
     want_y = (gate is not None) if want_y is None else want_y
     res = dict(out or {})
     dev = q.device
@@ -133,7 +153,7 @@ def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=
     if want_state and "S_T" not in res:
         res["S_T"] = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
     if workspace is None:
-        nbytes = workspace_size(desc, segment_tokens)
+        nbytes = workspace_size(desc, None if overlap else segment_tokens)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), _ptr(S0), _ptr(gate),
             _ptr(rms_w), _ptr(res.get("o")), _ptr(res.get("y")), _ptr(res.get("S_T")), _ptr(workspace),

@@ -1,13 +1,17 @@
 // Host side of the C ABI declared in include/kda.h: argument validation,
-// workspace carving, the segment loop and kernel launches.  No device memory
-// is allocated here and no host synchronisation happens (unless KDA_DEBUG=1,
-// which synchronises after every launch to localise failures).
+// workspace carving, the segment schedules and kernel launches.  No device
+// memory is allocated here and no host synchronisation happens (unless
+// KDA_DEBUG=1, which synchronises after every launch to localise failures).
+// The overlapped schedule keeps, per device, two streams restricted to
+// disjoint sets of compute units and a few events, created on first use.
 #include "kda.h"
 
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "kda_params.hpp"
 
@@ -15,7 +19,8 @@ namespace {
 
 using kda::kChunk;
 
-constexpr int32_t kDefaultSegmentTokens = 65536;
+constexpr int32_t kDefaultSegmentTokens = 65536;  // one-stream schedule
+constexpr int32_t kDefaultPipeTokens = 8192;      // overlapped schedule
 
 bool debug_sync() {
   const char* e = std::getenv("KDA_DEBUG");
@@ -50,6 +55,7 @@ kda_status validate_desc(const kda_desc* d) {
   if (d->chunk != kChunk) return KDA_ERR_UNSUPPORTED;
   if (!(d->g_min < 0.0f) || d->g_min < -5.5f) return KDA_ERR_UNSUPPORTED;
   if (!(d->l2_eps >= 0.0f) || !(d->rms_eps >= 0.0f)) return KDA_ERR_UNSUPPORTED;
+  if (d->segment_tokens < 0 || (d->overlap != 0 && d->overlap != 1)) return KDA_ERR_BAD_SHAPE;
   return KDA_OK;
 }
 
@@ -81,11 +87,127 @@ WsLayout layout_for(const kda_desc* d, int64_t seg_nc) {
 
 int64_t num_chunks(const kda_desc* d) { return ((int64_t)d->T + kChunk - 1) / kChunk; }
 
+int64_t pipe_chunks(const kda_desc* d) {
+  const int64_t toks = d->segment_tokens > 0 ? d->segment_tokens : kDefaultPipeTokens;
+  return (toks + kChunk - 1) / kChunk;
+}
+
+// The overlapped schedule is worth it when the sequence spans more than one
+// segment; its workspace holds two segments of records.
+bool pipe_wanted(const kda_desc* d) { return d->overlap != 0 && num_chunks(d) > pipe_chunks(d); }
+
+// ---- per-device streams and events of the overlapped schedule --------------
+struct StreamPair {
+  int n_scan;
+  hipStream_t intra, scan;
+};
+struct DeviceCtx {
+  std::mutex mu;
+  bool ready = false;
+  int cus = 0;
+  hipEvent_t fork = nullptr, join_intra = nullptr, join_scan = nullptr;
+  hipEvent_t intra_done[2] = {nullptr, nullptr}, scan_done[2] = {nullptr, nullptr};
+  std::vector<StreamPair> pairs;
+};
+constexpr int kMaxDevices = 64;
+DeviceCtx g_dev[kMaxDevices];
+
+// Called with c.mu held.
+bool ctx_ready(DeviceCtx& c, int dev) {
+  if (c.ready) return true;
+  if (hipDeviceGetAttribute(&c.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c.cus < 16) {
+    (void)hipGetLastError();
+    return false;
+  }
+  for (hipEvent_t* e : {&c.fork, &c.join_intra, &c.join_scan, &c.intra_done[0], &c.intra_done[1], &c.scan_done[0],
+                        &c.scan_done[1]})
+    if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+  c.ready = true;
+  return true;
+}
+
+// Streams for a scan of n_scan workgroups: the scan stream may use the first
+// n_scan compute units of the mask, the intra stream the others (the runtime
+// spreads consecutive mask bits over the device's XCDs).  Called with c.mu held.
+bool stream_pair(DeviceCtx& c, int n_scan, hipStream_t* si, hipStream_t* ss) {
+  for (const StreamPair& p : c.pairs)
+    if (p.n_scan == n_scan) {
+      *si = p.intra;
+      *ss = p.scan;
+      return true;
+    }
+  std::vector<uint32_t> ms((c.cus + 31) / 32, 0u), mi((c.cus + 31) / 32, 0u);
+  for (int i = 0; i < c.cus; ++i) (i < n_scan ? ms : mi)[i / 32] |= 1u << (i % 32);
+  StreamPair p{n_scan, nullptr, nullptr};
+  if (hipExtStreamCreateWithCUMask(&p.scan, (uint32_t)ms.size(), ms.data()) != hipSuccess ||
+      hipExtStreamCreateWithCUMask(&p.intra, (uint32_t)mi.size(), mi.data()) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  c.pairs.push_back(p);
+  *si = p.intra;
+  *ss = p.scan;
+  return true;
+}
+
+// Which schedule a call with this descriptor and workspace takes on the
+// current device: the segment length in chunks, and whether it overlaps.
+struct Plan {
+  int64_t seg_nc;
+  bool overlapped;
+  int dev;
+  int n_scan;
+};
+Plan make_plan(const kda_desc* d, size_t ws_bytes) {
+  Plan p{1, false, 0, 0};
+  const int64_t nc_total = num_chunks(d);
+  if (pipe_wanted(d)) {
+    const int64_t seg_nc = pipe_chunks(d);
+    int dev = 0;
+    if (ws_bytes >= layout_for(d, 2 * seg_nc).total && hipGetDevice(&dev) == hipSuccess && dev >= 0 &&
+        dev < kMaxDevices) {
+      DeviceCtx& c = g_dev[dev];
+      std::lock_guard<std::mutex> lock(c.mu);
+      const int64_t bh = (int64_t)d->B * d->H;
+      const int n_scan = (int)((bh + 7) / 8 * 8);
+      hipStream_t si = nullptr, ss = nullptr;
+      if (ctx_ready(c, dev) && bh * 8 <= (int64_t)c.cus * 5 && stream_pair(c, n_scan, &si, &ss))
+        return Plan{seg_nc, true, dev, n_scan};
+    }
+  }
+  // one stream: the largest segment whose workspace fits
+  int64_t lo = 1, hi = nc_total < 1 ? 1 : nc_total;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo + 1) / 2;
+    if (layout_for(d, mid).total <= ws_bytes)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  p.seg_nc = lo;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+kda_status kda_chunk_fwd_schedule(const kda_desc* d, size_t ws_bytes, int32_t* segment_tokens,
+                                  int32_t* overlapped) {
+  const kda_status st = validate_desc(d);
+  if (st != KDA_OK) return st;
+  if (!segment_tokens || !overlapped) return KDA_ERR_NULL_ARG;
+  if (ws_bytes < layout_for(d, 1).total) return KDA_ERR_WORKSPACE;
+  const Plan p = make_plan(d, ws_bytes);
+  *segment_tokens = (int32_t)(p.seg_nc * kChunk);
+  *overlapped = p.overlapped ? 1 : 0;
+  return KDA_OK;
+}
 
 const char* kda_status_str(kda_status s) {
   switch (s) {
@@ -118,6 +240,8 @@ kda_status kda_desc_init(kda_desc* d, int32_t B, int32_t T, int32_t H, int32_t h
   d->qk_l2norm = 1;
   d->in_dtype = in_dtype;
   d->out_dtype = out_dtype;
+  d->segment_tokens = 0;
+  d->overlap = 1;
   return validate_desc(d);
 }
 
@@ -129,6 +253,7 @@ size_t kda_chunk_fwd_workspace_size_for(const kda_desc* d, int32_t segment_token
 
 size_t kda_chunk_fwd_workspace_size(const kda_desc* d) {
   if (validate_desc(d) != KDA_OK) return 0;
+  if (pipe_wanted(d)) return layout_for(d, 2 * pipe_chunks(d)).total;
   const int32_t toks = d->T < kDefaultSegmentTokens ? (d->T > 0 ? d->T : 1) : kDefaultSegmentTokens;
   return kda_chunk_fwd_workspace_size_for(d, toks);
 }
@@ -179,35 +304,12 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   const int in_f32 = d->in_dtype == KDA_F32;
   const int out_f32 = d->out_dtype == KDA_F32;
   const int64_t nc_total = num_chunks(d);
-
-  // largest segment whose workspace fits
   const WsLayout one = layout_for(d, 1);
   if (!ws || ws_bytes < one.total) return KDA_ERR_WORKSPACE;
-  int64_t seg_nc = 1;
-  {
-    int64_t lo = 1, hi = nc_total;
-    while (lo < hi) {
-      const int64_t mid = lo + (hi - lo + 1) / 2;
-      if (layout_for(d, mid).total <= ws_bytes)
-        lo = mid;
-      else
-        hi = mid - 1;
-    }
-    seg_nc = lo;
-  }
-  const WsLayout L = layout_for(d, seg_nc);
   char* base = static_cast<char*>(ws);
-  kda::ChunkWs cw{};
-  cw.base = base + L.off_rec;
-  cw.rec_bytes = (int64_t)L.rec_bytes;
-  float* carry = reinterpret_cast<float*>(base + L.off_carry);
-  float* S_run = S_T ? S_T : carry;
 
-  const float* S_in = S0;
-  for (int64_t c0 = 0; c0 < nc_total; c0 += seg_nc) {
-    const int nc = (int)((nc_total - c0) < seg_nc ? (nc_total - c0) : seg_nc);
-    const int t0 = (int)(c0 * kChunk);
-
+  // one segment: records of chunks [c0, c0 + nc) in `recs`; state S_in -> S_out
+  auto launch_intra = [&](int64_t c0, int nc, const kda::ChunkWs& recs, hipStream_t st_) {
     kda::IntraParams ip{};
     ip.q = q;
     ip.k = k;
@@ -217,24 +319,26 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     ip.B = d->B;
     ip.T = d->T;
     ip.H = d->H;
-    ip.t0 = t0;
+    ip.t0 = (int)(c0 * kChunk);
     ip.nc = nc;
     ip.g_min = d->g_min;
     ip.q_scale = d->q_scale;
     ip.l2_eps = d->l2_eps;
     ip.l2norm = d->qk_l2norm;
-    ip.ws = cw;
-    tr.before(s);
-    st = check_launch(kda::launch_intra(ip, D, in_f32, s), s);
-    tr.after(s);
-    if (st != KDA_OK) return st;
-
+    ip.ws = recs;
+    tr.before(st_);
+    const kda_status r = check_launch(kda::launch_intra(ip, D, in_f32, st_), st_);
+    tr.after(st_);
+    return r;
+  };
+  auto launch_scan = [&](int64_t c0, int nc, const kda::ChunkWs& recs, const float* S_in, float* S_out,
+                         hipStream_t st_) {
     kda::ScanParams sp{};
     sp.v = v;
     sp.gate = y ? gate : nullptr;
     sp.rms_w = rms_w;
     sp.S_in = S_in;
-    sp.S_out = S_run;
+    sp.S_out = S_out;
     sp.o = o;  // NULL when only S_T (or only y) is requested
     sp.y = y;
     sp.out_f32 = out_f32;
@@ -242,12 +346,79 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     sp.B = d->B;
     sp.T = d->T;
     sp.H = d->H;
-    sp.t0 = t0;
+    sp.t0 = (int)(c0 * kChunk);
     sp.nc = nc;
-    sp.ws = cw;
-    tr.before(s);
-    st = check_launch(kda::launch_scan(sp, D, in_f32, s), s);
-    tr.after(s);
+    sp.ws = recs;
+    tr.before(st_);
+    const kda_status r = check_launch(kda::launch_scan(sp, D, in_f32, st_), st_);
+    tr.after(st_);
+    return r;
+  };
+
+  const Plan plan = make_plan(d, ws_bytes);
+
+  // ---- overlapped schedule: intra(s + 1) on one stream while scan(s) runs on another
+  if (plan.overlapped) {
+    const int64_t seg_nc = plan.seg_nc;
+    const WsLayout L = layout_for(d, 2 * seg_nc);
+    DeviceCtx& c = g_dev[plan.dev];
+    std::lock_guard<std::mutex> lock(c.mu);
+    hipStream_t si = nullptr, ss = nullptr;
+    if (stream_pair(c, plan.n_scan, &si, &ss)) {
+      const size_t buf_bytes = (size_t)d->B * d->H * seg_nc * L.rec_bytes;
+      kda::ChunkWs bufs[2];
+      for (int j = 0; j < 2; ++j) {
+        bufs[j].base = base + L.off_rec + j * buf_bytes;
+        bufs[j].rec_bytes = (int64_t)L.rec_bytes;
+      }
+      float* carry = reinterpret_cast<float*>(base + L.off_carry);
+      float* S_run = S_T ? S_T : carry;
+      auto ok = [](hipError_t e) {
+        if (e == hipSuccess) return true;
+        (void)hipGetLastError();
+        return false;
+      };
+      if (!ok(hipEventRecord(c.fork, s)) || !ok(hipStreamWaitEvent(si, c.fork, 0)) ||
+          !ok(hipStreamWaitEvent(ss, c.fork, 0)))
+        return KDA_ERR_HIP;
+      const float* S_in = S0;
+      int64_t seg = 0;
+      for (int64_t c0 = 0; c0 < nc_total; c0 += seg_nc, ++seg) {
+        const int nc = (int)((nc_total - c0) < seg_nc ? (nc_total - c0) : seg_nc);
+        const int j = (int)(seg & 1);
+        // buffer j was last read by the scan two segments back
+        if (seg >= 2 && !ok(hipStreamWaitEvent(si, c.scan_done[j], 0))) return KDA_ERR_HIP;
+        st = launch_intra(c0, nc, bufs[j], si);
+        if (st != KDA_OK) return st;
+        if (!ok(hipEventRecord(c.intra_done[j], si)) || !ok(hipStreamWaitEvent(ss, c.intra_done[j], 0)))
+          return KDA_ERR_HIP;
+        st = launch_scan(c0, nc, bufs[j], S_in, S_run, ss);
+        if (st != KDA_OK) return st;
+        if (!ok(hipEventRecord(c.scan_done[j], ss))) return KDA_ERR_HIP;
+        S_in = S_run;
+      }
+      if (!ok(hipEventRecord(c.join_intra, si)) || !ok(hipEventRecord(c.join_scan, ss)) ||
+          !ok(hipStreamWaitEvent(s, c.join_intra, 0)) || !ok(hipStreamWaitEvent(s, c.join_scan, 0)))
+        return KDA_ERR_HIP;
+      return KDA_OK;
+    }
+    return KDA_ERR_HIP;  // unreachable: make_plan created the pair
+  }
+
+  // ---- one stream: segments in turn
+  const int64_t seg_nc = plan.seg_nc;
+  const WsLayout L = layout_for(d, seg_nc);
+  kda::ChunkWs cw{};
+  cw.base = base + L.off_rec;
+  cw.rec_bytes = (int64_t)L.rec_bytes;
+  float* carry = reinterpret_cast<float*>(base + L.off_carry);
+  float* S_run = S_T ? S_T : carry;
+  const float* S_in = S0;
+  for (int64_t c0 = 0; c0 < nc_total; c0 += seg_nc) {
+    const int nc = (int)((nc_total - c0) < seg_nc ? (nc_total - c0) : seg_nc);
+    st = launch_intra(c0, nc, cw, s);
+    if (st != KDA_OK) return st;
+    st = launch_scan(c0, nc, cw, S_in, S_run, s);
     if (st != KDA_OK) return st;
     S_in = S_run;
   }

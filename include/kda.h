@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
   KDA_OK = 0,
@@ -75,6 +75,12 @@ typedef struct {
   int32_t qk_l2norm;     /* 1: L2-normalise q and k inside the kernel               */
   kda_dtype in_dtype;    /* q, k, v, beta, z, gate                                 */
   kda_dtype out_dtype;   /* o, y                                                   */
+  int32_t segment_tokens; /* tokens per internal segment of the overlapped
+                             schedule; 0: library default (8192)                */
+  int32_t overlap;       /* 1: run the intra-chunk kernel of the next segment
+                            concurrently with the scan of the current one
+                            (library-owned streams, see kda_chunk_fwd); 0: one
+                            stream, segments in turn                          */
 } kda_desc;
 
 /* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
@@ -87,15 +93,27 @@ const char* kda_status_str(kda_status s);
 kda_status kda_desc_init(kda_desc* d, int32_t B, int32_t T, int32_t H, int32_t head_dim, kda_dtype in_dtype,
                          kda_dtype out_dtype);
 
-/* Workspace bytes that let kda_chunk_fwd run the whole sequence (at most
- * 65536 tokens per internal segment) in one pass; 0 if *d is invalid.  A
- * smaller workspace also works as long as it holds one chunk: the sequence is
- * then processed in more, shorter segments. */
+/* Workspace bytes for kda_chunk_fwd's preferred schedule; 0 if *d is invalid.
+ * With d->overlap and a sequence longer than one segment this holds two
+ * segments of chunk records (the overlapped schedule); otherwise it holds the
+ * whole sequence (at most 65536 tokens per segment).  A smaller workspace also
+ * works as long as it holds one chunk: the sequence is then processed in more,
+ * shorter segments, one after the other. */
 size_t kda_chunk_fwd_workspace_size(const kda_desc* d);
 
-/* Bytes needed for a segment of `segment_tokens` tokens (rounded up to whole
- * chunks); 0 if *d is invalid. */
+/* Bytes needed for one segment of `segment_tokens` tokens (rounded up to whole
+ * chunks) processed in turn; 0 if *d is invalid. */
 size_t kda_chunk_fwd_workspace_size_for(const kda_desc* d, int32_t segment_tokens);
+
+/*
+ * The schedule kda_chunk_fwd takes on the current device for this descriptor
+ * and a workspace of ws_bytes bytes: *segment_tokens receives the tokens per
+ * segment (a multiple of the chunk), *overlapped 1 for the overlapped schedule
+ * and 0 for segments in turn.  KDA_ERR_WORKSPACE if the workspace is too
+ * small for one chunk.
+ */
+kda_status kda_chunk_fwd_schedule(const kda_desc* d, size_t ws_bytes, int32_t* segment_tokens,
+                                  int32_t* overlapped);
 
 /*
  * Chunked KDA forward over whole sequences (prefill / training forward),
@@ -112,6 +130,19 @@ size_t kda_chunk_fwd_workspace_size_for(const kda_desc* d, int32_t segment_token
  *         the caller; its contents are scratch.  May be NULL when T == 0.
  * At least one of o, y, S_T must be non-NULL.  When d->T == 0 nothing is read:
  * S_T receives S0 (or zeros) and q, k, v, beta, z, A and ws may be NULL.
+ *
+ * Schedule.  The sequence is processed in segments; per segment the
+ * intra-chunk kernel writes one record per chunk into the workspace and the
+ * state scan (with the fused gate) consumes them.  When d->overlap is set, the
+ * sequence spans more than one segment of d->segment_tokens tokens, B * H is
+ * at most 5/8 of the device's compute units and the workspace holds two
+ * segments, the work runs on two library-owned streams of the current device
+ * (created on first use, default priority, each restricted to its own set of
+ * compute units): the intra-chunk kernel of segment s + 1 runs while the scan
+ * of segment s runs, with HIP events ordering both against `stream` at the
+ * start and the end of the call.  The call still behaves as one operation
+ * enqueued on `stream`.  Calls that overlap in time on one device serialise
+ * their enqueue (a per-device lock); they must not share a workspace.
  */
 kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
                          const void* z, const float* A, const float* S0, const void* gate, const float* rms_w,
@@ -122,8 +153,10 @@ kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const 
  * addition, for the i-th kernel launch of the call (launch order per segment:
  * the intra-chunk kernel, then the state scan with the fused gate),
  * hipEventRecord(events[2i]) right before it and hipEventRecord(events[2i+1])
- * right after it on `stream`, while 2i+1 < n_events.  `events` are caller-owned
- * hipEvent_t handles.  Used to measure kernel durations on the launch stream.
+ * right after it on the stream that launch uses (`stream`, or the library's
+ * stream of that kernel in the overlapped schedule), while 2i+1 < n_events.
+ * `events` are caller-owned hipEvent_t handles.  Used to measure kernel
+ * durations on the launch stream.
  */
 kda_status kda_chunk_fwd_traced(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
                                 const void* z, const float* A, const float* S0, const void* gate,

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert {"kda_chunk_fwd", "kda_recurrent_step", "kda_state_io"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kda_abi_version() == 1
+    assert L.kda_abi_version() == 2
     assert L.kda_status_str(6) == b"workspace missing or too small"
 
 
