@@ -38,6 +38,40 @@ def kernel_bytes(name: str, token_heads: int, d: int, BH: int, T: int) -> float:
     raise KeyError(name)
 
 
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources of the library (what a traffic profile was taken with)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "gated_delta_rule_84_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(kernel: str, workload: str):
+    """Measured HBM bytes per launch of `kernel` from the committed counter
+    summary profiles/hbm_traffic_<workload>.txt (rocprofv3 FETCH_SIZE and
+    WRITE_SIZE scaled by a plain-copy calibration), or None when that summary
+    is missing or was taken with different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, _, val = line.partition(":")
+            vals[key.strip()] = val.strip()
+    if vals.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals[f"{kernel}_hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def path_flops_per_token_head(d: int, C: int = 64) -> float:
     # 6 d^2 (state products) + 5 (C + 16) d (sub-tile products) + C^2 / 3 (UT inverse)
     return 6 * d * d + 5 * (C + 16) * d + C * C / 3
@@ -188,7 +222,8 @@ def main() -> int:
                    "inputs": "bf16", "state": "fp32", "outputs": "y (bf16) + S_T (fp32)", "gate": True,
                    "segment_tokens": seg, "overlapped": overlapped},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(dom, wl.name),
+                     "algorithmic_bytes_per_launch": dom_bytes / launches[dom],
                      "launches_per_step": launches[dom], "avg_launch_ms": kern_ms[dom] / launches[dom]},
         "path_roofline": {"achieved_GBs": path_gbs, "frac_hbm": path_gbs / HBM_PEAK_GBS,
                           "achieved_TFLOPs": path_tflops, "frac_bf16_mfma": path_tflops / BF16_PEAK_TFLOPS,

@@ -7,6 +7,7 @@ not been built, every call raises.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 
@@ -60,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_workspace_size.argtypes = [dp]
         L.kda_chunk_fwd_workspace_size_for.restype = sz
         L.kda_chunk_fwd_workspace_size_for.argtypes = [dp, i32]
+        L.kda_release_resources.restype = ctypes.c_int
+        L.kda_release_resources.argtypes = []
         L.kda_chunk_fwd_schedule.restype = ctypes.c_int
         L.kda_chunk_fwd_schedule.argtypes = [dp, sz, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.kda_chunk_fwd.restype = ctypes.c_int
@@ -73,6 +76,7 @@ def lib() -> ctypes.CDLL:
         L.kda_prepass.restype = ctypes.c_int
         L.kda_prepass.argtypes = [dp] + [vp] * 7 + [vp]
         _lib = L
+        atexit.register(release_resources)
     return _lib
 
 
@@ -115,6 +119,14 @@ def workspace_size(desc: KdaDesc, segment_tokens: int | None = None) -> int:
     if segment_tokens is None:
         return int(lib().kda_chunk_fwd_workspace_size(ctypes.byref(desc)))
     return int(lib().kda_chunk_fwd_workspace_size_for(ctypes.byref(desc), int(segment_tokens)))
+
+
+def release_resources() -> None:
+    """Synchronise and destroy the library's own streams and events (the
+    overlapped schedule creates them again when needed).  Registered to run at
+    interpreter exit, while the HIP runtime is still up."""
+    if _lib is not None:
+        _lib.kda_release_resources()
 
 
 def schedule(desc: KdaDesc, ws_bytes: int) -> tuple[int, bool]:

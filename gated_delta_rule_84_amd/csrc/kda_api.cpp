@@ -197,6 +197,35 @@ extern "C" {
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
+kda_status kda_release_resources(void) {
+  kda_status st = KDA_OK;
+  int prev = -1;
+  const bool have_prev = hipGetDevice(&prev) == hipSuccess;
+  for (int dev = 0; dev < kMaxDevices; ++dev) {
+    DeviceCtx& c = g_dev[dev];
+    std::lock_guard<std::mutex> lock(c.mu);
+    if (!c.ready && c.pairs.empty()) continue;
+    if (hipSetDevice(dev) != hipSuccess) {
+      (void)hipGetLastError();
+      st = KDA_ERR_HIP;
+      continue;
+    }
+    for (StreamPair& p : c.pairs)
+      for (hipStream_t q : {p.intra, p.scan})
+        if (hipStreamSynchronize(q) != hipSuccess || hipStreamDestroy(q) != hipSuccess) st = KDA_ERR_HIP;
+    c.pairs.clear();
+    for (hipEvent_t* e : {&c.fork, &c.join_intra, &c.join_scan, &c.intra_done[0], &c.intra_done[1], &c.scan_done[0],
+                          &c.scan_done[1]}) {
+      if (*e != nullptr && hipEventDestroy(*e) != hipSuccess) st = KDA_ERR_HIP;
+      *e = nullptr;
+    }
+    c.ready = false;
+  }
+  if (have_prev) (void)hipSetDevice(prev);
+  (void)hipGetLastError();
+  return st;
+}
+
 kda_status kda_chunk_fwd_schedule(const kda_desc* d, size_t ws_bytes, int32_t* segment_tokens,
                                   int32_t* overlapped) {
   const kda_status st = validate_desc(d);

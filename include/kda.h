@@ -106,6 +106,15 @@ size_t kda_chunk_fwd_workspace_size(const kda_desc* d);
 size_t kda_chunk_fwd_workspace_size_for(const kda_desc* d, int32_t segment_tokens);
 
 /*
+ * Waits for and destroys the streams and events the overlapped schedule
+ * created (on every device); later calls create them again.  Optional: call
+ * before the process or the HIP runtime shuts down when tools that track
+ * queues (profilers) are attached.  Not thread-safe against concurrent calls
+ * of kda_chunk_fwd.
+ */
+kda_status kda_release_resources(void);
+
+/*
  * The schedule kda_chunk_fwd takes on the current device for this descriptor
  * and a workspace of ws_bytes bytes: *segment_tokens receives the tokens per
  * segment (a multiple of the chunk), *overlapped 1 for the overlapped schedule
