@@ -531,25 +531,41 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
 #pragma unroll
         for (int nt = 0; nt < NCT; ++nt) Sb[kk][nt] = Ops::from_acc(S[2 * kk][nt], S[2 * kk + 1][nt]);
 
+      // Every product step below issues the LDS reads of the next step's
+      // operands before its own MFMAs (scheduling fences keep that order), so
+      // the LDS latency overlaps the previous products.
+
       // R = V - (K . Gamma) S (the record holds kg negated; V enters through a
       // 0/1 selection product, rows past the end are zero) and O = (Q . Gamma) S
       f32x4 R[4][NCT];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const V8 vrow = Ops::ld(lds + L::VS + (16 * mt + n) * L::PQ + (32 * wave + 8 * g4) * L::ES);
-        R[mt][0] = mma32(vrow, vsel0, zero4());
-        R[mt][1] = mma32(vrow, vsel1, zero4());
-        O[mt][0] = O[mt][1] = zero4();
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
+      {
+        constexpr int G1 = 4 * KS;  // steps (mt, kk)
+        V8 ak[2], aq[2], av[2];
+        auto ld1 = [&](int g, int bf) {
+          const int mt = g / KS, kk = g % KS;
           const int off = (16 * mt + n) * L::PQ + (32 * kk + 8 * g4) * L::ES;
-          const V8 ak = Ops::ld(kg + off), aq = Ops::ld(qg + off);
+          ak[bf] = Ops::ld(kg + off);
+          aq[bf] = Ops::ld(qg + off);
+          if (kk == 0) av[bf] = Ops::ld(lds + L::VS + (16 * mt + n) * L::PQ + (32 * wave + 8 * g4) * L::ES);
+        };
+        ld1(0, 0);
+#pragma unroll
+        for (int g = 0; g < G1; ++g) {
+          const int bf = g & 1, mt = g / KS, kk = g % KS;
+          if (g + 1 < G1) ld1(g + 1, bf ^ 1);
+          __builtin_amdgcn_sched_barrier(0);
+          if (kk == 0) {
+            R[mt][0] = mma32(av[bf], vsel0, zero4());
+            R[mt][1] = mma32(av[bf], vsel1, zero4());
+            O[mt][0] = O[mt][1] = zero4();
+          }
 #pragma unroll
           for (int nt = 0; nt < NCT; ++nt) {
-            R[mt][nt] = mma32(ak, Sb[kk][nt], R[mt][nt]);
-            O[mt][nt] = mma32(aq, Sb[kk][nt], O[mt][nt]);
+            R[mt][nt] = mma32(ak[bf], Sb[kk][nt], R[mt][nt]);
+            O[mt][nt] = mma32(aq[bf], Sb[kk][nt], O[mt][nt]);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       typename Ops::Prec Rp[2][NCT];
 #pragma unroll
@@ -559,21 +575,42 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
       }
       __syncthreads();  // part A of chunk c consumed; part B of chunk c staged; tile c - 1 done
 
-      // U' = (T Diag(beta)) R   (block lower triangular: tile mt needs steps <= mt/2)
+      // lower-triangular (token tile, K-step) blocks of T Diag(beta) and Tril(A_qk)
+      constexpr int NB = 6;
+      constexpr int BMT[NB] = {0, 1, 2, 2, 3, 3}, BKK[NB] = {0, 0, 0, 1, 0, 1};
+      V8 at[2], ah[2], al[2], k0[2], k1[2];
+      f32x4 gm[2];
+      auto ld_t = [&](int i, int bf) { at[bf] = Ops::ld(tb + (16 * BMT[i] + n) * L::PK + (32 * BKK[i] + 8 * g4) * L::ES); };
+      auto ld_a = [&](int i, int bf) {
+        const int off = (16 * BMT[i] + n) * L::PK + (32 * BKK[i] + 8 * g4) * L::ES;
+        ah[bf] = Ops::ld(aqh + off);
+        al[bf] = Ops::ld(aql + off);
+      };
+      auto ld_s = [&](int mt, int bf) {
+        const int off = (16 * mt + n) * L::PK + 8 * g4 * L::ES;
+        k0[bf] = Ops::ld(kdt + off);
+        k1[bf] = Ops::ld(kdt + off + 32 * L::ES);
+        gm[bf] = *reinterpret_cast<const f32x4*>(gam + 16 * mt + 4 * g4);
+      };
+
+      // U' = (T Diag(beta)) R
       typename Ops::Prec Up[2][NCT];
       {
         f32x4 U[4][NCT];
+        ld_t(0, 0);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int i = 0; i < NB; ++i) {
+          const int bf = i & 1, mt = BMT[i], kk = BKK[i];
+          if (i + 1 < NB)
+            ld_t(i + 1, bf ^ 1);
+          else
+            ld_a(0, 0);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int nt = 0; nt < NCT; ++nt) U[mt][nt] = zero4();
-#pragma unroll
-          for (int kk = 0; kk <= (mt >> 1); ++kk) {
-            const V8 a = Ops::ld(tb + (16 * mt + n) * L::PK + (32 * kk + 8 * g4) * L::ES);
-#pragma unroll
-            for (int nt = 0; nt < NCT; ++nt) U[mt][nt] = Ops::mma_split_b(a, Rp[kk][nt], U[mt][nt]);
-          }
+          for (int nt = 0; nt < NCT; ++nt)
+            U[mt][nt] = Ops::mma_split_b(at[bf], Rp[kk][nt], kk == 0 ? zero4() : U[mt][nt]);
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int nt = 0; nt < NCT; ++nt) {
           Up[0][nt] = Ops::prec_from_acc(U[0][nt], U[1][nt]);
@@ -583,29 +620,32 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
 
       // O += Tril(A_qk) U'
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int i = 0; i < NB; ++i) {
+        const int bf = i & 1, mt = BMT[i], kk = BKK[i];
+        if (i + 1 < NB)
+          ld_a(i + 1, bf ^ 1);
+        else
+          ld_s(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kk = 0; kk <= (mt >> 1); ++kk) {
-          const int off = (16 * mt + n) * L::PK + (32 * kk + 8 * g4) * L::ES;
-          const V8 ah = Ops::ld(aqh + off), al = Ops::ld(aql + off);
-#pragma unroll
-          for (int nt = 0; nt < NCT; ++nt) O[mt][nt] = Ops::mma_prec(ah, al, Up[kk][nt], O[mt][nt]);
-        }
+        for (int nt = 0; nt < NCT; ++nt) O[mt][nt] = Ops::mma_prec(ah[bf], al[bf], Up[kk][nt], O[mt][nt]);
+      }
 
       // S <- Diag(Gamma_last) S + Kd^T U'
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const f32x4 gm = *reinterpret_cast<const f32x4*>(gam + 16 * mt + 4 * g4);
-        const int off = (16 * mt + n) * L::PK + 8 * g4 * L::ES;
-        const V8 a0 = Ops::ld(kdt + off), a1 = Ops::ld(kdt + off + 32 * L::ES);
+        const int bf = mt & 1;
+        if (mt + 1 < MT) ld_s(mt + 1, bf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int nt = 0; nt < NCT; ++nt) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) S[mt][nt][i] *= gm[i];
-          S[mt][nt] = Ops::mma_split_b(a0, Up[0][nt], S[mt][nt]);
-          S[mt][nt] = Ops::mma_split_b(a1, Up[1][nt], S[mt][nt]);
+          for (int i = 0; i < 4; ++i) S[mt][nt][i] *= gm[bf][i];
+          S[mt][nt] = Ops::mma_split_b(k0[bf], Up[0][nt], S[mt][nt]);
+          S[mt][nt] = Ops::mma_split_b(k1[bf], Up[1][nt], S[mt][nt]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
 
       write_tile();     // the helpers finished tile c - 1 before the barrier above
       __syncthreads();  // part B of chunk c consumed; tile c and part A of chunk c + 1 staged
