@@ -61,6 +61,10 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_workspace_size.argtypes = [dp]
         L.kda_chunk_fwd_workspace_size_for.restype = sz
         L.kda_chunk_fwd_workspace_size_for.argtypes = [dp, i32]
+        L.kda_chunk_fwd_snapshots.restype = ctypes.c_int
+        L.kda_chunk_fwd_snapshots.argtypes = [dp] + [vp] * 13 + [i32, vp, sz, vp]
+        L.kda_snapshot_count.restype = i32
+        L.kda_snapshot_count.argtypes = [dp, i32]
         L.kda_release_resources.restype = ctypes.c_int
         L.kda_release_resources.argtypes = []
         L.kda_chunk_fwd_schedule.restype = ctypes.c_int
@@ -141,7 +145,7 @@ def schedule(desc: KdaDesc, ws_bytes: int) -> tuple[int, bool]:
 
 def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=None, want_o=True,
               want_y=None, want_state=True, workspace=None, segment_tokens=None, overlap=True, out=None,
-              events=None, **opts):
+              events=None, snapshot_chunks=0, **opts):
     """KDA forward over whole sequences.  q, k, z: [B, T, H, D]; v (and gate):
     [B, T, H, D]; beta: [B, T, H]; A: [H] fp32; S0: [B, H, D, D] fp32 or None.
     Returns a dict with 'o' / 'y' (out_dtype, default the input dtype) and
@@ -149,7 +153,10 @@ def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=
     (raw hipEvent_t handles) selects the traced entry point.  With
     ``overlap`` the library may run the overlapped schedule in segments of
     ``segment_tokens`` tokens; without it, ``segment_tokens`` sizes the
-    segments processed in turn (default: the whole sequence)."""
+    segments processed in turn (default: the whole sequence).  With
+    ``snapshot_chunks`` = N > 0 the result also holds 'snapshots'
+    [B, n, H, D, D]: the state after every N-th chunk (prefix-cache resume
+    points, n = T // (64 N))."""
     B, T, H, D = q.shape
     in_dt = _dt(q)
     odt = q.dtype if out_dtype is None else out_dtype
@@ -167,6 +174,17 @@ def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=
     if workspace is None:
         nbytes = workspace_size(desc, None if overlap else segment_tokens)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if snapshot_chunks:
+        n = int(lib().kda_snapshot_count(ctypes.byref(desc), int(snapshot_chunks)))
+        if "snapshots" not in res:
+            res["snapshots"] = torch.empty((B, n, H, D, D), dtype=torch.float32, device=dev)
+        rc = lib().kda_chunk_fwd_snapshots(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), _ptr(S0), _ptr(gate),
+            _ptr(rms_w), _ptr(res.get("o")), _ptr(res.get("y")), _ptr(res.get("S_T")), _ptr(res["snapshots"]),
+            int(snapshot_chunks), _ptr(workspace), workspace.numel(), _stream(dev))
+        if rc != 0:
+            raise KdaError("kda_chunk_fwd_snapshots", rc)
+        return res
     args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), _ptr(S0), _ptr(gate),
             _ptr(rms_w), _ptr(res.get("o")), _ptr(res.get("y")), _ptr(res.get("S_T")), _ptr(workspace),
             workspace.numel(), _stream(dev))

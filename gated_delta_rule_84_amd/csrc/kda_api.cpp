@@ -305,12 +305,19 @@ struct Tracer {
   }
 };
 
+struct Snapshots {
+  float* ptr;  // [B, n, H, d_k, d_v] or nullptr
+  int every;   // chunks between snapshots
+  int n;
+};
+
 kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
                           const void* z, const float* A, const float* S0, const void* gate, const float* rms_w,
-                          void* o, void* y, float* S_T, void* ws, size_t ws_bytes, void* stream, Tracer tr) {
+                          void* o, void* y, float* S_T, void* ws, size_t ws_bytes, void* stream, Tracer tr,
+                          Snapshots snap = Snapshots{nullptr, 1, 0}) {
   kda_status st = validate_desc(d);
   if (st != KDA_OK) return st;
-  if (!o && !y && !S_T) return KDA_ERR_NULL_ARG;
+  if (!o && !y && !S_T && !snap.ptr) return KDA_ERR_NULL_ARG;
   if (d->T == 0) {  // nothing to read: S_T = S0 (or zero); inputs may be NULL
     if ((S0 && !aligned(S0, 4)) || (S_T && !aligned(S_T, 4))) return KDA_ERR_MISALIGNED;
     if (S_T && S_T != S0)
@@ -378,6 +385,9 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     sp.t0 = (int)(c0 * kChunk);
     sp.nc = nc;
     sp.ws = recs;
+    sp.snaps = snap.n > 0 ? snap.ptr : nullptr;
+    sp.snap_every = snap.every;
+    sp.n_snap = snap.n;
     tr.before(st_);
     const kda_status r = check_launch(kda::launch_scan(sp, D, in_f32, st_), st_);
     tr.after(st_);
@@ -471,6 +481,30 @@ kda_status kda_chunk_fwd_traced(const kda_desc* d, const void* q, const void* k,
                                 void* stream, void* const* events, int32_t n_events) {
   return chunk_fwd_impl(d, q, k, v, beta, z, A, S0, gate, rms_w, o, y, S_T, ws, ws_bytes, stream,
                         Tracer{events, n_events < 0 ? 0 : n_events});
+}
+
+kda_status kda_chunk_fwd_snapshots(const kda_desc* d, const void* q, const void* k, const void* v,
+                                   const void* beta, const void* z, const float* A, const float* S0,
+                                   const void* gate, const float* rms_w, void* o, void* y, float* S_T,
+                                   float* snapshots, int32_t every_chunks, void* ws, size_t ws_bytes, void* stream) {
+  const kda_status st = validate_desc(d);
+  if (st != KDA_OK) return st;
+  if (every_chunks < 1) return KDA_ERR_BAD_SHAPE;
+  const int32_t n = d->T / (kChunk * every_chunks);
+  if (n == 0) {  // no boundary to snapshot: the plain forward, if any output is asked for
+    if (!o && !y && !S_T) return KDA_OK;
+    return chunk_fwd_impl(d, q, k, v, beta, z, A, S0, gate, rms_w, o, y, S_T, ws, ws_bytes, stream,
+                          Tracer{nullptr, 0});
+  }
+  if (!snapshots) return KDA_ERR_NULL_ARG;
+  if (!aligned(snapshots, 4)) return KDA_ERR_MISALIGNED;
+  return chunk_fwd_impl(d, q, k, v, beta, z, A, S0, gate, rms_w, o, y, S_T, ws, ws_bytes, stream, Tracer{nullptr, 0},
+                        Snapshots{snapshots, every_chunks, n});
+}
+
+int32_t kda_snapshot_count(const kda_desc* d, int32_t every_chunks) {
+  if (validate_desc(d) != KDA_OK || every_chunks < 1) return 0;
+  return d->T / (kChunk * every_chunks);
 }
 
 kda_status kda_recurrent_step(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,

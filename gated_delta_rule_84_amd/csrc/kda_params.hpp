@@ -70,7 +70,17 @@ struct ScanParams {
   int B, T, H;
   int t0, nc;           // first token and number of chunks of the segment
   ChunkWs ws;
+  float* snaps;         // [B, n_snap, H, D, D] states at every snap_every-th chunk boundary, or nullptr
+  int snap_every;       // chunks between snapshots (snapshot j: state after chunk (j + 1) * snap_every - 1)
+  int n_snap;
 };
+
+// Whether the state after chunk `cg` (global index) is snapshot j, and which.
+__device__ __forceinline__ int snapshot_index(const ScanParams& p, int cg) {
+  if (p.snaps == nullptr || (cg + 1) % p.snap_every != 0) return -1;
+  const int j = (cg + 1) / p.snap_every - 1;
+  return j < p.n_snap ? j : -1;
+}
 
 struct DecodeParams {
   const void* q;

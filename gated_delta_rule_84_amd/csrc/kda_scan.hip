@@ -346,6 +346,18 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
       S[mt] = Ops::mma_split_b(Ops::ld(kdt + off + 32 * L::ES), Up[1], S[mt]);
     }
 
+    // prefix-cache snapshot of the state after this chunk
+    {
+      const int j = snapshot_index(p, p.t0 / kChunk + c);
+      if (j >= 0) {
+        float* sn = p.snaps + (((int64_t)b * p.n_snap + j) * p.H + h) * D * D;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sn[(16 * mt + 4 * g4 + i) * D + col] = S[mt][i];
+      }
+    }
+
     // O tile to LDS (when it shares the record's space, wait until no wave
     // reads the record any more)
     if constexpr (L::O_ALIAS) __syncthreads();
@@ -648,6 +660,19 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
       __builtin_amdgcn_sched_barrier(0);
 
       write_tile();     // the helpers finished tile c - 1 before the barrier above
+      {
+        // prefix-cache snapshot of the state after this chunk
+        const int j = snapshot_index(p, p.t0 / kChunk + c);
+        if (j >= 0) {
+          float* sn = p.snaps + (((int64_t)b * p.n_snap + j) * p.H + h) * D * D;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NCT; ++nt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sn[(16 * mt + 4 * g4 + i) * D + col0 + 16 * nt] = S[mt][nt][i];
+        }
+      }
       __syncthreads();  // part B of chunk c consumed; tile c and part A of chunk c + 1 staged
     }
 

@@ -173,6 +173,29 @@ kda_status kda_chunk_fwd_traced(const kda_desc* d, const void* q, const void* k,
                                 void* stream, void* const* events, int32_t n_events);
 
 /*
+ * Prefix-cache snapshots: kda_chunk_fwd plus the recurrent state at every
+ * `every_chunks`-th chunk boundary (K3 blog section 13.1: a cached prefix of
+ * a KDA layer is reusable only as the state at a chunk-aligned boundary).
+ * snapshots is fp32 [B, n, H, d_k, d_v] with n = kda_snapshot_count(d,
+ * every_chunks) = floor(T / (64 * every_chunks)); snapshot j of sequence b is
+ * the state after token (j + 1) * 64 * every_chunks - 1, i.e. the S0 with
+ * which a forward over the remaining tokens resumes (bit-identically).
+ * o, y and S_T may all be NULL here (then n == 0 does nothing and
+ * snapshots may be NULL whenever n == 0).  The snapshots share the forward's
+ * launches: each scan workgroup stores its head's state (64 KiB at d = 128)
+ * when it crosses a snapshot boundary.  KDA_ERR_BAD_SHAPE if
+ * every_chunks < 1.
+ */
+kda_status kda_chunk_fwd_snapshots(const kda_desc* d, const void* q, const void* k, const void* v,
+                                   const void* beta, const void* z, const float* A, const float* S0,
+                                   const void* gate, const float* rms_w, void* o, void* y, float* S_T,
+                                   float* snapshots, int32_t every_chunks, void* ws, size_t ws_bytes, void* stream);
+
+/* Number of snapshots kda_chunk_fwd_snapshots writes per sequence (0 if *d is
+ * invalid or every_chunks < 1). */
+int32_t kda_snapshot_count(const kda_desc* d, int32_t every_chunks);
+
+/*
  * One decode step (single token) for d->B sequences: the same recurrence,
  * section 2.1, applied to one token.  d->T must be 1.  Each sequence n reads
  * and updates its state in place at S_pool[slot[n]] (slot == NULL: slot n):

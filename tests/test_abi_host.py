@@ -100,3 +100,23 @@ def test_no_cpu_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(kda, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         kda.lib()
+
+
+def _snap(d, snaps=FAKE, every=1, o=FAKE, ST=None):
+    return kda.lib().kda_chunk_fwd_snapshots(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                                             o, None, ST, snaps, every, FAKE, 1 << 40, None)
+
+
+def test_snapshot_host_errors_and_count():
+    L = kda.lib()
+    d = _desc(T=1000)                                             # 15 full chunks + a tail
+    assert L.kda_snapshot_count(ctypes.byref(d), 1) == 15
+    assert L.kda_snapshot_count(ctypes.byref(d), 4) == 3
+    assert L.kda_snapshot_count(ctypes.byref(d), 16) == 0
+    assert L.kda_snapshot_count(ctypes.byref(d), 0) == 0
+    assert L.kda_snapshot_count(ctypes.byref(_desc(d_k=96, d_v=96)), 1) == 0
+    assert _snap(d, every=0) == 2
+    assert _snap(d, snaps=None) == 1                              # 15 boundaries need the buffer
+    assert _snap(d, snaps=FAKE + 2) == 4
+    assert _snap(_desc(T=1000, chunk=32)) == 5
+    assert _snap(d, every=16, snaps=None, o=None) == 0            # no boundary, no output: nothing to do
