@@ -4,12 +4,16 @@ One step = one kda_chunk_fwd call over the K3-shaped layer workload
 (B1, T65536, H96, d128, bf16 inputs, fp32 state, output gate, y and S_T
 outputs), inputs already resident in HBM.  Prints ONE JSON line.
 
-Per-kernel durations come from HIP events recorded by the library around each
-of its launches on the launch stream (kda_chunk_fwd_traced); the dominant
-kernel's roofline uses its algorithmic bytes:
+The library picks the schedule (the fused kernel when B * H fills the
+device, else the overlapped two-kernel schedule); --schedule forces one.  Per-kernel durations come from HIP events
+recorded by the library around each of its launches on the launch stream
+(kda_chunk_fwd_traced); the dominant kernel's roofline uses its algorithmic
+bytes:
+  fused       : q, k, z, v, gate logits (5 * 2d B) + beta (2 B) in, y out
+                (2d B) per token-head, + initial and final state
   intra-chunk : q, k, z (3 * 2d B) + beta (2 B) per token-head
   state scan  : v, gate logits in, y out (3 * 2d B) per token-head + final state
-which add up to the path's 1,538 B per token-head (2d = 256 B at d = 128).
+i.e. the path's 1,538 B per token-head (2d = 256 B at d = 128).
 The CPU baseline is the fp64 C oracle timed on a bounded sample of heads.
 """
 from __future__ import annotations
@@ -29,8 +33,11 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 
 
 def kernel_bytes(name: str, token_heads: int, d: int, BH: int, T: int) -> float:
-    """Algorithmic HBM bytes of one launch (its share of the path's inputs and
-    outputs; intermediates between the two kernels are not algorithmic)."""
+    """Algorithmic HBM bytes of one kernel's launches in a step (its share of
+    the path's inputs and outputs; intermediates between the two kernels are
+    not algorithmic)."""
+    if name == "fused":
+        return token_heads * (6 * 2 * d + 2) + 2 * BH * d * d * 4  # every input and output
     if name == "intra":
         return token_heads * (3 * 2 * d + 2)          # q, k, z, beta
     if name == "scan":
@@ -99,10 +106,10 @@ def main() -> int:
     ap.add_argument("--workload", default="k3_layer")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-baseline sample (0: all heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--schedule", choices=("auto", "fused", "overlapped", "segments"), default="auto",
+                    help="the library's choice (default), the fused kernel, or a two-kernel schedule")
     ap.add_argument("--segment-tokens", type=int, default=0,
-                    help="tokens per segment of the overlapped schedule; 0: library default")
-    ap.add_argument("--no-overlap", action="store_true",
-                    help="one stream, segments in turn (the whole sequence per segment by default)")
+                    help="tokens per segment of the two-kernel schedules; 0: library default")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of GIB GiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -150,20 +157,24 @@ def main() -> int:
     odt = torch.bfloat16
     out = {"y": torch.empty((B, T, H, D), dtype=odt, device=dev),
            "S_T": torch.empty((B, H, D, D), dtype=torch.float32, device=dev)}
-    overlap = not args.no_overlap
+    fused = {"auto": None, "fused": True}.get(args.schedule, False)
+    overlap = args.schedule in ("auto", "overlapped")
     seg_arg = args.segment_tokens or None
     desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg_arg if overlap else 0,
-                         overlap=overlap)
-    ws_bytes = kda.workspace_size(desc) if (overlap or not seg_arg) else kda.workspace_size(desc, seg_arg)
+                         overlap=overlap, fused=fused)
+    ws_bytes = kda.workspace_size(desc) if (overlap or fused or not seg_arg) else kda.workspace_size(desc, seg_arg)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    seg, overlapped = kda.schedule(desc, ws_bytes)
+    seg, sched = kda.schedule(desc, ws_bytes)
+    assert args.schedule == "auto" or sched == args.schedule or (args.schedule == "overlapped" and
+                                                                 sched == "segments"), sched
     n_seg = -(-T // seg)
-    names = ["intra", "scan"] * n_seg  # launch order: per segment, intra then scan
+    # launch order: one fused launch, or per segment the intra-chunk kernel then the scan
+    names = ["fused"] if sched == "fused" else ["intra", "scan"] * n_seg
 
     def step(events=None):
         kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t.get("S0"), gate=t["gate"],
                       want_o=False, out=out, workspace=ws, events=events, segment_tokens=seg_arg,
-                      overlap=overlap)
+                      overlap=overlap, fused=fused)
 
     for _ in range(args.warmup):
         step()
@@ -220,7 +231,7 @@ def main() -> int:
         "data": "synthetic (seeded; K3 layer shapes, no trained weights)",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "d_k": D, "d_v": D, "chunk": 64,
                    "inputs": "bf16", "state": "fp32", "outputs": "y (bf16) + S_T (fp32)", "gate": True,
-                   "segment_tokens": seg, "overlapped": overlapped},
+                   "schedule": sched, "segment_tokens": seg},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(dom, wl.name),
                      "algorithmic_bytes_per_launch": dom_bytes / launches[dom],

@@ -30,7 +30,7 @@ class KdaDesc(ctypes.Structure):
                 ("g_min", ctypes.c_float), ("q_scale", ctypes.c_float), ("l2_eps", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("qk_l2norm", ctypes.c_int32),
                 ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
-                ("segment_tokens", ctypes.c_int32), ("overlap", ctypes.c_int32)]
+                ("segment_tokens", ctypes.c_int32), ("overlap", ctypes.c_int32), ("fused", ctypes.c_int32)]
 
 
 class KdaError(RuntimeError):
@@ -107,13 +107,14 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 def make_desc(B, T, H, D, in_dtype, out_dtype, g_min=-5.0, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6,
-              qk_l2norm=True, segment_tokens=0, overlap=True) -> KdaDesc:
+              qk_l2norm=True, segment_tokens=0, overlap=True, fused=None) -> KdaDesc:
     d = KdaDesc()
     rc = lib().kda_desc_init(ctypes.byref(d), B, T, H, D, in_dtype, out_dtype)
     if rc != 0:
         raise KdaError("kda_desc_init", rc)
     d.g_min, d.q_scale, d.l2_eps, d.rms_eps, d.qk_l2norm = g_min, q_scale, l2_eps, rms_eps, int(bool(qk_l2norm))
     d.segment_tokens, d.overlap = int(segment_tokens or 0), int(bool(overlap))
+    d.fused = 1 if fused is None else (2 if fused else 0)  # None: the library decides
     return d
 
 
@@ -133,24 +134,29 @@ def release_resources() -> None:
         _lib.kda_release_resources()
 
 
-def schedule(desc: KdaDesc, ws_bytes: int) -> tuple[int, bool]:
-    """(tokens per segment, overlapped) that kda_chunk_fwd uses on the current
-    device for this descriptor and workspace size."""
-    seg, ovl = ctypes.c_int32(0), ctypes.c_int32(0)
-    rc = lib().kda_chunk_fwd_schedule(ctypes.byref(desc), int(ws_bytes), ctypes.byref(seg), ctypes.byref(ovl))
+SCHEDULES = {0: "segments", 1: "overlapped", 2: "fused"}
+
+
+def schedule(desc: KdaDesc, ws_bytes: int) -> tuple[int, str]:
+    """(tokens per segment, schedule name) that kda_chunk_fwd uses on the
+    current device for this descriptor and workspace size."""
+    seg, sch = ctypes.c_int32(0), ctypes.c_int32(0)
+    rc = lib().kda_chunk_fwd_schedule(ctypes.byref(desc), int(ws_bytes), ctypes.byref(seg), ctypes.byref(sch))
     if rc != 0:
         raise KdaError("kda_chunk_fwd_schedule", rc)
-    return int(seg.value), bool(ovl.value)
+    return int(seg.value), SCHEDULES[int(sch.value)]
 
 
 def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=None, want_o=True,
-              want_y=None, want_state=True, workspace=None, segment_tokens=None, overlap=True, out=None,
-              events=None, snapshot_chunks=0, **opts):
+              want_y=None, want_state=True, workspace=None, segment_tokens=None, overlap=True, fused=None,
+              out=None, events=None, snapshot_chunks=0, **opts):
     """KDA forward over whole sequences.  q, k, z: [B, T, H, D]; v (and gate):
     [B, T, H, D]; beta: [B, T, H]; A: [H] fp32; S0: [B, H, D, D] fp32 or None.
     Returns a dict with 'o' / 'y' (out_dtype, default the input dtype) and
     'S_T' (fp32).  ``out`` may supply preallocated output tensors; ``events``
     (raw hipEvent_t handles) selects the traced entry point.  With
+    ``fused`` True (bf16 inputs) one fused kernel runs the whole forward, with
+    None the library picks it when B * H fills the device; otherwise, with
     ``overlap`` the library may run the overlapped schedule in segments of
     ``segment_tokens`` tokens; without it, ``segment_tokens`` sizes the
     segments processed in turn (default: the whole sequence).  With
@@ -161,7 +167,7 @@ def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=
     in_dt = _dt(q)
     odt = q.dtype if out_dtype is None else out_dtype
     desc = make_desc(B, T, H, D, in_dt, _dt(torch.empty(0, dtype=odt)),
-                     segment_tokens=(segment_tokens or 0) if overlap else 0, overlap=overlap, **opts)
+                     segment_tokens=(segment_tokens or 0) if overlap else 0, overlap=overlap, fused=fused, **opts)
     want_y = (gate is not None) if want_y is None else want_y
     res = dict(out or {})
     dev = q.device

@@ -55,7 +55,8 @@ kda_status validate_desc(const kda_desc* d) {
   if (d->chunk != kChunk) return KDA_ERR_UNSUPPORTED;
   if (!(d->g_min < 0.0f) || d->g_min < -5.5f) return KDA_ERR_UNSUPPORTED;
   if (!(d->l2_eps >= 0.0f) || !(d->rms_eps >= 0.0f)) return KDA_ERR_UNSUPPORTED;
-  if (d->segment_tokens < 0 || (d->overlap != 0 && d->overlap != 1)) return KDA_ERR_BAD_SHAPE;
+  if (d->segment_tokens < 0 || (d->overlap != 0 && d->overlap != 1) || d->fused < 0 || d->fused > 2)
+    return KDA_ERR_BAD_SHAPE;
   return KDA_OK;
 }
 
@@ -95,6 +96,35 @@ int64_t pipe_chunks(const kda_desc* d) {
 // The overlapped schedule is worth it when the sequence spans more than one
 // segment; its workspace holds two segments of records.
 bool pipe_wanted(const kda_desc* d) { return d->overlap != 0 && num_chunks(d) > pipe_chunks(d); }
+
+// Compute units of the current device (0 if unknown), cached per device.
+int device_cus() {
+  static std::mutex mu;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0 && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    cus[dev] = 0;
+  }
+  return cus[dev];
+}
+
+// The fused kernel (records in LDS, no workspace) serves bf16 inputs.  One
+// workgroup per (head, sequence) carries the whole intra-chunk work of its
+// head on one compute unit, so it pays off once there are at least as many
+// (head, sequence) pairs as compute units (fused == 1); fused == 2 forces it.
+bool fused_wanted(const kda_desc* d) {
+  if (d->fused == 0 || !kda::fused_supported(d->d_k, d->in_dtype == KDA_F32)) return false;
+  if (d->fused == 2) return true;
+  const int cus = device_cus();
+  return cus > 0 && (int64_t)d->B * d->H >= cus;
+}
+constexpr size_t kFusedWorkspace = 256;  // what the size query reports for it (nothing is used)
 
 // ---- per-device streams and events of the overlapped schedule --------------
 struct StreamPair {
@@ -160,10 +190,12 @@ struct Plan {
   bool overlapped;
   int dev;
   int n_scan;
+  bool fused;
 };
 Plan make_plan(const kda_desc* d, size_t ws_bytes) {
-  Plan p{1, false, 0, 0};
+  Plan p{1, false, 0, 0, false};
   const int64_t nc_total = num_chunks(d);
+  if (fused_wanted(d)) return Plan{nc_total < 1 ? 1 : nc_total, false, 0, 0, true};
   if (pipe_wanted(d)) {
     const int64_t seg_nc = pipe_chunks(d);
     int dev = 0;
@@ -175,7 +207,7 @@ Plan make_plan(const kda_desc* d, size_t ws_bytes) {
       const int n_scan = (int)((bh + 7) / 8 * 8);
       hipStream_t si = nullptr, ss = nullptr;
       if (ctx_ready(c, dev) && bh * 8 <= (int64_t)c.cus * 5 && stream_pair(c, n_scan, &si, &ss))
-        return Plan{seg_nc, true, dev, n_scan};
+        return Plan{seg_nc, true, dev, n_scan, false};
     }
   }
   // one stream: the largest segment whose workspace fits
@@ -227,14 +259,14 @@ kda_status kda_release_resources(void) {
 }
 
 kda_status kda_chunk_fwd_schedule(const kda_desc* d, size_t ws_bytes, int32_t* segment_tokens,
-                                  int32_t* overlapped) {
+                                  int32_t* schedule) {
   const kda_status st = validate_desc(d);
   if (st != KDA_OK) return st;
-  if (!segment_tokens || !overlapped) return KDA_ERR_NULL_ARG;
-  if (ws_bytes < layout_for(d, 1).total) return KDA_ERR_WORKSPACE;
+  if (!segment_tokens || !schedule) return KDA_ERR_NULL_ARG;
+  if (!fused_wanted(d) && ws_bytes < layout_for(d, 1).total) return KDA_ERR_WORKSPACE;
   const Plan p = make_plan(d, ws_bytes);
   *segment_tokens = (int32_t)(p.seg_nc * kChunk);
-  *overlapped = p.overlapped ? 1 : 0;
+  *schedule = p.fused ? KDA_SCHEDULE_FUSED : p.overlapped ? KDA_SCHEDULE_OVERLAPPED : KDA_SCHEDULE_SEGMENTS;
   return KDA_OK;
 }
 
@@ -271,6 +303,7 @@ kda_status kda_desc_init(kda_desc* d, int32_t B, int32_t T, int32_t H, int32_t h
   d->out_dtype = out_dtype;
   d->segment_tokens = 0;
   d->overlap = 1;
+  d->fused = 1;
   return validate_desc(d);
 }
 
@@ -282,6 +315,7 @@ size_t kda_chunk_fwd_workspace_size_for(const kda_desc* d, int32_t segment_token
 
 size_t kda_chunk_fwd_workspace_size(const kda_desc* d) {
   if (validate_desc(d) != KDA_OK) return 0;
+  if (fused_wanted(d)) return kFusedWorkspace;
   if (pipe_wanted(d)) return layout_for(d, 2 * pipe_chunks(d)).total;
   const int32_t toks = d->T < kDefaultSegmentTokens ? (d->T > 0 ? d->T : 1) : kDefaultSegmentTokens;
   return kda_chunk_fwd_workspace_size_for(d, toks);
@@ -340,8 +374,8 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   const int in_f32 = d->in_dtype == KDA_F32;
   const int out_f32 = d->out_dtype == KDA_F32;
   const int64_t nc_total = num_chunks(d);
-  const WsLayout one = layout_for(d, 1);
-  if (!ws || ws_bytes < one.total) return KDA_ERR_WORKSPACE;
+  const bool fused = fused_wanted(d);
+  if (!fused && (!ws || ws_bytes < layout_for(d, 1).total)) return KDA_ERR_WORKSPACE;
   char* base = static_cast<char*>(ws);
 
   // one segment: records of chunks [c0, c0 + nc) in `recs`; state S_in -> S_out
@@ -395,6 +429,47 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   };
 
   const Plan plan = make_plan(d, ws_bytes);
+
+  // ---- fused schedule: one launch, records in LDS
+  if (plan.fused) {
+    kda::IntraParams ip{};
+    ip.q = q;
+    ip.k = k;
+    ip.z = z;
+    ip.beta = beta;
+    ip.A = A;
+    ip.B = d->B;
+    ip.T = d->T;
+    ip.H = d->H;
+    ip.t0 = 0;
+    ip.nc = (int)nc_total;
+    ip.g_min = d->g_min;
+    ip.q_scale = d->q_scale;
+    ip.l2_eps = d->l2_eps;
+    ip.l2norm = d->qk_l2norm;
+    kda::ScanParams sp{};
+    sp.v = v;
+    sp.gate = y ? gate : nullptr;
+    sp.rms_w = rms_w;
+    sp.S_in = S0;
+    sp.S_out = S_T;  // NULL: the final state is not stored
+    sp.o = o;
+    sp.y = y;
+    sp.out_f32 = out_f32;
+    sp.rms_eps = d->rms_eps;
+    sp.B = d->B;
+    sp.T = d->T;
+    sp.H = d->H;
+    sp.t0 = 0;
+    sp.nc = (int)nc_total;
+    sp.snaps = snap.n > 0 ? snap.ptr : nullptr;
+    sp.snap_every = snap.every;
+    sp.n_snap = snap.n;
+    tr.before(s);
+    const kda_status r = check_launch(kda::launch_fused(ip, sp, D, in_f32, s), s);
+    tr.after(s);
+    return r;
+  }
 
   // ---- overlapped schedule: intra(s + 1) on one stream while scan(s) runs on another
   if (plan.overlapped) {

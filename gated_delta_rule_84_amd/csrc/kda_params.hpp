@@ -126,6 +126,10 @@ struct PrepassParams {
 // Host launchers (one per kernel family).  in_f32: inputs are fp32 (else bf16).
 hipError_t launch_intra(const IntraParams& p, int D, int in_f32, hipStream_t s);
 hipError_t launch_scan(const ScanParams& p, int D, int in_f32, hipStream_t s);
+// Fused forward of whole sequences (ip.t0 = p.t0 = 0, p.nc = every chunk; the
+// record workspaces are not used).  Only where fused_supported().
+bool fused_supported(int D, int in_f32);
+hipError_t launch_fused(const IntraParams& ip, const ScanParams& p, int D, int in_f32, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int D, int in_f32, hipStream_t s);
 hipError_t launch_state_io(const StateIoParams& p, int D, hipStream_t s);
 hipError_t launch_prepass(const PrepassParams& p, int D, int in_f32, hipStream_t s);

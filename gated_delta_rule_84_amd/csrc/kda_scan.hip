@@ -27,63 +27,9 @@
 // fp32 accumulation; the residual V - (K . Gamma) S and U' are split into
 // hi/lo bf16 parts where they are multiplied (T R, Kd^T U'); Tril(A_qk) U'
 // uses hi/lo parts on both sides; S stays fp32.  The fp32 path uses fp32 MFMA.
-#include "kda_common.hpp"
-#include "kda_params.hpp"
-
-#include <type_traits>
+#include "kda_scan_core.hpp"
 
 namespace kda {
-
-template <typename T>
-struct ScanOps;
-
-template <>
-struct ScanOps<uint16_t> {
-  using V8 = bf16x8;
-  struct Prec {  // operand of a split product
-    bf16x8 hi, lo;
-  };
-  static __device__ __forceinline__ V8 ld(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
-  static __device__ __forceinline__ V8 from_acc(const f32x4& a, const f32x4& b) { return acc_pair_to_bf16(a, b); }
-  static __device__ __forceinline__ Prec prec_from_acc(const f32x4& a, const f32x4& b) {
-    Prec r;
-    acc_pair_split(a, b, r.hi, r.lo);
-    return r;
-  }
-  static __device__ __forceinline__ f32x4 mma_prec(const V8& ah, const V8& al, const Prec& b, f32x4 acc) {
-    return mma32_x3(ah, al, b.hi, b.lo, acc);
-  }
-  // a (bf16) times a split operand: a * hi + a * lo
-  static __device__ __forceinline__ f32x4 mma_split_b(const V8& a, const Prec& b, f32x4 acc) {
-    acc = mma32(a, b.lo, acc);
-    return mma32(a, b.hi, acc);
-  }
-  static __device__ __forceinline__ float in_f32(uint16_t x) { return bf16_to_f32(x); }
-};
-
-template <>
-struct ScanOps<float> {
-  using V8 = f32x8;
-  struct Prec {
-    f32x8 v;
-  };
-  static __device__ __forceinline__ V8 ld(const char* p) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 16);
-    return f32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  }
-  static __device__ __forceinline__ V8 from_acc(const f32x4& a, const f32x4& b) { return acc_pair_to_f32(a, b); }
-  static __device__ __forceinline__ Prec prec_from_acc(const f32x4& a, const f32x4& b) {
-    return Prec{acc_pair_to_f32(a, b)};
-  }
-  static __device__ __forceinline__ f32x4 mma_prec(const V8& ah, const V8&, const Prec& b, f32x4 acc) {
-    return mma32(ah, b.v, acc);
-  }
-  static __device__ __forceinline__ f32x4 mma_split_b(const V8& a, const Prec& b, f32x4 acc) {
-    return mma32(a, b.v, acc);
-  }
-  static __device__ __forceinline__ float in_f32(float x) { return x; }
-};
 
 // LDS image of one chunk record (rows padded by 16 bytes so that the 16 rows
 // read by one MFMA operand load hit distinct banks), the V slab and the output
@@ -469,220 +415,20 @@ struct WsLds {
   static constexpr bool FITS = BYTES <= 160 * 1024 && PA + PB + PG <= 40;
 };
 
-// 0/1 selection operand for the V product: K-slot j of lane group g is column
-// 8 g + j of the wave's 32 columns; output column n of tile nt is column
-// 16 nt + n.
-template <typename V8>
-__device__ __forceinline__ V8 v_select(int n, int g, int nt) {
-  V8 s;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) s[j] = (8 * g + j == 16 * nt + n) ? 1.0f : 0.0f;
-  return s;
-}
-
 template <typename T, int D, bool OUT_F32>
 __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const ScanParams p) {
-  using Ops = ScanOps<T>;
-  using V8 = typename Ops::V8;
   using L = WsLds<T, D>;
-  using OutT = typename std::conditional<OUT_F32, float, uint16_t>::type;
-  constexpr int MT = D / 16;
-  constexpr int KS = D / 32;
-  constexpr int NCT = 2;  // 16-column tiles per compute wave
   __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, g4 = lane >> 4;
   const int h = blockIdx.x, b = blockIdx.y;
   const int64_t bh = (int64_t)b * p.H + h;
   const int64_t tok_stride = (int64_t)p.H * D;
   const int64_t head_base = ((int64_t)b * p.T * p.H + h) * D;
-  float* otile = reinterpret_cast<float*>(lds + L::OT);
 
   if (wave < L::NCW) {
-    // ======================= compute waves =======================
-    const int col0 = 32 * wave + n;  // column of tile nt: col0 + 16 nt
-    f32x4 S[MT][NCT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NCT; ++nt) S[mt][nt] = zero4();
-    if (p.S_in != nullptr) {
-      const float* s0 = p.S_in + bh * D * D;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NCT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) S[mt][nt][i] = s0[(16 * mt + 4 * g4 + i) * D + col0 + 16 * nt];
-    }
-    const V8 vsel0 = v_select<V8>(n, g4, 0), vsel1 = v_select<V8>(n, g4, 1);
-    const char* qg = lds + L::QG;
-    const char* kg = lds + L::KG;
-    const char* kdt = lds + L::KDT;
-    const char* tb = lds + L::TB;
-    const char* aqh = lds + L::AQH;
-    const char* aql = lds + L::AQL;
-    const float* gam = reinterpret_cast<const float*>(lds + L::GAM);
-    __syncthreads();  // part A of chunk 0 staged
-
-    f32x4 O[4][NCT];  // outputs of the chunk
-    auto write_tile = [&]() {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NCT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) otile[(16 * mt + 4 * g4 + i) * L::PO + col0 + 16 * nt] = O[mt][nt][i];
-    };
-    for (int c = 0; c < p.nc; ++c) {
-      V8 Sb[KS][NCT];
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-        for (int nt = 0; nt < NCT; ++nt) Sb[kk][nt] = Ops::from_acc(S[2 * kk][nt], S[2 * kk + 1][nt]);
-
-      // Every product step below issues the LDS reads of the next step's
-      // operands before its own MFMAs (scheduling fences keep that order), so
-      // the LDS latency overlaps the previous products.
-
-      // R = V - (K . Gamma) S (the record holds kg negated; V enters through a
-      // 0/1 selection product, rows past the end are zero) and O = (Q . Gamma) S
-      f32x4 R[4][NCT];
-      {
-        constexpr int G1 = 4 * KS;  // steps (mt, kk)
-        V8 ak[2], aq[2], av[2];
-        auto ld1 = [&](int g, int bf) {
-          const int mt = g / KS, kk = g % KS;
-          const int off = (16 * mt + n) * L::PQ + (32 * kk + 8 * g4) * L::ES;
-          ak[bf] = Ops::ld(kg + off);
-          aq[bf] = Ops::ld(qg + off);
-          if (kk == 0) av[bf] = Ops::ld(lds + L::VS + (16 * mt + n) * L::PQ + (32 * wave + 8 * g4) * L::ES);
-        };
-        ld1(0, 0);
-#pragma unroll
-        for (int g = 0; g < G1; ++g) {
-          const int bf = g & 1, mt = g / KS, kk = g % KS;
-          if (g + 1 < G1) ld1(g + 1, bf ^ 1);
-          __builtin_amdgcn_sched_barrier(0);
-          if (kk == 0) {
-            R[mt][0] = mma32(av[bf], vsel0, zero4());
-            R[mt][1] = mma32(av[bf], vsel1, zero4());
-            O[mt][0] = O[mt][1] = zero4();
-          }
-#pragma unroll
-          for (int nt = 0; nt < NCT; ++nt) {
-            R[mt][nt] = mma32(ak[bf], Sb[kk][nt], R[mt][nt]);
-            O[mt][nt] = mma32(aq[bf], Sb[kk][nt], O[mt][nt]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      typename Ops::Prec Rp[2][NCT];
-#pragma unroll
-      for (int nt = 0; nt < NCT; ++nt) {
-        Rp[0][nt] = Ops::prec_from_acc(R[0][nt], R[1][nt]);
-        Rp[1][nt] = Ops::prec_from_acc(R[2][nt], R[3][nt]);
-      }
-      __syncthreads();  // part A of chunk c consumed; part B of chunk c staged; tile c - 1 done
-
-      // lower-triangular (token tile, K-step) blocks of T Diag(beta) and Tril(A_qk)
-      constexpr int NB = 6;
-      constexpr int BMT[NB] = {0, 1, 2, 2, 3, 3}, BKK[NB] = {0, 0, 0, 1, 0, 1};
-      V8 at[2], ah[2], al[2], k0[2], k1[2];
-      f32x4 gm[2];
-      auto ld_t = [&](int i, int bf) { at[bf] = Ops::ld(tb + (16 * BMT[i] + n) * L::PK + (32 * BKK[i] + 8 * g4) * L::ES); };
-      auto ld_a = [&](int i, int bf) {
-        const int off = (16 * BMT[i] + n) * L::PK + (32 * BKK[i] + 8 * g4) * L::ES;
-        ah[bf] = Ops::ld(aqh + off);
-        al[bf] = Ops::ld(aql + off);
-      };
-      auto ld_s = [&](int mt, int bf) {
-        const int off = (16 * mt + n) * L::PK + 8 * g4 * L::ES;
-        k0[bf] = Ops::ld(kdt + off);
-        k1[bf] = Ops::ld(kdt + off + 32 * L::ES);
-        gm[bf] = *reinterpret_cast<const f32x4*>(gam + 16 * mt + 4 * g4);
-      };
-
-      // U' = (T Diag(beta)) R
-      typename Ops::Prec Up[2][NCT];
-      {
-        f32x4 U[4][NCT];
-        ld_t(0, 0);
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-          const int bf = i & 1, mt = BMT[i], kk = BKK[i];
-          if (i + 1 < NB)
-            ld_t(i + 1, bf ^ 1);
-          else
-            ld_a(0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int nt = 0; nt < NCT; ++nt)
-            U[mt][nt] = Ops::mma_split_b(at[bf], Rp[kk][nt], kk == 0 ? zero4() : U[mt][nt]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int nt = 0; nt < NCT; ++nt) {
-          Up[0][nt] = Ops::prec_from_acc(U[0][nt], U[1][nt]);
-          Up[1][nt] = Ops::prec_from_acc(U[2][nt], U[3][nt]);
-        }
-      }
-
-      // O += Tril(A_qk) U'
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int bf = i & 1, mt = BMT[i], kk = BKK[i];
-        if (i + 1 < NB)
-          ld_a(i + 1, bf ^ 1);
-        else
-          ld_s(0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int nt = 0; nt < NCT; ++nt) O[mt][nt] = Ops::mma_prec(ah[bf], al[bf], Up[kk][nt], O[mt][nt]);
-      }
-
-      // S <- Diag(Gamma_last) S + Kd^T U'
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int bf = mt & 1;
-        if (mt + 1 < MT) ld_s(mt + 1, bf ^ 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int nt = 0; nt < NCT; ++nt) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) S[mt][nt][i] *= gm[bf][i];
-          S[mt][nt] = Ops::mma_split_b(k0[bf], Up[0][nt], S[mt][nt]);
-          S[mt][nt] = Ops::mma_split_b(k1[bf], Up[1][nt], S[mt][nt]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-
-      write_tile();     // the helpers finished tile c - 1 before the barrier above
-      {
-        // prefix-cache snapshot of the state after this chunk
-        const int j = snapshot_index(p, p.t0 / kChunk + c);
-        if (j >= 0) {
-          float* sn = p.snaps + (((int64_t)b * p.n_snap + j) * p.H + h) * D * D;
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NCT; ++nt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) sn[(16 * mt + 4 * g4 + i) * D + col0 + 16 * nt] = S[mt][nt][i];
-        }
-      }
-      __syncthreads();  // part B of chunk c consumed; tile c and part A of chunk c + 1 staged
-    }
-
-    float* so = p.S_out + bh * D * D;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NCT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) so[(16 * mt + 4 * g4 + i) * D + col0 + 16 * nt] = S[mt][nt][i];
+    scan_compute_waves<T, D, L>(p, lds, wave, lane, b, h);
   } else {
     // ======================= helper waves =======================
     constexpr int NH = L::NH, VPR = L::VPR;
@@ -766,69 +512,17 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
       for (int i = 0; i < L::PG; ++i) *reinterpret_cast<u32x4*>(lds + lofG[i]) = stG[i];
     };
 
-    // epilogue role: row er, columns ec .. ec + EC - 1
-    constexpr int EC = L::EC;
-    const int er = hid / L::TPR, ec = (hid % L::TPR) * EC;
-    float wv[EC];
-#pragma unroll
-    for (int j = 0; j < EC; ++j) wv[j] = (p.rms_w != nullptr) ? p.rms_w[h * D + ec + j] : 1.0f;
-    auto pack_store = [&](OutT* dst, const float* x) {
-      if constexpr (OUT_F32) {
-#pragma unroll
-        for (int q = 0; q < EC / 4; ++q)
-          reinterpret_cast<float4*>(dst)[q] = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < EC / 8; ++q) {
-          u32x4 w;
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            w[k] = static_cast<uint32_t>(f32_to_bf16(x[8 * q + 2 * k])) |
-                   (static_cast<uint32_t>(f32_to_bf16(x[8 * q + 2 * k + 1])) << 16);
-          reinterpret_cast<u32x4*>(dst)[q] = w;
-        }
-      }
+    // epilogue role: row er, columns ec .. ec + EC - 1; gate logits from the slab
+    using Epi = GateEpilogue<T, D, OUT_F32, NH, false>;
+    static_assert(Epi::TPR == L::TPR && Epi::EC == L::EC, "epilogue mapping");
+    Epi epi;
+    epi.init(p, h, hid);
+    const float* otile = reinterpret_cast<const float*>(lds + L::OT);
+    auto getg = [&](int q) {
+      return *reinterpret_cast<const u32x4*>(lds + L::GS + epi.er * L::PQ + epi.ec * L::ES + 16 * q);
     };
-    // o / y of chunk c from the output tile and the gate slab; only the last
-    // chunk can have rows past the end
     auto epilogue = [&](int c, auto check_rows) {
-      const int tok0 = p.t0 + c * kChunk;
-      float ov[EC];
-#pragma unroll
-      for (int q = 0; q < EC / 4; ++q) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(otile + er * L::PO + ec + 4 * q);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ov[4 * q + j] = t[j];
-      }
-      if (!decltype(check_rows)::value || er < p.T - tok0) {
-        const int64_t orow = head_base + (tok0 + er) * tok_stride + ec;
-        if (p.o != nullptr) pack_store(static_cast<OutT*>(p.o) + orow, ov);
-        if (gated) {
-          float ss = 0.f;
-#pragma unroll
-          for (int j = 0; j < EC; ++j) ss += ov[j] * ov[j];
-#pragma unroll
-          for (int m = 1; m < L::TPR; m <<= 1) ss += __shfl_xor(ss, m);
-          const float rinv = hw_rsqrt(ss / D + p.rms_eps);
-          float yv[EC];
-#pragma unroll
-          for (int q = 0; q < EC * L::ES / 16; ++q) {
-            const u32x4 graw = *reinterpret_cast<const u32x4*>(lds + L::GS + er * L::PQ + ec * L::ES + 16 * q);
-            constexpr int PER = 16 / L::ES;  // logits per 16-byte vector
-#pragma unroll
-            for (int j = 0; j < PER; ++j) {
-              float gl;
-              if constexpr (sizeof(T) == 2)
-                gl = __uint_as_float((graw[j >> 1] >> (16 * (j & 1))) << 16);
-              else
-                gl = __uint_as_float(graw[j]);
-              const int e = PER * q + j;
-              yv[e] = sigmoid_fast(gl) * ov[e] * (rinv * wv[e]);
-            }
-          }
-          pack_store(static_cast<OutT*>(p.y) + orow, yv);
-        }
-      }
+      epi.template run<decltype(check_rows)::value, L::PO>(p, h, head_base, p.t0 + c * kChunk, otile, getg);
     };
 
     // Loads past the last chunk are clamped to it (their commits land where

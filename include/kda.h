@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
   KDA_OK = 0,
@@ -57,6 +57,13 @@ typedef enum {
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
 typedef enum { KDA_STATE_ZERO = 0, KDA_STATE_IMPORT = 1, KDA_STATE_EXPORT = 2 } kda_state_op;
+
+/* Schedules of kda_chunk_fwd (see there). */
+typedef enum {
+  KDA_SCHEDULE_SEGMENTS = 0,   /* intra-chunk kernel, then scan, segment after segment */
+  KDA_SCHEDULE_OVERLAPPED = 1, /* the two kernels of consecutive segments overlapped   */
+  KDA_SCHEDULE_FUSED = 2       /* one fused kernel, chunk records kept in LDS          */
+} kda_schedule;
 
 typedef enum {
   KDA_LAYOUT_KV = 0, /* user state is [d_k][d_v], same as the pool               */
@@ -81,6 +88,10 @@ typedef struct {
                             concurrently with the scan of the current one
                             (library-owned streams, see kda_chunk_fwd); 0: one
                             stream, segments in turn                          */
+  int32_t fused;         /* the fused one-kernel schedule (bf16 inputs only):
+                            1 when B * H is at least the device's number of
+                            compute units (default), 2 always, 0 never; the
+                            two-kernel schedules above otherwise              */
 } kda_desc;
 
 /* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
@@ -94,6 +105,7 @@ kda_status kda_desc_init(kda_desc* d, int32_t B, int32_t T, int32_t H, int32_t h
                          kda_dtype out_dtype);
 
 /* Workspace bytes for kda_chunk_fwd's preferred schedule; 0 if *d is invalid.
+ * The fused schedule needs none (256 is reported; ws may also be NULL then).
  * With d->overlap and a sequence longer than one segment this holds two
  * segments of chunk records (the overlapped schedule); otherwise it holds the
  * whole sequence (at most 65536 tokens per segment).  A smaller workspace also
@@ -117,12 +129,12 @@ kda_status kda_release_resources(void);
 /*
  * The schedule kda_chunk_fwd takes on the current device for this descriptor
  * and a workspace of ws_bytes bytes: *segment_tokens receives the tokens per
- * segment (a multiple of the chunk), *overlapped 1 for the overlapped schedule
- * and 0 for segments in turn.  KDA_ERR_WORKSPACE if the workspace is too
- * small for one chunk.
+ * segment (a multiple of the chunk; the whole sequence for the fused
+ * schedule), *schedule a kda_schedule value.  KDA_ERR_WORKSPACE if a
+ * two-kernel schedule is taken and the workspace is too small for one chunk.
  */
 kda_status kda_chunk_fwd_schedule(const kda_desc* d, size_t ws_bytes, int32_t* segment_tokens,
-                                  int32_t* overlapped);
+                                  int32_t* schedule);
 
 /*
  * Chunked KDA forward over whole sequences (prefill / training forward),
@@ -136,11 +148,20 @@ kda_status kda_chunk_fwd_schedule(const kda_desc* d, size_t ws_bytes, int32_t* s
  *  y      [B, T, H, d_v] gated output (requires gate), or NULL.
  *  S_T    [B, H, d_k, d_v] fp32 final state, or NULL.  May alias S0.
  *  ws     device workspace of ws_bytes bytes (see the size queries), owned by
- *         the caller; its contents are scratch.  May be NULL when T == 0.
+ *         the caller; its contents are scratch.  May be NULL when T == 0 or
+ *         when the fused schedule is taken.
  * At least one of o, y, S_T must be non-NULL.  When d->T == 0 nothing is read:
  * S_T receives S0 (or zeros) and q, k, v, beta, z, A and ws may be NULL.
  *
- * Schedule.  The sequence is processed in segments; per segment the
+ * Fused schedule (see d->fused; bf16 inputs): one launch, one workgroup per
+ * (head, sequence).  Its compute waves run the state scan of chunk c while
+ * producer waves build chunk c + 1's intra-chunk record directly in LDS and
+ * write chunk c - 1's o / y, so no record goes through HBM.  Each head's
+ * intra-chunk work then runs on a single compute unit, which only pays once
+ * the (head, sequence) pairs fill the device.  Results are bit-identical to
+ * the two-kernel schedules.
+ *
+ * Two-kernel schedules.  The sequence is processed in segments; per segment the
  * intra-chunk kernel writes one record per chunk into the workspace and the
  * state scan (with the fused gate) consumes them.  When d->overlap is set, the
  * sequence spans more than one segment of d->segment_tokens tokens, B * H is
@@ -160,7 +181,8 @@ kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const 
 /*
  * kda_chunk_fwd with per-kernel timing: identical work and results, and in
  * addition, for the i-th kernel launch of the call (launch order per segment:
- * the intra-chunk kernel, then the state scan with the fused gate),
+ * the intra-chunk kernel, then the state scan with the fused gate; the fused
+ * schedule has one launch),
  * hipEventRecord(events[2i]) right before it and hipEventRecord(events[2i+1])
  * right after it on the stream that launch uses (`stream`, or the library's
  * stream of that kernel in the overlapped schedule), while 2i+1 < n_events.

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert {"kda_chunk_fwd", "kda_recurrent_step", "kda_state_io"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kda_abi_version() == 2
+    assert L.kda_abi_version() == 3
     assert L.kda_status_str(6) == b"workspace missing or too small"
 
 
@@ -59,8 +59,11 @@ def test_forward_host_errors():
     assert _fwd(_desc(), y=FAKE, gate=None) == 1                  # y needs the gate logits
     assert _fwd(_desc(), v=FAKE + 2) == 4                         # misaligned
     assert _fwd(_desc(), beta=FAKE + 1) == 4
-    assert _fwd(_desc(), ws=None) == 6
-    assert _fwd(_desc(), nbytes=1024) == 6                        # smaller than one chunk needs
+    # workspace errors exist only for the two-kernel schedules (the fused one
+    # needs none and would launch here)
+    assert _fwd(_desc(fused=0), ws=None) == 6
+    assert _fwd(_desc(fused=0), nbytes=1024) == 6                 # smaller than one chunk needs
+    assert _fwd(_desc(fused=3)) == 2                              # flag out of range
     assert _fwd(_desc(g_min=-6.0)) == 5                           # 16 * g_min < -88: e^80 bound lost
     assert _fwd(_desc(g_min=0.0)) == 5
     assert _fwd(_desc(chunk=32)) == 5
@@ -69,7 +72,7 @@ def test_forward_host_errors():
 
 def test_workspace_sizes():
     L = kda.lib()
-    d = _desc()
+    d = _desc(fused=0)
     one = L.kda_chunk_fwd_workspace_size_for(ctypes.byref(d), 1)
     two = L.kda_chunk_fwd_workspace_size_for(ctypes.byref(d), 65)
     full = L.kda_chunk_fwd_workspace_size(ctypes.byref(d))
@@ -120,3 +123,19 @@ def test_snapshot_host_errors_and_count():
     assert _snap(d, snaps=FAKE + 2) == 4
     assert _snap(_desc(T=1000, chunk=32)) == 5
     assert _snap(d, every=16, snaps=None, o=None) == 0            # no boundary, no output: nothing to do
+
+
+def test_schedule_query():
+    L = kda.lib()
+    seg, sch = ctypes.c_int32(0), ctypes.c_int32(0)
+    assert _desc().fused == 1                                     # the default: the library decides
+    d = _desc(T=70000, fused=2)                                   # forced
+    assert L.kda_chunk_fwd_schedule(ctypes.byref(d), 0, ctypes.byref(seg), ctypes.byref(sch)) == 0
+    assert sch.value == 2 and seg.value == 70016                  # fused: whole sequence, no workspace
+    assert L.kda_chunk_fwd_workspace_size(ctypes.byref(d)) == 256
+    d32 = _desc(T=70000, in_dtype=kda.KDA_F32, fused=2)           # fp32 inputs: two-kernel schedules
+    assert L.kda_chunk_fwd_schedule(ctypes.byref(d32), 0, ctypes.byref(seg), ctypes.byref(sch)) == 6
+    d2 = _desc(T=1000, fused=0, overlap=0)
+    ws = L.kda_chunk_fwd_workspace_size(ctypes.byref(d2))
+    assert L.kda_chunk_fwd_schedule(ctypes.byref(d2), ws, ctypes.byref(seg), ctypes.byref(sch)) == 0
+    assert sch.value == 0 and seg.value == 1024

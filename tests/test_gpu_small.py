@@ -61,15 +61,16 @@ def _custom(B, T, H, D, dtype, seed, z_std=2.0, s0=0.1):
                     gate=True, s0_std=s0)
 
 
+@pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("B,T,H,D", [(2, 200, 3, 128), (1, 64, 2, 128), (3, 77, 2, 64), (1, 1, 1, 128),
                                      (2, 333, 1, 64)])
-def test_bf16_small_ragged(kda, B, T, H, D):
+def test_bf16_small_ragged(kda, B, T, H, D, fused):
     wl = _custom(B, T, H, D, "bf16", seed=B * 1000 + T)
     x = gen_inputs(wl)
-    log(f"[bf16 small] B={B} T={T} H={H} D={D}")
+    log(f"[bf16 small] B={B} T={T} H={H} D={D} fused={fused}")
     ref = _oracle(x)
     for odt in (torch.float32, torch.bfloat16):
-        r = _run(kda, x, out_dtype=odt)
+        r = _run(kda, x, out_dtype=odt, fused=fused)
         e_o = rel_l2(host64(r["o"]), ref["o"])
         e_y = rel_l2(host64(r["y"]), ref["y"])
         e_s = rel_l2(host64(r["S_T"]), ref["S_T"])
@@ -119,8 +120,8 @@ def test_segmented_workspace_matches_single_pass(kda):
     segments (state carried through memory); results are bit-identical."""
     wl = _custom(2, 300, 2, 128, "bf16", seed=11)
     x = gen_inputs(wl)
-    full = _run(kda, x, overlap=False)
-    small = _run(kda, x, overlap=False, segment_tokens=64)
+    full = _run(kda, x, overlap=False, fused=False)
+    small = _run(kda, x, overlap=False, segment_tokens=64, fused=False)
     for key in ("o", "y", "S_T"):
         assert _bit_equal(full[key], small[key]), key
 
@@ -134,8 +135,8 @@ def test_overlapped_schedule_matches_one_stream(kda, B, T, H, D, seg):
     wl = _custom(B, T, H, D, "bf16", seed=B * 100 + T)
     x = gen_inputs(wl)
     log(f"[overlap] B={B} T={T} H={H} D={D} segment={seg}")
-    one = _run(kda, x, overlap=False)
-    two = _run(kda, x, overlap=True, segment_tokens=seg)
+    one = _run(kda, x, overlap=False, fused=False)
+    two = _run(kda, x, overlap=True, segment_tokens=seg, fused=False)
     for key in ("o", "y", "S_T"):
         assert _bit_equal(one[key], two[key]), key
     # work enqueued on the caller's stream after the call sees the finished
@@ -143,11 +144,44 @@ def test_overlapped_schedule_matches_one_stream(kda, B, T, H, D, seg):
     t = {n: dev(x[n]) for n in ("q", "k", "v", "beta", "z", "A", "gate", "S0")}
     torch.cuda.synchronize()
     r = kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t["S0"], gate=t["gate"],
-                      overlap=True, segment_tokens=seg)
+                      overlap=True, segment_tokens=seg, fused=False)
     snap = {key: val.clone() for key, val in r.items()}  # on the current stream
     torch.cuda.current_stream().synchronize()
     for key in ("o", "y", "S_T"):
         assert _bit_equal(one[key], snap[key]), key
+
+
+@pytest.mark.parametrize("B,T,H,D,opts", [
+    (2, 1000, 3, 128, {}),
+    (1, 777, 2, 64, {}),
+    (3, 130, 2, 128, {"out_dtype": torch.float32}),
+    (2, 64, 4, 128, {"S0": False}),
+    (1, 65, 2, 64, {"gate": False}),
+    (2, 300, 2, 128, {"rms_w": True}),
+    (1, 200, 3, 128, {"want_o": False}),
+    (2, 129, 2, 64, {"want_state": False, "out_dtype": torch.float32}),
+])
+def test_fused_matches_two_kernel_schedules(kda, B, T, H, D, opts):
+    """The fused kernel (records built in LDS by producer waves) and the
+    two-kernel schedules run the same arithmetic: bit-identical o, y, S_T."""
+    wl = _custom(B, T, H, D, "bf16", seed=7 * B + T + H)
+    x = gen_inputs(wl)
+    opts = dict(opts)
+    log(f"[fused] B={B} T={T} H={H} D={D} {opts}")
+    if opts.pop("rms_w", False):
+        opts["rms_w"] = torch.linspace(0.5, 1.5, H * D, device="cuda").reshape(H, D)
+    gate = opts.pop("gate", True)
+    S0 = opts.pop("S0", True)
+    ref = _run(kda, x, gate=gate, S0=S0, fused=False, overlap=False, **opts)
+    fus = _run(kda, x, gate=gate, S0=S0, fused=True, **opts)
+    assert set(ref) == set(fus)
+    for key in ref:
+        assert _bit_equal(ref[key], fus[key]), key
+    _, sched = kda.schedule(kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, fused=True), 0)
+    assert sched == "fused"
+    # left to the library, a few (head, sequence) pairs take a two-kernel schedule
+    desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16)
+    assert kda.schedule(desc, kda.workspace_size(desc))[1] != "fused"
 
 
 def test_state_only_and_zero_length(kda):

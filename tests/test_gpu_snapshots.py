@@ -51,7 +51,7 @@ def _fwd(kda, t, S0, **kw):
 
 
 @pytest.mark.parametrize("B,T,H,D,dtype,every", [(2, 1000, 3, 128, "bf16", 2), (1, 640, 2, 64, "f32", 1),
-                                                 (3, 512, 2, 128, "bf16", 4)])
+                                                 (3, 512, 2, 128, "bf16", 4), (1, 333, 2, 64, "bf16", 1)])
 def test_snapshots_match_oracle_prefix_states(kda, B, T, H, D, dtype, every):
     x = gen_inputs(_wl(B, T, H, D, dtype, seed=T + every))
     t = {n: dev(x[n]) for n in NAMES + ("A", "S0")}
@@ -71,13 +71,14 @@ def test_snapshots_match_oracle_prefix_states(kda, B, T, H, D, dtype, every):
         assert torch.equal(r["snapshots"][:, -1], r["S_T"])
 
 
-@pytest.mark.parametrize("overlap,seg", [(False, None), (True, 128)])
-def test_resume_from_snapshot_is_bit_identical(kda, overlap, seg):
+@pytest.mark.parametrize("fused,overlap,seg", [(True, True, None), (False, False, None), (False, True, 128)])
+def test_resume_from_snapshot_is_bit_identical(kda, fused, overlap, seg):
     B, T, H, D, every = 2, 900, 3, 128, 3
     x = gen_inputs(_wl(B, T, H, D, "bf16", seed=17))
     t = {n: dev(x[n]) for n in NAMES + ("A", "S0")}
-    plain = _fwd(kda, t, t["S0"], overlap=overlap, segment_tokens=seg)
-    full = _fwd(kda, t, t["S0"], overlap=overlap, segment_tokens=seg, snapshot_chunks=every)
+    kw = dict(overlap=overlap, segment_tokens=seg, fused=fused)
+    plain = _fwd(kda, t, t["S0"], **kw)
+    full = _fwd(kda, t, t["S0"], snapshot_chunks=every, **kw)
     for key in ("o", "y", "S_T"):
         assert _bit_equal(plain[key], full[key]), key
     n = full["snapshots"].shape[1]
@@ -86,21 +87,22 @@ def test_resume_from_snapshot_is_bit_identical(kda, overlap, seg):
         tj = (j + 1) * 64 * every
         rest = {m: t[m][:, tj:].contiguous() for m in NAMES}
         rest["A"] = t["A"]
-        r = _fwd(kda, rest, full["snapshots"][:, j].contiguous(), overlap=overlap, segment_tokens=seg)
-        log(f"[resume] overlap={overlap} from snapshot {j} (token {tj})")
+        r = _fwd(kda, rest, full["snapshots"][:, j].contiguous(), **kw)
+        log(f"[resume] {kw} from snapshot {j} (token {tj})")
         for key in ("o", "y"):
             assert _bit_equal(r[key], full[key][:, tj:].contiguous()), (j, key)
         assert _bit_equal(r["S_T"], full["S_T"]), j
 
 
-def test_snapshots_only(kda):
+@pytest.mark.parametrize("fused", [True, False])
+def test_snapshots_only(kda, fused):
     """Snapshots without o, y or S_T (a prefill that only fills the cache)."""
     B, T, H, D = 1, 300, 2, 64
     x = gen_inputs(_wl(B, T, H, D, "bf16", seed=5))
     t = {n: dev(x[n]) for n in NAMES + ("A", "S0")}
-    ref = _fwd(kda, t, t["S0"], overlap=False, snapshot_chunks=1)
+    ref = _fwd(kda, t, t["S0"], overlap=False, snapshot_chunks=1, fused=False)
     only = kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t["S0"], want_o=False,
-                         want_state=False, overlap=False, snapshot_chunks=1)
+                         want_state=False, overlap=False, snapshot_chunks=1, fused=fused)
     torch.cuda.synchronize()
     assert set(only) == {"snapshots"}
     assert torch.equal(only["snapshots"], ref["snapshots"])
