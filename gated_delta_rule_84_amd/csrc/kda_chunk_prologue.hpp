@@ -101,13 +101,15 @@ __device__ __forceinline__ float add_row_shr(float x) {
 
 // Decay of this lane's row and channels, and its inclusive prefix over the
 // sub-tile's rows 0..n (lanes n of the lane's row group):
-//     P[kk][j] = sum_{m <= n} g(m, lane_ch(kk, g, j)),  g = g_min Sigmoid(e^{A_h} z)
-// Rows past the end of the sequence (valid == false) contribute g = 0.
+//     P[kk][j] = sum_{m <= n} gscale Sigmoid(e^{A_h} z(m, lane_ch(kk, g, j)))
+// With gscale = g_min this is the log-decay prefix G (g = g_min Sigmoid(e^{A_h} z));
+// with gscale = g_min log2(e) it is G in base-2 units, ready for exp2.  Rows
+// past the end of the sequence (valid == false) contribute 0.
 template <typename T, int KS>
-__device__ __forceinline__ void subtile_decay_prefix(const typename Run8<T>::Raw* z, float A_h, float g_min,
+__device__ __forceinline__ void subtile_decay_prefix(const typename Run8<T>::Raw* z, float A_h, float gscale,
                                                      bool valid, float (&P)[KS][8]) {
   const float c1 = -hw_exp(A_h) * kLog2e;  // Sigmoid(e^A z) = 1 / (1 + 2^{c1 z})
-  const float gm = valid ? g_min : 0.0f;
+  const float gm = valid ? gscale : 0.0f;
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk)
 #pragma unroll

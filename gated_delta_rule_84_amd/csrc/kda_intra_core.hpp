@@ -18,9 +18,10 @@
 // the factors of every block stay within e^{+-40}:
 //     A(i, i) = (K_i . e^{G_i - B_i}) (K_i . e^{B_i - G_i})^T
 //     A(i, j) = (K_i . e^{G_i - B_i} . e^{B_i - B_j}) (K_j . e^{B_j - G_j})^T,  j < i.
-// Precision (bf16 path): A_qk's diagonal blocks multiply hi/lo bf16 splits of
-// both factors (three MFMAs per step); every other block is a plain bf16
-// product.  The fp32 path uses fp32 MFMA throughout.
+// Precision (bf16 path): A_qk's diagonal blocks are fp32 products of the fp32
+// factors (fp32 MFMA); every other block is a plain bf16 product.  The fp32
+// path uses fp32 MFMA throughout.  The log-decay is carried in base-2 units
+// (G log2(e)), so every decay factor is one exp2.
 //
 // The products are formed transposed -- column factors as the A operand, row
 // factors as the B operand -- so that each lane ends up with four consecutive
@@ -39,35 +40,25 @@
 
 namespace kda {
 
+// 8 fp32 values as the fp32 operand of one 32-wide K-step (eight 16x16x4 MFMAs).
+__device__ __forceinline__ f32x8 f32x8_of(const float* x) {
+  return f32x8{x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+}
+
 template <typename T>
 struct APolicy;
 template <>
 struct APolicy<uint16_t> {  // bf16 path
-  struct Split {
-    bf16x8 hi, lo;
-  };
   using Plain = bf16x8;
-  static __device__ __forceinline__ Split split(const float* x) {
-    Split o;
-    split8_bf16(x, o.hi, o.lo);
-    return o;
-  }
   static __device__ __forceinline__ Plain plain(const float* x) { return pack8_bf16(x); }
-  static __device__ __forceinline__ f32x4 mma(const Split& a, const Split& b, f32x4 acc) {
-    return mma32_x3(a.hi, a.lo, b.hi, b.lo, acc);
-  }
   static __device__ __forceinline__ f32x4 mma(const Plain& a, const Plain& b, f32x4 acc) { return mma32(a, b, acc); }
   static __device__ __forceinline__ Plain ld(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
   static constexpr bool kHasLo = true;
 };
 template <>
 struct APolicy<float> {  // fp32 path
-  using Split = f32x8;
   using Plain = f32x8;
-  static __device__ __forceinline__ f32x8 split(const float* x) {
-    return f32x8{x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
-  }
-  static __device__ __forceinline__ f32x8 plain(const float* x) { return split(x); }
+  static __device__ __forceinline__ f32x8 plain(const float* x) { return f32x8_of(x); }
   static __device__ __forceinline__ f32x4 mma(const f32x8& a, const f32x8& b, f32x4 acc) { return mma32(a, b, acc); }
   static __device__ __forceinline__ f32x8 ld(const float* p) {
     const float4 a = *reinterpret_cast<const float4*>(p);
@@ -187,11 +178,11 @@ struct IntraCore {
     beta_r = rvalid ? Elem<T>::to_f32(static_cast<const T*>(p.beta)[((int64_t)b * p.T + tok0 + r) * p.H + h]) : 0.0f;
   }
 
-  // Decay prefix within the sub-tile; anchor rows and totals to LDS; beta to
-  // LDS; inverse norms.
+  // Decay prefix within the sub-tile (base 2); anchor rows and totals to LDS;
+  // beta to LDS; inverse norms.
   __device__ __forceinline__ void prefix(const IntraParams& p, int h, const IntraScratch<T>& s) {
     if (g4 == 0) s.betas[r] = beta_r;
-    subtile_decay_prefix<T, KS>(zraw, p.A[h], p.g_min, rvalid, P);
+    subtile_decay_prefix<T, KS>(zraw, p.A[h], p.g_min * kLog2e, rvalid, P);
     if (n == 7)
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) put_run8(s.loc7 + ti * D, kk, g4, P[kk]);
@@ -205,7 +196,7 @@ struct IntraCore {
   }
 
   // Per-channel tables from the sub-tile totals and anchors (thread t of
-  // nthreads, all four waves):  G of sub-tile i = off_i + prefix,
+  // nthreads, all four waves), base 2:  G of sub-tile i = off_i + prefix,
   // off_i = sum_{j < i} tot_j;  B_i = off_i + loc7_i.  Gamma_last goes to gam.
   template <int NTHREADS>
   static __device__ __forceinline__ void tables(int t, const IntraScratch<T>& s, float* gam) {
@@ -223,16 +214,16 @@ struct IntraCore {
       const int item = part + TPC * it;
       if (item >= 15) {
       } else if (item < 4) {
-        s.eB[item * D + ch] = hw_exp(Bv[item]);
+        s.eB[item * D + ch] = hw_exp2(Bv[item]);
       } else if (item < 8) {
-        s.eL[(item - 4) * D + ch] = hw_exp(glast - Bv[item - 4]);
+        s.eL[(item - 4) * D + ch] = hw_exp2(glast - Bv[item - 4]);
       } else if (item < 14) {
         const int pi = item - 8;  // pair index -> (i, j)
         const int i = (pi < 1) ? 1 : (pi < 3) ? 2 : 3;
         const int j = pi - pair_index(i, 0);
-        s.Et[pi * D + ch] = hw_exp(Bv[i] - Bv[j]);
+        s.Et[pi * D + ch] = hw_exp2(Bv[i] - Bv[j]);
       } else {
-        gam[ch] = hw_exp(glast);
+        gam[ch] = hw_exp2(glast);
       }
     }
   }
@@ -253,14 +244,14 @@ struct IntraCore {
       float kc[8], xq[8], xk[8], xd[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float d = (P[kk][j] - p7[j]) * kLog2e;
-        const float rf = hw_exp2(d);   // e^{G_r - B_i}
-        const float cf = hw_exp2(-d);  // e^{B_i - G_r}
-        const float qf = R8::get(qraw[kk], j);
-        const float kf = R8::get(kraw[kk], j);
-        KR[kk][j] = kf * (rk * rf);
-        QR[kk][j] = qf * (rq * rf);
-        kc[j] = kf * (rk * cf);
+        const float d = P[kk][j] - p7[j];  // (G_r - B_i) log2(e)
+        const float rf = hw_exp2(d);       // e^{G_r - B_i}
+        const float cf = hw_exp2(-d);      // e^{B_i - G_r}
+        const float kn = R8::get(kraw[kk], j) * rk;  // normalised k, q
+        const float qn = R8::get(qraw[kk], j) * rq;
+        KR[kk][j] = kn * rf;
+        QR[kk][j] = qn * rf;
+        kc[j] = kn * cf;
         xq[j] = QR[kk][j] * eb[j];   // q^ . Gamma
         xk[j] = -KR[kk][j] * eb[j];  // -(k^ . Gamma)
         xd[j] = kc[j] * el[j];       // k^ . Gamma_last / Gamma
@@ -276,7 +267,7 @@ struct IntraCore {
       }
       // transposed diagonal blocks: lane (n, g4) gets row n, columns 4 g4 + i
       akk_d = AP::mma(AP::plain(kc), AP::plain(KR[kk]), akk_d);
-      aqk_d = AP::mma(AP::split(kc), AP::split(QR[kk]), aqk_d);
+      aqk_d = mma32(f32x8_of(kc), f32x8_of(QR[kk]), aqk_d);
     }
     f32x4 lv;
 #pragma unroll
