@@ -5,8 +5,9 @@ CPU-baseline leg may import this package.  It shares no code with the GPU
 library and the GPU library never calls it.
 
 Source pages: "Kimi K3: KDA, Attention Residuals and Stable LatentMoE"
-(hs-black.github.io/posts/kimi-k3), section 2.1 (the per-head recurrence and
-the chunked output formula), section 2.2 (the bounded decay map and the
+(hs-black.github.io/posts/kimi-k3), section 2.1 (the per-head recurrence, the
+chunked output formula and the input steps ShortConv / Swish / Sigmoid before
+the core), section 2.2 (the bounded decay map and the
 16-token sub-tile bound), section 2.3 (the full-rank output gate) and section
 10.2 (the (M, S~) pair composition used for context parallelism).
 
@@ -214,4 +215,56 @@ def kda_forward_heads(q, k, v, beta, z, A, S0=None, gate=None, w=None, g_min=G_M
     if gate is not None:
         wh = None if w is None else np.asarray(w)[None, None]
         out["y"] = output_gate(o, gate, wh, rms_eps)
+    return out
+
+
+def swish(x):
+    """Swish(x) = x * Sigmoid(x), applied after ShortConv to q, k and v
+    (section 2.1; section 4's SwiGLU discussion gives the same definition)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x * sigmoid(x)
+
+
+def short_conv(x, w, state=None):
+    """ShortConv of section 2.1: a depthwise causal convolution over time.
+    x: [T, C]; w: [C, W] taps -- w[:, W-1] multiplies the current token and
+    w[:, W-1-j] the token j steps back; state: [W-1, C] inputs before token 0,
+    oldest first (None: zeros).  Returns (y [T, C], new_state [W-1, C]), the
+    new state being the last W-1 inputs of the extended sequence.
+    Reading: the pages give neither the width nor a bias; the width is a
+    parameter and there is no bias."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    T, C = x.shape
+    W = w.shape[1]
+    prev = np.zeros((W - 1, C)) if state is None else np.asarray(state, dtype=np.float64).reshape(W - 1, C)
+    ext = np.concatenate([prev, x], axis=0)  # ext[i] = input at time i - (W - 1)
+    y = np.zeros((T, C))
+    for j in range(W):  # tap j meets the input at time t - (W - 1) + j
+        y += w[:, j] * ext[j:j + T]
+    return y, ext[T:].copy()
+
+
+def input_prep(xq, xk, xv, beta_logit, wq, wk, wv, state=None):
+    """The core's inputs from the projections (section 2.1):
+        q = Swish(ShortConv(x_q)), k = Swish(ShortConv(x_k)),
+        v = Swish(ShortConv(x_v)), beta = Sigmoid(beta_logit).
+    The L2Norm of q and k belongs to the core (kda_recurrent / kda_chunked
+    apply it).  xq, xk, xv: [B, T, H, d]; beta_logit: [B, T, H]; w*: [H d, W];
+    state: [B, 3, W-1, H d] (q, k, v windows) or None.  Returns a dict with
+    q, k, v [B, T, H, d], beta [B, T, H] and the new state [B, 3, W-1, H d]."""
+    xs = [np.asarray(a, dtype=np.float64) for a in (xq, xk, xv)]
+    ws = (wq, wk, wv)
+    B, T, H, d = xs[0].shape
+    C = H * d
+    W = np.asarray(wq).shape[1]
+    out = {n: np.empty((B, T, H, d)) for n in ("q", "k", "v")}
+    new_state = np.empty((B, 3, W - 1, C))
+    for b in range(B):
+        for i, n in enumerate(("q", "k", "v")):
+            st = None if state is None else np.asarray(state, dtype=np.float64)[b, i]
+            y, new_state[b, i] = short_conv(xs[i][b].reshape(T, C), ws[i], st)
+            out[n][b] = swish(y).reshape(T, H, d)
+    out["beta"] = sigmoid(beta_logit)
+    out["state"] = new_state
     return out

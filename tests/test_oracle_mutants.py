@@ -39,6 +39,11 @@ MUTANTS = [
     ("step_matrix_order",
      "return (np.eye(k_t.size) - beta_t * np.outer(k_t, k_t)) @ np.diag(np.asarray(alpha_t, dtype=np.float64))",
      "return np.diag(np.asarray(alpha_t, dtype=np.float64)) @ (np.eye(k_t.size) - beta_t * np.outer(k_t, k_t))"),
+    ("conv_taps_flipped", "y += w[:, j] * ext[j:j + T]", "y += w[:, W - 1 - j] * ext[j:j + T]"),
+    ("conv_state_newest_first", "ext = np.concatenate([prev, x], axis=0)",
+     "ext = np.concatenate([prev[::-1], x], axis=0)"),
+    ("conv_state_not_advanced", "return y, ext[T:].copy()", "return y, ext[:W - 1].copy()"),
+    ("swish_sign", "return x * sigmoid(x)", "return x * sigmoid(-x)"),
 ]
 
 

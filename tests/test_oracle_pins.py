@@ -293,3 +293,69 @@ def test_c_oracle_bf16_inputs_and_head_subset():
     b = oracle.forward_c(part["q"], part["k"], part["v"], part["beta"], part["z"], part["A"], S0=part["S0"],
                          gate=part["gate"])
     assert np.array_equal(a["o"][:, :, 2:5], b["o"]) and np.array_equal(a["S_T"][:, 2:5], b["S_T"])
+
+
+# ---- input steps before the core (section 2.1: ShortConv, Swish, Sigmoid) ----
+
+def test_swish_and_sigmoid_values():
+    # Sigmoid(0) = 1/2, Sigmoid(ln 3) = 3/4 exactly; Swish(x) = x Sigmoid(x)
+    assert R.sigmoid(np.array([0.0]))[0] == 0.5
+    assert abs(R.sigmoid(np.array([math.log(3.0)]))[0] - 0.75) < 1e-15
+    assert R.swish(np.array([0.0]))[0] == 0.0
+    assert abs(R.swish(np.array([math.log(3.0)]))[0] - 0.75 * math.log(3.0)) < 1e-15
+    # Swish(-x) = Swish(x) - x (Sigmoid(-x) = 1 - Sigmoid(x)); limits
+    x = np.linspace(-6, 6, 25)
+    assert np.allclose(R.swish(-x), R.swish(x) - x, atol=1e-14)
+    assert abs(R.swish(np.array([40.0]))[0] - 40.0) < 1e-12 and abs(R.swish(np.array([-40.0]))[0]) < 1e-12
+
+
+def test_short_conv_is_causal_convolution():
+    """Against numpy's convolution (an independent routine): y[t] =
+    sum_m h[m] x[t - m] with h[m] = w[W - 1 - m] and zeros before token 0."""
+    rng = np.random.default_rng(3)
+    T, C, W = 37, 5, 4
+    x = rng.standard_normal((T, C))
+    w = rng.standard_normal((C, W))
+    y, st = R.short_conv(x, w)
+    for c in range(C):
+        ref = np.convolve(x[:, c], w[c, ::-1])[:T]
+        assert np.allclose(y[:, c], ref, atol=1e-13)
+    assert np.array_equal(st, x[T - (W - 1):])          # last W-1 inputs, oldest first
+
+
+def test_short_conv_tap_direction_and_state():
+    """The last tap multiplies the current token; the first tap the token
+    W-1 steps back, which before token 0 comes from the state (oldest first)."""
+    T, C, W = 6, 2, 4
+    x = np.arange(1.0, T * C + 1).reshape(T, C)
+    state = -np.arange(1.0, (W - 1) * C + 1).reshape(W - 1, C)     # times -3, -2, -1
+    cur = np.zeros((C, W)); cur[:, W - 1] = 1.0
+    first = np.zeros((C, W)); first[:, 0] = 1.0
+    y, _ = R.short_conv(x, cur, state)
+    assert np.array_equal(y, x)
+    y, _ = R.short_conv(x, first, state)
+    assert np.array_equal(y[:W - 1], state) and np.array_equal(y[W - 1:], x[:T - (W - 1)])
+    y, _ = R.short_conv(x, first)                                   # no state: zeros
+    assert np.array_equal(y[:W - 1], np.zeros((W - 1, C)))
+    # a sequence shorter than the window: the new state mixes old state and inputs
+    _, st = R.short_conv(x[:1], first, state)
+    assert np.array_equal(st, np.concatenate([state[1:], x[:1]]))
+
+
+def test_input_prep_chains_through_its_state():
+    """Running T tokens at once equals running them in two calls with the
+    state carried (the decode / prefix-resume contract)."""
+    rng = np.random.default_rng(4)
+    B, T, H, d, W = 2, 23, 2, 4, 4
+    xs = [rng.standard_normal((B, T, H, d)) for _ in range(3)]
+    bl = rng.standard_normal((B, T, H))
+    ws = [rng.standard_normal((H * d, W)) for _ in range(3)]
+    full = R.input_prep(*xs, bl, *ws)
+    a = R.input_prep(*(x[:, :9] for x in xs), bl[:, :9], *ws)
+    b = R.input_prep(*(x[:, 9:] for x in xs), bl[:, 9:], *ws, state=a["state"])
+    for n in ("q", "k", "v", "beta"):
+        assert np.allclose(np.concatenate([a[n], b[n]], axis=1), full[n], atol=1e-14), n
+    assert np.array_equal(b["state"], full["state"])
+    # the output is Swish of the convolution, per stream
+    y, _ = R.short_conv(xs[1][0].reshape(T, H * d), ws[1])
+    assert np.allclose(full["k"][0].reshape(T, H * d), y / (1.0 + np.exp(-y)), atol=1e-14)
