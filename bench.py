@@ -98,6 +98,38 @@ def cpu_baseline(wl, heads: int, threads: int) -> dict:
                       f"of the {wl.name} workload, all {wl.T} tokens ({th} token-heads, {dt:.1f} s)"}
 
 
+def time_input_prep(kda, t, B, T, H, D, steps, warmup, W=4):
+    """The input steps before the core (q, k, v = Swish(ShortConv(x)), beta =
+    Sigmoid(logit)) at the workload's shapes: the workload's q, k, v, beta
+    tensors stand in for the projections (the timing does not depend on the
+    values); taps seeded.  Algorithmic bytes: x_q, x_k, x_v and the beta
+    logit read, q, k, v and beta written = 3 * 2 * 2D + 2 * 2 per token-head."""
+    import torch
+    from synth.workloads import gen_prep_inputs
+    w = gen_prep_inputs(1, 1, H, D, W, "bf16", seed=5, with_state=False)
+    ws = [torch.from_numpy(w[n]).cuda() for n in ("wq", "wk", "wv")]
+    out = {n: torch.empty_like(t["q"]) for n in ("q", "k", "v")}
+    out["beta"] = torch.empty_like(t["beta"])
+
+    def call():
+        kda.input_prep(t["q"], t["k"], t["v"], *ws, beta_logits=t["beta"], out=out)
+
+    for _ in range(warmup):
+        call()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    nbytes = B * T * H * (3 * 2 * 2 * D + 2 * 2)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"conv_width": W, "ms": ms, "algorithmic_bytes": nbytes, "achieved_GBs": gbs,
+            "frac_hbm": gbs / HBM_PEAK_GBS, "launches": 2}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +142,8 @@ def main() -> int:
                     help="the library's choice (default), the fused kernel, or a two-kernel schedule")
     ap.add_argument("--segment-tokens", type=int, default=0,
                     help="tokens per segment of the two-kernel schedules; 0: library default")
+    ap.add_argument("--no-input-prep", action="store_true",
+                    help="skip timing the input steps (ShortConv + Swish, Sigmoid) on the workload's shapes")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of GIB GiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -242,6 +276,8 @@ def main() -> int:
         "kernel_ms": kern_ms,
         "input_setup_s": t_gen,
     }
+    if not args.no_input_prep:
+        result["input_prep"] = time_input_prep(kda, t, B, T, H, D, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
         heads = args.cpu_heads or H

@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_workspace_size_for.argtypes = [dp, i32]
         L.kda_chunk_fwd_snapshots.restype = ctypes.c_int
         L.kda_chunk_fwd_snapshots.argtypes = [dp] + [vp] * 13 + [i32, vp, sz, vp]
+        L.kda_input_prep.restype = ctypes.c_int
+        L.kda_input_prep.argtypes = [dp, i32] + [vp] * 14
         L.kda_snapshot_count.restype = i32
         L.kda_snapshot_count.argtypes = [dp, i32]
         L.kda_release_resources.restype = ctypes.c_int
@@ -201,6 +203,30 @@ def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=
         rc = lib().kda_chunk_fwd_traced(*args, arr, len(events))
     if rc != 0:
         raise KdaError("kda_chunk_fwd", rc)
+    return res
+
+
+def input_prep(xq, xk, xv, wq, wk, wv, beta_logits=None, state_in=None, state_out=None, *, out=None):
+    """Input steps before the core: q, k, v = Swish(ShortConv(x)), beta =
+    Sigmoid(beta_logits).  x*: [B, T, H, D] (bf16 or fp32); w*: [H * D, W]
+    fp32 taps (W = 1..4, the last tap on the current token); state_in /
+    state_out: [B, 3, W - 1, H * D] fp32 conv windows (None: zeros / not
+    written; they may be the same tensor).  Returns a dict with q, k, v (and
+    beta)."""
+    B, T, H, D = xq.shape
+    W = wq.shape[1]
+    desc = make_desc(B, T, H, D, _dt(xq), _dt(xq))
+    res = dict(out or {})
+    for n in ("q", "k", "v"):
+        if n not in res:
+            res[n] = torch.empty((B, T, H, D), dtype=xq.dtype, device=xq.device)
+    if beta_logits is not None and "beta" not in res:
+        res["beta"] = torch.empty((B, T, H), dtype=xq.dtype, device=xq.device)
+    rc = lib().kda_input_prep(ctypes.byref(desc), int(W), _ptr(xq), _ptr(xk), _ptr(xv), _ptr(beta_logits),
+                              _ptr(wq), _ptr(wk), _ptr(wv), _ptr(state_in), _ptr(state_out), _ptr(res["q"]),
+                              _ptr(res["k"]), _ptr(res["v"]), _ptr(res.get("beta")), _stream(xq.device))
+    if rc != 0:
+        raise KdaError("kda_input_prep", rc)
     return res
 
 

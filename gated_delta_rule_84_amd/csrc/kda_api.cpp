@@ -577,6 +577,49 @@ kda_status kda_chunk_fwd_snapshots(const kda_desc* d, const void* q, const void*
                         Snapshots{snapshots, every_chunks, n});
 }
 
+kda_status kda_input_prep(const kda_desc* d, int32_t conv_width, const void* xq, const void* xk, const void* xv,
+                          const void* beta_logits, const float* wq, const float* wk, const float* wv,
+                          const float* state_in, float* state_out, void* q, void* k, void* v, void* beta,
+                          void* stream) {
+  const kda_status st = validate_desc(d);
+  if (st != KDA_OK) return st;
+  if (conv_width < 1 || conv_width > 4) return KDA_ERR_UNSUPPORTED;
+  if ((beta_logits == nullptr) != (beta == nullptr)) return KDA_ERR_NULL_ARG;
+  const size_t es = elem_size(d->in_dtype);
+  for (const float* p : {state_in, (const float*)state_out})
+    if (p && !aligned(p, 4)) return KDA_ERR_MISALIGNED;
+  kda::InputPrepParams p{};
+  p.B = d->B;
+  p.T = d->T;
+  p.H = d->H;
+  p.C = d->H * d->d_k;
+  p.W = conv_width;
+  p.state_in = conv_width > 1 ? state_in : nullptr;
+  p.state_out = conv_width > 1 ? state_out : nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->T == 0) return check_launch(kda::launch_input_prep(p, d->in_dtype == KDA_F32, s), s);
+  if (!xq || !xk || !xv || !wq || !wk || !wv || !q || !k || !v) return KDA_ERR_NULL_ARG;
+  for (const void* ptr : {xq, xk, xv, (const void*)q, (const void*)k, (const void*)v})
+    if (!aligned(ptr, 16)) return KDA_ERR_MISALIGNED;
+  if (!aligned(wq, 4) || !aligned(wk, 4) || !aligned(wv, 4) || (beta && (!aligned(beta, es) || !aligned(beta_logits, es))))
+    return KDA_ERR_MISALIGNED;
+  p.x[0] = xq;
+  p.x[1] = xk;
+  p.x[2] = xv;
+  p.w[0] = wq;
+  p.w[1] = wk;
+  p.w[2] = wv;
+  p.y[0] = q;
+  p.y[1] = k;
+  p.y[2] = v;
+  p.beta_logit = beta_logits;
+  p.beta = beta;
+  // in place: one block of tokens per channel group, so that the state is
+  // read before it is overwritten by the same thread
+  p.tokens_per_block = (p.state_out != nullptr && p.state_out == p.state_in) ? d->T : 128;
+  return check_launch(kda::launch_input_prep(p, d->in_dtype == KDA_F32, s), s);
+}
+
 int32_t kda_snapshot_count(const kda_desc* d, int32_t every_chunks) {
   if (validate_desc(d) != KDA_OK || every_chunks < 1) return 0;
   return d->T / (kChunk * every_chunks);

@@ -123,6 +123,19 @@ struct PrepassParams {
   float* rk;   // [B, T, H]
 };
 
+// Input steps before the core: ShortConv + Swish on q, k, v; Sigmoid on beta.
+struct InputPrepParams {
+  const void* x[3];        // q, k, v projections [B, T, H * D] (input dtype)
+  const float* w[3];       // taps [H * D, W]; tap W - 1 multiplies the current token
+  const float* state_in;   // [B, 3, W - 1, H * D] inputs before token 0, oldest first, or nullptr (zeros)
+  float* state_out;        // [B, 3, W - 1, H * D] the W - 1 inputs before token T, or nullptr
+  void* y[3];              // outputs [B, T, H * D] (input dtype)
+  const void* beta_logit;  // [B, T, H] or nullptr
+  void* beta;              // [B, T, H]
+  int B, T, H, C, W;       // C = H * D (a multiple of 8)
+  int tokens_per_block;    // tokens per workgroup row; T when state_out aliases state_in
+};
+
 // Host launchers (one per kernel family).  in_f32: inputs are fp32 (else bf16).
 hipError_t launch_intra(const IntraParams& p, int D, int in_f32, hipStream_t s);
 hipError_t launch_scan(const ScanParams& p, int D, int in_f32, hipStream_t s);
@@ -134,5 +147,6 @@ hipError_t launch_decode(const DecodeParams& p, int D, int in_f32, hipStream_t s
 hipError_t launch_state_io(const StateIoParams& p, int D, hipStream_t s);
 hipError_t launch_prepass(const PrepassParams& p, int D, int in_f32, hipStream_t s);
 hipError_t launch_copy_state(const float* src, float* dst, int64_t n_floats, hipStream_t s);
+hipError_t launch_input_prep(const InputPrepParams& p, int in_f32, hipStream_t s);
 
 }  // namespace kda

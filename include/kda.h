@@ -218,6 +218,36 @@ kda_status kda_chunk_fwd_snapshots(const kda_desc* d, const void* q, const void*
 int32_t kda_snapshot_count(const kda_desc* d, int32_t every_chunks);
 
 /*
+ * Input steps before the core (K3 blog section 2.1): from the projections
+ * x_q, x_k, x_v [B, T, H, d] and the beta logits [B, T, H] (all d->in_dtype),
+ *     q = Swish(ShortConv(x_q)),  k = Swish(ShortConv(x_k)),
+ *     v = Swish(ShortConv(x_v)),  beta = Sigmoid(beta_logits),
+ * written to q, k, v [B, T, H, d] and beta [B, T, H] in d->in_dtype; Swish(x)
+ * = x Sigmoid(x).  The L2Norm of q and k is applied by kda_chunk_fwd /
+ * kda_recurrent_step (d->qk_l2norm), not here.  ShortConv is a depthwise
+ * causal convolution over time with conv_width (1..4) taps per channel and no
+ * bias (the pages give neither a width nor a bias): wq, wk, wv are fp32
+ * [H * d, conv_width], tap conv_width - 1 multiplying the current token and
+ * tap conv_width - 1 - j the token j steps back.
+ *  state_in   fp32 [B, 3, conv_width - 1, H * d]: the conv_width - 1 inputs
+ *             of q, k, v (in that order) before token 0, oldest first; NULL
+ *             for zeros (the start of a sequence).
+ *  state_out  same layout: receives the conv_width - 1 inputs before token T
+ *             (the state a later call, e.g. a decode step with T = 1,
+ *             continues from); NULL to skip.  May equal state_in (the
+ *             sequence is then processed in one block of tokens per channel
+ *             group: fine for decode, slow for long prefills).
+ *  beta_logits, beta  both NULL to skip beta.
+ * With T == 0 only state_out is written (state_in copied, or zeros).
+ * KDA_ERR_UNSUPPORTED if conv_width is outside 1..4.  Chaining calls through
+ * the state gives the same outputs as one call over the concatenated tokens.
+ */
+kda_status kda_input_prep(const kda_desc* d, int32_t conv_width, const void* xq, const void* xk, const void* xv,
+                          const void* beta_logits, const float* wq, const float* wk, const float* wv,
+                          const float* state_in, float* state_out, void* q, void* k, void* v, void* beta,
+                          void* stream);
+
+/*
  * One decode step (single token) for d->B sequences: the same recurrence,
  * section 2.1, applied to one token.  d->T must be 1.  Each sequence n reads
  * and updates its state in place at S_pool[slot[n]] (slot == NULL: slot n):

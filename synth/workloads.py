@@ -112,3 +112,19 @@ def gen_inputs(wl: Workload, batch=None, time=None, heads=None, with_gate=None) 
                  std=wl.s0_std)
         out["S0"] = s.reshape(nb, nh, wl.D, wl.D)
     return out
+
+
+def gen_prep_inputs(B: int, T: int, H: int, D: int, W: int, dtype: str, seed: int, with_state: bool = True) -> dict:
+    """Inputs of the input steps before the core (projections of q, k, v and
+    the beta logits, N(0, 1); depthwise conv taps N(0, 0.5^2) [H D, W] fp32;
+    a conv state N(0, 1) [B, 3, W - 1, H D] fp32).  bf16 tensors are uint16
+    bit patterns."""
+    dt = BF16 if dtype == "bf16" else F32
+    shp = (B, T, H, D)
+    out = {n: fill(NORMAL, dt, seed, 40 + i, shp) for i, n in enumerate(("xq", "xk", "xv"))}
+    out["beta_logits"] = fill(NORMAL, dt, seed, 43, (B, T, H, 1)).reshape(B, T, H)
+    for i, n in enumerate(("wq", "wk", "wv")):
+        out[n] = fill(NORMAL, F32, seed, 44 + i, (1, 1, H * D, W), std=0.5).reshape(H * D, W)
+    if with_state and W > 1:
+        out["state"] = fill(NORMAL, F32, seed, 47, (B, 3, W - 1, H * D))
+    return out

@@ -139,3 +139,19 @@ def test_schedule_query():
     ws = L.kda_chunk_fwd_workspace_size(ctypes.byref(d2))
     assert L.kda_chunk_fwd_schedule(ctypes.byref(d2), ws, ctypes.byref(seg), ctypes.byref(sch)) == 0
     assert sch.value == 0 and seg.value == 1024
+
+
+def _prep(d, width=4, xq=FAKE, beta_logits=FAKE, beta=FAKE, st_in=None, st_out=None, q=FAKE):
+    return kda.lib().kda_input_prep(ctypes.byref(d), width, xq, FAKE, FAKE, beta_logits, FAKE, FAKE, FAKE,
+                                    st_in, st_out, q, FAKE, FAKE, beta, None)
+
+
+def test_input_prep_host_errors():
+    d = _desc()
+    assert _prep(d, width=0) == 5 and _prep(d, width=5) == 5          # widths 1..4
+    assert _prep(d, beta=None) == 1                                  # beta logits without an output
+    assert _prep(d, beta_logits=None) == 1
+    assert _prep(d, xq=None) == 1 and _prep(d, q=None) == 1
+    assert _prep(d, xq=FAKE + 2) == 4                                # 16-byte vectors
+    assert _prep(d, st_in=FAKE + 2) == 4
+    assert _prep(_desc(d_k=96, d_v=96)) == 5
