@@ -98,7 +98,7 @@ def cpu_baseline(wl, heads: int, threads: int) -> dict:
                       f"of the {wl.name} workload, all {wl.T} tokens ({th} token-heads, {dt:.1f} s)"}
 
 
-def time_input_prep(kda, t, B, T, H, D, steps, warmup, W=4):
+def time_input_prep(kda, t, B, T, H, D, steps, warmup, workload, W=4):
     """The input steps before the core (q, k, v = Swish(ShortConv(x)), beta =
     Sigmoid(logit)) at the workload's shapes: the workload's q, k, v, beta
     tensors stand in for the projections (the timing does not depend on the
@@ -127,7 +127,8 @@ def time_input_prep(kda, t, B, T, H, D, steps, warmup, W=4):
     nbytes = B * T * H * (3 * 2 * 2 * D + 2 * 2)
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"conv_width": W, "ms": ms, "algorithmic_bytes": nbytes, "achieved_GBs": gbs,
-            "frac_hbm": gbs / HBM_PEAK_GBS, "launches": 2}
+            "frac_hbm": gbs / HBM_PEAK_GBS, "launches": 2,
+            "traffic": profiled_traffic("prep_conv", workload)}
 
 
 def main() -> int:
@@ -277,7 +278,7 @@ def main() -> int:
         "input_setup_s": t_gen,
     }
     if not args.no_input_prep:
-        result["input_prep"] = time_input_prep(kda, t, B, T, H, D, args.steps, args.warmup)
+        result["input_prep"] = time_input_prep(kda, t, B, T, H, D, args.steps, args.warmup, wl.name)
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
         heads = args.cpu_heads or H
