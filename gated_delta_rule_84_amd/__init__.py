@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_workspace_size_for.argtypes = [dp, i32]
         L.kda_chunk_fwd_snapshots.restype = ctypes.c_int
         L.kda_chunk_fwd_snapshots.argtypes = [dp] + [vp] * 13 + [i32, vp, sz, vp]
+        L.kda_chunk_fwd_kcp.restype = ctypes.c_int
+        L.kda_chunk_fwd_kcp.argtypes = [dp, i32] + [vp] * 13 + [sz, vp]
+        L.kda_chunk_fwd_kcp_workspace_size.restype = sz
+        L.kda_chunk_fwd_kcp_workspace_size.argtypes = [dp, i32]
         L.kda_input_prep.restype = ctypes.c_int
         L.kda_input_prep.argtypes = [dp, i32] + [vp] * 14
         L.kda_snapshot_count.restype = i32
@@ -151,7 +155,7 @@ def schedule(desc: KdaDesc, ws_bytes: int) -> tuple[int, str]:
 
 def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=None, want_o=True,
               want_y=None, want_state=True, workspace=None, segment_tokens=None, overlap=True, fused=None,
-              out=None, events=None, snapshot_chunks=0, **opts):
+              out=None, events=None, snapshot_chunks=0, kcp_parts=0, **opts):
     """KDA forward over whole sequences.  q, k, z: [B, T, H, D]; v (and gate):
     [B, T, H, D]; beta: [B, T, H]; A: [H] fp32; S0: [B, H, D, D] fp32 or None.
     Returns a dict with 'o' / 'y' (out_dtype, default the input dtype) and
@@ -164,7 +168,8 @@ def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=
     segments processed in turn (default: the whole sequence).  With
     ``snapshot_chunks`` = N > 0 the result also holds 'snapshots'
     [B, n, H, D, D]: the state after every N-th chunk (prefix-cache resume
-    points, n = T // (64 N))."""
+    points, n = T // (64 N)).  With ``kcp_parts`` = P > 1 the sequence runs as P
+    parallel segments folded through their (M, S~) pairs (kda_chunk_fwd_kcp)."""
     B, T, H, D = q.shape
     in_dt = _dt(q)
     odt = q.dtype if out_dtype is None else out_dtype
@@ -182,6 +187,18 @@ def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=
     if workspace is None:
         nbytes = workspace_size(desc, None if overlap else segment_tokens)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if kcp_parts and kcp_parts > 1:
+        nb = int(lib().kda_chunk_fwd_kcp_workspace_size(ctypes.byref(desc), int(kcp_parts)))
+        if nb == 0:
+            raise KdaError("kda_chunk_fwd_kcp_workspace_size", 5)
+        kws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        rc = lib().kda_chunk_fwd_kcp(
+            ctypes.byref(desc), int(kcp_parts), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A), _ptr(S0),
+            _ptr(gate), _ptr(rms_w), _ptr(res.get("o")), _ptr(res.get("y")), _ptr(res.get("S_T")), _ptr(kws),
+            kws.numel(), _stream(dev))
+        if rc != 0:
+            raise KdaError("kda_chunk_fwd_kcp", rc)
+        return res
     if snapshot_chunks:
         n = int(lib().kda_snapshot_count(ctypes.byref(desc), int(snapshot_chunks)))
         if "snapshots" not in res:

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_intra.hip", "kda_scan.hip", "kda_fused.hip", "kda_prep.hip", "kda_aux.hip", "kda_decode.hip"]
+SOURCES = ["kda_api.cpp", "kda_intra.hip", "kda_scan.hip", "kda_fused.hip", "kda_prep.hip", "kda_kcp.hip", "kda_aux.hip", "kda_decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

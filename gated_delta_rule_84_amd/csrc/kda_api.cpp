@@ -348,7 +348,7 @@ struct Snapshots {
 kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
                           const void* z, const float* A, const float* S0, const void* gate, const float* rms_w,
                           void* o, void* y, float* S_T, void* ws, size_t ws_bytes, void* stream, Tracer tr,
-                          Snapshots snap = Snapshots{nullptr, 1, 0}) {
+                          Snapshots snap = Snapshots{nullptr, 1, 0}, bool v_optional = false) {
   kda_status st = validate_desc(d);
   if (st != KDA_OK) return st;
   if (!o && !y && !S_T && !snap.ptr) return KDA_ERR_NULL_ARG;
@@ -360,7 +360,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
                           static_cast<hipStream_t>(stream));
     return KDA_OK;
   }
-  if (!q || !k || !v || !beta || !z || !A) return KDA_ERR_NULL_ARG;
+  if (!q || !k || (!v && !v_optional) || !beta || !z || !A) return KDA_ERR_NULL_ARG;  // no V: V = 0
   if (y && !gate) return KDA_ERR_NULL_ARG;
   const size_t es = elem_size(d->in_dtype);
   for (const void* p : {q, k, v, z, (const void*)o, (const void*)y, gate, (const void*)ws})
@@ -618,6 +618,82 @@ kda_status kda_input_prep(const kda_desc* d, int32_t conv_width, const void* xq,
   // read before it is overwritten by the same thread
   p.tokens_per_block = (p.state_out != nullptr && p.state_out == p.state_in) ? d->T : 128;
   return check_launch(kda::launch_input_prep(p, d->in_dtype == KDA_F32, s), s);
+}
+
+namespace {
+// KCP: n_parts equal segments per sequence, each a multiple of the chunk.
+bool kcp_shape(const kda_desc* d, int32_t n_parts, kda_desc* inner) {
+  if (n_parts < 2 || d->T % (n_parts * kChunk) != 0 || (int64_t)d->B * n_parts > 0x7fffffff) return false;
+  *inner = *d;
+  inner->B = d->B * n_parts;
+  inner->T = d->T / n_parts;
+  return true;
+}
+size_t kcp_state_bytes(const kda_desc* d, int32_t n_parts) {
+  return align256((size_t)d->B * n_parts * d->H * d->d_k * d->d_v * sizeof(float));
+}
+}  // namespace
+
+size_t kda_chunk_fwd_kcp_workspace_size(const kda_desc* d, int32_t n_parts) {
+  if (validate_desc(d) != KDA_OK) return 0;
+  if (n_parts == 1 || d->T == 0) return kda_chunk_fwd_workspace_size(d);
+  kda_desc inner;
+  if (!kcp_shape(d, n_parts, &inner)) return 0;
+  return 3 * kcp_state_bytes(d, n_parts) + kda_chunk_fwd_workspace_size(&inner);
+}
+
+kda_status kda_chunk_fwd_kcp(const kda_desc* d, int32_t n_parts, const void* q, const void* k, const void* v,
+                             const void* beta, const void* z, const float* A, const float* S0, const void* gate,
+                             const float* rms_w, void* o, void* y, float* S_T, void* ws, size_t ws_bytes,
+                             void* stream) {
+  kda_status st = validate_desc(d);
+  if (st != KDA_OK) return st;
+  if (n_parts < 1) return KDA_ERR_BAD_SHAPE;
+  if (n_parts == 1 || d->T == 0)
+    return chunk_fwd_impl(d, q, k, v, beta, z, A, S0, gate, rms_w, o, y, S_T, ws, ws_bytes, stream,
+                          Tracer{nullptr, 0});
+  kda_desc inner;
+  if (!kcp_shape(d, n_parts, &inner)) return KDA_ERR_UNSUPPORTED;
+  if (!o && !y && !S_T) return KDA_ERR_NULL_ARG;
+  if (!q || !k || !v || !beta || !z || !A) return KDA_ERR_NULL_ARG;
+  if (y && !gate) return KDA_ERR_NULL_ARG;
+  if ((S0 && !aligned(S0, 4)) || (S_T && !aligned(S_T, 4))) return KDA_ERR_MISALIGNED;
+  const size_t sb = kcp_state_bytes(d, n_parts);
+  if (!ws || !aligned(ws, 16) || ws_bytes < 3 * sb) return KDA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  float* M = reinterpret_cast<float*>(base);
+  float* St = reinterpret_cast<float*>(base + sb);
+  float* Sin = reinterpret_cast<float*>(base + 2 * sb);
+  void* iws = base + 3 * sb;
+  const size_t ibytes = ws_bytes - 3 * sb;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = d->d_k;
+  const Tracer none{nullptr, 0};
+  // pass 1: every segment's transfer (from the identity with V = 0) and its
+  // state from zero, all segments at once
+  st = check_launch(kda::launch_identity_states(M, (int64_t)inner.B * inner.H, D, s), s);
+  if (st != KDA_OK) return st;
+  st = chunk_fwd_impl(&inner, q, k, nullptr, beta, z, A, M, nullptr, nullptr, nullptr, nullptr, M, iws, ibytes, s,
+                      none, Snapshots{nullptr, 1, 0}, true);
+  if (st != KDA_OK) return st;
+  st = chunk_fwd_impl(&inner, q, k, v, beta, z, A, nullptr, nullptr, nullptr, nullptr, nullptr, St, iws, ibytes, s,
+                      none);
+  if (st != KDA_OK) return st;
+  // fold along each sequence: the entry state of every segment
+  st = check_launch(kda::launch_kcp_fold(M, St, S0, Sin, d->B, n_parts, d->H, D, s), s);
+  if (st != KDA_OK) return st;
+  // pass 2: every segment from its entry state, with outputs; final states in place
+  st = chunk_fwd_impl(&inner, q, k, v, beta, z, A, Sin, gate, rms_w, o, y, Sin, iws, ibytes, s, none);
+  if (st != KDA_OK) return st;
+  if (S_T) {
+    const int64_t per = (int64_t)d->H * D * D;
+    for (int b = 0; b < d->B; ++b) {
+      st = check_launch(
+          kda::launch_copy_state(Sin + ((int64_t)b * n_parts + n_parts - 1) * per, S_T + b * per, per, s), s);
+      if (st != KDA_OK) return st;
+    }
+  }
+  return KDA_OK;
 }
 
 int32_t kda_snapshot_count(const kda_desc* d, int32_t every_chunks) {

@@ -166,7 +166,8 @@ __global__ __launch_bounds__((FusedLds<T, D>::NT), 1) void kda_fused_kernel(cons
 #pragma unroll
     for (int i = 0; i < L::VU; ++i) {
       const int u = pt + L::NP * i;
-      vst[i] = reinterpret_cast<const u32x4*>(v0 + min(u / L::VPR, last) * tok_stride)[u % L::VPR];
+      vst[i] = p.v != nullptr ? reinterpret_cast<const u32x4*>(v0 + min(u / L::VPR, last) * tok_stride)[u % L::VPR]
+                              : u32x4{0u, 0u, 0u, 0u};  // no V: V = 0
     }
   };
   auto commit_V = [&](int c) {

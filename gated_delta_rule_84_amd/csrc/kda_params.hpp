@@ -58,7 +58,7 @@ struct IntraParams {
 };
 
 struct ScanParams {
-  const void* v;
+  const void* v;        // [B, T, H, D], or nullptr for V = 0 (the transfer of a segment, see kda_chunk_fwd_kcp)
   const void* gate;     // [B, T, H, D] gate logits (input dtype) or nullptr
   const float* rms_w;   // [H, D] or nullptr (weight 1)
   const float* S_in;    // [B, H, D, D] or nullptr (zero state)
@@ -148,5 +148,12 @@ hipError_t launch_state_io(const StateIoParams& p, int D, hipStream_t s);
 hipError_t launch_prepass(const PrepassParams& p, int D, int in_f32, hipStream_t s);
 hipError_t launch_copy_state(const float* src, float* dst, int64_t n_floats, hipStream_t s);
 hipError_t launch_input_prep(const InputPrepParams& p, int in_f32, hipStream_t s);
+// States of a B x P grid of segments: M, St [B, P, H, D, D] (transfer and
+// zero-start state of each segment), S0 [B, H, D, D] or nullptr; writes
+// Sin [B, P, H, D, D], the entry state of every segment.
+hipError_t launch_kcp_fold(const float* M, const float* St, const float* S0, float* Sin, int B, int P, int H, int D,
+                           hipStream_t s);
+// dst[i] = identity (D x D) for i < n
+hipError_t launch_identity_states(float* dst, int64_t n, int D, hipStream_t s);
 
 }  // namespace kda

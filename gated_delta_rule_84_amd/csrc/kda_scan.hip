@@ -147,15 +147,15 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
     for (int i = 0; i < L::PER_THREAD; ++i) {
       const int u = tid + NT * i;
       if (i < L::FULL || tail_ok) {
-        const u32x4* src;
         if (u < L::REC_UNITS) {
-          src = reinterpret_cast<const u32x4*>(rec) + u;
-        } else {  // V rows past the end are clamped (and zeroed where used)
+          stg[i] = reinterpret_cast<const u32x4*>(rec)[u];
+        } else if (vin != nullptr) {  // V rows past the end are clamped (and zeroed where used)
           const int vu = u - L::REC_UNITS;
           const int r = min(vu / VPR, last);
-          src = reinterpret_cast<const u32x4*>(vin + head_base + (tok0 + r) * tok_stride) + (vu % VPR);
+          stg[i] = reinterpret_cast<const u32x4*>(vin + head_base + (tok0 + r) * tok_stride)[vu % VPR];
+        } else {  // no V: V = 0
+          stg[i] = u32x4{0u, 0u, 0u, 0u};
         }
-        stg[i] = *src;
       }
     }
   };
@@ -218,7 +218,8 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          vreg[4 * mt + i] = vin[head_base + (tok0 + min(16 * mt + 4 * g4 + i, nvalid - 1)) * tok_stride + col];
+          vreg[4 * mt + i] =
+              vin ? vin[head_base + (tok0 + min(16 * mt + 4 * g4 + i, nvalid - 1)) * tok_stride + col] : T{};
     }
     if (more) fetch(c + 1);
 
@@ -435,7 +436,7 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
     const int hid = tid - 64 * L::NCW;
     const bool gated = p.y != nullptr;
     const T* vin = static_cast<const T*>(p.v);
-    const T* gin = gated ? static_cast<const T*>(p.gate) : vin;  // never read when ungated
+    const T* gin = static_cast<const T*>(p.gate);  // staged only when gated
 
     // LDS offsets of this thread's units (loop invariant).  Part A and the gate
     // slab split evenly over the helper threads; part B's last units are
@@ -470,9 +471,11 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
         const int u = hid + NH * i;
         if (i < AR) {
           stA[i] = rp[u];
-        } else {
+        } else if (vin != nullptr) {
           const int vu = u - L::A_REC;
           stA[i] = reinterpret_cast<const u32x4*>(v0 + min(vu / VPR, last) * tok_stride)[vu % VPR];
+        } else {  // no V: V = 0
+          stA[i] = u32x4{0u, 0u, 0u, 0u};
         }
       }
     };
@@ -534,7 +537,7 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
     load_B(0);
     commit_A(0);
     load_A(min(1, cl));
-    load_G(0);
+    if (gated) load_G(0);
     __syncthreads();
     for (int c = 0; c < p.nc; ++c) {
       // first half of step c: the compute waves read part A of chunk c
@@ -544,9 +547,9 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
       __syncthreads();
       // second half: the compute waves read part B of chunk c and write tile c
       commit_A(min(c + 1, cl));
-      commit_G();                                        // gate logits of chunk c
+      if (gated) commit_G();                             // gate logits of chunk c
       load_A(min(c + 2, cl));
-      load_G(min(c + 1, cl));
+      if (gated) load_G(min(c + 1, cl));
       __syncthreads();
     }
     epilogue(cl, std::true_type{});

@@ -140,44 +140,53 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
         for (int i = 0; i < 4; ++i) otile[(16 * mt + 4 * g4 + i) * L::PO + col0 + 16 * nt] = O[mt][nt][i];
   };
   for (int c = 0; c < p.nc; ++c) {
-    V8 Sb[KS][NCT];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-      for (int nt = 0; nt < NCT; ++nt) Sb[kk][nt] = Ops::from_acc(S[2 * kk][nt], S[2 * kk + 1][nt]);
-
     // Every product step below issues the LDS reads of the next step's
     // operands before its own MFMAs (scheduling fences keep that order), so
     // the LDS latency overlaps the previous products.
 
     // R = V - (K . Gamma) S (the record holds kg negated; V enters through a
-    // 0/1 selection product, rows past the end are zero) and O = (Q . Gamma) S
+    // 0/1 selection product, rows past the end are zero) and O = (Q . Gamma) S.
+    // S enters as hi/lo bf16 parts (two MFMAs per step): with little decay
+    // its rounding would otherwise accumulate from chunk to chunk.  The steps
+    // run K-step major, so only one K-step's parts of S are live at a time.
     f32x4 R[4][NCT];
     {
-      constexpr int G1 = 4 * KS;  // steps (mt, kk)
-      V8 ak[2], aq[2], av[2];
+      V8 av[2];
+      auto ldv = [&](int mt, int bf) {
+        av[bf] = Ops::ld(lds + L::VS + (16 * mt + n) * L::PQ + (32 * wave + 8 * g4) * L::ES);
+      };
+      ldv(0, 0);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int bf = mt & 1;
+        if (mt + 1 < 4) ldv(mt + 1, bf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+        R[mt][0] = mma32(av[bf], vsel0, zero4());
+        R[mt][1] = mma32(av[bf], vsel1, zero4());
+        O[mt][0] = O[mt][1] = zero4();
+      }
+      constexpr int G1 = 4 * KS;  // steps (kk, mt)
+      V8 ak[2], aq[2];
       auto ld1 = [&](int g, int bf) {
-        const int mt = g / KS, kk = g % KS;
+        const int kk = g / 4, mt = g % 4;
         const int off = (16 * mt + n) * L::PQ + (32 * kk + 8 * g4) * L::ES;
         ak[bf] = Ops::ld(kg + off);
         aq[bf] = Ops::ld(qg + off);
-        if (kk == 0) av[bf] = Ops::ld(lds + L::VS + (16 * mt + n) * L::PQ + (32 * wave + 8 * g4) * L::ES);
       };
       ld1(0, 0);
+      typename Ops::Prec Sp[NCT];
 #pragma unroll
       for (int g = 0; g < G1; ++g) {
-        const int bf = g & 1, mt = g / KS, kk = g % KS;
+        const int bf = g & 1, kk = g / 4, mt = g % 4;
         if (g + 1 < G1) ld1(g + 1, bf ^ 1);
+        if (mt == 0)
+#pragma unroll
+          for (int nt = 0; nt < NCT; ++nt) Sp[nt] = Ops::prec_from_acc(S[2 * kk][nt], S[2 * kk + 1][nt]);
         __builtin_amdgcn_sched_barrier(0);
-        if (kk == 0) {
-          R[mt][0] = mma32(av[bf], vsel0, zero4());
-          R[mt][1] = mma32(av[bf], vsel1, zero4());
-          O[mt][0] = O[mt][1] = zero4();
-        }
 #pragma unroll
         for (int nt = 0; nt < NCT; ++nt) {
-          R[mt][nt] = mma32(ak[bf], Sb[kk][nt], R[mt][nt]);
-          O[mt][nt] = mma32(aq[bf], Sb[kk][nt], O[mt][nt]);
+          R[mt][nt] = Ops::mma_split_b(ak[bf], Sp[nt], R[mt][nt]);
+          O[mt][nt] = Ops::mma_split_b(aq[bf], Sp[nt], O[mt][nt]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);

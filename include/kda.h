@@ -218,6 +218,32 @@ kda_status kda_chunk_fwd_snapshots(const kda_desc* d, const void* q, const void*
 int32_t kda_snapshot_count(const kda_desc* d, int32_t every_chunks);
 
 /*
+ * kda_chunk_fwd with the sequence cut into n_parts equal segments that are
+ * processed in parallel (KCP, K3 blog section 10.2, on one GPU): over a
+ * segment the state map is affine, S_out = M S_in + S~.  Pass 1 runs every
+ * segment at once from S = I with V = 0 (giving M) and from S = 0 (giving
+ * S~); a fold along each sequence gives every segment's entry state
+ * (S_in[p + 1] = M[p] S_in[p] + S~[p], S_in[0] = S0); pass 2 runs every
+ * segment at once from its entry state and writes o / y.  S_T is pass 2's
+ * state after the last segment.  Arguments as kda_chunk_fwd; ws of
+ * kda_chunk_fwd_kcp_workspace_size(d, n_parts) bytes (three fp32 state sets
+ * of B * n_parts * H * d_k * d_v plus the segments' own workspace).
+ * T must be a multiple of 64 * n_parts (KDA_ERR_UNSUPPORTED otherwise);
+ * n_parts == 1 is kda_chunk_fwd.  Outputs equal kda_chunk_fwd's up to fp32
+ * rounding of the folded entry states.  The work is about three forward
+ * passes: this is the one-GPU share of sequence parallelism across GPUs, not
+ * a faster single-GPU schedule.
+ */
+kda_status kda_chunk_fwd_kcp(const kda_desc* d, int32_t n_parts, const void* q, const void* k, const void* v,
+                             const void* beta, const void* z, const float* A, const float* S0, const void* gate,
+                             const float* rms_w, void* o, void* y, float* S_T, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* Workspace bytes for kda_chunk_fwd_kcp (0 if *d is invalid or T is not a
+ * multiple of 64 * n_parts). */
+size_t kda_chunk_fwd_kcp_workspace_size(const kda_desc* d, int32_t n_parts);
+
+/*
  * Input steps before the core (K3 blog section 2.1): from the projections
  * x_q, x_k, x_v [B, T, H, d] and the beta logits [B, T, H] (all d->in_dtype),
  *     q = Swish(ShortConv(x_q)),  k = Swish(ShortConv(x_k)),

@@ -155,3 +155,17 @@ def test_input_prep_host_errors():
     assert _prep(d, xq=FAKE + 2) == 4                                # 16-byte vectors
     assert _prep(d, st_in=FAKE + 2) == 4
     assert _prep(_desc(d_k=96, d_v=96)) == 5
+
+
+def test_kcp_host_errors():
+    L = kda.lib()
+    d = _desc(T=1000)                                                # 1000 is not a multiple of 128
+    assert L.kda_chunk_fwd_kcp_workspace_size(ctypes.byref(d), 2) == 0
+    assert L.kda_chunk_fwd_kcp(ctypes.byref(d), 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None,
+                               None, FAKE, 1 << 40, None) == 5
+    assert L.kda_chunk_fwd_kcp(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None,
+                               None, FAKE, 1 << 40, None) == 2
+    d2 = _desc(T=1024)
+    one = L.kda_chunk_fwd_kcp_workspace_size(ctypes.byref(d2), 1)
+    four = L.kda_chunk_fwd_kcp_workspace_size(ctypes.byref(d2), 4)
+    assert one == L.kda_chunk_fwd_workspace_size(ctypes.byref(d2)) and four >= 3 * 2 * 4 * 3 * 128 * 128 * 4
