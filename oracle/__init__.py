@@ -43,7 +43,7 @@ def _load():
         L.kda_oracle_forward.restype = ctypes.c_int
         L.kda_oracle_forward.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
                                          dbl, dbl, ctypes.c_int, dbl, vp, vp, vp, dbl, vp, vp, vp,
-                                         ctypes.c_int]
+                                         ctypes.c_int, ctypes.c_int]
         _lib = L
     return _lib
 
@@ -61,7 +61,7 @@ def _ptr(a):
 
 
 def forward_c(q, k, v, beta, z, A, S0=None, gate=None, w=None, g_min=-5.0, scale=1.0,
-              l2norm=True, l2_eps=1e-6, rms_eps=1e-6, want_o=True, nthreads=0):
+              l2norm=True, l2_eps=1e-6, rms_eps=1e-6, want_o=True, nthreads=0, decay="k3"):
     """Run the C oracle.  q, k, z: [B, T, H, dk]; v, gate: [B, T, H, dv];
     beta: [B, T, H]; A: [H]; S0: [B, H, dk, dv] fp64/fp32 or None.
     Returns dict with S_T (fp64) and o / y when requested."""
@@ -80,7 +80,8 @@ def forward_c(q, k, v, beta, z, A, S0=None, gate=None, w=None, g_min=-5.0, scale
     ST = np.empty((B, H, dk, dv))
     rc = _load().kda_oracle_forward(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z),
                                     _ptr(A), g_min, scale, int(bool(l2norm)), l2_eps, _ptr(s0),
-                                    _ptr(g), _ptr(wh), rms_eps, _ptr(o), _ptr(y), _ptr(ST), int(nthreads))
+                                    _ptr(g), _ptr(wh), rms_eps, _ptr(o), _ptr(y), _ptr(ST), int(nthreads),
+                                    {"k3": 0, "softplus": 1}[decay])
     if rc != 0:
         raise RuntimeError(f"kda_oracle_forward failed ({rc})")
     out = {"S_T": ST}

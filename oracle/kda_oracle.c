@@ -11,8 +11,10 @@
  *     o_t = S_t^T q_t,
  * applied in the equivalent rank-1 order
  *     S <- Diag(alpha_t) S;  S <- S + beta_t k_t (v_t - S^T k_t)^T,
- * with alpha_t = exp(g_min * sigmoid(exp(A_h) z_t)) (section 2.2) and the
- * gate y_t = sigmoid(gate_t) * RMSNorm(o_t) (section 2.3).
+ * with alpha_t = exp(g_min * sigmoid(exp(A_h) z_t)) (section 2.2; decay == 0)
+ * or, for the Kimi Linear map that section 2.2 compares it with (decay == 1),
+ * alpha_t = exp(-exp(A_h) softplus(z_t)), and the gate
+ * y_t = sigmoid(gate_t) * RMSNorm(o_t) (section 2.3).
  * q and k are L2-normalised first when l2norm != 0: x / sqrt(sum x^2 + eps).
  *
  * Layouts: q, k, z [B, T, H, dk]; v, gate [B, T, H, dv]; beta [B, T, H];
@@ -34,13 +36,17 @@ static double sigmoid_stable(double x) {
   return e / (1.0 + e);
 }
 
+/* softplus(x) = log(1 + e^x) without overflow */
+static double softplus_stable(double x) { return (x > 0 ? x : 0.0) + log1p(exp(-fabs(x))); }
+
 int kda_oracle_forward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                        const float* q, const float* k, const float* v, const float* beta,
                        const float* z, const float* A, double g_min, double scale, int l2norm,
                        double l2_eps, const double* S0, const float* gate, const float* w,
-                       double rms_eps, double* o, double* y, double* S_T, int nthreads) {
+                       double rms_eps, double* o, double* y, double* S_T, int nthreads, int decay) {
   if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
   if (!q || !k || !v || !beta || !z || !A) return -1;
+  if (decay != 0 && decay != 1) return -1;
   if (y && !gate) return -1;
   const int64_t tasks = B * H;
   int fail = 0;
@@ -83,7 +89,8 @@ int kda_oracle_forward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
         for (int64_t i = 0; i < dk; ++i) {
           qv[i] *= rq * scale;
           kv[i] *= rk;
-          al[i] = exp(g_min * sigmoid_stable(eA * (double)zr[i]));
+          al[i] = decay == 0 ? exp(g_min * sigmoid_stable(eA * (double)zr[i]))
+                             : exp(-eA * softplus_stable((double)zr[i]));
         }
         /* S <- Diag(alpha) S */
         for (int64_t i = 0; i < dk; ++i) {

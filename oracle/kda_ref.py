@@ -45,6 +45,13 @@ def decay_log(z, A_h, g_min: float = G_MIN):
     return g_min * sigmoid(np.exp(np.float64(A_h)) * np.asarray(z, dtype=np.float64))
 
 
+def decay_log_softplus(z, A_h):
+    """Kimi Linear's log-decay map, the one section 2.2 replaces:
+    g = -e^{A_h} Softplus(z), unbounded below (Softplus(z) = log(1 + e^z))."""
+    z = np.asarray(z, dtype=np.float64)
+    return -np.exp(np.float64(A_h)) * np.logaddexp(0.0, z)
+
+
 def l2_normalize(x, eps: float = L2_EPS):
     """Per-row L2 normalisation (section 2.1 applies L2Norm to q and k).
     Reading: eps is added under the square root, x / sqrt(sum x^2 + eps)."""
@@ -62,14 +69,15 @@ def _prep(q, k, l2norm, eps, scale):
 
 
 def kda_recurrent(q, k, v, beta, z=None, A_h=0.0, g=None, S0=None, g_min=G_MIN,
-                  l2norm=True, l2_eps=L2_EPS, scale=1.0, literal=False):
+                  l2norm=True, l2_eps=L2_EPS, scale=1.0, literal=False, decay="k3"):
     """Token-by-token KDA recurrence of section 2.1, single head, fp64:
 
         S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
         o_t = S_t^T q_t
 
-    alpha_t = e^{g_t} with g_t from ``decay_log(z_t, A_h)`` unless the log
-    decay ``g`` ([T, dk]) is given directly (used by tests only).
+    alpha_t = e^{g_t} with g_t from ``decay_log(z_t, A_h)`` (``decay`` "k3")
+    or ``decay_log_softplus(z_t, A_h)`` ("softplus", the Kimi Linear map),
+    unless the log decay ``g`` ([T, dk]) is given directly (tests only).
 
     ``literal=True`` forms the d_k x d_k matrix (I - beta k k^T) Diag(alpha)
     and multiplies, exactly as printed.  The default applies the same step
@@ -87,7 +95,7 @@ def kda_recurrent(q, k, v, beta, z=None, A_h=0.0, g=None, S0=None, g_min=G_MIN,
     T, dk = k.shape
     dv = v.shape[1]
     if g is None:
-        g = decay_log(z, A_h, g_min)
+        g = decay_log(z, A_h, g_min) if decay == "k3" else decay_log_softplus(z, A_h)
     g = np.asarray(g, dtype=np.float64)
     alpha = np.exp(g)
     S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64, copy=True)

@@ -44,6 +44,10 @@ MUTANTS = [
      "ext = np.concatenate([prev[::-1], x], axis=0)"),
     ("conv_state_not_advanced", "return y, ext[T:].copy()", "return y, ext[:W - 1].copy()"),
     ("swish_sign", "return x * sigmoid(x)", "return x * sigmoid(-x)"),
+    ("softplus_scale_dropped", "return -np.exp(np.float64(A_h)) * np.logaddexp(0.0, z)",
+     "return -np.logaddexp(0.0, z)"),
+    ("softplus_as_relu", "return -np.exp(np.float64(A_h)) * np.logaddexp(0.0, z)",
+     "return -np.exp(np.float64(A_h)) * np.maximum(z, 0.0)"),
 ]
 
 

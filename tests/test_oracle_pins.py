@@ -359,3 +359,46 @@ def test_input_prep_chains_through_its_state():
     # the output is Swish of the convolution, per stream
     y, _ = R.short_conv(xs[1][0].reshape(T, H * d), ws[1])
     assert np.allclose(full["k"][0].reshape(T, H * d), y / (1.0 + np.exp(-y)), atol=1e-14)
+
+
+# ---- Kimi Linear decay map (the one K3's section 2.2 replaces) ----
+
+def test_softplus_decay_values():
+    # Softplus(0) = ln 2, so g(0) = -ln 2 and alpha = 1/2 exactly at A = 0
+    assert abs(R.decay_log_softplus(np.array([0.0]), 0.0)[0] + math.log(2.0)) < 1e-15
+    assert abs(R.decay_log_softplus(np.array([0.0]), math.log(3.0))[0] + 3.0 * math.log(2.0)) < 1e-14
+    # unbounded below, close to -z e^A for large z; close to -e^{z + A} for very negative z
+    assert abs(R.decay_log_softplus(np.array([60.0]), 0.0)[0] + 60.0) < 1e-12
+    assert abs(R.decay_log_softplus(np.array([-30.0]), 0.5)[0] + math.exp(-30.0 + 0.5)) < 1e-25
+    assert np.all(R.decay_log_softplus(np.linspace(-20, 20, 41), -0.3) < 0)
+
+
+def test_softplus_decay_halves_the_state():
+    """beta = 0 and z = 0, A = 0: every step multiplies the state by exactly
+    1/2 (powers of two are exact in fp64), for the numpy and the C oracle."""
+    rng = np.random.default_rng(8)
+    T, d = 7, 4
+    q, k, v = rng.standard_normal((T, d)), rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    S0 = rng.standard_normal((d, d))
+    o, S = R.kda_recurrent(q, k, v, np.zeros(T), z=np.zeros((T, d)), A_h=0.0, S0=S0, decay="softplus")
+    assert np.array_equal(S, S0 * 2.0 ** -T)
+    qn = q / np.sqrt((q * q).sum(1, keepdims=True) + 1e-6)
+    assert np.allclose(o, np.stack([(S0 * 2.0 ** -(t + 1)).T @ qn[t] for t in range(T)]), atol=1e-15)
+    f32 = lambda a: a.astype(np.float32)[None, :, None]
+    rc = oracle.forward_c(f32(q), f32(k), f32(v), np.zeros((1, T, 1), np.float32), np.zeros((1, T, 1, d), np.float32),
+                          np.zeros(1, np.float32), S0=S0[None, None], decay="softplus")
+    assert np.array_equal(rc["S_T"][0, 0], S0 * 2.0 ** -T)
+
+
+def test_c_oracle_softplus_matches_numpy():
+    rng = np.random.default_rng(9)
+    T, d, H = 40, 8, 2
+    q, k, v = (rng.standard_normal((1, T, H, d)).astype(np.float32) for _ in range(3))
+    z = rng.standard_normal((1, T, H, d)).astype(np.float32) * 3
+    beta = (1 / (1 + np.exp(-rng.standard_normal((1, T, H))))).astype(np.float32)
+    A = np.array([0.4, -0.7], np.float32)
+    rc = oracle.forward_c(q, k, v, beta, z, A, decay="softplus")
+    for h in range(H):
+        o, S = R.kda_recurrent(q[0, :, h], k[0, :, h], v[0, :, h], beta[0, :, h], z=z[0, :, h], A_h=A[h],
+                               decay="softplus")
+        assert np.allclose(rc["o"][0, :, h], o, atol=1e-12) and np.allclose(rc["S_T"][0, h], S, atol=1e-12)
