@@ -143,6 +143,8 @@ def main() -> int:
                     help="the library's choice (default), the fused kernel, or a two-kernel schedule")
     ap.add_argument("--segment-tokens", type=int, default=0,
                     help="tokens per segment of the two-kernel schedules; 0: library default")
+    ap.add_argument("--decay", choices=("k3", "softplus"), default="k3",
+                    help="decay map: K3's bounded map (the method), or Kimi Linear's softplus map (ablation)")
     ap.add_argument("--no-input-prep", action="store_true",
                     help="skip timing the input steps (ShortConv + Swish, Sigmoid) on the workload's shapes")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -196,7 +198,7 @@ def main() -> int:
     overlap = args.schedule in ("auto", "overlapped")
     seg_arg = args.segment_tokens or None
     desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg_arg if overlap else 0,
-                         overlap=overlap, fused=fused)
+                         overlap=overlap, fused=fused, decay=args.decay)
     ws_bytes = kda.workspace_size(desc) if (overlap or fused or not seg_arg) else kda.workspace_size(desc, seg_arg)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     seg, sched = kda.schedule(desc, ws_bytes)
@@ -209,7 +211,7 @@ def main() -> int:
     def step(events=None):
         kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t.get("S0"), gate=t["gate"],
                       want_o=False, out=out, workspace=ws, events=events, segment_tokens=seg_arg,
-                      overlap=overlap, fused=fused)
+                      overlap=overlap, fused=fused, decay=args.decay)
 
     for _ in range(args.warmup):
         step()
@@ -266,7 +268,7 @@ def main() -> int:
         "data": "synthetic (seeded; K3 layer shapes, no trained weights)",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "d_k": D, "d_v": D, "chunk": 64,
                    "inputs": "bf16", "state": "fp32", "outputs": "y (bf16) + S_T (fp32)", "gate": True,
-                   "schedule": sched, "segment_tokens": seg},
+                   "schedule": sched, "segment_tokens": seg, "decay": args.decay},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(dom, wl.name),
                      "algorithmic_bytes_per_launch": dom_bytes / launches[dom],

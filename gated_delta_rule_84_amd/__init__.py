@@ -30,7 +30,11 @@ class KdaDesc(ctypes.Structure):
                 ("g_min", ctypes.c_float), ("q_scale", ctypes.c_float), ("l2_eps", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("qk_l2norm", ctypes.c_int32),
                 ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
-                ("segment_tokens", ctypes.c_int32), ("overlap", ctypes.c_int32), ("fused", ctypes.c_int32)]
+                ("segment_tokens", ctypes.c_int32), ("overlap", ctypes.c_int32), ("fused", ctypes.c_int32),
+                ("decay", ctypes.c_int)]
+
+
+DECAYS = {"k3": 0, "softplus": 1}
 
 
 class KdaError(RuntimeError):
@@ -113,7 +117,7 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 def make_desc(B, T, H, D, in_dtype, out_dtype, g_min=-5.0, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6,
-              qk_l2norm=True, segment_tokens=0, overlap=True, fused=None) -> KdaDesc:
+              qk_l2norm=True, segment_tokens=0, overlap=True, fused=None, decay="k3") -> KdaDesc:
     d = KdaDesc()
     rc = lib().kda_desc_init(ctypes.byref(d), B, T, H, D, in_dtype, out_dtype)
     if rc != 0:
@@ -121,6 +125,7 @@ def make_desc(B, T, H, D, in_dtype, out_dtype, g_min=-5.0, q_scale=1.0, l2_eps=1
     d.g_min, d.q_scale, d.l2_eps, d.rms_eps, d.qk_l2norm = g_min, q_scale, l2_eps, rms_eps, int(bool(qk_l2norm))
     d.segment_tokens, d.overlap = int(segment_tokens or 0), int(bool(overlap))
     d.fused = 1 if fused is None else (2 if fused else 0)  # None: the library decides
+    d.decay = DECAYS[decay]
     return d
 
 

@@ -57,6 +57,7 @@ kda_status validate_desc(const kda_desc* d) {
   if (!(d->l2_eps >= 0.0f) || !(d->rms_eps >= 0.0f)) return KDA_ERR_UNSUPPORTED;
   if (d->segment_tokens < 0 || (d->overlap != 0 && d->overlap != 1) || d->fused < 0 || d->fused > 2)
     return KDA_ERR_BAD_SHAPE;
+  if (d->decay != KDA_DECAY_K3 && d->decay != KDA_DECAY_SOFTPLUS) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
 }
 
@@ -119,7 +120,8 @@ int device_cus() {
 // head on one compute unit, so it pays off once there are at least as many
 // (head, sequence) pairs as compute units (fused == 1); fused == 2 forces it.
 bool fused_wanted(const kda_desc* d) {
-  if (d->fused == 0 || !kda::fused_supported(d->d_k, d->in_dtype == KDA_F32)) return false;
+  if (d->fused == 0 || d->decay != KDA_DECAY_K3 || !kda::fused_supported(d->d_k, d->in_dtype == KDA_F32))
+    return false;
   if (d->fused == 2) return true;
   const int cus = device_cus();
   return cus > 0 && (int64_t)d->B * d->H >= cus;
@@ -304,6 +306,7 @@ kda_status kda_desc_init(kda_desc* d, int32_t B, int32_t T, int32_t H, int32_t h
   d->segment_tokens = 0;
   d->overlap = 1;
   d->fused = 1;
+  d->decay = KDA_DECAY_K3;
   return validate_desc(d);
 }
 
@@ -395,6 +398,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     ip.q_scale = d->q_scale;
     ip.l2_eps = d->l2_eps;
     ip.l2norm = d->qk_l2norm;
+    ip.decay = d->decay;
     ip.ws = recs;
     tr.before(st_);
     const kda_status r = check_launch(kda::launch_intra(ip, D, in_f32, st_), st_);
@@ -447,6 +451,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     ip.q_scale = d->q_scale;
     ip.l2_eps = d->l2_eps;
     ip.l2norm = d->qk_l2norm;
+    ip.decay = d->decay;
     kda::ScanParams sp{};
     sp.v = v;
     sp.gate = y ? gate : nullptr;
@@ -737,6 +742,7 @@ kda_status kda_recurrent_step(const kda_desc* d, const void* q, const void* k, c
   p.l2_eps = d->l2_eps;
   p.rms_eps = d->rms_eps;
   p.l2norm = d->qk_l2norm;
+  p.decay = d->decay;
   p.out_f32 = d->out_dtype == KDA_F32;
   return check_launch(kda::launch_decode(p, d->d_k, d->in_dtype == KDA_F32, s), s);
 }
@@ -784,6 +790,7 @@ kda_status kda_prepass(const kda_desc* d, const void* q, const void* k, const vo
   p.g_min = d->g_min;
   p.l2_eps = d->l2_eps;
   p.l2norm = d->qk_l2norm;
+  p.decay = d->decay;
   p.G = G;
   p.rq = rq;
   p.rk = rk;

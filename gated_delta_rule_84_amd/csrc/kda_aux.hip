@@ -62,7 +62,7 @@ hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_
 // Runs the same device routines as the intra-chunk kernel's prologue: wave i
 // forms sub-tile i's decay prefix in registers; the sub-tile totals are then
 // added up across the chunk through LDS.
-template <typename T, int D>
+template <typename T, int D, bool SP>
 __global__ __launch_bounds__(256) void kda_prepass_kernel(const PrepassParams p) {
   constexpr int KS = D / 32;
   __shared__ __attribute__((aligned(16))) float tot[4 * D];
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void kda_prepass_kernel(const PrepassParams p)
     zraw[kk] = R8::load(static_cast<const T*>(p.z) + rowp, kk, g4);
   }
   float P[KS][8];
-  subtile_decay_prefix<T, KS>(zraw, p.A[h], p.g_min, rvalid, P);
+  subtile_decay_prefix<T, KS, SP>(zraw, p.A[h], p.g_min, 1.0f, rvalid, P);
   if (n == 15)
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) put_run8(tot + wave * D, kk, g4, P[kk]);
@@ -115,15 +115,21 @@ __global__ __launch_bounds__(256) void kda_prepass_kernel(const PrepassParams p)
   }
 }
 
-hipError_t launch_prepass(const PrepassParams& p, int D, int in_f32, hipStream_t s) {
+template <bool SP>
+static void launch_prepass_t(const PrepassParams& p, int D, int in_f32, hipStream_t s) {
   const dim3 grid((p.T + kChunk - 1) / kChunk, p.H, p.B), block(256);
   if (in_f32) {
-    if (D == 64) hipLaunchKernelGGL((kda_prepass_kernel<float, 64>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((kda_prepass_kernel<float, 128>), grid, block, 0, s, p);
+    if (D == 64) hipLaunchKernelGGL((kda_prepass_kernel<float, 64, SP>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((kda_prepass_kernel<float, 128, SP>), grid, block, 0, s, p);
   } else {
-    if (D == 64) hipLaunchKernelGGL((kda_prepass_kernel<uint16_t, 64>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((kda_prepass_kernel<uint16_t, 128>), grid, block, 0, s, p);
+    if (D == 64) hipLaunchKernelGGL((kda_prepass_kernel<uint16_t, 64, SP>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((kda_prepass_kernel<uint16_t, 128, SP>), grid, block, 0, s, p);
   }
+}
+
+hipError_t launch_prepass(const PrepassParams& p, int D, int in_f32, hipStream_t s) {
+  if (p.decay) launch_prepass_t<true>(p, D, in_f32, s);
+  else launch_prepass_t<false>(p, D, in_f32, s);
   return hipGetLastError();
 }
 

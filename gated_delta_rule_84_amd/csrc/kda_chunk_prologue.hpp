@@ -101,20 +101,28 @@ __device__ __forceinline__ float add_row_shr(float x) {
 
 // Decay of this lane's row and channels, and its inclusive prefix over the
 // sub-tile's rows 0..n (lanes n of the lane's row group):
-//     P[kk][j] = sum_{m <= n} gscale Sigmoid(e^{A_h} z(m, lane_ch(kk, g, j)))
-// With gscale = g_min this is the log-decay prefix G (g = g_min Sigmoid(e^{A_h} z));
-// with gscale = g_min log2(e) it is G in base-2 units, ready for exp2.  Rows
-// past the end of the sequence (valid == false) contribute 0.
-template <typename T, int KS>
-__device__ __forceinline__ void subtile_decay_prefix(const typename Run8<T>::Raw* z, float A_h, float gscale,
-                                                     bool valid, float (&P)[KS][8]) {
-  const float c1 = -hw_exp(A_h) * kLog2e;  // Sigmoid(e^A z) = 1 / (1 + 2^{c1 z})
-  const float gm = valid ? gscale : 0.0f;
+//     P[kk][j] = sum_{m <= n} g(m, lane_ch(kk, g, j)) * unit
+// with the K3 map g = g_min Sigmoid(e^{A_h} z) (section 2.2) or, with
+// SOFTPLUS, Kimi Linear's g = -e^{A_h} Softplus(z) (the map section 2.2
+// replaces; unbounded below).  unit = 1 gives the log-decay prefix G,
+// unit = log2(e) gives G in base-2 units, ready for exp2.  Rows past the end
+// of the sequence (valid == false) contribute 0.
+template <typename T, int KS, bool SOFTPLUS = false>
+__device__ __forceinline__ void subtile_decay_prefix(const typename Run8<T>::Raw* z, float A_h, float g_min,
+                                                     float unit, bool valid, float (&P)[KS][8]) {
+  const float eA = hw_exp(A_h);
+  const float c1 = -eA * kLog2e;                            // Sigmoid(e^A z) = 1 / (1 + 2^{c1 z})
+  const float gm = valid ? g_min * unit : 0.0f;             // K3 scale
+  const float sp = valid ? -eA * unit * (1.0f / kLog2e) : 0.0f;  // softplus scale (softplus_log2 is in base 2)
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float x = gm * hw_rcp(1.0f + hw_exp2(c1 * Run8<T>::get(z[kk], j)));
+      float x;
+      if constexpr (SOFTPLUS)
+        x = sp * softplus_log2(Run8<T>::get(z[kk], j));
+      else
+        x = gm * hw_rcp(1.0f + hw_exp2(c1 * Run8<T>::get(z[kk], j)));
       x = add_row_shr<1>(x);
       x = add_row_shr<2>(x);
       x = add_row_shr<4>(x);

@@ -134,6 +134,14 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float hw_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
 __device__ __forceinline__ float hw_exp(float x) { return hw_exp2(x * kLog2e); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Softplus(x) log2(e) = log2(1 + e^x) = max(x, 0) log2(e) + log2(1 + 2^{-|x| log2(e)}).
+// Where 1 + e^{-|x|} rounds to 1 the last term is below fp32 resolution of
+// the result (or the decay it feeds is 1 to fp32 accuracy).
+__device__ __forceinline__ float softplus_log2(float x) {
+  return fmaxf(x, 0.0f) * kLog2e + hw_log2(1.0f + hw_exp2(-fabsf(x) * kLog2e));
+}
 
 // Logistic function: 1 / (1 + e^{-x}); saturates to 0 and 1 at the extremes.
 __device__ __forceinline__ float sigmoid_fast(float x) { return hw_rcp(1.0f + hw_exp2(-x * kLog2e)); }

@@ -41,7 +41,9 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const DecodeParams p) {
     kx = Elem<T>::to_f32(k[tid]);
     qx = Elem<T>::to_f32(q[tid]);
     const float eA = hw_exp2(p.A[h] * kLog2e);
-    const float g = p.g_min * sigmoid_fast(eA * Elem<T>::to_f32(z[tid]));
+    // K3 map g = g_min Sigmoid(e^A z), or Kimi Linear's g = -e^A Softplus(z)
+    const float zt = Elem<T>::to_f32(z[tid]);
+    const float g = p.decay ? -eA * softplus_log2(zt) * (1.0f / kLog2e) : p.g_min * sigmoid_fast(eA * zt);
     as[tid] = hw_exp2(g * kLog2e);
   }
   {

@@ -28,10 +28,12 @@ struct IntraLds {
   static constexpr int BYTES = TM + 64 * LP * 4;
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256, (sizeof(T) == 2 ? 3 : 2)) void kda_intra_kernel(const IntraParams p) {
+// SP: the unbounded softplus decay (pairwise diagonal blocks, more registers:
+// two workgroups per CU).
+template <typename T, int D, bool SP>
+__global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intra_kernel(const IntraParams p) {
   using L = IntraLds<T, D>;
-  using Core = IntraCore<T, D, D, kChunk>;
+  using Core = IntraCore<T, D, D, kChunk, SP>;
   static_assert(Core::KP == L::KP && Core::LP == L::LP, "scratch pitches");
   __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
   const IntraScratch<T> s{reinterpret_cast<float*>(lds + L::LOC7), reinterpret_cast<float*>(lds + L::TOT),
@@ -69,15 +71,21 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 3 : 2)) void kda_intra_kerne
   Core::template tb_pass<256>(tid, s, reinterpret_cast<T*>(recp + RL.tb));
 }
 
-hipError_t launch_intra(const IntraParams& p, int D, int in_f32, hipStream_t s) {
+template <bool SP>
+static void launch_intra_t(const IntraParams& p, int D, int in_f32, hipStream_t s) {
   const dim3 grid(p.nc, p.H, p.B), block(256);
   if (in_f32) {
-    if (D == 64) hipLaunchKernelGGL((kda_intra_kernel<float, 64>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((kda_intra_kernel<float, 128>), grid, block, 0, s, p);
+    if (D == 64) hipLaunchKernelGGL((kda_intra_kernel<float, 64, SP>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((kda_intra_kernel<float, 128, SP>), grid, block, 0, s, p);
   } else {
-    if (D == 64) hipLaunchKernelGGL((kda_intra_kernel<uint16_t, 64>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((kda_intra_kernel<uint16_t, 128>), grid, block, 0, s, p);
+    if (D == 64) hipLaunchKernelGGL((kda_intra_kernel<uint16_t, 64, SP>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((kda_intra_kernel<uint16_t, 128, SP>), grid, block, 0, s, p);
   }
+}
+
+hipError_t launch_intra(const IntraParams& p, int D, int in_f32, hipStream_t s) {
+  if (p.decay) launch_intra_t<true>(p, D, in_f32, s);
+  else launch_intra_t<false>(p, D, in_f32, s);
   return hipGetLastError();
 }
 

@@ -136,7 +136,17 @@ struct IntraScratch {
 //   load -> prefix | tables | factors | offdiag, solve | level 1 | 2 | 3 | tb_pass
 // PQE / PKE: row pitches (elements) of the record's [64][D] parts (qg, kg) and
 // of its 64-column parts (kdt, tb, aq).
-template <typename T, int D, int PQE, int PKE>
+//
+// SP: Kimi Linear's unbounded decay g = -e^{A_h} Softplus(z), the map the K3
+// blog's section 2.2 replaces.  Without the sub-tile bound the factors of a
+// diagonal block overflow, so (as section 2.2 describes for Kimi Linear) the
+// diagonal blocks are computed pair by pair, with e^{G_r - G_c} <= 1 per
+// channel; the off-diagonal blocks are anchored at sub-tile ends so that
+// every factor is at most 1:
+//     A(i, j) = (K_i . e^{G_i - E_{i-1}} . e^{E_{i-1} - E_j}) (K_j . e^{E_j - G_j})^T,
+// E_j the log-decay at the end of sub-tile j (E_{i-1} - E_j = the totals of
+// sub-tiles j + 1 .. i - 1).
+template <typename T, int D, int PQE, int PKE, bool SP = false>
 struct IntraCore {
   using AP = APolicy<T>;
   using R8 = Run8<T>;
@@ -182,7 +192,7 @@ struct IntraCore {
   // beta to LDS; inverse norms.
   __device__ __forceinline__ void prefix(const IntraParams& p, int h, const IntraScratch<T>& s) {
     if (g4 == 0) s.betas[r] = beta_r;
-    subtile_decay_prefix<T, KS>(zraw, p.A[h], p.g_min * kLog2e, rvalid, P);
+    subtile_decay_prefix<T, KS, SP>(zraw, p.A[h], p.g_min, kLog2e, rvalid, P);
     if (n == 7)
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) put_run8(s.loc7 + ti * D, kk, g4, P[kk]);
@@ -202,13 +212,19 @@ struct IntraCore {
   static __device__ __forceinline__ void tables(int t, const IntraScratch<T>& s, float* gam) {
     constexpr int TPC = NTHREADS / D;
     const int ch = t % D, part = t / D;
-    float off[4], Bv[4];
+    float off[4], Bv[4], Ev[4];
     off[0] = 0.0f;
 #pragma unroll
     for (int i = 1; i < 4; ++i) off[i] = off[i - 1] + s.tot[(i - 1) * D + ch];
     const float glast = off[3] + s.tot[3 * D + ch];
+    // K3: one anchor per sub-tile (its 8th row) for rows and columns.  SP:
+    // rows anchored at the previous sub-tile's end (off_i), columns at their
+    // own sub-tile's end (off_{i + 1}).
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Bv[i] = off[i] + s.loc7[i * D + ch];
+    for (int i = 0; i < 4; ++i) {
+      Bv[i] = SP ? off[i] : off[i] + s.loc7[i * D + ch];
+      Ev[i] = SP ? (i < 3 ? off[i + 1] : glast) : Bv[i];
+    }
 #pragma unroll
     for (int it = 0; it < (15 + TPC - 1) / TPC; ++it) {
       const int item = part + TPC * it;
@@ -216,12 +232,12 @@ struct IntraCore {
       } else if (item < 4) {
         s.eB[item * D + ch] = hw_exp2(Bv[item]);
       } else if (item < 8) {
-        s.eL[(item - 4) * D + ch] = hw_exp2(glast - Bv[item - 4]);
+        s.eL[(item - 4) * D + ch] = hw_exp2(glast - Ev[item - 4]);
       } else if (item < 14) {
         const int pi = item - 8;  // pair index -> (i, j)
         const int i = (pi < 1) ? 1 : (pi < 3) ? 2 : 3;
         const int j = pi - pair_index(i, 0);
-        s.Et[pi * D + ch] = hw_exp2(Bv[i] - Bv[j]);
+        s.Et[pi * D + ch] = hw_exp2(Bv[i] - Ev[j]);
       } else {
         gam[ch] = hw_exp2(glast);
       }
@@ -235,20 +251,28 @@ struct IntraCore {
     aqk_d = zero4();
     const typename AP::Plain sel0 = select_operand<typename AP::Plain>(n, g4, 0);
     const typename AP::Plain sel1 = select_operand<typename AP::Plain>(n, g4, 1);
+    float KN[SP ? KS : 1][8], QN[SP ? KS : 1][8];  // SP: normalised rows for the pairwise diagonal
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       float p7[8], eb[8], el[8];
-      lds_run8(s.loc7 + ti * D, kk, g4, p7);
+      // K3: the anchor row; SP: the sub-tile total (the column anchor)
+      lds_run8((SP ? s.tot : s.loc7) + ti * D, kk, g4, p7);
       lds_run8(s.eB + ti * D, kk, g4, eb);
       lds_run8(s.eL + ti * D, kk, g4, el);
       float kc[8], xq[8], xk[8], xd[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float d = P[kk][j] - p7[j];  // (G_r - B_i) log2(e)
-        const float rf = hw_exp2(d);       // e^{G_r - B_i}
-        const float cf = hw_exp2(-d);      // e^{B_i - G_r}
+        // K3: rf = e^{G_r - B_i}, cf = e^{B_i - G_r}.  SP: rf = e^{G_r - E_{i-1}}
+        // = 2^{P}, cf = e^{E_i - G_r} = 2^{tot - P}, both at most 1.
+        const float d = P[kk][j] - p7[j];  // log2 units
+        const float rf = hw_exp2(SP ? P[kk][j] : d);
+        const float cf = hw_exp2(-d);
         const float kn = R8::get(kraw[kk], j) * rk;  // normalised k, q
         const float qn = R8::get(qraw[kk], j) * rq;
+        if constexpr (SP) {
+          KN[kk][j] = kn;
+          QN[kk][j] = qn;
+        }
         KR[kk][j] = kn * rf;
         QR[kk][j] = qn * rf;
         kc[j] = kn * cf;
@@ -265,14 +289,73 @@ struct IntraCore {
         kd[kk][0] = P4::pack(AP::mma(xdp, sel0, zero4()));
         kd[kk][1] = P4::pack(AP::mma(xdp, sel1, zero4()));
       }
-      // transposed diagonal blocks: lane (n, g4) gets row n, columns 4 g4 + i
-      akk_d = AP::mma(AP::plain(kc), AP::plain(KR[kk]), akk_d);
-      aqk_d = mma32(f32x8_of(kc), f32x8_of(QR[kk]), aqk_d);
+      if constexpr (!SP) {
+        // transposed diagonal blocks: lane (n, g4) gets row n, columns 4 g4 + i
+        akk_d = AP::mma(AP::plain(kc), AP::plain(KR[kk]), akk_d);
+        aqk_d = mma32(f32x8_of(kc), f32x8_of(QR[kk]), aqk_d);
+      }
     }
+    if constexpr (SP) pairwise_diagonal(s, KN, QN);
     f32x4 lv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) lv[i] = (4 * g4 + i < n) ? beta_r * akk_d[i] : 0.0f;
     *reinterpret_cast<f32x4*>(s.Tm + r * LP + 16 * ti + 4 * g4) = lv;
+  }
+
+  // SP diagonal block, pair by pair: for c <= n,
+  //     A_kk(i, i)[n][c] = sum_ch kn_n kn_c e^{G_n - G_c},  A_qk likewise with qn_n,
+  // every exponent <= 0 (a sub-tile's prefix P is non-increasing).  Each lane
+  // sums its 32 channels; row c's prefix and keys come through a strip of LDS
+  // inside this sub-tile's own rows of Tm (wave-private until the workgroup
+  // synchronises after the factors), one K-step at a time; the four lane
+  // groups of a row then add their partial sums.
+  template <int KN_ROWS>
+  __device__ __forceinline__ void pairwise_diagonal(const IntraScratch<T>& s, const float (&kn)[KN_ROWS][8],
+                                                    const float (&qn)[KN_ROWS][8]) {
+    static_assert(16 * 64 <= 16 * LP, "strip inside the sub-tile's rows of Tm");
+    float* strip = s.Tm + (16 * ti) * LP;  // [16 rows][32 P | 32 k] of one K-step
+    float ak[16], aq[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) ak[c] = aq[c] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      __builtin_amdgcn_wave_barrier();  // every lane has read the previous K-step's strip
+      *reinterpret_cast<float4*>(strip + n * 64 + 8 * g4) = make_float4(P[kk][0], P[kk][1], P[kk][2], P[kk][3]);
+      *reinterpret_cast<float4*>(strip + n * 64 + 8 * g4 + 4) = make_float4(P[kk][4], P[kk][5], P[kk][6], P[kk][7]);
+      *reinterpret_cast<float4*>(strip + n * 64 + 32 + 8 * g4) = make_float4(kn[kk][0], kn[kk][1], kn[kk][2], kn[kk][3]);
+      *reinterpret_cast<float4*>(strip + n * 64 + 32 + 8 * g4 + 4) =
+          make_float4(kn[kk][4], kn[kk][5], kn[kk][6], kn[kk][7]);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const float4 p0 = *reinterpret_cast<const float4*>(strip + c * 64 + 8 * g4);
+        const float4 p1 = *reinterpret_cast<const float4*>(strip + c * 64 + 8 * g4 + 4);
+        const float4 k0 = *reinterpret_cast<const float4*>(strip + c * 64 + 32 + 8 * g4);
+        const float4 k1 = *reinterpret_cast<const float4*>(strip + c * 64 + 32 + 8 * g4 + 4);
+        const float pc[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        const float kc[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          // c > n gives positive exponents: clamped (those entries are masked later)
+          const float w = kc[j] * hw_exp2(fminf(P[kk][j] - pc[j], 0.0f));
+          ak[c] = __builtin_fmaf(kn[kk][j], w, ak[c]);
+          aq[c] = __builtin_fmaf(qn[kk][j], w, aq[c]);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      ak[c] += __shfl_xor(ak[c], 16);
+      ak[c] += __shfl_xor(ak[c], 32);
+      aq[c] += __shfl_xor(aq[c], 16);
+      aq[c] += __shfl_xor(aq[c], 32);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      akk_d[i] = (g4 == 0) ? ak[i] : (g4 == 1) ? ak[4 + i] : (g4 == 2) ? ak[8 + i] : ak[12 + i];
+      aqk_d[i] = (g4 == 0) ? aq[i] : (g4 == 1) ? aq[4 + i] : (g4 == 2) ? aq[8 + i] : aq[12 + i];
+    }
+    __builtin_amdgcn_wave_barrier();  // the strip is read out before L_ii overwrites these rows
   }
 
   // Kd^T pieces to the record: record position of the four tokens

@@ -54,6 +54,7 @@ struct IntraParams {
   int nc;          // chunks in the segment
   float g_min, q_scale, l2_eps;
   int l2norm;
+  int decay;       // 0: K3 bounded map; 1: Kimi Linear softplus map (pairwise diagonal blocks)
   ChunkWs ws;
 };
 
@@ -99,6 +100,7 @@ struct DecodeParams {
   float g_min, q_scale, l2_eps, rms_eps;
   int l2norm;
   int out_f32;
+  int decay;              // as IntraParams::decay
 };
 
 struct StateIoParams {
@@ -118,6 +120,7 @@ struct PrepassParams {
   int B, T, H;
   float g_min, l2_eps;
   int l2norm;
+  int decay;   // as IntraParams::decay
   float* G;    // [B, T, H, D] chunk-local inclusive cumulative log-decay
   float* rq;   // [B, T, H]
   float* rk;   // [B, T, H]

@@ -58,6 +58,13 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
 typedef enum { KDA_STATE_ZERO = 0, KDA_STATE_IMPORT = 1, KDA_STATE_EXPORT = 2 } kda_state_op;
 
+/* Decay maps.  KDA_DECAY_K3 is the method (section 2.2): g = g_min
+ * Sigmoid(e^{A_h} z), bounded below.  KDA_DECAY_SOFTPLUS is Kimi Linear's
+ * g = -e^{A_h} Softplus(z), the unbounded map section 2.2 replaces, kept as
+ * an ablation: without the bound the diagonal 16-token blocks are computed
+ * pair by pair (slower), which is what the bound removes. */
+typedef enum { KDA_DECAY_K3 = 0, KDA_DECAY_SOFTPLUS = 1 } kda_decay;
+
 /* Schedules of kda_chunk_fwd (see there). */
 typedef enum {
   KDA_SCHEDULE_SEGMENTS = 0,   /* intra-chunk kernel, then scan, segment after segment */
@@ -88,10 +95,14 @@ typedef struct {
                             concurrently with the scan of the current one
                             (library-owned streams, see kda_chunk_fwd); 0: one
                             stream, segments in turn                          */
-  int32_t fused;         /* the fused one-kernel schedule (bf16 inputs only):
-                            1 when B * H is at least the device's number of
-                            compute units (default), 2 always, 0 never; the
-                            two-kernel schedules above otherwise              */
+  int32_t fused;         /* the fused one-kernel schedule (bf16 inputs, K3
+                            decay only): 1 when B * H is at least the device's
+                            number of compute units (default), 2 always, 0
+                            never; the two-kernel schedules above otherwise   */
+  kda_decay decay;       /* decay map: KDA_DECAY_K3 (default) or the
+                            KDA_DECAY_SOFTPLUS ablation; used by
+                            kda_chunk_fwd*, kda_recurrent_step, kda_prepass;
+                            g_min applies to the K3 map only                  */
 } kda_desc;
 
 /* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */

@@ -169,3 +169,8 @@ def test_kcp_host_errors():
     one = L.kda_chunk_fwd_kcp_workspace_size(ctypes.byref(d2), 1)
     four = L.kda_chunk_fwd_kcp_workspace_size(ctypes.byref(d2), 4)
     assert one == L.kda_chunk_fwd_workspace_size(ctypes.byref(d2)) and four >= 3 * 2 * 4 * 3 * 128 * 128 * 4
+
+
+def test_decay_map_field():
+    assert _desc().decay == 0                                        # K3 map by default
+    assert _fwd(_desc(decay=2)) == 5                                 # unknown map
