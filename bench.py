@@ -4,8 +4,9 @@ One step = one kda_chunk_fwd call over the K3-shaped layer workload
 (B1, T65536, H96, d128, bf16 inputs, fp32 state, output gate, y and S_T
 outputs), inputs already resident in HBM.  Prints ONE JSON line.
 
-The library picks the schedule (the fused kernel when B * H fills the
-device, else the overlapped two-kernel schedule); --schedule forces one.  Per-kernel durations come from HIP events
+The library picks the schedule (the overlapped two-kernel schedule for
+sequences longer than one segment); --schedule forces one (the fused kernel
+measured slower at every size tried).  Per-kernel durations come from HIP events
 recorded by the library around each of its launches on the launch stream
 (kda_chunk_fwd_traced); the dominant kernel's roofline uses its algorithmic
 bytes:

@@ -166,8 +166,8 @@ def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=
     Returns a dict with 'o' / 'y' (out_dtype, default the input dtype) and
     'S_T' (fp32).  ``out`` may supply preallocated output tensors; ``events``
     (raw hipEvent_t handles) selects the traced entry point.  With
-    ``fused`` True (bf16 inputs) one fused kernel runs the whole forward, with
-    None the library picks it when B * H fills the device; otherwise, with
+    ``fused`` True (bf16 inputs) one fused kernel runs the whole forward (None:
+    the library's choice, currently the two-kernel schedules); otherwise, with
     ``overlap`` the library may run the overlapped schedule in segments of
     ``segment_tokens`` tokens; without it, ``segment_tokens`` sizes the
     segments processed in turn (default: the whole sequence).  With

@@ -98,33 +98,15 @@ int64_t pipe_chunks(const kda_desc* d) {
 // segment; its workspace holds two segments of records.
 bool pipe_wanted(const kda_desc* d) { return d->overlap != 0 && num_chunks(d) > pipe_chunks(d); }
 
-// Compute units of the current device (0 if unknown), cached per device.
-int device_cus() {
-  static std::mutex mu;
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  std::lock_guard<std::mutex> lock(mu);
-  if (cus[dev] == 0 && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
-    (void)hipGetLastError();
-    cus[dev] = 0;
-  }
-  return cus[dev];
-}
-
-// The fused kernel (records in LDS, no workspace) serves bf16 inputs.  One
-// workgroup per (head, sequence) carries the whole intra-chunk work of its
-// head on one compute unit, so it pays off once there are at least as many
-// (head, sequence) pairs as compute units (fused == 1); fused == 2 forces it.
+// The fused kernel (records in LDS, no workspace) serves bf16 inputs with the
+// K3 decay, on request only (fused == 2).  One workgroup per (head,
+// sequence) carries its head's whole intra-chunk work on one compute unit's
+// four producer waves (about 43K cycles per chunk against about 6K for the
+// scan's product chain), which measured slower than the two-kernel schedules
+// at every B * H tried (96 to 768 pairs), so the library does not pick it by
+// itself (fused == 1).
 bool fused_wanted(const kda_desc* d) {
-  if (d->fused == 0 || d->decay != KDA_DECAY_K3 || !kda::fused_supported(d->d_k, d->in_dtype == KDA_F32))
-    return false;
-  if (d->fused == 2) return true;
-  const int cus = device_cus();
-  return cus > 0 && (int64_t)d->B * d->H >= cus;
+  return d->fused == 2 && d->decay == KDA_DECAY_K3 && kda::fused_supported(d->d_k, d->in_dtype == KDA_F32);
 }
 constexpr size_t kFusedWorkspace = 256;  // what the size query reports for it (nothing is used)
 

@@ -96,9 +96,9 @@ typedef struct {
                             (library-owned streams, see kda_chunk_fwd); 0: one
                             stream, segments in turn                          */
   int32_t fused;         /* the fused one-kernel schedule (bf16 inputs, K3
-                            decay only): 1 when B * H is at least the device's
-                            number of compute units (default), 2 always, 0
-                            never; the two-kernel schedules above otherwise   */
+                            decay only): 2 forces it; 1 (default) lets the
+                            library choose, which currently always takes the
+                            two-kernel schedules (measured faster); 0 never */
   kda_decay decay;       /* decay map: KDA_DECAY_K3 (default) or the
                             KDA_DECAY_SOFTPLUS ablation; used by
                             kda_chunk_fwd*, kda_recurrent_step, kda_prepass;
@@ -164,13 +164,13 @@ kda_status kda_chunk_fwd_schedule(const kda_desc* d, size_t ws_bytes, int32_t* s
  * At least one of o, y, S_T must be non-NULL.  When d->T == 0 nothing is read:
  * S_T receives S0 (or zeros) and q, k, v, beta, z, A and ws may be NULL.
  *
- * Fused schedule (see d->fused; bf16 inputs): one launch, one workgroup per
- * (head, sequence).  Its compute waves run the state scan of chunk c while
- * producer waves build chunk c + 1's intra-chunk record directly in LDS and
- * write chunk c - 1's o / y, so no record goes through HBM.  Each head's
- * intra-chunk work then runs on a single compute unit, which only pays once
- * the (head, sequence) pairs fill the device.  Results are bit-identical to
- * the two-kernel schedules.
+ * Fused schedule (d->fused == 2; bf16 inputs, K3 decay): one launch, one
+ * workgroup per (head, sequence).  Its compute waves run the state scan of
+ * chunk c while producer waves build chunk c + 1's intra-chunk record
+ * directly in LDS and write chunk c - 1's o / y, so no record goes through
+ * HBM.  Each head's intra-chunk work then runs on a single compute unit,
+ * which measured slower than the two-kernel schedules at every size tried.
+ * Results are bit-identical to the two-kernel schedules.
  *
  * Two-kernel schedules.  The sequence is processed in segments; per segment the
  * intra-chunk kernel writes one record per chunk into the workspace and the

@@ -179,7 +179,7 @@ def test_fused_matches_two_kernel_schedules(kda, B, T, H, D, opts):
         assert _bit_equal(ref[key], fus[key]), key
     _, sched = kda.schedule(kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, fused=True), 0)
     assert sched == "fused"
-    # left to the library, a few (head, sequence) pairs take a two-kernel schedule
+    # left to the library, a two-kernel schedule is taken
     desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16)
     assert kda.schedule(desc, kda.workspace_size(desc))[1] != "fused"
 
@@ -269,15 +269,15 @@ def test_state_io_layouts(kda):
     assert torch.all(pool[1] == 7.0) and torch.all(pool[3] == 7.0)
 
 
-def test_library_picks_fused_when_heads_fill_the_device(kda):
-    """Left to the library, B * H >= the CU count takes the fused kernel;
-    the results equal the two-kernel schedule bit for bit."""
+def test_fused_with_heads_filling_the_device(kda):
+    """B * H at the CU count: left to the library a two-kernel schedule is
+    taken; the forced fused kernel gives the same results bit for bit."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     B, T, H, D = 2, 130, (cus + 1) // 2, 64
     desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16)
-    assert kda.schedule(desc, kda.workspace_size(desc))[1] == "fused"
+    assert kda.schedule(desc, kda.workspace_size(desc))[1] != "fused"
     x = gen_inputs(_custom(B, T, H, D, "bf16", seed=4))
-    auto = _run(kda, x)
+    auto = _run(kda, x, fused=True)
     ref = _run(kda, x, fused=False, overlap=False)
     for key in ("o", "y", "S_T"):
         assert _bit_equal(auto[key], ref[key]), key
