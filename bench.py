@@ -132,6 +132,41 @@ def time_input_prep(kda, t, B, T, H, D, steps, warmup, workload, W=4):
             "traffic": profiled_traffic("prep_conv", workload)}
 
 
+def time_decode(kda, H, D, steps, warmup, n=256):
+    """Decode steps (kda_recurrent_step) for n sequences of H heads, one token
+    each, with the fp32 state pool [n, H, D, D] updated in place and y = the
+    gated output (bf16), as in the decode workload.  Inputs are seeded random
+    values (the timing does not depend on them).  Algorithmic bytes per
+    call: the state read and written (8 D^2) plus q, k, v, z, gate read and y
+    written (12 D) and beta (2) per token-head."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(7)
+    bf = torch.bfloat16
+    x = {nm: torch.randn((n, H, D), generator=g, device="cuda").to(bf) for nm in ("q", "k", "v", "z", "gate")}
+    beta = torch.sigmoid(torch.randn((n, H), generator=g, device="cuda")).to(bf)
+    A = torch.rand((H,), generator=g, device="cuda") * 2 - 1
+    pool = torch.randn((n, H, D, D), generator=g, device="cuda") * 0.1
+    out = {"y": torch.empty((n, H, D), dtype=bf, device="cuda")}
+
+    def call():
+        kda.recurrent_step(x["q"], x["k"], x["v"], beta, x["z"], A, pool, gate=x["gate"], want_o=False, out=out)
+
+    for _ in range(warmup):
+        call()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    nbytes = n * H * (8 * D * D + 12 * D + 2)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"sequences": n, "heads": H, "d": D, "ms": ms, "token_heads_per_s": n * H / (ms * 1e-3),
+            "algorithmic_bytes": nbytes, "achieved_GBs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "launches": 1}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +181,7 @@ def main() -> int:
                     help="tokens per segment of the two-kernel schedules; 0: library default")
     ap.add_argument("--decay", choices=("k3", "softplus"), default="k3",
                     help="decay map: K3's bounded map (the method), or Kimi Linear's softplus map (ablation)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step side measurement")
     ap.add_argument("--no-input-prep", action="store_true",
                     help="skip timing the input steps (ShortConv + Swish, Sigmoid) on the workload's shapes")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -282,6 +318,8 @@ def main() -> int:
     }
     if not args.no_input_prep:
         result["input_prep"] = time_input_prep(kda, t, B, T, H, D, args.steps, args.warmup, wl.name)
+    if not args.no_decode:
+        result["decode"] = time_decode(kda, H, D, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
         heads = args.cpu_heads or H
