@@ -63,6 +63,15 @@ kda_status validate_desc(const kda_desc* d) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Whether the byte ranges [a, a + na) and [b, b + nb) share a byte (NULL or
+// empty ranges share none).
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
 struct WsLayout {
   size_t off_rec, rec_bytes, off_carry, total;
 };
@@ -353,6 +362,24 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   if (!aligned(beta, es) || !aligned(A, 4) || (S0 && !aligned(S0, 4)) || (S_T && !aligned(S_T, 4)) ||
       (rms_w && !aligned(rms_w, 4)))
     return KDA_ERR_MISALIGNED;
+  {
+    // o, y and S_T overlap no input and no other output (S_T may equal S0)
+    const size_t es_out = elem_size(d->out_dtype);
+    const size_t row = (size_t)d->B * d->T * d->H;
+    const size_t sb = (size_t)d->B * d->H * d->d_k * d->d_v * 4;
+    const void* ins[9] = {q, k, v, beta, z, A, S0, gate, rms_w};
+    const size_t in_b[9] = {row * d->d_k * es, row * d->d_k * es, row * d->d_v * es, row * es, row * d->d_k * es,
+                            (size_t)d->H * 4, sb, row * d->d_v * es, (size_t)d->H * d->d_v * 4};
+    const void* outs[3] = {o, y, S_T};
+    const size_t out_b[3] = {row * d->d_v * es_out, row * d->d_v * es_out, sb};
+    for (int i = 0; i < 3; ++i) {
+      for (int j = 0; j < 9; ++j)
+        if (!(i == 2 && j == 6 && outs[i] == ins[j]) && ranges_overlap(outs[i], out_b[i], ins[j], in_b[j]))
+          return KDA_ERR_UNSUPPORTED;
+      for (int j = i + 1; j < 3; ++j)
+        if (ranges_overlap(outs[i], out_b[i], outs[j], out_b[j])) return KDA_ERR_UNSUPPORTED;
+    }
+  }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int D = d->d_k;
@@ -590,6 +617,27 @@ kda_status kda_input_prep(const kda_desc* d, int32_t conv_width, const void* xq,
     if (!aligned(ptr, 16)) return KDA_ERR_MISALIGNED;
   if (!aligned(wq, 4) || !aligned(wk, 4) || !aligned(wv, 4) || (beta && (!aligned(beta, es) || !aligned(beta_logits, es))))
     return KDA_ERR_MISALIGNED;
+  // No output may overlap an input it does not equal: a token block re-reads
+  // the conv_width - 1 inputs before it, which a neighbouring block's outputs
+  // would already have replaced.  beta may equal beta_logits (elementwise);
+  // state_out may equal state_in (handled by a single token block).
+  {
+    const size_t xb = (size_t)d->B * d->T * d->H * d->d_k * es;
+    const size_t sb = (size_t)d->B * 3 * (conv_width - 1) * d->H * d->d_k * 4;
+    const size_t bb = (size_t)d->B * d->T * d->H * es;
+    const void* ins[5] = {xq, xk, xv, conv_width > 1 ? state_in : nullptr, beta_logits};
+    const size_t in_b[5] = {xb, xb, xb, sb, bb};
+    const void* outs[5] = {q, k, v, conv_width > 1 ? state_out : nullptr, beta};
+    const size_t out_b[5] = {xb, xb, xb, sb, bb};
+    for (int i = 0; i < 5; ++i)
+      for (int j = 0; j < 5; ++j) {
+        const bool same_ok = outs[i] == ins[j] && ((i == 3 && j == 3) || (i == 4 && j == 4));
+        if (!same_ok && ranges_overlap(outs[i], out_b[i], ins[j], in_b[j])) return KDA_ERR_UNSUPPORTED;
+      }
+    for (int i = 0; i < 5; ++i)
+      for (int j = i + 1; j < 5; ++j)
+        if (ranges_overlap(outs[i], out_b[i], outs[j], out_b[j])) return KDA_ERR_UNSUPPORTED;
+  }
   p.x[0] = xq;
   p.x[1] = xk;
   p.x[2] = xv;

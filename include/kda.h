@@ -161,7 +161,9 @@ kda_status kda_chunk_fwd_schedule(const kda_desc* d, size_t ws_bytes, int32_t* s
  *  ws     device workspace of ws_bytes bytes (see the size queries), owned by
  *         the caller; its contents are scratch.  May be NULL when T == 0 or
  *         when the fused schedule is taken.
- * At least one of o, y, S_T must be non-NULL.  When d->T == 0 nothing is read:
+ * At least one of o, y, S_T must be non-NULL.  o, y and S_T must not overlap
+ * any input or each other, except S_T == S0 (KDA_ERR_UNSUPPORTED otherwise).
+ * When d->T == 0 nothing is read:
  * S_T receives S0 (or zeros) and q, k, v, beta, z, A and ws may be NULL.
  *
  * Fused schedule (d->fused == 2; bf16 inputs, K3 decay): one launch, one
@@ -276,6 +278,9 @@ size_t kda_chunk_fwd_kcp_workspace_size(const kda_desc* d, int32_t n_parts);
  *             group: fine for decode, slow for long prefills).
  *  beta_logits, beta  both NULL to skip beta.
  * With T == 0 only state_out is written (state_in copied, or zeros).
+ * Outputs must not overlap the inputs or each other, except beta ==
+ * beta_logits and state_out == state_in (KDA_ERR_UNSUPPORTED otherwise: a
+ * block of tokens re-reads the inputs just before it).
  * KDA_ERR_UNSUPPORTED if conv_width is outside 1..4.  Chaining calls through
  * the state gives the same outputs as one call over the concatenated tokens.
  */

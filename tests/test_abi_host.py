@@ -36,8 +36,13 @@ def _desc(**kw):
     return d
 
 
-def _fwd(d, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, z=FAKE, A=FAKE, S0=None, gate=None, w=None, o=FAKE, y=None,
-         ST=None, ws=FAKE, nbytes=1 << 40):
+def P(i):
+    """The i-th of several disjoint fake device ranges (4 GiB apart)."""
+    return FAKE + i * (1 << 32)
+
+
+def _fwd(d, q=P(0), k=P(1), v=P(2), beta=P(3), z=P(4), A=P(5), S0=None, gate=None, w=None, o=P(6), y=None,
+         ST=None, ws=P(7), nbytes=1 << 40):
     return kda.lib().kda_chunk_fwd(ctypes.byref(d), q, k, v, beta, z, A, S0, gate, w, o, y, ST, ws, nbytes, None)
 
 
@@ -56,9 +61,9 @@ def test_desc_validation():
 def test_forward_host_errors():
     assert _fwd(_desc(), q=None) == 1
     assert _fwd(_desc(), o=None, y=None, ST=None) == 1
-    assert _fwd(_desc(), y=FAKE, gate=None) == 1                  # y needs the gate logits
-    assert _fwd(_desc(), v=FAKE + 2) == 4                         # misaligned
-    assert _fwd(_desc(), beta=FAKE + 1) == 4
+    assert _fwd(_desc(), y=P(8), gate=None) == 1                  # y needs the gate logits
+    assert _fwd(_desc(), v=P(2) + 2) == 4                         # misaligned
+    assert _fwd(_desc(), beta=P(3) + 1) == 4
     # workspace errors exist only for the two-kernel schedules (the fused one
     # needs none and would launch here)
     assert _fwd(_desc(fused=0), ws=None) == 6
@@ -68,6 +73,20 @@ def test_forward_host_errors():
     assert _fwd(_desc(g_min=0.0)) == 5
     assert _fwd(_desc(chunk=32)) == 5
     assert _fwd(_desc(d_v=64)) == 5
+
+
+def test_forward_rejects_overlapping_outputs():
+    """o, y, S_T over an input or over each other are refused before any
+    launch (S_T over S0 is the allowed in-place update)."""
+    d = _desc(fused=0)
+    assert _fwd(d, o=P(0)) == 5                                   # o over q
+    assert _fwd(d, o=P(2) + 1024) == 5                            # o starts inside v
+    assert _fwd(d, o=None, y=P(4), gate=P(9)) == 5                # y over z
+    assert _fwd(d, o=P(9), y=P(10), gate=P(9)) == 5               # o over the gate logits
+    assert _fwd(d, y=P(6) + 512, gate=P(9)) == 5                  # y overlaps o
+    assert _fwd(d, S0=P(10), ST=P(10) + 4) == 5                   # S_T overlaps S0 without equalling it
+    assert _fwd(d, ST=P(5)) == 5                                  # S_T over A
+    assert _fwd(d, S0=P(10), ST=P(10), ws=None) == 6              # S_T == S0 passes on to the workspace check
 
 
 def test_workspace_sizes():
@@ -105,9 +124,9 @@ def test_no_cpu_fallback(monkeypatch, tmp_path):
         kda.lib()
 
 
-def _snap(d, snaps=FAKE, every=1, o=FAKE, ST=None):
-    return kda.lib().kda_chunk_fwd_snapshots(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
-                                             o, None, ST, snaps, every, FAKE, 1 << 40, None)
+def _snap(d, snaps=P(8), every=1, o=P(6), ST=None):
+    return kda.lib().kda_chunk_fwd_snapshots(ctypes.byref(d), P(0), P(1), P(2), P(3), P(4), P(5), None, None, None,
+                                             o, None, ST, snaps, every, P(7), 1 << 40, None)
 
 
 def test_snapshot_host_errors_and_count():
@@ -120,7 +139,7 @@ def test_snapshot_host_errors_and_count():
     assert L.kda_snapshot_count(ctypes.byref(_desc(d_k=96, d_v=96)), 1) == 0
     assert _snap(d, every=0) == 2
     assert _snap(d, snaps=None) == 1                              # 15 boundaries need the buffer
-    assert _snap(d, snaps=FAKE + 2) == 4
+    assert _snap(d, snaps=P(8) + 2) == 4
     assert _snap(_desc(T=1000, chunk=32)) == 5
     assert _snap(d, every=16, snaps=None, o=None) == 0            # no boundary, no output: nothing to do
 
@@ -155,6 +174,25 @@ def test_input_prep_host_errors():
     assert _prep(d, xq=FAKE + 2) == 4                                # 16-byte vectors
     assert _prep(d, st_in=FAKE + 2) == 4
     assert _prep(_desc(d_k=96, d_v=96)) == 5
+
+
+def test_input_prep_rejects_overlapping_outputs():
+    """q, k, v written over an input (or each other) are rejected before any
+    launch.  (The allowed aliases, beta over its logits and the state updated
+    in place, are exercised on the GPU by the input-step tests.)"""
+    L = kda.lib()
+    d = _desc(B=1, T=8, H=2, d_k=64, d_v=64)
+    xb = 8 * 2 * 64 * 2                                               # bytes of one [B, T, H, d] bf16 tensor
+    X = [FAKE + i * (1 << 20) for i in range(10)]                     # disjoint fake device ranges
+
+    def call(q=X[3], k=X[4], v=X[5], beta=X[6], bl=X[7], st_in=X[8], st_out=X[9]):
+        return L.kda_input_prep(ctypes.byref(d), 4, X[0], X[1], X[2], bl, X[0], X[1], X[2], st_in, st_out,
+                                q, k, v, beta, None)
+    assert call(q=X[0]) == 5                                          # q over x_q
+    assert call(k=X[0] + xb - 16) == 5                                # k starts inside x_q
+    assert call(v=X[3] + 16) == 5                                     # v overlaps q
+    assert call(st_out=X[8] + 16) == 5                                # state_out overlaps state_in, not equal
+    assert call(beta=X[2]) == 5                                       # beta over x_v
 
 
 def test_kcp_host_errors():

@@ -100,6 +100,25 @@ def test_input_prep_chains_through_state(kda):
     assert torch.equal(st, full_state)
 
 
+def test_input_prep_beta_in_place_and_overlap_rejected(kda):
+    """beta written over its own logits equals the out-of-place result bit
+    for bit; q written over x_q is refused before any launch."""
+    B, T, H, D, W = 1, 70, 2, 64, 3
+    x = gen_prep_inputs(B, T, H, D, W, "bf16", seed=31, with_state=False)
+    ref = _gpu(kda, x)
+    t = {n: dev(x[n]) for n in ("xq", "xk", "xv", "beta_logits")}
+    w = {n: dev(x[n]) for n in ("wq", "wk", "wv")}
+    logits = t["beta_logits"]
+    r = kda.input_prep(t["xq"], t["xk"], t["xv"], w["wq"], w["wk"], w["wv"], beta_logits=logits,
+                       out={"beta": logits})
+    torch.cuda.synchronize()
+    assert _bit_equal(logits, ref["beta"])
+    for n in ("q", "k", "v"):
+        assert _bit_equal(r[n], ref[n]), n
+    with pytest.raises(kda.KdaError):
+        kda.input_prep(t["xq"], t["xk"], t["xv"], w["wq"], w["wk"], w["wv"], out={"q": t["xq"]})
+
+
 def test_input_prep_zero_tokens_copies_state(kda):
     B, H, D, W = 2, 2, 64, 3
     x = gen_prep_inputs(B, 4, H, D, W, "bf16", seed=2)
