@@ -89,7 +89,7 @@ WsLayout layout_for(const kda_desc* d, int64_t seg_nc) {
     o = align256(o + bytes);
     return at;
   };
-  L.rec_bytes = (size_t)kda::rec_layout(es, (int)D).bytes;
+  L.rec_bytes = (size_t)kda::rec_units(es, (int)D).bytes;
   L.off_rec = take(R * L.rec_bytes);
   L.off_carry = take((size_t)d->B * d->H * D * D * 4);
   L.total = o;

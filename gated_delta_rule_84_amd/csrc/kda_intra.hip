@@ -33,7 +33,7 @@ struct IntraLds {
 template <typename T, int D, bool SP>
 __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intra_kernel(const IntraParams p) {
   using L = IntraLds<T, D>;
-  using Core = IntraCore<T, D, D, kChunk, SP>;
+  using Core = IntraCore<T, D, D, kChunk, SP, true>;  // record in the workspace's unit layout
   static_assert(Core::KP == L::KP && Core::LP == L::LP, "scratch pitches");
   __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
   const IntraScratch<T> s{reinterpret_cast<float*>(lds + L::LOC7), reinterpret_cast<float*>(lds + L::TOT),
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
   const int tok0 = p.t0 + c * kChunk;
   const int nvalid = min(kChunk, p.T - tok0);
   const int64_t rec = ((int64_t)b * p.H + h) * p.nc + c;
-  constexpr RecLayout RL = rec_layout((int)sizeof(T), D);
+  constexpr RecUnits RU = rec_units((int)sizeof(T), D);
   char* recp = p.ws.base + rec * p.ws.rec_bytes;
 
   Core ic;
@@ -54,13 +54,13 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
   ic.load(p, b, h, tok0, nvalid);
   ic.prefix(p, h, s);
   __syncthreads();
-  Core::template tables<256>(tid, s, reinterpret_cast<float*>(recp + RL.gam));
+  Core::template tables<256>(tid, s, reinterpret_cast<float*>(recp + 16 * RU.gam));
   __syncthreads();
-  ic.factors(s, reinterpret_cast<T*>(recp + RL.qg), reinterpret_cast<T*>(recp + RL.kg));
-  ic.store_kd(reinterpret_cast<T*>(recp + RL.kdt));
+  ic.factors(s, reinterpret_cast<T*>(recp + 16 * RU.qg), reinterpret_cast<T*>(recp + 16 * RU.kg));
+  ic.store_kd(reinterpret_cast<T*>(recp + 16 * RU.kdt));
   __syncthreads();  // column factors and the L_ii stages are visible
   ic.offdiag(s);
-  ic.store_aq(reinterpret_cast<T*>(recp + RL.aqh), reinterpret_cast<T*>(recp + RL.aql));
+  ic.store_aq(reinterpret_cast<T*>(recp + 16 * RU.aq), nullptr);  // hi and lo share units
   ic.solve(s);
   __syncthreads();  // every T_ii is in LDS
 #pragma unroll
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
     ic.level(dist, s);
     __syncthreads();
   }
-  Core::template tb_pass<256>(tid, s, reinterpret_cast<T*>(recp + RL.tb));
+  Core::template tb_pass<256>(tid, s, reinterpret_cast<T*>(recp + 16 * RU.tb));
 }
 
 template <bool SP>

@@ -135,7 +135,9 @@ struct IntraScratch {
 // The steps, in order (the caller synchronises the four waves where marked):
 //   load -> prefix | tables | factors | offdiag, solve | level 1 | 2 | 3 | tb_pass
 // PQE / PKE: row pitches (elements) of the record's [64][D] parts (qg, kg) and
-// of its 64-column parts (kdt, tb, aq).
+// of its 64-column parts (kdt, tb, aq), when the record is an LDS image
+// (UNITS = false); with UNITS the record is the workspace's unit layout
+// (rec_units: each wave store writes 1 KB of consecutive bytes).
 //
 // SP: Kimi Linear's unbounded decay g = -e^{A_h} Softplus(z), the map the K3
 // blog's section 2.2 replaces.  Without the sub-tile bound the factors of a
@@ -146,7 +148,7 @@ struct IntraScratch {
 //     A(i, j) = (K_i . e^{G_i - E_{i-1}} . e^{E_{i-1} - E_j}) (K_j . e^{E_j - G_j})^T,
 // E_j the log-decay at the end of sub-tile j (E_{i-1} - E_j = the totals of
 // sub-tiles j + 1 .. i - 1).
-template <typename T, int D, int PQE, int PKE, bool SP = false>
+template <typename T, int D, int PQE, int PKE, bool SP = false, bool UNITS = false>
 struct IntraCore {
   using AP = APolicy<T>;
   using R8 = Run8<T>;
@@ -280,8 +282,14 @@ struct IntraCore {
         xk[j] = -KR[kk][j] * eb[j];  // -(k^ . Gamma)
         xd[j] = kc[j] * el[j];       // k^ . Gamma_last / Gamma
       }
-      store8<T>(qg + r * PQE + 32 * kk + 8 * g4, xq);
-      store8<T>(kg + r * PQE + 32 * kk + 8 * g4, xk);
+      if constexpr (UNITS) {
+        const int pc = (ti * KS + kk) * 64 + 16 * g4 + n;  // piece of this lane
+        store8<T>(qg + 8 * pc, xq);
+        store8<T>(kg + 8 * pc, xk);
+      } else {
+        store8<T>(qg + r * PQE + 32 * kk + 8 * g4, xq);
+        store8<T>(kg + r * PQE + 32 * kk + 8 * g4, xk);
+      }
       if (ti < 3) store8<T>(s.KC + r * KP + 32 * kk + 8 * g4, kc);  // column factors for later sub-tiles
       {
         // lane (n, g4) receives Kd[16 ti + 4 g4 + i][32 kk + 16 half + n]
@@ -364,8 +372,18 @@ struct IntraCore {
     const int tpos = 32 * (ti >> 1) + 8 * g4 + 4 * (ti & 1);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      P4::store(kdt + (32 * kk + n) * PKE + tpos, kd[kk][0]);
-      P4::store(kdt + (32 * kk + 16 + n) * PKE + tpos, kd[kk][1]);
+      if constexpr (UNITS) {
+        T* dst = kdt + 8 * ((ti * KS + kk) * 64 + 16 * g4 + n);  // the two pieces side by side
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<u32x4*>(dst) = u32x4{kd[kk][0].x, kd[kk][0].y, kd[kk][1].x, kd[kk][1].y};
+        } else {
+          P4::store(dst, kd[kk][0]);
+          P4::store(dst + 4, kd[kk][1]);
+        }
+      } else {
+        P4::store(kdt + (32 * kk + n) * PKE + tpos, kd[kk][0]);
+        P4::store(kdt + (32 * kk + 16 + n) * PKE + tpos, kd[kk][1]);
+      }
     }
   }
 
@@ -416,9 +434,17 @@ struct IntraCore {
       const bool lower = jt <= ti;
       const bool zero_blk = (ti == 0 && jt == 1) || (ti == 2 && jt == 3);
       if (lower || zero_blk) {
-        const int off = r * PKE + 32 * (jt >> 1) + 8 * g4 + 4 * (jt & 1);
-        P4::store(aqh + off, aqs[jt][0]);
-        if constexpr (AP::kHasLo) P4::store(aql + off, aqs[jt][1]);
+        if constexpr (UNITS) {  // hi then lo of one block row piece per 16-byte unit
+          T* dst = aqh + (16 / (int)sizeof(T)) * (64 * aq_block_index(ti, jt) + 16 * g4 + n);
+          if constexpr (AP::kHasLo)
+            *reinterpret_cast<u32x4*>(dst) = u32x4{aqs[jt][0].x, aqs[jt][0].y, aqs[jt][1].x, aqs[jt][1].y};
+          else
+            P4::store(dst, aqs[jt][0]);
+        } else {
+          const int off = r * PKE + 32 * (jt >> 1) + 8 * g4 + 4 * (jt & 1);
+          P4::store(aqh + off, aqs[jt][0]);
+          if constexpr (AP::kHasLo) P4::store(aql + off, aqs[jt][1]);
+        }
       }
     }
   }
@@ -492,13 +518,17 @@ struct IntraCore {
   static __device__ __forceinline__ void tb_pass(int t, const IntraScratch<T>& s, T* tb) {
     for (int idx = t; idx < kChunk * 8; idx += NTHREADS) {
       const int rr = idx >> 3, pg = idx & 7;
+      if (UNITS && rr < 32 && pg >= 4) continue;  // never read: not stored
       float x[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int sc = slot_row64(8 * pg + j);
         x[j] = ((sc >> 4) <= (rr >> 4)) ? s.Tm[rr * LP + sc] * s.betas[sc] : 0.0f;
       }
-      store8<T>(tb + rr * PKE + 8 * pg, x);
+      if constexpr (UNITS)
+        store8<T>(tb + (rr < 32 ? 32 * rr : 1024 + 64 * (rr - 32)) + 8 * pg, x);
+      else
+        store8<T>(tb + rr * PKE + 8 * pg, x);
     }
   }
 };

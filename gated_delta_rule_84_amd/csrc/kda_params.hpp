@@ -23,20 +23,40 @@ constexpr int kSub = 16;     // tokens per sub-tile
 //   aql [64][64]  Tril(A_qk) - aqh (bf16 path only)
 //   gam [D]       Gamma_last, fp32
 // padded to a multiple of 256 bytes.
-struct RecLayout {
-  int qg, kg, kdt, tb, aqh, aql, gam, bytes;
-};
 __host__ __device__ constexpr int round256(int x) { return (x + 255) & ~255; }
-__host__ __device__ constexpr RecLayout rec_layout(int es, int D) {
-  return RecLayout{0,
-                   64 * D * es,
-                   2 * 64 * D * es,
-                   3 * 64 * D * es,
-                   3 * 64 * D * es + 64 * 64 * es,
-                   3 * 64 * D * es + 2 * 64 * 64 * es,
-                   3 * 64 * D * es + (es == 2 ? 3 : 2) * 64 * 64 * es,
-                   round256(3 * 64 * D * es + (es == 2 ? 3 : 2) * 64 * 64 * es + 4 * D)};
+
+// Chunk record in the workspace: 16-byte units in the order the intra-chunk
+// kernel's lanes hold them, so that every store instruction of a wave writes
+// 1 KB of consecutive bytes, and only what the scan reads.  Offsets in units
+// (es = element size: 2 bf16, 4 fp32; a "piece" is 8 elements = es / 2 units):
+//   qg, kg  piece (ti, kk, lane) = (ti KS + kk) 64 + lane: row 16 ti + n,
+//           channels 32 kk + 8 g4 .. + 7 (n = lane % 16, g4 = lane / 16)
+//   kdt     the same pieces, each Kd^T rows 32 kk + n and 32 kk + 16 + n
+//           (4 elements each) at token slots 32 (ti / 2) + 8 g4 + 4 (ti % 2)
+//   aq      the 12 blocks (ti, jt) of Tril(A_qk) that the scan multiplies
+//           (jt <= ti, plus the zero blocks (0, 1) and (2, 3)), block index
+//           2 ti + jt for ti < 2 and 4 + 4 (ti - 2) + jt after: unit
+//           64 block + lane = hi (4 elements) then, for bf16, lo (4 elements)
+//           of row 16 ti + n at slots 32 (jt / 2) + 8 g4 + 4 (jt % 2)
+//   tb      T Diag(beta) rows, slot order: slots 0..31 of rows 0..31, then
+//           slots 0..63 of rows 32..63 (the rest is never read)
+//   gam     Gamma_last, D fp32
+struct RecUnits {
+  int qg, kg, kdt, aq, tb, gam, units, bytes;
+};
+__host__ __device__ constexpr RecUnits rec_units(int es, int D) {
+  // qg, kg, kdt: 64 D es / 16 = 4 D es units each; aq: 12 blocks x 64 lanes;
+  // tb: 32 rows x 32 slots + 32 rows x 64 slots = 192 es units; gam: D / 4
+  return RecUnits{0,
+                  4 * D * es,
+                  8 * D * es,
+                  12 * D * es,
+                  12 * D * es + 768,
+                  12 * D * es + 768 + 192 * es,
+                  12 * D * es + 768 + 192 * es + D / 4,
+                  round256(16 * (12 * D * es + 768 + 192 * es + D / 4))};
 }
+__host__ __device__ constexpr int aq_block_index(int ti, int jt) { return ti < 2 ? 2 * ti + jt : 4 + 4 * (ti - 2) + jt; }
 
 struct ChunkWs {
   char* base;       // record 0

@@ -60,8 +60,8 @@ struct ScanLds {
   static constexpr int BYTES = O_ALIAS ? AFTER_V : AFTER_V + 64 * PO * 4;
   static_assert(BYTES <= LIMIT, "scan LDS image too large");
   static_assert(!O_ALIAS || 64 * PO * 4 <= KDT, "aliased output tile must fit in qg / kg");
-  static constexpr RecLayout RL = rec_layout(ES, D);
-  static constexpr int REC_UNITS = (RL.gam + 4 * D) / 16;   // 16-byte units
+  static constexpr RecUnits RU = rec_units(ES, D);
+  static constexpr int REC_UNITS = RU.units;   // 16-byte units
   static constexpr int V_UNITS = V_LDS ? 64 * D * ES / 16 : 0;
   static constexpr int UNITS = REC_UNITS + V_UNITS;
   static constexpr int PER_THREAD = (UNITS + NT - 1) / NT;
@@ -71,20 +71,40 @@ struct ScanLds {
   static constexpr int GV = 16 * ES / 16;  // 16-byte vectors of gate logits per thread
 };
 
-// Record byte offset of 16-byte unit u -> byte offset in the padded LDS image.
+// Record unit u (the workspace layout of rec_units) -> byte offset in the
+// padded LDS image.  A bf16 unit of Kd^T or of Tril(A_qk) carries two 8-byte
+// pieces: the offset is the first one's; the second goes kdt_second (16 rows
+// further down) or aq_second (the same place in the lo array) beyond it.
 template <typename L, int D>
 __device__ __forceinline__ int lds_offset_of_unit(int u) {
-  constexpr RecLayout RL = L::RL;
-  constexpr int RQ = D * L::ES;   // bytes per row of qg / kg
-  constexpr int RK = 64 * L::ES;  // bytes per row of the 64-wide arrays
-  const int b = u * 16;
-  if (b < RL.kg) return L::QG + (b / RQ) * L::PQ + b % RQ;
-  if (b < RL.kdt) { const int o = b - RL.kg; return L::KG + (o / RQ) * L::PQ + o % RQ; }
-  if (b < RL.tb) { const int o = b - RL.kdt; return L::KDT + (o / RK) * L::PK + o % RK; }
-  if (b < RL.aqh) { const int o = b - RL.tb; return L::TB + (o / RK) * L::PK + o % RK; }
-  if (b < RL.aql) { const int o = b - RL.aqh; return L::AQH + (o / RK) * L::PK + o % RK; }
-  if (b < RL.gam) { const int o = b - RL.aql; return L::AQL + (o / RK) * L::PK + o % RK; }
-  return L::GAM + (b - RL.gam);
+  constexpr RecUnits RU = L::RU;
+  constexpr int KS = D / 32, UPP = L::ES / 2;  // units per 8-element piece
+  if (u < RU.aq) {  // qg, kg, kdt: piece (ti, kk, lane), part h of it (fp32)
+    const int region = u < RU.kg ? 0 : u < RU.kdt ? 1 : 2;
+    const int v = u - (region == 0 ? RU.qg : region == 1 ? RU.kg : RU.kdt);
+    const int pc = v / UPP, h = v % UPP;
+    const int ti = pc / (64 * KS), kk = (pc / 64) % KS, lane = pc % 64;
+    const int n = lane & 15, g4 = lane >> 4;
+    if (region < 2) return (region == 0 ? L::QG : L::KG) + (16 * ti + n) * L::PQ + (32 * kk + 8 * g4 + 4 * h) * L::ES;
+    const int tpos = 32 * (ti >> 1) + 8 * g4 + 4 * (ti & 1);
+    return L::KDT + (32 * kk + 16 * h + n) * L::PK + tpos * L::ES;
+  }
+  if (u < RU.tb) {  // Tril(A_qk) block (ti, jt), lane: hi at row 16 ti + n, its slot column
+    const int v = u - RU.aq;
+    const int bi = v / 64, lane = v % 64;
+    const int ti = bi < 4 ? bi / 2 : 2 + (bi - 4) / 4;
+    const int jt = bi < 4 ? bi % 2 : (bi - 4) % 4;
+    const int n = lane & 15, g4 = lane >> 4;
+    return L::AQH + (16 * ti + n) * L::PK + (32 * (jt >> 1) + 8 * g4 + 4 * (jt & 1)) * L::ES;
+  }
+  if (u < RU.gam) {  // T Diag(beta): 32 slots of rows 0..31, then 64 slots of rows 32..63
+    constexpr int W32 = 32 * L::ES / 16, W64 = 64 * L::ES / 16;
+    const int v = u - RU.tb;
+    const int rr = v < 32 * W32 ? v / W32 : 32 + (v - 32 * W32) / W64;
+    const int w = v < 32 * W32 ? v % W32 : (v - 32 * W32) % W64;
+    return L::TB + rr * L::PK + 16 * w;
+  }
+  return L::GAM + 16 * (u - RU.gam);
 }
 
 // 16 consecutive fp32 values -> 16 outputs (fp32 or bf16) at dst.
@@ -110,6 +130,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
   using Ops = ScanOps<T>;
   using V8 = typename Ops::V8;
   using L = ScanLds<T, D>;
+  static_assert(sizeof(T) == 4, "one LDS place per record unit: fp32 records");
   constexpr int MT = D / 16;  // 16-row tiles of the state (key channels)
   constexpr int KS = D / 32;  // K-steps over key channels
   constexpr int NT = L::NT;
@@ -401,12 +422,17 @@ struct WsLds {
   static constexpr int PO = D + 4;
   static constexpr int OT = GS + 64 * PQ;      // output tile [64][PO] fp32
   static constexpr int BYTES = OT + 64 * PO * 4;
-  static constexpr RecLayout RL = rec_layout(ES, D);
+  static constexpr RecUnits RU = rec_units(ES, D);
   static constexpr int VPR = D * ES / 16;      // 16-byte units per slab row
   static constexpr int SLAB_UNITS = 64 * VPR;
-  static constexpr int A_REC = RL.kdt / 16;    // record units of part A (qg, kg)
+  static constexpr int A_REC = RU.kdt;         // record units of part A (qg, kg)
   static constexpr int A_UNITS = A_REC + SLAB_UNITS;
-  static constexpr int B_UNITS = (RL.gam + 4 * D - RL.kdt) / 16;
+  static constexpr int B_UNITS = RU.units - RU.kdt;
+  // part B steps of split units (bf16): Kd^T, then Tril(A_qk) (hi | lo)
+  static constexpr int KDT_STEPS = (RU.aq - RU.kdt) / NH;
+  static constexpr int AQ_STEPS = (RU.tb - RU.aq) / NH;
+  static constexpr int KDT_SECOND = 16 * PK;   // second piece of a Kd^T unit: 16 rows down
+  static constexpr int AQ_SECOND = AQL - AQH;  // second piece of an A_qk unit: the lo array
   static constexpr int PA = (A_UNITS + NH - 1) / NH;
   static constexpr int PB = (B_UNITS + NH - 1) / NH;
   static constexpr int PG = (SLAB_UNITS + NH - 1) / NH;
@@ -419,6 +445,7 @@ struct WsLds {
 template <typename T, int D, bool OUT_F32>
 __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const ScanParams p) {
   using L = WsLds<T, D>;
+  static_assert(sizeof(T) == 2, "the split commits of part B assume bf16 records");
   __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -497,9 +524,19 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
 #pragma unroll
       for (int i = 0; i < L::PB; ++i) stB[i] = rp[min(hid + NH * i, L::B_UNITS - 1)];
     };
+    static_assert((L::RU.aq - L::RU.kdt) % NH == 0 && (L::RU.tb - L::RU.aq) % NH == 0,
+                  "split units must fill whole steps");
     auto commit_B = [&]() {
 #pragma unroll
-      for (int i = 0; i < L::PB; ++i) *reinterpret_cast<u32x4*>(lds + lofB[i]) = stB[i];
+      for (int i = 0; i < L::PB; ++i) {
+        if (i < L::KDT_STEPS + L::AQ_STEPS) {  // two 8-byte pieces
+          const int second = i < L::KDT_STEPS ? L::KDT_SECOND : L::AQ_SECOND;
+          *reinterpret_cast<uint2*>(lds + lofB[i]) = uint2{stB[i][0], stB[i][1]};
+          *reinterpret_cast<uint2*>(lds + lofB[i] + second) = uint2{stB[i][2], stB[i][3]};
+        } else {
+          *reinterpret_cast<u32x4*>(lds + lofB[i]) = stB[i];
+        }
+      }
     };
     auto load_G = [&](int c) {
       const T* g0 = gin + head_base + (int64_t)(p.t0 + c * kChunk) * tok_stride;
