@@ -433,7 +433,7 @@ struct IntraCore {
     for (int jt = 0; jt < 4; ++jt) {
       const bool lower = jt <= ti;
       const bool zero_blk = (ti == 0 && jt == 1) || (ti == 2 && jt == 3);
-      if (lower || zero_blk) {
+      if (UNITS ? lower : (lower || zero_blk)) {
         if constexpr (UNITS) {  // hi then lo of one block row piece per 16-byte unit
           T* dst = aqh + (16 / (int)sizeof(T)) * (64 * aq_block_index(ti, jt) + 16 * g4 + n);
           if constexpr (AP::kHasLo)

@@ -33,30 +33,30 @@ __host__ __device__ constexpr int round256(int x) { return (x + 255) & ~255; }
 //           channels 32 kk + 8 g4 .. + 7 (n = lane % 16, g4 = lane / 16)
 //   kdt     the same pieces, each Kd^T rows 32 kk + n and 32 kk + 16 + n
 //           (4 elements each) at token slots 32 (ti / 2) + 8 g4 + 4 (ti % 2)
-//   aq      the 12 blocks (ti, jt) of Tril(A_qk) that the scan multiplies
-//           (jt <= ti, plus the zero blocks (0, 1) and (2, 3)), block index
-//           2 ti + jt for ti < 2 and 4 + 4 (ti - 2) + jt after: unit
-//           64 block + lane = hi (4 elements) then, for bf16, lo (4 elements)
-//           of row 16 ti + n at slots 32 (jt / 2) + 8 g4 + 4 (jt % 2)
 //   tb      T Diag(beta) rows, slot order: slots 0..31 of rows 0..31, then
 //           slots 0..63 of rows 32..63 (the rest is never read)
+//   aq      the 10 blocks (ti, jt <= ti) of Tril(A_qk), block index
+//           ti (ti + 1) / 2 + jt: unit 64 block + lane = hi (4 elements) then,
+//           for bf16, lo (4 elements) of row 16 ti + n at slots
+//           32 (jt / 2) + 8 g4 + 4 (jt % 2).  The scan also multiplies the
+//           zero blocks (0, 1) and (2, 3): it keeps them zero in LDS.
 //   gam     Gamma_last, D fp32
 struct RecUnits {
-  int qg, kg, kdt, aq, tb, gam, units, bytes;
+  int qg, kg, kdt, tb, aq, gam, units, bytes;
 };
 __host__ __device__ constexpr RecUnits rec_units(int es, int D) {
-  // qg, kg, kdt: 64 D es / 16 = 4 D es units each; aq: 12 blocks x 64 lanes;
-  // tb: 32 rows x 32 slots + 32 rows x 64 slots = 192 es units; gam: D / 4
+  // qg, kg, kdt: 64 D es / 16 = 4 D es units each; tb: 32 rows x 32 slots +
+  // 32 rows x 64 slots = 192 es units; aq: 10 blocks x 64 lanes; gam: D / 4
   return RecUnits{0,
                   4 * D * es,
                   8 * D * es,
                   12 * D * es,
-                  12 * D * es + 768,
-                  12 * D * es + 768 + 192 * es,
-                  12 * D * es + 768 + 192 * es + D / 4,
-                  round256(16 * (12 * D * es + 768 + 192 * es + D / 4))};
+                  12 * D * es + 192 * es,
+                  12 * D * es + 192 * es + 640,
+                  12 * D * es + 192 * es + 640 + D / 4,
+                  round256(16 * (12 * D * es + 192 * es + 640 + D / 4))};
 }
-__host__ __device__ constexpr int aq_block_index(int ti, int jt) { return ti < 2 ? 2 * ti + jt : 4 + 4 * (ti - 2) + jt; }
+__host__ __device__ constexpr int aq_block_index(int ti, int jt) { return ti * (ti + 1) / 2 + jt; }
 
 struct ChunkWs {
   char* base;       // record 0

@@ -79,7 +79,7 @@ template <typename L, int D>
 __device__ __forceinline__ int lds_offset_of_unit(int u) {
   constexpr RecUnits RU = L::RU;
   constexpr int KS = D / 32, UPP = L::ES / 2;  // units per 8-element piece
-  if (u < RU.aq) {  // qg, kg, kdt: piece (ti, kk, lane), part h of it (fp32)
+  if (u < RU.tb) {  // qg, kg, kdt: piece (ti, kk, lane), part h of it (fp32)
     const int region = u < RU.kg ? 0 : u < RU.kdt ? 1 : 2;
     const int v = u - (region == 0 ? RU.qg : region == 1 ? RU.kg : RU.kdt);
     const int pc = v / UPP, h = v % UPP;
@@ -89,22 +89,40 @@ __device__ __forceinline__ int lds_offset_of_unit(int u) {
     const int tpos = 32 * (ti >> 1) + 8 * g4 + 4 * (ti & 1);
     return L::KDT + (32 * kk + 16 * h + n) * L::PK + tpos * L::ES;
   }
-  if (u < RU.tb) {  // Tril(A_qk) block (ti, jt), lane: hi at row 16 ti + n, its slot column
-    const int v = u - RU.aq;
-    const int bi = v / 64, lane = v % 64;
-    const int ti = bi < 4 ? bi / 2 : 2 + (bi - 4) / 4;
-    const int jt = bi < 4 ? bi % 2 : (bi - 4) % 4;
-    const int n = lane & 15, g4 = lane >> 4;
-    return L::AQH + (16 * ti + n) * L::PK + (32 * (jt >> 1) + 8 * g4 + 4 * (jt & 1)) * L::ES;
-  }
-  if (u < RU.gam) {  // T Diag(beta): 32 slots of rows 0..31, then 64 slots of rows 32..63
+  if (u < RU.aq) {  // T Diag(beta): 32 slots of rows 0..31, then 64 slots of rows 32..63
     constexpr int W32 = 32 * L::ES / 16, W64 = 64 * L::ES / 16;
     const int v = u - RU.tb;
     const int rr = v < 32 * W32 ? v / W32 : 32 + (v - 32 * W32) / W64;
     const int w = v < 32 * W32 ? v % W32 : (v - 32 * W32) % W64;
     return L::TB + rr * L::PK + 16 * w;
   }
+  if (u < RU.gam) {  // Tril(A_qk) block (ti, jt <= ti), lane: hi at row 16 ti + n, its slot column
+    const int v = u - RU.aq;
+    const int bi = v / 64, lane = v % 64;
+    const int ti = bi >= 6 ? 3 : bi >= 3 ? 2 : bi >= 1 ? 1 : 0;
+    const int jt = bi - ti * (ti + 1) / 2;
+    const int n = lane & 15, g4 = lane >> 4;
+    return L::AQH + (16 * ti + n) * L::PK + (32 * (jt >> 1) + 8 * g4 + 4 * (jt & 1)) * L::ES;
+  }
   return L::GAM + 16 * (u - RU.gam);
+}
+
+// The zero blocks (0, 1) and (2, 3) of Tril(A_qk) that the scan multiplies
+// are not in the record: zero their LDS places (hi and, for bf16, lo) once.
+// Thread t of nthreads; nothing else writes these bytes.
+template <typename L>
+__device__ __forceinline__ void zero_aq_blocks(char* lds, int t, int nthreads) {
+  constexpr int ARRAYS = L::ES == 2 ? 2 : 1;
+  constexpr int PIECES = 2 * 16 * 4 * ARRAYS;  // blocks x rows x 4-slot groups x arrays
+  for (int i = t; i < PIECES; i += nthreads) {
+    const int arr = i % ARRAYS, g4 = (i / ARRAYS) % 4, n = (i / (4 * ARRAYS)) % 16, blk = i / (64 * ARRAYS);
+    const int ti = blk == 0 ? 0 : 2, jt = ti + 1;
+    const int off = (arr == 0 ? L::AQH : L::AQL) + (16 * ti + n) * L::PK + (32 * (jt >> 1) + 8 * g4 + 4 * (jt & 1)) * L::ES;
+    if constexpr (L::ES == 2)
+      *reinterpret_cast<uint2*>(lds + off) = uint2{0u, 0u};
+    else
+      *reinterpret_cast<u32x4*>(lds + off) = u32x4{0u, 0u, 0u, 0u};
+  }
 }
 
 // 16 consecutive fp32 values -> 16 outputs (fp32 or bf16) at dst.
@@ -206,6 +224,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
       for (int i = 0; i < 4; ++i) S[mt][i] = s0[(16 * mt + 4 * g4 + i) * D + col];
   }
 
+  zero_aq_blocks<L>(lds, tid, NT);
   fetch(0);
   commit();
   __syncthreads();
@@ -428,9 +447,10 @@ struct WsLds {
   static constexpr int A_REC = RU.kdt;         // record units of part A (qg, kg)
   static constexpr int A_UNITS = A_REC + SLAB_UNITS;
   static constexpr int B_UNITS = RU.units - RU.kdt;
-  // part B steps of split units (bf16): Kd^T, then Tril(A_qk) (hi | lo)
-  static constexpr int KDT_STEPS = (RU.aq - RU.kdt) / NH;
-  static constexpr int AQ_STEPS = (RU.tb - RU.aq) / NH;
+  // part B (relative units): Kd^T (split, whole steps), T Diag(beta) (plain),
+  // Tril(A_qk) (split: hi | lo), Gamma_last (plain)
+  static constexpr int KDT_STEPS = (RU.tb - RU.kdt) / NH;
+  static constexpr int AQ_LO = RU.aq - RU.kdt, AQ_HI = RU.gam - RU.kdt;
   static constexpr int KDT_SECOND = 16 * PK;   // second piece of a Kd^T unit: 16 rows down
   static constexpr int AQ_SECOND = AQL - AQH;  // second piece of an A_qk unit: the lo array
   static constexpr int PA = (A_UNITS + NH - 1) / NH;
@@ -524,15 +544,18 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
 #pragma unroll
       for (int i = 0; i < L::PB; ++i) stB[i] = rp[min(hid + NH * i, L::B_UNITS - 1)];
     };
-    static_assert((L::RU.aq - L::RU.kdt) % NH == 0 && (L::RU.tb - L::RU.aq) % NH == 0,
-                  "split units must fill whole steps");
+    static_assert((L::RU.tb - L::RU.kdt) % NH == 0 && L::AQ_LO % 64 == 0,
+                  "Kd^T units fill whole steps; A_qk starts at a wave boundary");
     auto commit_B = [&]() {
 #pragma unroll
       for (int i = 0; i < L::PB; ++i) {
-        if (i < L::KDT_STEPS + L::AQ_STEPS) {  // two 8-byte pieces
-          const int second = i < L::KDT_STEPS ? L::KDT_SECOND : L::AQ_SECOND;
+        const int u = min(hid + NH * i, L::B_UNITS - 1);  // as loaded (clamped)
+        if (i < L::KDT_STEPS) {  // Kd^T: two 8-byte pieces, 16 rows apart
           *reinterpret_cast<uint2*>(lds + lofB[i]) = uint2{stB[i][0], stB[i][1]};
-          *reinterpret_cast<uint2*>(lds + lofB[i] + second) = uint2{stB[i][2], stB[i][3]};
+          *reinterpret_cast<uint2*>(lds + lofB[i] + L::KDT_SECOND) = uint2{stB[i][2], stB[i][3]};
+        } else if (u >= L::AQ_LO && u < L::AQ_HI) {  // A_qk: hi and lo pieces (wave-uniform)
+          *reinterpret_cast<uint2*>(lds + lofB[i]) = uint2{stB[i][0], stB[i][1]};
+          *reinterpret_cast<uint2*>(lds + lofB[i] + L::AQ_SECOND) = uint2{stB[i][2], stB[i][3]};
         } else {
           *reinterpret_cast<u32x4*>(lds + lofB[i]) = stB[i];
         }
@@ -570,6 +593,7 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
     const int cl = p.nc - 1;
     // prologue: part A of chunk 0 into LDS; part B of chunk 0, part A of
     // chunk 1 and the gate logits of chunk 0 into registers
+    zero_aq_blocks<L>(lds, hid, NH);
     load_A(0);
     load_B(0);
     commit_A(0);
