@@ -163,8 +163,24 @@ def time_decode(kda, H, D, steps, warmup, n=256):
     ms = start.elapsed_time(stop) / steps
     nbytes = n * H * (8 * D * D + 12 * D + 2)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"sequences": n, "heads": H, "d": D, "ms": ms, "token_heads_per_s": n * H / (ms * 1e-3),
-            "algorithmic_bytes": nbytes, "achieved_GBs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "launches": 1}
+    res = {"sequences": n, "heads": H, "d": D, "ms": ms, "token_heads_per_s": n * H / (ms * 1e-3),
+           "algorithmic_bytes": nbytes, "achieved_GBs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "launches": 1}
+    # state export of the same pool (kda_state_io, KV layout): 4 D^2 bytes read and written per head-slot
+    user = torch.empty_like(pool)
+    for _ in range(warmup):
+        kda.state_io(kda.STATE_EXPORT, pool, user)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        kda.state_io(kda.STATE_EXPORT, pool, user)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_io = start.elapsed_time(stop) / steps
+    io_bytes = 2 * n * H * D * D * 4
+    res["state_export"] = {"ms": ms_io, "algorithmic_bytes": io_bytes,
+                           "achieved_GBs": io_bytes / (ms_io * 1e-3) / 1e9,
+                           "frac_hbm": io_bytes / (ms_io * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return res
 
 
 def main() -> int:
