@@ -13,7 +13,10 @@ constexpr int kSub = 16;     // tokens per sub-tile
 // Per-chunk intermediates written by the intra-chunk kernel and read by the
 // state scan: one contiguous record per (b, h, chunk of the current segment),
 // record index ((b * H + h) * nc + c).  Element type T = the input type (bf16
-// bits or fp32).  Byte layout of one record (D = head dim, ES = sizeof(T)):
+// bits or fp32).  What one record holds (D = head dim), as the arrays that
+// the LDS images of the scan and of the fused kernel keep (rows padded); in
+// the workspace the same values are stored in the unit layout of rec_units
+// below:
 //   qg  [64][D]   q^ . Gamma, columns in slot order per 32-group
 //   kg  [64][D]   -(k^ . Gamma), columns in slot order (negated, so that the
 //                 scan forms V - (K . Gamma) S in one accumulator chain)
@@ -22,7 +25,6 @@ constexpr int kSub = 16;     // tokens per sub-tile
 //   aqh [64][64]  Tril(A_qk): high bf16 part (bf16 path) or value (fp32 path)
 //   aql [64][64]  Tril(A_qk) - aqh (bf16 path only)
 //   gam [D]       Gamma_last, fp32
-// padded to a multiple of 256 bytes.
 __host__ __device__ constexpr int round256(int x) { return (x + 255) & ~255; }
 
 // Chunk record in the workspace: 16-byte units in the order the intra-chunk
