@@ -73,11 +73,13 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 struct WsLayout {
-  size_t off_rec, rec_bytes, off_carry, total;
+  size_t off_rec, rec_bytes, off_carry, off_done, total;
 };
 
-// Workspace for a segment of seg_nc chunks: one record per (b, h, chunk) and
-// the fp32 state carried between segments.
+// Workspace for a segment of seg_nc chunks: one record per (b, h, chunk), the
+// fp32 state carried between segments and one record counter per (segment,
+// b, h) of the sequence (the overlapped schedule's hand-over; at most one
+// segment per chunk).
 WsLayout layout_for(const kda_desc* d, int64_t seg_nc) {
   const int es = (int)elem_size(d->in_dtype);
   const int64_t D = d->d_k;
@@ -92,6 +94,7 @@ WsLayout layout_for(const kda_desc* d, int64_t seg_nc) {
   L.rec_bytes = (size_t)kda::rec_units(es, (int)D).bytes;
   L.off_rec = take(R * L.rec_bytes);
   L.off_carry = take((size_t)d->B * d->H * D * D * 4);
+  L.off_done = take((size_t)(((int64_t)d->T + kChunk - 1) / kChunk + 1) * d->B * d->H * 4);
   L.total = o;
   return L;
 }
@@ -129,7 +132,7 @@ struct DeviceCtx {
   bool ready = false;
   int cus = 0;
   hipEvent_t fork = nullptr, join_intra = nullptr, join_scan = nullptr;
-  hipEvent_t intra_done[2] = {nullptr, nullptr}, scan_done[2] = {nullptr, nullptr};
+  hipEvent_t scan_done[2] = {nullptr, nullptr};
   std::vector<StreamPair> pairs;
 };
 constexpr int kMaxDevices = 64;
@@ -142,7 +145,7 @@ bool ctx_ready(DeviceCtx& c, int dev) {
     (void)hipGetLastError();
     return false;
   }
-  for (hipEvent_t* e : {&c.fork, &c.join_intra, &c.join_scan, &c.intra_done[0], &c.intra_done[1], &c.scan_done[0],
+  for (hipEvent_t* e : {&c.fork, &c.join_intra, &c.join_scan, &c.scan_done[0],
                         &c.scan_done[1]})
     if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess) {
       (void)hipGetLastError();
@@ -239,7 +242,7 @@ kda_status kda_release_resources(void) {
       for (hipStream_t q : {p.intra, p.scan})
         if (hipStreamSynchronize(q) != hipSuccess || hipStreamDestroy(q) != hipSuccess) st = KDA_ERR_HIP;
     c.pairs.clear();
-    for (hipEvent_t* e : {&c.fork, &c.join_intra, &c.join_scan, &c.intra_done[0], &c.intra_done[1], &c.scan_done[0],
+    for (hipEvent_t* e : {&c.fork, &c.join_intra, &c.join_scan, &c.scan_done[0],
                           &c.scan_done[1]}) {
       if (*e != nullptr && hipEventDestroy(*e) != hipSuccess) st = KDA_ERR_HIP;
       *e = nullptr;
@@ -391,7 +394,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   char* base = static_cast<char*>(ws);
 
   // one segment: records of chunks [c0, c0 + nc) in `recs`; state S_in -> S_out
-  auto launch_intra = [&](int64_t c0, int nc, const kda::ChunkWs& recs, hipStream_t st_) {
+  auto launch_intra = [&](int64_t c0, int nc, const kda::ChunkWs& recs, hipStream_t st_, uint32_t* done = nullptr) {
     kda::IntraParams ip{};
     ip.q = q;
     ip.k = k;
@@ -409,13 +412,14 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     ip.l2norm = d->qk_l2norm;
     ip.decay = d->decay;
     ip.ws = recs;
+    ip.done = done;
     tr.before(st_);
     const kda_status r = check_launch(kda::launch_intra(ip, D, in_f32, st_), st_);
     tr.after(st_);
     return r;
   };
   auto launch_scan = [&](int64_t c0, int nc, const kda::ChunkWs& recs, const float* S_in, float* S_out,
-                         hipStream_t st_) {
+                         hipStream_t st_, const uint32_t* done = nullptr) {
     kda::ScanParams sp{};
     sp.v = v;
     sp.gate = y ? gate : nullptr;
@@ -432,6 +436,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     sp.t0 = (int)(c0 * kChunk);
     sp.nc = nc;
     sp.ws = recs;
+    sp.done = done;
     sp.snaps = snap.n > 0 ? snap.ptr : nullptr;
     sp.snap_every = snap.every;
     sp.n_snap = snap.n;
@@ -485,7 +490,14 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     return r;
   }
 
-  // ---- overlapped schedule: intra(s + 1) on one stream while scan(s) runs on another
+  // ---- overlapped schedule: intra(s + 1) on one stream while scan(s) runs on
+  // another.  The scan of segment s does not wait for the intra launch of
+  // segment s through an event (a cross-stream dependency costs ≈50 µs per
+  // segment here); it waits inside the kernel for the segment's record
+  // counter (count_record / wait_records), which the intra workgroups raise
+  // as their device-scope record stores complete.  Reusing a record buffer
+  // (segment s + 2) still waits for the scan that read it through an event.
+  // The counters are zeroed on the caller's stream first.
   if (plan.overlapped) {
     const int64_t seg_nc = plan.seg_nc;
     const WsLayout L = layout_for(d, 2 * seg_nc);
@@ -501,11 +513,17 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
       }
       float* carry = reinterpret_cast<float*>(base + L.off_carry);
       float* S_run = S_T ? S_T : carry;
+      uint32_t* done = reinterpret_cast<uint32_t*>(base + L.off_done);
       auto ok = [](hipError_t e) {
         if (e == hipSuccess) return true;
         (void)hipGetLastError();
         return false;
       };
+      const int64_t n_seg = (nc_total + seg_nc - 1) / seg_nc;
+      // zero bits: the fp32 fill of a state copy from nothing
+      const int64_t bh_n = (int64_t)d->B * d->H;
+      st = check_launch(kda::launch_copy_state(nullptr, reinterpret_cast<float*>(done), n_seg * bh_n, s), s);
+      if (st != KDA_OK) return st;
       if (!ok(hipEventRecord(c.fork, s)) || !ok(hipStreamWaitEvent(si, c.fork, 0)) ||
           !ok(hipStreamWaitEvent(ss, c.fork, 0)))
         return KDA_ERR_HIP;
@@ -516,11 +534,9 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
         const int j = (int)(seg & 1);
         // buffer j was last read by the scan two segments back
         if (seg >= 2 && !ok(hipStreamWaitEvent(si, c.scan_done[j], 0))) return KDA_ERR_HIP;
-        st = launch_intra(c0, nc, bufs[j], si);
+        st = launch_intra(c0, nc, bufs[j], si, done + seg * bh_n);
         if (st != KDA_OK) return st;
-        if (!ok(hipEventRecord(c.intra_done[j], si)) || !ok(hipStreamWaitEvent(ss, c.intra_done[j], 0)))
-          return KDA_ERR_HIP;
-        st = launch_scan(c0, nc, bufs[j], S_in, S_run, ss);
+        st = launch_scan(c0, nc, bufs[j], S_in, S_run, ss, done + seg * bh_n);
         if (st != KDA_OK) return st;
         if (!ok(hipEventRecord(c.scan_done[j], ss))) return KDA_ERR_HIP;
         S_in = S_run;

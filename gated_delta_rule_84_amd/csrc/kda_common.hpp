@@ -146,4 +146,59 @@ __device__ __forceinline__ float softplus_log2(float x) {
 // Logistic function: 1 / (1 + e^{-x}); saturates to 0 and 1 at the extremes.
 __device__ __forceinline__ float sigmoid_fast(float x) { return hw_rcp(1.0f + hw_exp2(-x * kLog2e)); }
 
+// ---- hand-over of chunk records between two kernels that run at once -------
+// The producer stores the record with device-scope buffer stores (the sc1
+// cache-policy bit: written through to memory, so a load from another
+// compute unit or XCD sees them once the store has completed) and, once every
+// wave's stores have completed, adds 1 to a counter with a device-scope
+// atomic.  The consumer waits until the counter reaches the number of records
+// and then acquires at device scope (invalidating its caches once), after
+// which plain loads see the records.  No cache-wide write-back per record.
+constexpr int kDeviceScope = 16;            // buffer-op cache policy: sc1
+constexpr uint32_t kPoison = 0x7FC07FC0u;  // a NaN as fp32 and as both bf16 halves
+constexpr int kCountSpinLimit = 1 << 18;   // polls (about a second) before giving up
+
+struct RecSink {
+  __amdgpu_buffer_rsrc_t rsrc;  // the record (uniform)
+  const char* base;
+  __device__ __forceinline__ int off(const void* p) const { return (int)(static_cast<const char*>(p) - base); }
+  __device__ __forceinline__ void st16(const void* p, u32x4 v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, off(p), 0, kDeviceScope);
+  }
+  __device__ __forceinline__ void st4(const void* p, float v) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc, off(p), 0, kDeviceScope);
+  }
+};
+__device__ __forceinline__ RecSink rec_sink(char* rec, int bytes) {
+  return RecSink{__builtin_amdgcn_make_buffer_rsrc(rec, (short)0, bytes, 0x00020000), rec};
+}
+
+// Producer side: after every wave of the workgroup has issued its record
+// stores, wait for them (vmcnt(0) in each wave), then count the record.
+__device__ __forceinline__ void count_record(uint32_t* done) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Consumer side (one wave per workgroup: every poll is a load of the same
+// word, so few pollers, ≈3 µs apart): wait until *done >= target, then
+// acquire; the caller's workgroup barrier orders the other waves' loads after
+// it.  Returns false when the bounded wait gave up (the caller then poisons
+// what it stages, so that a producer that never ran shows as NaN, not a hang).
+__device__ __forceinline__ bool wait_records(const uint32_t* done, uint32_t target) {
+  uint32_t* d = const_cast<uint32_t*>(done);
+  int spin = 0;
+  bool ok = true;
+  while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < target) {
+    if (++spin > kCountSpinLimit) {
+      ok = false;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(127);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return ok;
+}
+
 }  // namespace kda

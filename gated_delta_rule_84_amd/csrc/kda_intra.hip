@@ -51,10 +51,11 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
 
   Core ic;
   ic.init(tid >> 6, tid & 63);
+  ic.sink = rec_sink(recp, (int)p.ws.rec_bytes);
   ic.load(p, b, h, tok0, nvalid);
   ic.prefix(p, h, s);
   __syncthreads();
-  Core::template tables<256>(tid, s, reinterpret_cast<float*>(recp + 16 * RU.gam));
+  Core::template tables<256>(tid, s, reinterpret_cast<float*>(recp + 16 * RU.gam), &ic.sink);
   __syncthreads();
   ic.factors(s, reinterpret_cast<T*>(recp + 16 * RU.qg), reinterpret_cast<T*>(recp + 16 * RU.kg));
   ic.store_kd(reinterpret_cast<T*>(recp + 16 * RU.kdt));
@@ -68,7 +69,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
     ic.level(dist, s);
     __syncthreads();
   }
-  Core::template tb_pass<256>(tid, s, reinterpret_cast<T*>(recp + 16 * RU.tb));
+  Core::template tb_pass<256>(tid, s, reinterpret_cast<T*>(recp + 16 * RU.tb), &ic.sink);
+  if (p.done != nullptr) count_record(p.done + (int64_t)b * p.H + h);
 }
 
 template <bool SP>

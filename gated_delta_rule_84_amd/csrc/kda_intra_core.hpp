@@ -137,7 +137,8 @@ struct IntraScratch {
 // PQE / PKE: row pitches (elements) of the record's [64][D] parts (qg, kg) and
 // of its 64-column parts (kdt, tb, aq), when the record is an LDS image
 // (UNITS = false); with UNITS the record is the workspace's unit layout
-// (rec_units: each wave store writes 1 KB of consecutive bytes).
+// (rec_units: each wave store writes 1 KB of consecutive bytes), written
+// through `sink` with device-scope stores (see RecSink).
 //
 // SP: Kimi Linear's unbounded decay g = -e^{A_h} Softplus(z), the map the K3
 // blog's section 2.2 replaces.  Without the sub-tile bound the factors of a
@@ -166,6 +167,21 @@ struct IntraCore {
   f32x4 akk_d, aqk_d, akk[3], aqk[3], tii;
   typename P4::Raw kd[KS][2];  // Kd^T pieces awaiting their store
   typename P4::Raw aqs[4][2];  // Tril(A_qk) row pieces (hi, lo) awaiting their store
+  RecSink sink;                // UNITS: the record's device-scope stores
+
+  // 8 fp32 values as 8 elements of T through the sink (one or two units)
+  static __device__ __forceinline__ void sink_store8(const RecSink& k, T* p, const float* x) {
+    if constexpr (sizeof(T) == 2) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = static_cast<uint32_t>(f32_to_bf16(x[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * i + 1])) << 16);
+      k.st16(p, w);
+    } else {
+      k.st16(p, u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])});
+      k.st16(p + 4, u32x4{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])});
+    }
+  }
 
   __device__ __forceinline__ void init(int wave, int lane) {
     ti = wave;
@@ -211,7 +227,8 @@ struct IntraCore {
   // nthreads, all four waves), base 2:  G of sub-tile i = off_i + prefix,
   // off_i = sum_{j < i} tot_j;  B_i = off_i + loc7_i.  Gamma_last goes to gam.
   template <int NTHREADS>
-  static __device__ __forceinline__ void tables(int t, const IntraScratch<T>& s, float* gam) {
+  static __device__ __forceinline__ void tables(int t, const IntraScratch<T>& s, float* gam,
+                                                const RecSink* sink = nullptr) {
     constexpr int TPC = NTHREADS / D;
     const int ch = t % D, part = t / D;
     float off[4], Bv[4], Ev[4];
@@ -241,7 +258,10 @@ struct IntraCore {
         const int j = pi - pair_index(i, 0);
         s.Et[pi * D + ch] = hw_exp2(Bv[i] - Ev[j]);
       } else {
-        gam[ch] = hw_exp2(glast);
+        if constexpr (UNITS)
+          sink->st4(gam + ch, hw_exp2(glast));
+        else
+          gam[ch] = hw_exp2(glast);
       }
     }
   }
@@ -284,8 +304,8 @@ struct IntraCore {
       }
       if constexpr (UNITS) {
         const int pc = (ti * KS + kk) * 64 + 16 * g4 + n;  // piece of this lane
-        store8<T>(qg + 8 * pc, xq);
-        store8<T>(kg + 8 * pc, xk);
+        sink_store8(sink, qg + 8 * pc, xq);
+        sink_store8(sink, kg + 8 * pc, xk);
       } else {
         store8<T>(qg + r * PQE + 32 * kk + 8 * g4, xq);
         store8<T>(kg + r * PQE + 32 * kk + 8 * g4, xk);
@@ -375,10 +395,10 @@ struct IntraCore {
       if constexpr (UNITS) {
         T* dst = kdt + 8 * ((ti * KS + kk) * 64 + 16 * g4 + n);  // the two pieces side by side
         if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<u32x4*>(dst) = u32x4{kd[kk][0].x, kd[kk][0].y, kd[kk][1].x, kd[kk][1].y};
+          sink.st16(dst, u32x4{kd[kk][0].x, kd[kk][0].y, kd[kk][1].x, kd[kk][1].y});
         } else {
-          P4::store(dst, kd[kk][0]);
-          P4::store(dst + 4, kd[kk][1]);
+          sink.st16(dst, __builtin_bit_cast(u32x4, kd[kk][0]));
+          sink.st16(dst + 4, __builtin_bit_cast(u32x4, kd[kk][1]));
         }
       } else {
         P4::store(kdt + (32 * kk + n) * PKE + tpos, kd[kk][0]);
@@ -437,9 +457,9 @@ struct IntraCore {
         if constexpr (UNITS) {  // hi then lo of one block row piece per 16-byte unit
           T* dst = aqh + (16 / (int)sizeof(T)) * (64 * aq_block_index(ti, jt) + 16 * g4 + n);
           if constexpr (AP::kHasLo)
-            *reinterpret_cast<u32x4*>(dst) = u32x4{aqs[jt][0].x, aqs[jt][0].y, aqs[jt][1].x, aqs[jt][1].y};
+            sink.st16(dst, u32x4{aqs[jt][0].x, aqs[jt][0].y, aqs[jt][1].x, aqs[jt][1].y});
           else
-            P4::store(dst, aqs[jt][0]);
+            sink.st16(dst, __builtin_bit_cast(u32x4, aqs[jt][0]));
         } else {
           const int off = r * PKE + 32 * (jt >> 1) + 8 * g4 + 4 * (jt & 1);
           P4::store(aqh + off, aqs[jt][0]);
@@ -515,7 +535,8 @@ struct IntraCore {
   // tb = T Diag(beta), columns in slot order; upper blocks are zero (thread t
   // of NTHREADS, all four waves; every block of T in LDS).
   template <int NTHREADS>
-  static __device__ __forceinline__ void tb_pass(int t, const IntraScratch<T>& s, T* tb) {
+  static __device__ __forceinline__ void tb_pass(int t, const IntraScratch<T>& s, T* tb,
+                                                 const RecSink* sink = nullptr) {
     for (int idx = t; idx < kChunk * 8; idx += NTHREADS) {
       const int rr = idx >> 3, pg = idx & 7;
       if (UNITS && rr < 32 && pg >= 4) continue;  // never read: not stored
@@ -526,7 +547,7 @@ struct IntraCore {
         x[j] = ((sc >> 4) <= (rr >> 4)) ? s.Tm[rr * LP + sc] * s.betas[sc] : 0.0f;
       }
       if constexpr (UNITS)
-        store8<T>(tb + (rr < 32 ? 32 * rr : 1024 + 64 * (rr - 32)) + 8 * pg, x);
+        sink_store8(*sink, tb + (rr < 32 ? 32 * rr : 1024 + 64 * (rr - 32)) + 8 * pg, x);
       else
         store8<T>(tb + rr * PKE + 8 * pg, x);
     }

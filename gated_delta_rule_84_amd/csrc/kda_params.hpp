@@ -78,6 +78,7 @@ struct IntraParams {
   int l2norm;
   int decay;       // 0: K3 bounded map; 1: Kimi Linear softplus map (pairwise diagonal blocks)
   ChunkWs ws;
+  uint32_t* done;  // [B * H] finished records of each (b, h) in the segment (count_record), or nullptr
 };
 
 struct ScanParams {
@@ -93,6 +94,7 @@ struct ScanParams {
   int B, T, H;
   int t0, nc;           // first token and number of chunks of the segment
   ChunkWs ws;
+  const uint32_t* done;  // [B * H]: wait until done[b H + h] >= nc before reading records, or nullptr
   float* snaps;         // [B, n_snap, H, D, D] states at every snap_every-th chunk boundary, or nullptr
   int snap_every;       // chunks between snapshots (snapshot j: state after chunk (j + 1) * snap_every - 1)
   int n_snap;

@@ -178,6 +178,18 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
   const bool tail_ok = tid + NT * L::FULL < L::UNITS;
   const T* vin = static_cast<const T*>(p.v);
   u32x4 stg[L::PER_THREAD];
+  // records of a producer running at the same time: wave 0 waits until all
+  // are written; the barrier orders every wave's record loads after that
+  __shared__ int gave_up;
+  bool poison = false;
+  if (p.done != nullptr) {
+    if (wave == 0) {
+      const bool ok = wait_records(p.done + bh, (uint32_t)p.nc);
+      if (lane == 0) gave_up = ok ? 0 : 1;
+    }
+    __syncthreads();
+    poison = gave_up != 0;
+  }
   auto fetch = [&](int c) {
     const char* rec = p.ws.base + (bh * p.nc + c) * p.ws.rec_bytes;
     const int tok0 = p.t0 + c * kChunk;
@@ -199,6 +211,9 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
     }
   };
   auto commit = [&]() {
+    if (poison)  // wave-uniform: the records never became complete
+#pragma unroll
+      for (int i = 0; i < L::PER_THREAD; ++i) stg[i] = u32x4{kPoison, kPoison, kPoison, kPoison};
 #pragma unroll
     for (int i = 0; i < L::PER_THREAD; ++i)
       if (i < L::FULL || tail_ok) *reinterpret_cast<u32x4*>(lds + lofs[i]) = stg[i];
@@ -475,6 +490,21 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
   const int64_t tok_stride = (int64_t)p.H * D;
   const int64_t head_base = ((int64_t)b * p.T * p.H + h) * D;
 
+  // Records of a producer running at the same time (the overlapped
+  // schedule): the first helper wave waits until all are written; the
+  // barrier orders every wave's record loads after that.  The outcome goes
+  // through the output tile's first word (free until step 0 ends).
+  bool poison = false;
+  if (p.done != nullptr) {
+    int* gave_up = reinterpret_cast<int*>(lds + L::OT);
+    if (wave == L::NCW) {
+      const bool ok = wait_records(p.done + bh, (uint32_t)p.nc);
+      if (lane == 0) *gave_up = ok ? 0 : 1;
+    }
+    __syncthreads();
+    poison = *gave_up != 0;
+  }
+
   if (wave < L::NCW) {
     scan_compute_waves<T, D, L>(p, lds, wave, lane, b, h);
   } else {
@@ -507,6 +537,7 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
     }
     u32x4 stA[L::PA], stB[L::PB], stG[L::PG];
     auto rec_ptr = [&](int c) { return p.ws.base + (bh * p.nc + c) * p.ws.rec_bytes; };
+    // `poison`: the records never became complete (staged values become NaN)
     auto last_row = [&](int c) { return min(kChunk, p.T - (p.t0 + c * kChunk)) - 1; };
     // part A of chunk c: qg, kg and the V slab (rows past the end are clamped)
     auto load_A = [&](int c) {
@@ -525,6 +556,9 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
           stA[i] = u32x4{0u, 0u, 0u, 0u};
         }
       }
+      if (poison)
+#pragma unroll
+        for (int i = 0; i < L::PA; ++i) stA[i] = u32x4{kPoison, kPoison, kPoison, kPoison};
     };
     auto commit_A = [&](int c) {
       const int last = last_row(c);
@@ -543,6 +577,9 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
       const u32x4* rp = reinterpret_cast<const u32x4*>(rec_ptr(c)) + L::A_REC;
 #pragma unroll
       for (int i = 0; i < L::PB; ++i) stB[i] = rp[min(hid + NH * i, L::B_UNITS - 1)];
+      if (poison)
+#pragma unroll
+        for (int i = 0; i < L::PB; ++i) stB[i] = u32x4{kPoison, kPoison, kPoison, kPoison};
     };
     static_assert((L::RU.tb - L::RU.kdt) % NH == 0 && L::AQ_LO % 64 == 0,
                   "Kd^T units fill whole steps; A_qk starts at a wave boundary");

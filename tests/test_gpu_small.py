@@ -151,6 +151,30 @@ def test_overlapped_schedule_matches_one_stream(kda, B, T, H, D, seg):
         assert _bit_equal(one[key], snap[key]), key
 
 
+def test_overlapped_schedule_reuses_workspace(kda):
+    """Many short segments (the scan of each waits inside the kernel for its
+    records' counters) and three consecutive calls on different inputs with
+    one workspace: every call equals the one-stream schedule bit for bit, so
+    no counter of an earlier call lets a scan start early."""
+    B, T, H, D, seg = 2, 2048, 4, 128, 64
+    desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg, overlap=True, fused=False)
+    ws = torch.empty(kda.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    assert kda.schedule(desc, ws.numel())[1] == "overlapped"
+    outs = []
+    for seed in (1, 2, 3):
+        x = gen_inputs(_custom(B, T, H, D, "bf16", seed=700 + seed))
+        log(f"[overlap reuse] seed={seed} segments={T // seg}")
+        t = {n: dev(x[n]) for n in ("q", "k", "v", "beta", "z", "A", "gate", "S0")}
+        r = kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t["S0"], gate=t["gate"],
+                          overlap=True, segment_tokens=seg, fused=False, workspace=ws)
+        outs.append((x, r))
+    torch.cuda.synchronize()
+    for x, r in outs:
+        one = _run(kda, x, overlap=False, fused=False)
+        for key in ("o", "y", "S_T"):
+            assert _bit_equal(one[key], r[key]), key
+
+
 @pytest.mark.parametrize("B,T,H,D,opts", [
     (2, 1000, 3, 128, {}),
     (1, 777, 2, 64, {}),
