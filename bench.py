@@ -80,6 +80,36 @@ def profiled_traffic(kernel: str, workload: str):
         return None
 
 
+def profiled_counters(workload: str):
+    """MFMA figures measured by rocprofv3 SQ counters, from the committed
+    summary profiles/counters_<workload>.txt (MFMA busy share of the SIMDs a
+    kernel occupies, achieved MFMA TFLOP/s, LDS bank-conflict share), or None
+    when that summary is missing or was taken with different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals, sha = {}, None
+    for line in open(path):
+        if line.startswith("# source_sha256:"):
+            sha = line.split(":", 1)[1].strip()
+        elif ":" in line and not line.startswith(("#", "[")):
+            key, _, val = line.partition(":")
+            vals[key.strip()] = val.strip()
+    if sha != kernel_source_hash():
+        return None
+    keys = ("scan_mfma_busy_own_cus", "scan_mfma_busy_chip", "scan_mfma_tflops", "intra_mfma_busy_chip",
+            "intra_mfma_tflops", "scan_lds_bank_conflict_share", "intra_lds_bank_conflict_share")
+    try:
+        out = {k: float(vals[k]) for k in keys if k in vals}
+    except ValueError:
+        return None
+    if not out:
+        return None
+    out["bf16_mfma_peak_TFLOPs"] = BF16_PEAK_TFLOPS
+    out["source"] = f"profiles/counters_{workload}.txt"
+    return out
+
+
 def path_flops_per_token_head(d: int, C: int = 64) -> float:
     # 6 d^2 (state products) + 5 (C + 16) d (sub-tile products) + C^2 / 3 (UT inverse)
     return 6 * d * d + 5 * (C + 16) * d + C * C / 3
@@ -329,6 +359,7 @@ def main() -> int:
         "path_roofline": {"achieved_GBs": path_gbs, "frac_hbm": path_gbs / HBM_PEAK_GBS,
                           "achieved_TFLOPs": path_tflops, "frac_bf16_mfma": path_tflops / BF16_PEAK_TFLOPS,
                           "algorithmic_bytes": path_bytes},
+        "counters": profiled_counters(wl.name),
         "kernel_ms": kern_ms,
         "input_setup_s": t_gen,
     }
