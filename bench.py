@@ -221,8 +221,9 @@ def main() -> int:
     ap.add_argument("--workload", default="k3_layer")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-baseline sample (0: all heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--schedule", choices=("auto", "fused", "overlapped", "segments"), default="auto",
-                    help="the library's choice (default), the fused kernel, or a two-kernel schedule")
+    ap.add_argument("--schedule", choices=("auto", "fused", "overlapped", "pipelined", "segments"), default="auto",
+                    help="the library's choice (default), the fused kernel, or a two-kernel schedule "
+                         "(overlapped: two segments of records, double-buffered; pipelined: every record)")
     ap.add_argument("--segment-tokens", type=int, default=0,
                     help="tokens per segment of the two-kernel schedules; 0: library default")
     ap.add_argument("--decay", choices=("k3", "softplus"), default="k3",
@@ -278,18 +279,22 @@ def main() -> int:
     out = {"y": torch.empty((B, T, H, D), dtype=odt, device=dev),
            "S_T": torch.empty((B, H, D, D), dtype=torch.float32, device=dev)}
     fused = {"auto": None, "fused": True}.get(args.schedule, False)
-    overlap = args.schedule in ("auto", "overlapped")
+    overlap = args.schedule in ("auto", "overlapped", "pipelined")
     seg_arg = args.segment_tokens or None
     desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg_arg if overlap else 0,
                          overlap=overlap, fused=fused, decay=args.decay)
-    ws_bytes = kda.workspace_size(desc) if (overlap or fused or not seg_arg) else kda.workspace_size(desc, seg_arg)
+    if args.schedule == "overlapped":   # two segments of records: the double-buffered schedule
+        ws_bytes = kda.workspace_size(desc, 2 * (seg_arg or 8192))
+    elif overlap or fused or not seg_arg:
+        ws_bytes = kda.workspace_size(desc)
+    else:
+        ws_bytes = kda.workspace_size(desc, seg_arg)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     seg, sched = kda.schedule(desc, ws_bytes)
-    assert args.schedule == "auto" or sched == args.schedule or (args.schedule == "overlapped" and
-                                                                 sched == "segments"), sched
-    n_seg = -(-T // seg)
-    # launch order: one fused launch, or per segment the intra-chunk kernel then the scan
-    names = ["fused"] if sched == "fused" else ["intra", "scan"] * n_seg
+    assert args.schedule == "auto" or sched == args.schedule or (
+        args.schedule == "overlapped" and sched in ("segments", "pipelined")), sched
+    # the kernel launches of one call, in the order the library brackets them with events
+    names = kda.launches(desc, ws_bytes)
 
     def step(events=None):
         kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t.get("S0"), gate=t["gate"],

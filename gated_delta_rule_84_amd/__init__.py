@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.kda_release_resources.argtypes = []
         L.kda_chunk_fwd_schedule.restype = ctypes.c_int
         L.kda_chunk_fwd_schedule.argtypes = [dp, sz, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        L.kda_chunk_fwd_launches.restype = ctypes.c_int
+        L.kda_chunk_fwd_launches.argtypes = [dp, sz, ctypes.POINTER(i32), i32, ctypes.POINTER(i32)]
         L.kda_chunk_fwd.restype = ctypes.c_int
         L.kda_chunk_fwd.argtypes = [dp] + [vp] * 13 + [sz, vp]
         L.kda_chunk_fwd_traced.restype = ctypes.c_int
@@ -145,7 +147,8 @@ def release_resources() -> None:
         _lib.kda_release_resources()
 
 
-SCHEDULES = {0: "segments", 1: "overlapped", 2: "fused"}
+SCHEDULES = {0: "segments", 1: "overlapped", 2: "fused", 3: "pipelined"}
+LAUNCH_KINDS = {0: "intra", 1: "scan", 2: "fused"}
 
 
 def schedule(desc: KdaDesc, ws_bytes: int) -> tuple[int, str]:
@@ -156,6 +159,21 @@ def schedule(desc: KdaDesc, ws_bytes: int) -> tuple[int, str]:
     if rc != 0:
         raise KdaError("kda_chunk_fwd_schedule", rc)
     return int(seg.value), SCHEDULES[int(sch.value)]
+
+
+def launches(desc: KdaDesc, ws_bytes: int) -> list[str]:
+    """Kinds of the kernel launches ('intra', 'scan', 'fused'), in the order
+    that chunk_fwd(..., events=...) brackets them, for this descriptor and
+    workspace size on the current device."""
+    n = ctypes.c_int32(0)
+    rc = lib().kda_chunk_fwd_launches(ctypes.byref(desc), int(ws_bytes), None, 0, ctypes.byref(n))
+    if rc != 0:
+        raise KdaError("kda_chunk_fwd_launches", rc)
+    kinds = (ctypes.c_int32 * max(n.value, 1))()
+    rc = lib().kda_chunk_fwd_launches(ctypes.byref(desc), int(ws_bytes), kinds, n.value, ctypes.byref(n))
+    if rc != 0:
+        raise KdaError("kda_chunk_fwd_launches", rc)
+    return [LAUNCH_KINDS[int(kinds[i])] for i in range(n.value)]
 
 
 def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=None, want_o=True,

@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -122,6 +123,46 @@ bool fused_wanted(const kda_desc* d) {
 }
 constexpr size_t kFusedWorkspace = 256;  // what the size query reports for it (nothing is used)
 
+// Pipelined schedule: every record of the sequence stays in the workspace.
+// The intra-chunk kernel runs segment by segment on one library stream while
+// one scan launch over the whole sequence runs on the other and waits inside
+// the kernel for each segment's records.  Segments grow from 16 chunks to the
+// steady length (d->segment_tokens), so the scan of every head starts after
+// the first 1,024 tokens' records instead of after a whole segment, and the
+// scan has no per-segment restart (state reload, pipeline fill and drain,
+// launch gap).  No record buffer is reused, so no intra-chunk launch ever
+// waits for the scan.  It needs the specialised scan workgroup (bf16 inputs)
+// and a workspace that holds every record; the size query offers that
+// workspace up to kPipelinedWorkspaceCap.
+constexpr int64_t kRamp[] = {16, 16, 24, 32, 48, 64, 96};
+constexpr int kRampLen = sizeof(kRamp) / sizeof(kRamp[0]);
+constexpr size_t kPipelinedWorkspaceCap = size_t(8) << 30;
+
+bool pipelined_eligible(const kda_desc* d) {
+  return d->overlap != 0 && d->in_dtype == KDA_BF16 && !fused_wanted(d) && num_chunks(d) > kRamp[0];
+}
+
+// Cumulative chunk ends of the pipelined schedule's segments (at most
+// kda::kMaxSegs, each at least one chunk); returns their number.
+int segment_table(const kda_desc* d, int32_t* ends) {
+  const int64_t nc = num_chunks(d), steady = pipe_chunks(d);
+  int n = 0;
+  int64_t at = 0;
+  for (int i = 0; i < kRampLen && at < nc; ++i) {
+    at = std::min(nc, at + std::min(kRamp[i], steady));
+    ends[n++] = (int32_t)at;
+  }
+  if (at < nc) {  // steady segments, lengthened when needed to stay within the table
+    const int64_t slots = kda::kMaxSegs - n;
+    const int64_t len = std::max(steady, (nc - at + slots - 1) / slots);
+    while (at < nc) {
+      at = std::min(nc, at + len);
+      ends[n++] = (int32_t)at;
+    }
+  }
+  return n;
+}
+
 // ---- per-device streams and events of the overlapped schedule --------------
 struct StreamPair {
   int n_scan;
@@ -187,24 +228,54 @@ struct Plan {
   int dev;
   int n_scan;
   bool fused;
+  bool pipelined;
+  int n_seg;                      // pipelined: segments and their chunk ends
+  int32_t seg_end[kda::kMaxSegs];
 };
+
+// The two library streams can be used for B * H scan workgroups on the
+// current device (B * H at most 5/8 of its compute units).
+bool two_streams(const kda_desc* d, int* dev_out, int* n_scan_out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return false;
+  }
+  DeviceCtx& c = g_dev[dev];
+  std::lock_guard<std::mutex> lock(c.mu);
+  const int64_t bh = (int64_t)d->B * d->H;
+  const int n_scan = (int)((bh + 7) / 8 * 8);
+  hipStream_t si = nullptr, ss = nullptr;
+  if (!(ctx_ready(c, dev) && bh * 8 <= (int64_t)c.cus * 5 && stream_pair(c, n_scan, &si, &ss))) return false;
+  *dev_out = dev;
+  *n_scan_out = n_scan;
+  return true;
+}
+
 Plan make_plan(const kda_desc* d, size_t ws_bytes) {
-  Plan p{1, false, 0, 0, false};
+  Plan p{};
+  p.seg_nc = 1;
   const int64_t nc_total = num_chunks(d);
-  if (fused_wanted(d)) return Plan{nc_total < 1 ? 1 : nc_total, false, 0, 0, true};
-  if (pipe_wanted(d)) {
-    const int64_t seg_nc = pipe_chunks(d);
-    int dev = 0;
-    if (ws_bytes >= layout_for(d, 2 * seg_nc).total && hipGetDevice(&dev) == hipSuccess && dev >= 0 &&
-        dev < kMaxDevices) {
-      DeviceCtx& c = g_dev[dev];
-      std::lock_guard<std::mutex> lock(c.mu);
-      const int64_t bh = (int64_t)d->B * d->H;
-      const int n_scan = (int)((bh + 7) / 8 * 8);
-      hipStream_t si = nullptr, ss = nullptr;
-      if (ctx_ready(c, dev) && bh * 8 <= (int64_t)c.cus * 5 && stream_pair(c, n_scan, &si, &ss))
-        return Plan{seg_nc, true, dev, n_scan, false};
-    }
+  if (fused_wanted(d)) {
+    p.seg_nc = nc_total < 1 ? 1 : nc_total;
+    p.fused = true;
+    return p;
+  }
+  int dev = 0, n_scan = 0;
+  if (pipelined_eligible(d) && ws_bytes >= layout_for(d, nc_total).total && two_streams(d, &dev, &n_scan)) {
+    p.seg_nc = pipe_chunks(d);
+    p.pipelined = true;
+    p.dev = dev;
+    p.n_scan = n_scan;
+    p.n_seg = segment_table(d, p.seg_end);
+    return p;
+  }
+  if (pipe_wanted(d) && ws_bytes >= layout_for(d, 2 * pipe_chunks(d)).total && two_streams(d, &dev, &n_scan)) {
+    p.seg_nc = pipe_chunks(d);
+    p.overlapped = true;
+    p.dev = dev;
+    p.n_scan = n_scan;
+    return p;
   }
   // one stream: the largest segment whose workspace fits
   int64_t lo = 1, hi = nc_total < 1 ? 1 : nc_total;
@@ -217,6 +288,30 @@ Plan make_plan(const kda_desc* d, size_t ws_bytes) {
   }
   p.seg_nc = lo;
   return p;
+}
+
+// Kinds of the traced kernel launches of a call with this plan, in order
+// (KDA_LAUNCH_*); returns how many there are.
+int32_t plan_launches(const kda_desc* d, const Plan& p, int32_t* kinds, int32_t max_kinds) {
+  int32_t n = 0;
+  auto put = [&](int32_t k) {
+    if (kinds && n < max_kinds) kinds[n] = k;
+    ++n;
+  };
+  if (p.fused) {
+    put(KDA_LAUNCH_FUSED);
+  } else if (p.pipelined) {
+    put(KDA_LAUNCH_INTRA);
+    put(KDA_LAUNCH_SCAN);
+    for (int s = 1; s < p.n_seg; ++s) put(KDA_LAUNCH_INTRA);
+  } else {
+    const int64_t nc_total = num_chunks(d);
+    for (int64_t c0 = 0; c0 < nc_total; c0 += p.seg_nc) {
+      put(KDA_LAUNCH_INTRA);
+      put(KDA_LAUNCH_SCAN);
+    }
+  }
+  return n;
 }
 
 }  // namespace
@@ -262,7 +357,20 @@ kda_status kda_chunk_fwd_schedule(const kda_desc* d, size_t ws_bytes, int32_t* s
   if (!fused_wanted(d) && ws_bytes < layout_for(d, 1).total) return KDA_ERR_WORKSPACE;
   const Plan p = make_plan(d, ws_bytes);
   *segment_tokens = (int32_t)(p.seg_nc * kChunk);
-  *schedule = p.fused ? KDA_SCHEDULE_FUSED : p.overlapped ? KDA_SCHEDULE_OVERLAPPED : KDA_SCHEDULE_SEGMENTS;
+  *schedule = p.fused        ? KDA_SCHEDULE_FUSED
+              : p.pipelined  ? KDA_SCHEDULE_PIPELINED
+              : p.overlapped ? KDA_SCHEDULE_OVERLAPPED
+                             : KDA_SCHEDULE_SEGMENTS;
+  return KDA_OK;
+}
+
+kda_status kda_chunk_fwd_launches(const kda_desc* d, size_t ws_bytes, int32_t* kinds, int32_t max_kinds,
+                                  int32_t* n_launches) {
+  const kda_status st = validate_desc(d);
+  if (st != KDA_OK) return st;
+  if (!n_launches || max_kinds < 0 || (max_kinds > 0 && !kinds)) return KDA_ERR_NULL_ARG;
+  if (!fused_wanted(d) && ws_bytes < layout_for(d, 1).total) return KDA_ERR_WORKSPACE;
+  *n_launches = plan_launches(d, make_plan(d, ws_bytes), kinds, max_kinds);
   return KDA_OK;
 }
 
@@ -313,6 +421,10 @@ size_t kda_chunk_fwd_workspace_size_for(const kda_desc* d, int32_t segment_token
 size_t kda_chunk_fwd_workspace_size(const kda_desc* d) {
   if (validate_desc(d) != KDA_OK) return 0;
   if (fused_wanted(d)) return kFusedWorkspace;
+  if (pipelined_eligible(d)) {
+    const size_t all = layout_for(d, num_chunks(d)).total;
+    if (all <= kPipelinedWorkspaceCap) return all;
+  }
   if (pipe_wanted(d)) return layout_for(d, 2 * pipe_chunks(d)).total;
   const int32_t toks = d->T < kDefaultSegmentTokens ? (d->T > 0 ? d->T : 1) : kDefaultSegmentTokens;
   return kda_chunk_fwd_workspace_size_for(d, toks);
@@ -394,7 +506,8 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   char* base = static_cast<char*>(ws);
 
   // one segment: records of chunks [c0, c0 + nc) in `recs`; state S_in -> S_out
-  auto launch_intra = [&](int64_t c0, int nc, const kda::ChunkWs& recs, hipStream_t st_, uint32_t* done = nullptr) {
+  auto launch_intra = [&](int64_t c0, int nc, const kda::ChunkWs& recs, hipStream_t st_, uint32_t* done = nullptr,
+                          int rec_stride = 0, int rec_c0 = 0) {
     kda::IntraParams ip{};
     ip.q = q;
     ip.k = k;
@@ -413,13 +526,15 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     ip.decay = d->decay;
     ip.ws = recs;
     ip.done = done;
+    ip.rec_stride = rec_stride;
+    ip.rec_c0 = rec_c0;
     tr.before(st_);
     const kda_status r = check_launch(kda::launch_intra(ip, D, in_f32, st_), st_);
     tr.after(st_);
     return r;
   };
   auto launch_scan = [&](int64_t c0, int nc, const kda::ChunkWs& recs, const float* S_in, float* S_out,
-                         hipStream_t st_, const uint32_t* done = nullptr) {
+                         hipStream_t st_, const uint32_t* done = nullptr, const Plan* segs = nullptr) {
     kda::ScanParams sp{};
     sp.v = v;
     sp.gate = y ? gate : nullptr;
@@ -440,6 +555,10 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     sp.snaps = snap.n > 0 ? snap.ptr : nullptr;
     sp.snap_every = snap.every;
     sp.n_snap = snap.n;
+    if (segs != nullptr) {
+      sp.n_seg = segs->n_seg;
+      for (int i = 0; i < segs->n_seg; ++i) sp.seg_end[i] = segs->seg_end[i];
+    }
     tr.before(st_);
     const kda_status r = check_launch(kda::launch_scan(sp, D, in_f32, st_), st_);
     tr.after(st_);
@@ -488,6 +607,49 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     const kda_status r = check_launch(kda::launch_fused(ip, sp, D, in_f32, s), s);
     tr.after(s);
     return r;
+  }
+
+  // ---- pipelined schedule (see pipelined_eligible): every record in the
+  // workspace, [B H][nc_total]; intra-chunk launches per segment on one
+  // library stream, one scan launch over the sequence on the other, which
+  // waits inside the kernel for each segment's record counters (zeroed on the
+  // caller's stream first).  Launch order: intra(0), scan, intra(1), ... so
+  // that the scan is queued before the later segments' producers.
+  if (plan.pipelined) {
+    const WsLayout L = layout_for(d, nc_total);
+    DeviceCtx& c = g_dev[plan.dev];
+    std::lock_guard<std::mutex> lock(c.mu);
+    hipStream_t si = nullptr, ss = nullptr;
+    if (!stream_pair(c, plan.n_scan, &si, &ss)) return KDA_ERR_HIP;  // make_plan created the pair
+    kda::ChunkWs recs{};
+    recs.base = base + L.off_rec;
+    recs.rec_bytes = (int64_t)L.rec_bytes;
+    uint32_t* done = reinterpret_cast<uint32_t*>(base + L.off_done);
+    auto ok = [](hipError_t e) {
+      if (e == hipSuccess) return true;
+      (void)hipGetLastError();
+      return false;
+    };
+    const int64_t bh_n = (int64_t)d->B * d->H;
+    st = check_launch(kda::launch_copy_state(nullptr, reinterpret_cast<float*>(done), plan.n_seg * bh_n, s), s);
+    if (st != KDA_OK) return st;
+    if (!ok(hipEventRecord(c.fork, s)) || !ok(hipStreamWaitEvent(si, c.fork, 0)) ||
+        !ok(hipStreamWaitEvent(ss, c.fork, 0)))
+      return KDA_ERR_HIP;
+    float* S_out = S_T ? S_T : reinterpret_cast<float*>(base + L.off_carry);
+    for (int sg = 0; sg < plan.n_seg; ++sg) {
+      const int c0 = sg == 0 ? 0 : plan.seg_end[sg - 1];
+      st = launch_intra(c0, plan.seg_end[sg] - c0, recs, si, done + sg * bh_n, (int)nc_total, c0);
+      if (st != KDA_OK) return st;
+      if (sg == 0) {
+        st = launch_scan(0, (int)nc_total, recs, S0, S_out, ss, done, &plan);
+        if (st != KDA_OK) return st;
+      }
+    }
+    if (!ok(hipEventRecord(c.join_intra, si)) || !ok(hipEventRecord(c.join_scan, ss)) ||
+        !ok(hipStreamWaitEvent(s, c.join_intra, 0)) || !ok(hipStreamWaitEvent(s, c.join_scan, 0)))
+      return KDA_ERR_HIP;
+    return KDA_OK;
   }
 
   // ---- overlapped schedule: intra(s + 1) on one stream while scan(s) runs on

@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
   const int tid = threadIdx.x;
   const int tok0 = p.t0 + c * kChunk;
   const int nvalid = min(kChunk, p.T - tok0);
-  const int64_t rec = ((int64_t)b * p.H + h) * p.nc + c;
+  const int64_t stride = p.rec_stride > 0 ? p.rec_stride : p.nc;
+  const int64_t rec = ((int64_t)b * p.H + h) * stride + p.rec_c0 + c;
   constexpr RecUnits RU = rec_units((int)sizeof(T), D);
   char* recp = p.ws.base + rec * p.ws.rec_bytes;
 

@@ -79,7 +79,16 @@ struct IntraParams {
   int decay;       // 0: K3 bounded map; 1: Kimi Linear softplus map (pairwise diagonal blocks)
   ChunkWs ws;
   uint32_t* done;  // [B * H] finished records of each (b, h) in the segment (count_record), or nullptr
+  // Record of chunk c of the segment: ((b H + h) rec_stride + rec_c0 + c).
+  // rec_stride = 0 means nc (records of this segment only, rec_c0 = 0).
+  int rec_stride, rec_c0;
 };
+
+// Segment table of a scan launch that covers several intra-chunk launches
+// (the pipelined schedule): segment s holds the launch's chunks
+// [seg_end[s - 1], seg_end[s]) (seg_end[-1] = 0), and its records are
+// complete once done[s B H + b H + h] reaches seg_end[s] - seg_end[s - 1].
+constexpr int kMaxSegs = 48;
 
 struct ScanParams {
   const void* v;        // [B, T, H, D], or nullptr for V = 0 (the transfer of a segment, see kda_chunk_fwd_kcp)
@@ -98,6 +107,12 @@ struct ScanParams {
   float* snaps;         // [B, n_snap, H, D, D] states at every snap_every-th chunk boundary, or nullptr
   int snap_every;       // chunks between snapshots (snapshot j: state after chunk (j + 1) * snap_every - 1)
   int n_snap;
+  // Pipelined schedule (specialised scan kernel only): n_seg > 0 segments of
+  // records produced by intra-chunk launches running beside this one; done
+  // then holds one counter per (segment, b, h) (see kMaxSegs).  n_seg = 0:
+  // all records exist, or done (if not nullptr) is one counter per (b, h).
+  int n_seg;
+  int seg_end[kMaxSegs];
 };
 
 // Whether the state after chunk `cg` (global index) is snapshot j, and which.

@@ -455,7 +455,8 @@ struct WsLds {
   static constexpr int GS = VS + 64 * PQ;      // gate slab [64][PQ]
   static constexpr int PO = D + 4;
   static constexpr int OT = GS + 64 * PQ;      // output tile [64][PO] fp32
-  static constexpr int BYTES = OT + 64 * PO * 4;
+  static constexpr int FLAG = OT + 64 * PO * 4;  // outcome of the record waits (int)
+  static constexpr int BYTES = FLAG + 16;
   static constexpr RecUnits RU = rec_units(ES, D);
   static constexpr int VPR = D * ES / 16;      // 16-byte units per slab row
   static constexpr int SLAB_UNITS = 64 * VPR;
@@ -490,15 +491,31 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
   const int64_t tok_stride = (int64_t)p.H * D;
   const int64_t head_base = ((int64_t)b * p.T * p.H + h) * D;
 
-  // Records of a producer running at the same time (the overlapped
-  // schedule): the first helper wave waits until all are written; the
-  // barrier orders every wave's record loads after that.  The outcome goes
-  // through the output tile's first word (free until step 0 ends).
+  // Records of a producer running at the same time: the first helper wave
+  // waits until they are written, and a workgroup barrier orders every
+  // wave's record loads after that.  The overlapped schedule waits here for
+  // the whole launch; the pipelined schedule waits here for the segments of
+  // chunks 0 and 1 (the prologue loads) and, in the helper loop, for each
+  // later segment two chunk steps before its first record is loaded.  The
+  // outcome goes through an LDS word; a wait that gave up poisons what the
+  // helpers stage from then on (and no later wait is made).
+  auto seg_start = [&](int s) { return s == 0 ? 0 : p.seg_end[s - 1]; };
+  auto seg_done = [&](int s) { return p.done + ((int64_t)s * p.B * p.H + bh); };
+  int* gave_up = reinterpret_cast<int*>(lds + L::FLAG);
+  int wseg = 0;  // segments waited for (pipelined schedule); uniform
+  if (p.n_seg > 0) {
+    const int first = min(1, p.nc - 1);
+    while (wseg < p.n_seg && seg_start(wseg) <= first) ++wseg;
+  }
   bool poison = false;
   if (p.done != nullptr) {
-    int* gave_up = reinterpret_cast<int*>(lds + L::OT);
     if (wave == L::NCW) {
-      const bool ok = wait_records(p.done + bh, (uint32_t)p.nc);
+      bool ok = true;
+      if (p.n_seg == 0) {
+        ok = wait_records(p.done + bh, (uint32_t)p.nc);
+      } else {
+        for (int s = 0; s < wseg && ok; ++s) ok = wait_records(seg_done(s), (uint32_t)(p.seg_end[s] - seg_start(s)));
+      }
       if (lane == 0) *gave_up = ok ? 0 : 1;
     }
     __syncthreads();
@@ -642,7 +659,17 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
       commit_B();                                        // part B of chunk c
       load_B(min(c + 1, cl));
       if (c > 0) epilogue(c - 1, std::false_type{});     // tile and gate logits of chunk c - 1
+      // pipelined schedule: chunk c + 2 (loaded in the second half) opens a segment
+      const bool opens = wseg < p.n_seg && c + 2 <= cl && c + 2 == seg_start(wseg);
+      if (opens && wave == L::NCW && !poison) {
+        const bool ok = wait_records(seg_done(wseg), (uint32_t)(p.seg_end[wseg] - seg_start(wseg)));
+        if (lane == 0) *gave_up = ok ? 0 : 1;
+      }
       __syncthreads();
+      if (opens) {
+        ++wseg;
+        poison = poison || *gave_up != 0;
+      }
       // second half: the compute waves read part B of chunk c and write tile c
       commit_A(min(c + 1, cl));
       if (gated) commit_G();                             // gate logits of chunk c

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
   KDA_OK = 0,
@@ -69,8 +69,13 @@ typedef enum { KDA_DECAY_K3 = 0, KDA_DECAY_SOFTPLUS = 1 } kda_decay;
 typedef enum {
   KDA_SCHEDULE_SEGMENTS = 0,   /* intra-chunk kernel, then scan, segment after segment */
   KDA_SCHEDULE_OVERLAPPED = 1, /* the two kernels of consecutive segments overlapped   */
-  KDA_SCHEDULE_FUSED = 2       /* one fused kernel, chunk records kept in LDS          */
+  KDA_SCHEDULE_FUSED = 2,      /* one fused kernel, chunk records kept in LDS          */
+  KDA_SCHEDULE_PIPELINED = 3   /* every record in the workspace: intra-chunk launches
+                                  per segment beside one scan launch over the sequence */
 } kda_schedule;
+
+/* Kernel launches that kda_chunk_fwd_traced times (kda_chunk_fwd_launches). */
+typedef enum { KDA_LAUNCH_INTRA = 0, KDA_LAUNCH_SCAN = 1, KDA_LAUNCH_FUSED = 2 } kda_launch_kind;
 
 typedef enum {
   KDA_LAYOUT_KV = 0, /* user state is [d_k][d_v], same as the pool               */
@@ -117,11 +122,15 @@ kda_status kda_desc_init(kda_desc* d, int32_t B, int32_t T, int32_t H, int32_t h
 
 /* Workspace bytes for kda_chunk_fwd's preferred schedule; 0 if *d is invalid.
  * The fused schedule needs none (256 is reported; ws may also be NULL then).
- * With d->overlap and a sequence longer than one segment this holds two
- * segments of chunk records (the overlapped schedule); otherwise it holds the
- * whole sequence (at most 65536 tokens per segment).  A smaller workspace also
- * works as long as it holds one chunk: the sequence is then processed in more,
- * shorter segments, one after the other. */
+ * With d->overlap, bf16 inputs and more than 1,024 tokens this holds every
+ * chunk record of the call (the pipelined schedule: 66,048 bytes per chunk and
+ * (b, h) at d = 128, e.g. 6.5 GB for B 1, T 65,536, H 96) as long as that is at
+ * most 8 GiB; otherwise, with d->overlap and a sequence longer than one
+ * segment, it holds two segments of chunk records (the overlapped schedule),
+ * and else the whole sequence (at most 65536 tokens per segment).  A smaller
+ * workspace also works as long as it holds one chunk: the library then takes
+ * the overlapped schedule if two segments fit, else it processes the sequence
+ * in shorter segments, one after the other. */
 size_t kda_chunk_fwd_workspace_size(const kda_desc* d);
 
 /* Bytes needed for one segment of `segment_tokens` tokens (rounded up to whole
@@ -146,6 +155,16 @@ kda_status kda_release_resources(void);
  */
 kda_status kda_chunk_fwd_schedule(const kda_desc* d, size_t ws_bytes, int32_t* segment_tokens,
                                   int32_t* schedule);
+
+/* The kernel launches, in order, that kda_chunk_fwd_traced brackets with
+ * events for this descriptor and workspace size on the current device:
+ * *n_launches receives their number and kinds[i] (i < max_kinds) the
+ * kda_launch_kind of the i-th.  Segments and overlapped: per segment the
+ * intra-chunk kernel, then the scan; pipelined: intra-chunk kernel of segment
+ * 0, the scan (one launch), then the intra-chunk kernels of segments 1, 2, ...;
+ * fused: one launch.  kinds may be NULL when max_kinds is 0. */
+kda_status kda_chunk_fwd_launches(const kda_desc* d, size_t ws_bytes, int32_t* kinds, int32_t max_kinds,
+                                  int32_t* n_launches);
 
 /*
  * Chunked KDA forward over whole sequences (prefill / training forward),
@@ -186,6 +205,16 @@ kda_status kda_chunk_fwd_schedule(const kda_desc* d, size_t ws_bytes, int32_t* s
  * start and the end of the call.  The call still behaves as one operation
  * enqueued on `stream`.  Calls that overlap in time on one device serialise
  * their enqueue (a per-device lock); they must not share a workspace.
+ *
+ * Pipelined schedule (the same conditions, bf16 inputs, more than 16 chunks,
+ * and a workspace that holds every chunk record of the call): the intra-chunk
+ * kernel runs segment by segment on one library stream (segments of 16, 16,
+ * 24, 32, 48, 64 and 96 chunks, then d->segment_tokens each) and a single
+ * scan launch over the whole sequence runs on the other, waiting inside the
+ * kernel for each segment's records (device-scope record stores, one counter
+ * per segment and (b, h); bounded waits, so a producer that never runs shows
+ * as NaN output, not a hang).  Results are bit-identical to the other
+ * two-kernel schedules.
  */
 kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
                          const void* z, const float* A, const float* S0, const void* gate, const float* rms_w,
@@ -193,9 +222,8 @@ kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const 
 
 /*
  * kda_chunk_fwd with per-kernel timing: identical work and results, and in
- * addition, for the i-th kernel launch of the call (launch order per segment:
- * the intra-chunk kernel, then the state scan with the fused gate; the fused
- * schedule has one launch),
+ * addition, for the i-th kernel launch of the call (the order that
+ * kda_chunk_fwd_launches reports),
  * hipEventRecord(events[2i]) right before it and hipEventRecord(events[2i+1])
  * right after it on the stream that launch uses (`stream`, or the library's
  * stream of that kernel in the overlapped schedule), while 2i+1 < n_events.

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert {"kda_chunk_fwd", "kda_recurrent_step", "kda_state_io"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kda_abi_version() == 3
+    assert L.kda_abi_version() == 4
     assert L.kda_status_str(6) == b"workspace missing or too small"
 
 
@@ -158,6 +158,38 @@ def test_schedule_query():
     ws = L.kda_chunk_fwd_workspace_size(ctypes.byref(d2))
     assert L.kda_chunk_fwd_schedule(ctypes.byref(d2), ws, ctypes.byref(seg), ctypes.byref(sch)) == 0
     assert sch.value == 0 and seg.value == 1024
+
+
+def _launches(d, ws):
+    L = kda.lib()
+    n = ctypes.c_int32(0)
+    assert L.kda_chunk_fwd_launches(ctypes.byref(d), ws, None, 0, ctypes.byref(n)) == 0
+    kinds = (ctypes.c_int32 * max(n.value, 1))()
+    assert L.kda_chunk_fwd_launches(ctypes.byref(d), ws, kinds, n.value, ctypes.byref(n)) == 0
+    return [kinds[i] for i in range(n.value)]
+
+
+def test_workspace_and_launch_queries():
+    """Without a GPU the two-stream schedules are unavailable, so the library
+    plans the one-stream segments; the size query still offers the pipelined
+    schedule's workspace (every record) for bf16 inputs up to its cap."""
+    L = kda.lib()
+    rec = 66048                                                   # bytes per chunk record at d = 128, bf16
+    d = _desc(B=1, T=65536, H=96, fused=0)
+    ws = L.kda_chunk_fwd_workspace_size(ctypes.byref(d))
+    assert ws >= 96 * 1024 * rec and ws < 96 * 1024 * rec + (64 << 20)   # every record, plus state and counters
+    big = _desc(B=1, T=1 << 20, H=96, fused=0)                    # every record would be 104 GB: two segments
+    ws_big = L.kda_chunk_fwd_workspace_size(ctypes.byref(big))
+    assert 2 * 96 * 128 * rec <= ws_big < 2 * 96 * 128 * rec + (64 << 20)
+    f32 = _desc(B=1, T=65536, H=96, fused=0, in_dtype=kda.KDA_F32)  # fp32: no pipelined schedule
+    assert L.kda_chunk_fwd_workspace_size(ctypes.byref(f32)) < 96 * 1024 * rec
+    # launch order of the one-stream plan: (intra, scan) per segment
+    seg = L.kda_chunk_fwd_workspace_size_for(ctypes.byref(d), 8192)
+    assert _launches(d, seg) == [0, 1] * 8
+    assert _launches(_desc(T=70000, fused=2), 0) == [2]
+    n = ctypes.c_int32(0)
+    assert L.kda_chunk_fwd_launches(ctypes.byref(d), seg, None, 4, ctypes.byref(n)) == 1      # kinds NULL
+    assert L.kda_chunk_fwd_launches(ctypes.byref(d), 0, None, 0, ctypes.byref(n)) == 6        # no workspace
 
 
 def _prep(d, width=4, xq=FAKE, beta_logits=FAKE, beta=FAKE, st_in=None, st_out=None, q=FAKE):

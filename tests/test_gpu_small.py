@@ -158,7 +158,8 @@ def test_overlapped_schedule_reuses_workspace(kda):
     no counter of an earlier call lets a scan start early."""
     B, T, H, D, seg = 2, 2048, 4, 128, 64
     desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg, overlap=True, fused=False)
-    ws = torch.empty(kda.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    # two segments of records (every record would select the pipelined schedule)
+    ws = torch.empty(kda.workspace_size(desc, 2 * seg), dtype=torch.uint8, device="cuda")
     assert kda.schedule(desc, ws.numel())[1] == "overlapped"
     outs = []
     for seed in (1, 2, 3):
@@ -169,6 +170,67 @@ def test_overlapped_schedule_reuses_workspace(kda):
                           overlap=True, segment_tokens=seg, fused=False, workspace=ws)
         outs.append((x, r))
     torch.cuda.synchronize()
+    for x, r in outs:
+        one = _run(kda, x, overlap=False, fused=False)
+        for key in ("o", "y", "S_T"):
+            assert _bit_equal(one[key], r[key]), key
+
+
+@pytest.mark.parametrize("B,T,H,D,seg,opts", [
+    (1, 4096, 4, 128, 0, {}),                                   # default: segments of 16, 16, 24, ... chunks
+    (2, 3000, 3, 128, 256, {}),                                 # ragged last chunk, 4-chunk steady segments
+    (1, 2065, 2, 64, 64, {"out_dtype": torch.float32}),         # d = 64, 33 one-chunk segments, fp32 outputs
+    (3, 1100, 2, 128, 128, {"gate": False}),                    # o only; 18 chunks in 2-chunk segments
+])
+def test_pipelined_schedule_matches_one_stream(kda, B, T, H, D, seg, opts):
+    """The pipelined schedule (every chunk record in the workspace, the
+    intra-chunk kernel launched per segment on one library stream beside ONE
+    scan launch over the sequence that waits inside the kernel for each
+    segment's record counters) gives bit-identical results to the one-stream
+    schedule; the launch-order query matches what the call does."""
+    wl = _custom(B, T, H, D, "bf16", seed=B * 1000 + T)
+    x = gen_inputs(wl)
+    desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg, overlap=True, fused=False)
+    nbytes = kda.workspace_size(desc)
+    assert kda.schedule(desc, nbytes)[1] == "pipelined"
+    order = kda.launches(desc, nbytes)
+    assert order[:2] == ["intra", "scan"] and order.count("scan") == 1 and len(order) >= 3
+    log(f"[pipelined] B={B} T={T} H={H} D={D} segment={seg} launches={len(order)}")
+    one = _run(kda, x, overlap=False, fused=False, **opts)
+    pip = _run(kda, x, overlap=True, segment_tokens=seg, fused=False, **opts)
+    keys = [k for k in ("o", "y", "S_T") if k in one]
+    assert keys and all(k in pip for k in keys)
+    for key in keys:
+        assert _bit_equal(one[key], pip[key]), key
+
+
+def test_pipelined_schedule_reuses_workspace_and_traces(kda):
+    """Three consecutive pipelined calls on different inputs with one
+    workspace (counters re-zeroed by each call; 32 one-chunk segments) each
+    equal the one-stream schedule bit for bit; events bracket every launch in
+    the reported order."""
+    B, T, H, D, seg = 2, 2048, 4, 128, 64
+    desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg, overlap=True, fused=False)
+    ws = torch.empty(kda.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    assert kda.schedule(desc, ws.numel())[1] == "pipelined"
+    order = kda.launches(desc, ws.numel())
+    assert order == ["intra", "scan"] + ["intra"] * 31
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(order))]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    outs = []
+    for seed in (1, 2, 3):
+        x = gen_inputs(_custom(B, T, H, D, "bf16", seed=900 + seed))
+        log(f"[pipelined reuse] seed={seed}")
+        t = {n: dev(x[n]) for n in ("q", "k", "v", "beta", "z", "A", "gate", "S0")}
+        r = kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t["S0"], gate=t["gate"],
+                          overlap=True, segment_tokens=seg, fused=False, workspace=ws,
+                          events=[e.cuda_event for e in ev] if seed == 3 else None)
+        outs.append((x, r))
+    torch.cuda.synchronize()
+    ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(len(order))]
+    assert all(m >= 0.0 for m in ms) and ms[1] > 0.0
     for x, r in outs:
         one = _run(kda, x, overlap=False, fused=False)
         for key in ("o", "y", "S_T"):
