@@ -352,6 +352,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        "baseline_note": "the source pages give no KDA throughput figure on stated hardware; none is invented",
         "dtype": "bf16",
         "data": "synthetic (seeded; K3 layer shapes, no trained weights)",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "d_k": D, "d_v": D, "chunk": 64,

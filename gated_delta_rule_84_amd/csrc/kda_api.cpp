@@ -138,8 +138,12 @@ constexpr int64_t kRamp[] = {16, 16, 24, 32, 48, 64, 96};
 constexpr int kRampLen = sizeof(kRamp) / sizeof(kRamp[0]);
 constexpr size_t kPipelinedWorkspaceCap = size_t(8) << 30;
 
+// Like the overlapped schedule, only for sequences longer than one segment:
+// for shorter ones the intra-chunk kernel on every compute unit followed by
+// the scan is faster (B 4, T 4096, H 32: 0.55 ms one stream, 0.71 ms
+// pipelined).
 bool pipelined_eligible(const kda_desc* d) {
-  return d->overlap != 0 && d->in_dtype == KDA_BF16 && !fused_wanted(d) && num_chunks(d) > kRamp[0];
+  return d->overlap != 0 && d->in_dtype == KDA_BF16 && !fused_wanted(d) && pipe_wanted(d);
 }
 
 // Cumulative chunk ends of the pipelined schedule's segments (at most

@@ -122,7 +122,8 @@ kda_status kda_desc_init(kda_desc* d, int32_t B, int32_t T, int32_t H, int32_t h
 
 /* Workspace bytes for kda_chunk_fwd's preferred schedule; 0 if *d is invalid.
  * The fused schedule needs none (256 is reported; ws may also be NULL then).
- * With d->overlap, bf16 inputs and more than 1,024 tokens this holds every
+ * With d->overlap, bf16 inputs and a sequence longer than one segment
+ * (d->segment_tokens, default 8192) this holds every
  * chunk record of the call (the pipelined schedule: 66,048 bytes per chunk and
  * (b, h) at d = 128, e.g. 6.5 GB for B 1, T 65,536, H 96) as long as that is at
  * most 8 GiB; otherwise, with d->overlap and a sequence longer than one
@@ -206,8 +207,8 @@ kda_status kda_chunk_fwd_launches(const kda_desc* d, size_t ws_bytes, int32_t* k
  * enqueued on `stream`.  Calls that overlap in time on one device serialise
  * their enqueue (a per-device lock); they must not share a workspace.
  *
- * Pipelined schedule (the same conditions, bf16 inputs, more than 16 chunks,
- * and a workspace that holds every chunk record of the call): the intra-chunk
+ * Pipelined schedule (the same conditions, bf16 inputs, and a workspace that
+ * holds every chunk record of the call): the intra-chunk
  * kernel runs segment by segment on one library stream (segments of 16, 16,
  * 24, 32, 48, 64 and 96 chunks, then d->segment_tokens each) and a single
  * scan launch over the whole sequence runs on the other, waiting inside the

@@ -177,7 +177,7 @@ def test_overlapped_schedule_reuses_workspace(kda):
 
 
 @pytest.mark.parametrize("B,T,H,D,seg,opts", [
-    (1, 4096, 4, 128, 0, {}),                                   # default: segments of 16, 16, 24, ... chunks
+    (1, 9000, 4, 128, 0, {}),                                   # default: segments of 16, 16, 24, ..., 128 chunks
     (2, 3000, 3, 128, 256, {}),                                 # ragged last chunk, 4-chunk steady segments
     (1, 2065, 2, 64, 64, {"out_dtype": torch.float32}),         # d = 64, 33 one-chunk segments, fp32 outputs
     (3, 1100, 2, 128, 128, {"gate": False}),                    # o only; 18 chunks in 2-chunk segments
