@@ -236,8 +236,9 @@ def main() -> int:
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(every box here has a single MI355X). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(heads and sequence would shard as described in the design notes). Run with --gpus 1.",
+              file=sys.stderr)
         return 2
 
     import numpy as np
