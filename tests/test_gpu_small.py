@@ -135,8 +135,12 @@ def test_overlapped_schedule_matches_one_stream(kda, B, T, H, D, seg):
     wl = _custom(B, T, H, D, "bf16", seed=B * 100 + T)
     x = gen_inputs(wl)
     log(f"[overlap] B={B} T={T} H={H} D={D} segment={seg}")
+    # two segments of records (every record would select the pipelined schedule)
+    desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg, overlap=True, fused=False)
+    ws = torch.empty(kda.workspace_size(desc, 2 * seg), dtype=torch.uint8, device="cuda")
+    assert kda.schedule(desc, ws.numel())[1] == "overlapped"
     one = _run(kda, x, overlap=False, fused=False)
-    two = _run(kda, x, overlap=True, segment_tokens=seg, fused=False)
+    two = _run(kda, x, overlap=True, segment_tokens=seg, fused=False, workspace=ws)
     for key in ("o", "y", "S_T"):
         assert _bit_equal(one[key], two[key]), key
     # work enqueued on the caller's stream after the call sees the finished
@@ -144,7 +148,7 @@ def test_overlapped_schedule_matches_one_stream(kda, B, T, H, D, seg):
     t = {n: dev(x[n]) for n in ("q", "k", "v", "beta", "z", "A", "gate", "S0")}
     torch.cuda.synchronize()
     r = kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t["S0"], gate=t["gate"],
-                      overlap=True, segment_tokens=seg, fused=False)
+                      overlap=True, segment_tokens=seg, fused=False, workspace=ws)
     snap = {key: val.clone() for key, val in r.items()}  # on the current stream
     torch.cuda.current_stream().synchronize()
     for key in ("o", "y", "S_T"):

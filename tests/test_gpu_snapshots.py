@@ -71,12 +71,20 @@ def test_snapshots_match_oracle_prefix_states(kda, B, T, H, D, dtype, every):
         assert torch.equal(r["snapshots"][:, -1], r["S_T"])
 
 
-@pytest.mark.parametrize("fused,overlap,seg", [(True, True, None), (False, False, None), (False, True, 128)])
-def test_resume_from_snapshot_is_bit_identical(kda, fused, overlap, seg):
+@pytest.mark.parametrize("fused,overlap,seg,sched", [(True, True, None, "fused"), (False, False, None, "segments"),
+                                                     (False, True, 128, "pipelined"), (False, True, 128, "overlapped")])
+def test_resume_from_snapshot_is_bit_identical(kda, fused, overlap, seg, sched):
     B, T, H, D, every = 2, 900, 3, 128, 3
     x = gen_inputs(_wl(B, T, H, D, "bf16", seed=17))
     t = {n: dev(x[n]) for n in NAMES + ("A", "S0")}
     kw = dict(overlap=overlap, segment_tokens=seg, fused=fused)
+    if sched == "overlapped":  # two segments of records: the double-buffered schedule
+        desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg, overlap=True, fused=False)
+        kw["workspace"] = torch.empty(kda.workspace_size(desc, 2 * seg), dtype=torch.uint8, device="cuda")
+        assert kda.schedule(desc, kw["workspace"].numel())[1] == "overlapped"
+    elif sched == "pipelined":
+        desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg, overlap=True, fused=False)
+        assert kda.schedule(desc, kda.workspace_size(desc))[1] == "pipelined"
     plain = _fwd(kda, t, t["S0"], **kw)
     full = _fwd(kda, t, t["S0"], snapshot_chunks=every, **kw)
     for key in ("o", "y", "S_T"):
