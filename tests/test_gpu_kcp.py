@@ -60,6 +60,31 @@ def test_kcp_matches_oracle_and_one_pass(kda, B, T, H, D, dtype, P, weak):
         assert e_one <= (3e-3 if dtype == "bf16" else 1e-5), n
 
 
+@pytest.mark.parametrize("seg,sched", [(64, "pipelined"), (128, "pipelined"), (None, "segments")])
+def test_kcp_inner_schedules_are_bit_identical(kda, seg, sched):
+    """KCP's passes run the forward over B * P sequences of T / P tokens; with
+    short internal segments that forward takes the pipelined schedule (one
+    scan launch waiting in-kernel per segment, with V = 0 in the transfer
+    pass), otherwise one stream.  The results are bit-identical either way."""
+    B, T, H, D, P = 2, 1536, 3, 128, 3
+    desc = kda.make_desc(B * P, T // P, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg or 0, fused=False)
+    assert kda.schedule(desc, kda.workspace_size(desc))[1] == sched
+    wl = Workload("kcp_sched", 77, B=B, T=T, H=H, D=D, dtype="bf16", z_std=2.0, A_kind="uniform", gate=True,
+                  s0_std=0.1)
+    x = gen_inputs(wl)
+    t = {n: dev(x[n]) for n in ("q", "k", "v", "beta", "z", "A", "gate", "S0")}
+    args = (t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"])
+    log(f"[kcp schedule] segment_tokens={seg} inner={sched}")
+    ref = kda.chunk_fwd(*args, S0=t["S0"], gate=t["gate"], kcp_parts=P, overlap=False, fused=False)
+    got = kda.chunk_fwd(*args, S0=t["S0"], gate=t["gate"], kcp_parts=P, segment_tokens=seg, fused=False)
+    torch.cuda.synchronize()
+    for n in ("o", "y", "S_T"):
+        a, b = ref[n], got[n]
+        if a.dtype == torch.bfloat16:
+            a, b = a.view(torch.int16), b.view(torch.int16)
+        assert torch.equal(a, b), n
+
+
 def test_kcp_rejects_unaligned_segments(kda):
     import ctypes
     desc = kda.make_desc(1, 500, 2, 64, kda.KDA_BF16, kda.KDA_BF16)
