@@ -978,6 +978,7 @@ kda_status kda_state_io(kda_state_op op, int32_t n, int32_t H, int32_t d_k, int3
   p.pool = pool;
   p.slot = slot;
   p.user = user;
+  p.vec16 = aligned(pool, 16) && (user == nullptr || aligned(user, 16));
   return check_launch(kda::launch_state_io(p, d_k, s), s);
 }
 

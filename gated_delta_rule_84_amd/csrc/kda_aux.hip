@@ -16,15 +16,33 @@ __global__ __launch_bounds__(256) void kda_state_io_kernel(const StateIoParams p
   const int64_t slot = (p.slot != nullptr) ? (int64_t)p.slot[n] : (int64_t)n;
   float* pool = p.pool + (slot * p.H + h) * D * D;
   float* user = (p.user != nullptr) ? p.user + ((int64_t)n * p.H + h) * D * D : nullptr;
-  if (p.op == 0) {
-    for (int i = tid; i < D * D; i += 256) pool[i] = 0.f;
-    return;
-  }
-  if (!p.transpose) {
-    if (p.op == 1)
+  // Same layout: a copy of the head's D x D floats in 16-byte vectors (each
+  // element is read and written by the same thread, so an in-place call is
+  // still exact); element by element when a pointer is only 4-byte aligned.
+  // Measured on the decode pool (256 x 96 states): 5.3 TB/s against 4.8 TB/s
+  // element by element, and 3.7 TB/s with all of a thread's 16 loads issued
+  // before its stores.
+  constexpr int N4 = D * D / 4 / 256;  // 16-byte vectors per thread
+  if (!p.vec16 && (p.op == 0 || !p.transpose)) {
+    if (p.op == 0)
+      for (int i = tid; i < D * D; i += 256) pool[i] = 0.f;
+    else if (p.op == 1)
       for (int i = tid; i < D * D; i += 256) pool[i] = user[i];
     else
       for (int i = tid; i < D * D; i += 256) user[i] = pool[i];
+    return;
+  }
+  if (p.op == 0) {
+    float4* d4 = reinterpret_cast<float4*>(pool);
+#pragma unroll
+    for (int j = 0; j < N4; ++j) d4[tid + 256 * j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  if (!p.transpose) {
+    const float4* s4 = reinterpret_cast<const float4*>(p.op == 1 ? user : pool);
+    float4* d4 = reinterpret_cast<float4*>(p.op == 1 ? pool : user);
+#pragma unroll 4
+    for (int j = 0; j < N4; ++j) d4[tid + 256 * j] = s4[tid + 256 * j];
     return;
   }
   // transposed user layout [d_v][d_k]: 32x32 tiles through LDS

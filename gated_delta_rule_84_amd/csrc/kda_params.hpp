@@ -149,6 +149,7 @@ struct StateIoParams {
   float* pool;
   const int32_t* slot;
   float* user;
+  int vec16;       // pool and user (if any) 16-byte aligned: copy in 16-byte vectors
 };
 
 struct PrepassParams {

@@ -359,6 +359,41 @@ def test_state_io_layouts(kda):
     assert torch.all(pool[1] == 7.0) and torch.all(pool[3] == 7.0)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_state_io_vector_and_element_paths(kda, D):
+    """Same-layout import / export / zero: 16-byte vectors when both pointers
+    are 16-byte aligned, element by element when one is only 4-byte aligned
+    (buffers offset by one float); both give exact copies."""
+    H = 3
+    user = torch.randn((4, H, D, D), device="cuda")
+    pool = torch.randn((6, H, D, D), device="cuda")
+    keep = pool.clone()
+    slot = torch.tensor([5, 1, 3, 0], dtype=torch.int32, device="cuda")
+
+    def offset(shape):  # a view whose data pointer is 4 bytes past a 256-byte boundary
+        flat = torch.empty(int(np.prod(shape)) + 1, device="cuda")
+        return flat[1:].view(shape)
+
+    kda.state_io(kda.STATE_IMPORT, pool, user=user, slot=slot)
+    out = torch.empty_like(user)
+    kda.state_io(kda.STATE_EXPORT, pool, user=out, slot=slot)
+    p1, u1, out1 = offset(pool.shape), offset(user.shape), offset(user.shape)
+    assert p1.data_ptr() % 16 == 4
+    p1.copy_(keep)
+    u1.copy_(user * 2)
+    kda.state_io(kda.STATE_IMPORT, p1, user=u1, slot=slot)
+    kda.state_io(kda.STATE_EXPORT, p1, user=out1, slot=slot)
+    kda.state_io(kda.STATE_ZERO, p1, slot=slot[:2], n=2)
+    kda.state_io(kda.STATE_ZERO, pool, slot=slot[2:], n=2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, user) and torch.equal(out1, user * 2)
+    for i, r in enumerate(slot.tolist()):
+        assert torch.equal(pool[r], torch.zeros_like(pool[r]) if i >= 2 else user[i])
+        assert torch.equal(p1[r], torch.zeros_like(p1[r]) if i < 2 else user[i] * 2)
+    for r in (2, 4):  # rows no slot names are untouched
+        assert torch.equal(pool[r], keep[r]) and torch.equal(p1[r], keep[r])
+
+
 def test_fused_with_heads_filling_the_device(kda):
     """B * H at the CU count: left to the library a two-kernel schedule is
     taken; the forced fused kernel gives the same results bit for bit."""
