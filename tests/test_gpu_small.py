@@ -185,6 +185,8 @@ def test_overlapped_schedule_reuses_workspace(kda):
     (2, 3000, 3, 128, 256, {}),                                 # ragged last chunk, 4-chunk steady segments
     (1, 2065, 2, 64, 64, {"out_dtype": torch.float32}),         # d = 64, 33 one-chunk segments, fp32 outputs
     (3, 1100, 2, 128, 128, {"gate": False}),                    # o only; 18 chunks in 2-chunk segments
+    (2, 1300, 3, 128, 192, {"S0": False}),                      # zero initial state, 3-chunk segments
+    (1, 2000, 2, 128, 128, {"want_state": False}),              # no S_T: the scan ends in the workspace
 ])
 def test_pipelined_schedule_matches_one_stream(kda, B, T, H, D, seg, opts):
     """The pipelined schedule (every chunk record in the workspace, the
