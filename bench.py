@@ -263,7 +263,6 @@ def main() -> int:
     kda.lib()
 
     t_gen = time.perf_counter()
-    x = gen_inputs(wl)
 
     def to_dev(a):
         a = np.ascontiguousarray(a)
@@ -271,8 +270,27 @@ def main() -> int:
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    t = {k: to_dev(v) for k, v in x.items()}
-    del x
+    slab = 65536
+    if wl.T > slab and wl.T % slab == 0:
+        # long sequences: the same seeded values, generated slab by slab straight
+        # into the device tensors (the whole host copy would be ~150 GB at 1M tokens)
+        t = {}
+        for t0 in range(0, wl.T, slab):
+            x = gen_inputs(wl, time=(t0, slab))
+            for k, v in x.items():
+                if k in ("A", "S0"):
+                    t.setdefault(k, to_dev(v))
+                    continue
+                if k not in t:
+                    t[k] = torch.empty((wl.B, wl.T) + v.shape[2:],
+                                       dtype=torch.bfloat16 if v.dtype == np.uint16 else torch.float32, device=dev)
+                t[k][:, t0:t0 + slab].copy_(to_dev(v))
+            del x
+            print(f"inputs: tokens {t0 + slab}/{wl.T}", file=sys.stderr, flush=True)
+    else:
+        x = gen_inputs(wl)
+        t = {k: to_dev(v) for k, v in x.items()}
+        del x
     t_gen = time.perf_counter() - t_gen
     B, T, H, D = wl.B, wl.T, wl.H, wl.D
     token_heads = B * T * H
@@ -286,6 +304,8 @@ def main() -> int:
                          overlap=overlap, fused=fused, decay=args.decay)
     if args.schedule == "overlapped":   # two segments of records: the double-buffered schedule
         ws_bytes = kda.workspace_size(desc, 2 * (seg_arg or 8192))
+    elif args.schedule == "pipelined":  # every record of the call (also past the size query's cap)
+        ws_bytes = kda.workspace_size(desc, T)
     elif overlap or fused or not seg_arg:
         ws_bytes = kda.workspace_size(desc)
     else:
