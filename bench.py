@@ -4,12 +4,15 @@ One step = one kda_chunk_fwd call over the K3-shaped layer workload
 (B1, T65536, H96, d128, bf16 inputs, fp32 state, output gate, y and S_T
 outputs), inputs already resident in HBM.  Prints ONE JSON line.
 
-The library picks the schedule (the overlapped two-kernel schedule for
-sequences longer than one segment); --schedule forces one (the fused kernel
-measured slower at every size tried).  Per-kernel durations come from HIP events
-recorded by the library around each of its launches on the launch stream
-(kda_chunk_fwd_traced); the dominant kernel's roofline uses its algorithmic
-bytes:
+The library picks the schedule for the workspace the size query offers (the
+pipelined two-kernel schedule for long sequences: every chunk record resident,
+one scan launch; two-segment records beyond the query's cap); --schedule
+forces one (the fused kernel measured slower at every size tried).
+--workload selects another configuration (long ones are generated slab by
+slab on the device).  Per-kernel durations come from HIP events recorded by
+the library around each of its launches on the launch stream
+(kda_chunk_fwd_traced, in the order kda_chunk_fwd_launches reports); the
+dominant kernel's roofline uses its algorithmic bytes:
   fused       : q, k, z, v, gate logits (5 * 2d B) + beta (2 B) in, y out
                 (2d B) per token-head, + initial and final state
   intra-chunk : q, k, z (3 * 2d B) + beta (2 B) per token-head
