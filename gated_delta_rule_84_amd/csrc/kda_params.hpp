@@ -88,7 +88,7 @@ struct IntraParams {
 // (the pipelined schedule): segment s holds the launch's chunks
 // [seg_end[s - 1], seg_end[s]) (seg_end[-1] = 0), and its records are
 // complete once done[s B H + b H + h] reaches seg_end[s] - seg_end[s - 1].
-constexpr int kMaxSegs = 48;
+constexpr int kMaxSegs = 128;
 
 struct ScanParams {
   const void* v;        // [B, T, H, D], or nullptr for V = 0 (the transfer of a segment, see kda_chunk_fwd_kcp)

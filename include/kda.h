@@ -95,7 +95,8 @@ typedef struct {
   kda_dtype in_dtype;    /* q, k, v, beta, z, gate                                 */
   kda_dtype out_dtype;   /* o, y                                                   */
   int32_t segment_tokens; /* tokens per internal segment of the overlapped
-                             schedule; 0: library default (8192)                */
+                             and pipelined schedules; 0: library default
+                             (8192 overlapped, 4096 pipelined)               */
   int32_t overlap;       /* 1: run the intra-chunk kernel of the next segment
                             concurrently with the scan of the current one
                             (library-owned streams, see kda_chunk_fwd); 0: one
@@ -210,7 +211,8 @@ kda_status kda_chunk_fwd_launches(const kda_desc* d, size_t ws_bytes, int32_t* k
  * Pipelined schedule (the same conditions, bf16 inputs, and a workspace that
  * holds every chunk record of the call): the intra-chunk
  * kernel runs segment by segment on one library stream (segments of 16, 16,
- * 24, 32, 48, 64 and 96 chunks, then d->segment_tokens each) and a single
+ * 24, 32, 48, 64 and 96 chunks, each at most the steady length, then
+ * d->segment_tokens each, 4096 by default) and a single
  * scan launch over the whole sequence runs on the other, waiting inside the
  * kernel for each segment's records (device-scope record stores, one counter
  * per segment and (b, h); bounded waits, so a producer that never runs shows
