@@ -181,7 +181,7 @@ def test_overlapped_schedule_reuses_workspace(kda):
 
 
 @pytest.mark.parametrize("B,T,H,D,seg,opts", [
-    (1, 9000, 4, 128, 0, {}),                                   # default: segments of 16, 16, 24, ..., 128 chunks
+    (1, 9000, 4, 128, 0, {}),                                   # default: segments of 16, 16, 24, 32, 48, 5 chunks
     (2, 3000, 3, 128, 256, {}),                                 # ragged last chunk, 4-chunk steady segments
     (1, 2065, 2, 64, 64, {"out_dtype": torch.float32}),         # d = 64, 33 one-chunk segments, fp32 outputs
     (3, 1100, 2, 128, 128, {"gate": False}),                    # o only; 18 chunks in 2-chunk segments
@@ -207,6 +207,24 @@ def test_pipelined_schedule_matches_one_stream(kda, B, T, H, D, seg, opts):
     keys = [k for k in ("o", "y", "S_T") if k in one]
     assert keys and all(k in pip for k in keys)
     for key in keys:
+        assert _bit_equal(one[key], pip[key]), key
+
+
+def test_pipelined_segment_table_overflow(kda):
+    """More segments than the scan's 128-entry table: 201 chunks (ragged) in
+    one-chunk segments become 7 ramp segments of one chunk and 97 of two, and
+    the results still equal the one-stream schedule bit for bit."""
+    B, T, H, D, seg = 1, 64 * 201 - 30, 2, 64, 64
+    x = gen_inputs(_custom(B, T, H, D, "bf16", seed=4201))
+    desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg, overlap=True, fused=False)
+    nbytes = kda.workspace_size(desc)
+    assert kda.schedule(desc, nbytes)[1] == "pipelined"
+    order = kda.launches(desc, nbytes)
+    assert order.count("scan") == 1 and order.count("intra") == 7 + 97, len(order)
+    log(f"[pipelined overflow] T={T} launches={len(order)}")
+    one = _run(kda, x, overlap=False, fused=False)
+    pip = _run(kda, x, overlap=True, segment_tokens=seg, fused=False)
+    for key in ("o", "y", "S_T"):
         assert _bit_equal(one[key], pip[key]), key
 
 
