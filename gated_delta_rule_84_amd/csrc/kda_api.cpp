@@ -277,11 +277,12 @@ Plan make_plan(const kda_desc* d, size_t ws_bytes) {
   }
   int dev = 0, n_scan = 0;
   if (pipelined_eligible(d) && ws_bytes >= layout_for(d, nc_total).total && two_streams(d, &dev, &n_scan)) {
-    p.seg_nc = pipelined_chunks(d);
     p.pipelined = true;
     p.dev = dev;
     p.n_scan = n_scan;
     p.n_seg = segment_table(d, p.seg_end);
+    for (int s = 0; s < p.n_seg; ++s)  // reported: the longest segment (steady ones may be lengthened)
+      p.seg_nc = std::max<int64_t>(p.seg_nc, p.seg_end[s] - (s > 0 ? p.seg_end[s - 1] : 0));
     return p;
   }
   if (pipe_wanted(d) && ws_bytes >= layout_for(d, 2 * pipe_chunks(d)).total && two_streams(d, &dev, &n_scan)) {

@@ -152,7 +152,8 @@ kda_status kda_release_resources(void);
  * The schedule kda_chunk_fwd takes on the current device for this descriptor
  * and a workspace of ws_bytes bytes: *segment_tokens receives the tokens per
  * segment (a multiple of the chunk; the whole sequence for the fused
- * schedule), *schedule a kda_schedule value.  KDA_ERR_WORKSPACE if a
+ * schedule, the longest segment for the pipelined one), *schedule a
+ * kda_schedule value.  KDA_ERR_WORKSPACE if a
  * two-kernel schedule is taken and the workspace is too small for one chunk.
  */
 kda_status kda_chunk_fwd_schedule(const kda_desc* d, size_t ws_bytes, int32_t* segment_tokens,

@@ -218,7 +218,7 @@ def test_pipelined_segment_table_overflow(kda):
     x = gen_inputs(_custom(B, T, H, D, "bf16", seed=4201))
     desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg, overlap=True, fused=False)
     nbytes = kda.workspace_size(desc)
-    assert kda.schedule(desc, nbytes)[1] == "pipelined"
+    assert kda.schedule(desc, nbytes) == (128, "pipelined")
     order = kda.launches(desc, nbytes)
     assert order.count("scan") == 1 and order.count("intra") == 7 + 97, len(order)
     log(f"[pipelined overflow] T={T} launches={len(order)}")
