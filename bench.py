@@ -18,6 +18,9 @@ dominant kernel's roofline uses its algorithmic bytes:
   intra-chunk : q, k, z (3 * 2d B) + beta (2 B) per token-head
   state scan  : v, gate logits in, y out (3 * 2d B) per token-head + final state
 i.e. the path's 1,538 B per token-head (2d = 256 B at d = 128).
+Side measurements (skipped with their --no-* flags): the same forward
+without the output gate (o and S_T out, 1,282 B per token-head; sequences up
+to 65,536 tokens), the input steps, the decode step and the state export.
 The CPU baseline is the fp64 C oracle timed on a bounded sample of heads.
 """
 from __future__ import annotations
@@ -232,6 +235,7 @@ def main() -> int:
     ap.add_argument("--decay", choices=("k3", "softplus"), default="k3",
                     help="decay map: K3's bounded map (the method), or Kimi Linear's softplus map (ablation)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step side measurement")
+    ap.add_argument("--no-o-only", action="store_true", help="skip the side measurement without the output gate")
     ap.add_argument("--no-input-prep", action="store_true",
                     help="skip timing the input steps (ShortConv + Swish, Sigmoid) on the workload's shapes")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -393,6 +397,29 @@ def main() -> int:
         "kernel_ms": kern_ms,
         "input_setup_s": t_gen,
     }
+    if not args.no_o_only and T <= 65536:
+        # the same forward without the output gate: o (bf16) and S_T out (skipped for
+        # the long workloads, whose extra o buffer would not fit beside the records)
+        out_o = {"o": torch.empty((B, T, H, D), dtype=odt, device=dev), "S_T": out["S_T"]}
+
+        def step_o():
+            kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t.get("S0"), out=out_o,
+                          workspace=ws, segment_tokens=seg_arg, overlap=overlap, fused=fused, decay=args.decay)
+
+        for _ in range(args.warmup):
+            step_o()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            step_o()
+        stop.record()
+        torch.cuda.synchronize()
+        ms_o = start.elapsed_time(stop) / args.steps
+        o_bytes = token_heads * (5 * 2 * D + 2) + 2 * B * H * D * D * 4  # q, k, z, v, beta in; o out; S0, S_T
+        result["o_only"] = {"ms": ms_o, "token_heads_per_s": token_heads / (ms_o * 1e-3),
+                            "algorithmic_bytes": o_bytes, "achieved_GBs": o_bytes / (ms_o * 1e-3) / 1e9,
+                            "frac_hbm": o_bytes / (ms_o * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del out_o
     if not args.no_input_prep:
         result["input_prep"] = time_input_prep(kda, t, B, T, H, D, args.steps, args.warmup, wl.name)
     if not args.no_decode:
