@@ -48,6 +48,8 @@ MUTANTS = [
      "return -np.logaddexp(0.0, z)"),
     ("softplus_as_relu", "return -np.exp(np.float64(A_h)) * np.logaddexp(0.0, z)",
      "return -np.exp(np.float64(A_h)) * np.maximum(z, 0.0)"),
+    ("q_scale_on_keys", "return q * scale, k", "return q, k * scale"),
+    ("l2norm_flag_ignored", "    if l2norm:\n        q = l2_normalize(q, eps)", "    if True:\n        q = l2_normalize(q, eps)"),
 ]
 
 

@@ -402,3 +402,90 @@ def test_c_oracle_softplus_matches_numpy():
         o, S = R.kda_recurrent(q[0, :, h], k[0, :, h], v[0, :, h], beta[0, :, h], z=z[0, :, h], A_h=A[h],
                                decay="softplus")
         assert np.allclose(rc["o"][0, :, h], o, atol=1e-12) and np.allclose(rc["S_T"][0, h], S, atol=1e-12)
+
+
+# ---- the C oracle's optional branches: RMSNorm weight, q scale, L2Norm off ----
+
+def _c_and_numpy(x, S0, g, **kw):
+    c = oracle.forward_c(x["q"], x["k"], x["v"], x["beta"], x["z"], x["A"], S0=S0, gate=g, **kw)
+    ref = R.kda_forward_heads(x["q"], x["k"], x["v"], x["beta"], x["z"], x["A"], S0=S0, gate=g,
+                              **{k: v for k, v in kw.items() if k in ("w", "scale", "l2norm")})
+    return c, ref
+
+
+@pytest.mark.parametrize("scale,l2norm", [(0.37, True), (1.0, False), (2.5, False)])
+def test_c_oracle_options_match_numpy_oracle(scale, l2norm):
+    """Section 2.1 (L2Norm on q, k; q scale, reading R5) and section 2.3 (RMSNorm
+    weight): the C twin takes the same branches as the numpy oracle."""
+    wl = WORKLOADS["tiny"]
+    x = gen_inputs(wl)
+    rng = np.random.default_rng(77)
+    if not l2norm:  # rows of norm in [0.5, 1] so that the recurrence stays bounded without L2Norm
+        for key in ("q", "k"):
+            x[key] = (x[key] * rng.uniform(0.5, 1.0, x[key].shape[:3] + (1,))).astype(np.float32)
+    g = rng.standard_normal(x["v"].shape).astype(np.float32)
+    w = rng.uniform(0.25, 2.0, (wl.H, wl.D)).astype(np.float32)
+    S0 = rng.standard_normal((wl.B, wl.H, wl.D, wl.D)) * 0.1
+    c, ref = _c_and_numpy(x, S0, g, w=w, scale=scale, l2norm=l2norm)
+    for key in ("o", "y", "S_T"):
+        np.testing.assert_allclose(c[key], ref[key], rtol=1e-11, atol=1e-12)
+
+
+def test_q_scale_is_linear_in_the_output():
+    """o_t = S_t^T (scale q_t) (section 2.1): o scales with the query scale and
+    the state does not see it, in both oracles."""
+    wl = WORKLOADS["tiny"]
+    x = gen_inputs(wl)
+    S0 = np.random.default_rng(5).standard_normal((wl.B, wl.H, wl.D, wl.D)) * 0.1
+    for fwd in (lambda **kw: oracle.forward_c(x["q"], x["k"], x["v"], x["beta"], x["z"], x["A"], S0=S0, **kw),
+                lambda **kw: R.kda_forward_heads(x["q"], x["k"], x["v"], x["beta"], x["z"], x["A"], S0=S0, **kw)):
+        a, b = fwd(scale=1.0), fwd(scale=0.125)
+        np.testing.assert_allclose(b["o"], 0.125 * a["o"], rtol=1e-13, atol=1e-15)
+        np.testing.assert_array_equal(a["S_T"], b["S_T"])
+
+
+def test_l2norm_off_on_prenormalised_rows_equals_l2norm_on():
+    """Section 2.1 puts L2Norm on q and k inside the layer: switching it off and
+    feeding rows already divided by sqrt(|x|^2 + eps) (done here with plain
+    numpy) gives the same result, in both oracles."""
+    rng = np.random.default_rng(9)
+    B, T, H, D = 1, 40, 2, 16
+    q = rng.standard_normal((B, T, H, D)) * rng.uniform(0.2, 5.0, (B, T, H, 1))
+    k = rng.standard_normal((B, T, H, D)) * rng.uniform(0.2, 5.0, (B, T, H, 1))
+    v = rng.standard_normal((B, T, H, D))
+    beta = rng.uniform(0.1, 0.9, (B, T, H))
+    z = rng.standard_normal((B, T, H, D))
+    A = rng.uniform(-1, 1, H)
+    qn = q / np.sqrt((q * q).sum(-1, keepdims=True) + 1e-6)
+    kn = k / np.sqrt((k * k).sum(-1, keepdims=True) + 1e-6)
+    f32 = lambda a: a.astype(np.float32)
+    # the C oracle reads fp32: round the inputs once and normalise the rounded values
+    q32, k32 = f32(q), f32(k)
+    qn32 = q32 / np.sqrt((q32.astype(np.float64) ** 2).sum(-1, keepdims=True) + 1e-6)
+    kn32 = k32 / np.sqrt((k32.astype(np.float64) ** 2).sum(-1, keepdims=True) + 1e-6)
+    on = R.kda_forward_heads(q, k, v, beta, z, A)
+    off = R.kda_forward_heads(qn, kn, v, beta, z, A, l2norm=False)
+    for key in ("o", "S_T"):
+        np.testing.assert_allclose(off[key], on[key], rtol=1e-12, atol=1e-13)
+    con = oracle.forward_c(q32, k32, f32(v), f32(beta), f32(z), f32(A))
+    # fp32 inputs of the normalised rows lose ~1e-8 relative; the check allows that
+    coff = oracle.forward_c(f32(qn32), f32(kn32), f32(v), f32(beta), f32(z), f32(A), l2norm=False)
+    for key in ("o", "S_T"):
+        np.testing.assert_allclose(coff[key], con[key], rtol=0, atol=1e-6 * np.abs(con[key]).max())
+    # and without normalisation the result really differs (the branch is taken)
+    raw = oracle.forward_c(q32, k32, f32(v), f32(beta), f32(z), f32(A), l2norm=False)
+    assert np.abs(raw["o"] - con["o"]).max() > 1e-2
+
+
+def test_c_oracle_rms_weight_scales_each_channel():
+    """Section 2.3 with a per-(head, channel) RMSNorm weight [H, d_v]: y(w) =
+    y(1) * w channel by channel, per head (C oracle)."""
+    wl = WORKLOADS["tiny"]
+    x = gen_inputs(wl)
+    rng = np.random.default_rng(13)
+    g = rng.standard_normal(x["v"].shape).astype(np.float32)
+    w = rng.uniform(0.25, 2.0, (wl.H, wl.D)).astype(np.float32)
+    a = oracle.forward_c(x["q"], x["k"], x["v"], x["beta"], x["z"], x["A"], gate=g)
+    b = oracle.forward_c(x["q"], x["k"], x["v"], x["beta"], x["z"], x["A"], gate=g, w=w)
+    np.testing.assert_allclose(b["y"], a["y"] * w.astype(np.float64)[None, None], rtol=1e-14, atol=1e-300)
+    np.testing.assert_array_equal(a["o"], b["o"])
