@@ -25,6 +25,8 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -67,16 +69,6 @@ __device__ __forceinline__ bf16x8 pack8_bf16(const float* x) {
   for (int j = 0; j < 8; ++j) r[j] = static_cast<__bf16>(x[j]);
   return r;
 }
-// hi = bf16(x), lo = bf16(x - hi): x ~= hi + lo to about 16 bits.
-__device__ __forceinline__ void split8_bf16(const float* x, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    __bf16 h = static_cast<__bf16>(x[j]);
-    hi[j] = h;
-    lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
-  }
-}
-
 // ---- one K=32 step: acc += A(16x32) * B(32x16) ---------------------------
 __device__ __forceinline__ f32x4 mma32(const bf16x8& a, const bf16x8& b, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
@@ -86,34 +78,12 @@ __device__ __forceinline__ f32x4 mma32(const f32x8& a, const f32x8& b, f32x4 acc
   for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc, 0, 0, 0);
   return acc;
 }
-// Three-term split product: (ah + al)(bh + bl) without the al*bl term.
-__device__ __forceinline__ f32x4 mma32_x3(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
-                                          const bf16x8& bl, f32x4 acc) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+__device__ __forceinline__ f32x4 mma32(const f16x8& a, const f16x8& b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
 }
 
 // Accumulator pair (rows 4g..4g+3 of two 16-row tiles) -> B operand in slot
 // order.
-__device__ __forceinline__ bf16x8 acc_pair_to_bf16(const f32x4& t0, const f32x4& t1) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = static_cast<__bf16>(t0[i]);
-    r[4 + i] = static_cast<__bf16>(t1[i]);
-  }
-  return r;
-}
-__device__ __forceinline__ void acc_pair_split(const f32x4& t0, const f32x4& t1, bf16x8& hi, bf16x8& lo) {
-  float x[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = t0[i];
-    x[4 + i] = t1[i];
-  }
-  split8_bf16(x, hi, lo);
-}
 __device__ __forceinline__ f32x8 acc_pair_to_f32(const f32x4& t0, const f32x4& t1) {
   f32x8 r;
 #pragma unroll
@@ -125,6 +95,67 @@ __device__ __forceinline__ f32x8 acc_pair_to_f32(const f32x4& t0, const f32x4& t
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---- precision of the chunk record and of the state scan's products --------
+// bf16 inputs: the record entries, the state and the residuals enter the
+// scan's products as fp16 (11-bit significands, round to nearest even,
+// v_cvt_pk_f16_f32), accumulated in fp32.  Every record entry is bounded:
+// |q^ . Gamma|, |k^ . Gamma|, |Kd| <= 1 (unit rows, retentions <= 1),
+// |Tril(A_qk)| <= 1 and |T Diag(beta)| <= 1 (the UT transform maps each value
+// row to the delta-rule update of a state built from the chunk's own earlier
+// rows, whose norm the unit keys and beta <= 1 bound).  The state itself is
+// unbounded in principle, so it is held scaled by a power of two, S * 2^-4:
+// q^ . Gamma and k^ . Gamma are stored times 2^4 and Kd times 2^-4, which
+// leaves every product unchanged and lets |S| reach ~1e6 before its fp16
+// copy overflows.  fp32 inputs: fp32 everywhere, no scaling.
+template <typename T>
+struct RecOps;
+template <>
+struct RecOps<uint16_t> {  // bf16 inputs
+  using Elem = uint16_t;   // fp16 bits
+  using V8 = f16x8;
+  static constexpr float kLog2Up = 4.0f;        // log2 of the factor on q^ . Gamma and k^ . Gamma
+  static constexpr float kStateScale = 0.0625f;  // the state is held as S * 2^-4
+  static __device__ __forceinline__ V8 plain(const float* x) {
+    V8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = static_cast<_Float16>(x[j]);
+    return r;
+  }
+  static __device__ __forceinline__ V8 plain_acc(const f32x4& a, const f32x4& b) {
+    V8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r[i] = static_cast<_Float16>(a[i]);
+      r[4 + i] = static_cast<_Float16>(b[i]);
+    }
+    return r;
+  }
+  // 8 values as 16 bytes (one record unit)
+  static __device__ __forceinline__ u32x4 pack8(const float* x) { return __builtin_bit_cast(u32x4, plain(x)); }
+  // 4 values as 8 bytes
+  static __device__ __forceinline__ uint2 pack4(const f32x4& x) {
+    f16x4 h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(x[i]);
+    return __builtin_bit_cast(uint2, h);
+  }
+  static __device__ __forceinline__ f32x4 mma(const V8& a, const V8& b, f32x4 acc) { return mma32(a, b, acc); }
+};
+template <>
+struct RecOps<float> {  // fp32 inputs
+  using Elem = float;
+  using V8 = f32x8;
+  static constexpr float kLog2Up = 0.0f;
+  static constexpr float kStateScale = 1.0f;
+  static __device__ __forceinline__ V8 plain(const float* x) {
+    return f32x8{x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  }
+  static __device__ __forceinline__ V8 plain_acc(const f32x4& a, const f32x4& b) { return acc_pair_to_f32(a, b); }
+  static __device__ __forceinline__ f32x4 pack4(const f32x4& x) { return x; }
+  static __device__ __forceinline__ f32x4 mma(const V8& a, const V8& b, f32x4 acc) { return mma32(a, b, acc); }
+};
+
 
 // Hardware transcendental approximations (about 1 ulp): 2^x, 1/x and
 // 1/sqrt(x).  2^x flushes results below the normal range to 0, which is the

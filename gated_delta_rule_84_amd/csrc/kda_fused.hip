@@ -43,17 +43,18 @@ struct FusedLds {
   static constexpr int NPW = 4;                // producer waves
   static constexpr int NT = 64 * (NCW + NPW);  // threads
   static constexpr int NP = 64 * NPW;          // producer threads
+  static constexpr int RS = sizeof(typename RecOps<T>::Elem);  // record element
+  static_assert(RS == ES, "one row pitch for the record and the V slab");
   static constexpr int PQ = D * ES + 16;       // row pitch of qg / kg / V slab (bytes)
-  static constexpr int PK = 64 * ES + 16;      // row pitch of kdt / tb / aqh / aql (bytes)
+  static constexpr int PK = 64 * RS + 16;      // row pitch of kdt / tb / aq (bytes)
   static constexpr int PO = D + 4;             // output tile row pitch (floats)
   // record image read by the compute waves
   static constexpr int QG = 0;
   static constexpr int KG = QG + 64 * PQ;
   static constexpr int KDT = KG + 64 * PQ;
   static constexpr int TB = KDT + D * PK;
-  static constexpr int AQH = TB + 64 * PK;
-  static constexpr int AQL = AQH + 64 * PK;
-  static constexpr int GAM = AQL + 64 * PK;
+  static constexpr int AQ = TB + 64 * PK;
+  static constexpr int GAM = AQ + 64 * PK;
   static constexpr int VS = GAM + 4 * D;       // V slab [64][PQ]
   static constexpr int OT = VS + 64 * PQ;      // output tile [64][PO] fp32
   // intra-chunk work areas (producers only)
@@ -139,8 +140,7 @@ __global__ __launch_bounds__((FusedLds<T, D>::NT), 1) void kda_fused_kernel(cons
   T* kg = reinterpret_cast<T*>(lds + L::KG);
   T* kdt = reinterpret_cast<T*>(lds + L::KDT);
   T* tb = reinterpret_cast<T*>(lds + L::TB);
-  T* aqh = reinterpret_cast<T*>(lds + L::AQH);
-  T* aql = reinterpret_cast<T*>(lds + L::AQL);
+  T* aq = reinterpret_cast<T*>(lds + L::AQ);
   float* gam = reinterpret_cast<float*>(lds + L::GAM);
   float* gams = reinterpret_cast<float*>(lds + L::GAMS);
   const float* otile = reinterpret_cast<const float*>(lds + L::OT);
@@ -210,7 +210,7 @@ __global__ __launch_bounds__((FusedLds<T, D>::NT), 1) void kda_fused_kernel(cons
     psync();
     Core::template tb_pass<L::NP>(pt, s, tb);
     ic.store_kd(kdt);
-    ic.store_aq(aqh, aql);
+    ic.store_aq(aq);
     if (pt < D) gam[pt] = gams[pt];
   };
 

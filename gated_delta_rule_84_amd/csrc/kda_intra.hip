@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
   ic.store_kd(reinterpret_cast<T*>(recp + 16 * RU.kdt));
   __syncthreads();  // column factors and the L_ii stages are visible
   ic.offdiag(s);
-  ic.store_aq(reinterpret_cast<T*>(recp + 16 * RU.aq), nullptr);  // hi and lo share units
+  ic.store_aq(reinterpret_cast<T*>(recp + 16 * RU.aq));
   ic.solve(s);
   __syncthreads();  // every T_ii is in LDS
 #pragma unroll

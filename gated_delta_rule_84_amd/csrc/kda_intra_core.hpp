@@ -30,7 +30,7 @@
 // inverse.  Kd^T is transposed the other way by multiplying with a 0/1
 // selection matrix on MFMA (exact).
 //
-// Record parts (layout in kda_params.hpp):
+// Record parts (layout in kda_params.hpp, precision and scaling in RecOps):
 //   qg = q^ . Gamma, kg = -(k^ . Gamma), kdt = (k^ . Gamma_last / Gamma)^T,
 //   tb = T Diag(beta) with T = (I + Diag(beta) StrictTril(A_kk))^{-1},
 //   aq = Tril(A_qk) (diagonal included), gam = Gamma_last.
@@ -53,7 +53,6 @@ struct APolicy<uint16_t> {  // bf16 path
   static __device__ __forceinline__ Plain plain(const float* x) { return pack8_bf16(x); }
   static __device__ __forceinline__ f32x4 mma(const Plain& a, const Plain& b, f32x4 acc) { return mma32(a, b, acc); }
   static __device__ __forceinline__ Plain ld(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-  static constexpr bool kHasLo = true;
 };
 template <>
 struct APolicy<float> {  // fp32 path
@@ -64,31 +63,6 @@ struct APolicy<float> {  // fp32 path
     const float4 a = *reinterpret_cast<const float4*>(p);
     const float4 b = *reinterpret_cast<const float4*>(p + 4);
     return f32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  }
-  static constexpr bool kHasLo = false;
-};
-
-// Four fp32 values in the storage type (the rounding store4 applies), kept in
-// registers until they are stored.
-template <typename T>
-struct Pack4;
-template <>
-struct Pack4<uint16_t> {
-  using Raw = uint2;
-  static __device__ __forceinline__ Raw pack(const f32x4& x) {
-    uint2 w;
-    w.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
-    w.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
-    return w;
-  }
-  static __device__ __forceinline__ void store(uint16_t* p, const Raw& w) { *reinterpret_cast<uint2*>(p) = w; }
-};
-template <>
-struct Pack4<float> {
-  using Raw = f32x4;
-  static __device__ __forceinline__ Raw pack(const f32x4& x) { return x; }
-  static __device__ __forceinline__ void store(float* p, const Raw& w) {
-    *reinterpret_cast<float4*>(p) = make_float4(w[0], w[1], w[2], w[3]);
   }
 };
 
@@ -153,7 +127,9 @@ template <typename T, int D, int PQE, int PKE, bool SP = false, bool UNITS = fal
 struct IntraCore {
   using AP = APolicy<T>;
   using R8 = Run8<T>;
-  using P4 = Pack4<T>;
+  using RO = RecOps<T>;                          // record precision
+  using RE = typename RO::Elem;                  // record element (fp16 bits or fp32)
+  using Rec4 = decltype(RO::pack4(f32x4{}));     // 4 record elements in registers
   static constexpr int KS = D / 32;
   static constexpr int KP = D + 16 / (int)sizeof(T);  // KC row pitch (elements)
   static constexpr int LP = 68;                       // Tm row pitch (floats)
@@ -165,21 +141,27 @@ struct IntraCore {
   float P[KS][8];
   float KR[KS][8], QR[KS][8];  // row factors (kept for the off-diagonal blocks)
   f32x4 akk_d, aqk_d, akk[3], aqk[3], tii;
-  typename P4::Raw kd[KS][2];  // Kd^T pieces awaiting their store
-  typename P4::Raw aqs[4][2];  // Tril(A_qk) row pieces (hi, lo) awaiting their store
+  Rec4 kd[KS][2];              // Kd^T pieces awaiting their store
+  Rec4 aqs[4];                 // Tril(A_qk) row pieces (4 columns of each block) awaiting their store
   RecSink sink;                // UNITS: the record's device-scope stores
 
-  // 8 fp32 values as 8 elements of T through the sink (one or two units)
-  static __device__ __forceinline__ void sink_store8(const RecSink& k, T* p, const float* x) {
-    if constexpr (sizeof(T) == 2) {
-      u32x4 w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = static_cast<uint32_t>(f32_to_bf16(x[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * i + 1])) << 16);
-      k.st16(p, w);
+  // 8 fp32 values as 8 record elements through the sink (one or two units)
+  static __device__ __forceinline__ void sink_store8(const RecSink& k, RE* p, const float* x) {
+    if constexpr (sizeof(RE) == 2) {
+      k.st16(p, RO::pack8(x));
     } else {
       k.st16(p, u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])});
       k.st16(p + 4, u32x4{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])});
+    }
+  }
+
+  // 8 fp32 values as 8 record elements at p (an LDS image)
+  static __device__ __forceinline__ void rec_store8(RE* p, const float* x) {
+    if constexpr (sizeof(RE) == 2) {
+      *reinterpret_cast<u32x4*>(p) = RO::pack8(x);
+    } else {
+      *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+      *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
     }
   }
 
@@ -249,9 +231,9 @@ struct IntraCore {
       const int item = part + TPC * it;
       if (item >= 15) {
       } else if (item < 4) {
-        s.eB[item * D + ch] = hw_exp2(Bv[item]);
+        s.eB[item * D + ch] = hw_exp2(Bv[item] + RO::kLog2Up);  // the record's factor on q^ . Gamma, k^ . Gamma
       } else if (item < 8) {
-        s.eL[(item - 4) * D + ch] = hw_exp2(glast - Ev[item - 4]);
+        s.eL[(item - 4) * D + ch] = hw_exp2(glast - Ev[item - 4] - RO::kLog2Up);  // and its inverse on Kd
       } else if (item < 14) {
         const int pi = item - 8;  // pair index -> (i, j)
         const int i = (pi < 1) ? 1 : (pi < 3) ? 2 : 3;
@@ -271,8 +253,8 @@ struct IntraCore {
   __device__ __forceinline__ void factors(const IntraScratch<T>& s, T* qg, T* kg) {
     akk_d = zero4();
     aqk_d = zero4();
-    const typename AP::Plain sel0 = select_operand<typename AP::Plain>(n, g4, 0);
-    const typename AP::Plain sel1 = select_operand<typename AP::Plain>(n, g4, 1);
+    const typename RO::V8 sel0 = select_operand<typename RO::V8>(n, g4, 0);
+    const typename RO::V8 sel1 = select_operand<typename RO::V8>(n, g4, 1);
     float KN[SP ? KS : 1][8], QN[SP ? KS : 1][8];  // SP: normalised rows for the pairwise diagonal
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -307,15 +289,16 @@ struct IntraCore {
         sink_store8(sink, qg + 8 * pc, xq);
         sink_store8(sink, kg + 8 * pc, xk);
       } else {
-        store8<T>(qg + r * PQE + 32 * kk + 8 * g4, xq);
-        store8<T>(kg + r * PQE + 32 * kk + 8 * g4, xk);
+        rec_store8(qg + r * PQE + 32 * kk + 8 * g4, xq);
+        rec_store8(kg + r * PQE + 32 * kk + 8 * g4, xk);
       }
       if (ti < 3) store8<T>(s.KC + r * KP + 32 * kk + 8 * g4, kc);  // column factors for later sub-tiles
       {
         // lane (n, g4) receives Kd[16 ti + 4 g4 + i][32 kk + 16 half + n]
-        const typename AP::Plain xdp = AP::plain(xd);
-        kd[kk][0] = P4::pack(AP::mma(xdp, sel0, zero4()));
-        kd[kk][1] = P4::pack(AP::mma(xdp, sel1, zero4()));
+        // (a 0/1 product in the record's precision: exact)
+        const typename RO::V8 xdp = RO::plain(xd);
+        kd[kk][0] = RO::pack4(RO::mma(xdp, sel0, zero4()));
+        kd[kk][1] = RO::pack4(RO::mma(xdp, sel1, zero4()));
       }
       if constexpr (!SP) {
         // transposed diagonal blocks: lane (n, g4) gets row n, columns 4 g4 + i
@@ -401,14 +384,14 @@ struct IntraCore {
           sink.st16(dst + 4, __builtin_bit_cast(u32x4, kd[kk][1]));
         }
       } else {
-        P4::store(kdt + (32 * kk + n) * PKE + tpos, kd[kk][0]);
-        P4::store(kdt + (32 * kk + 16 + n) * PKE + tpos, kd[kk][1]);
+        *reinterpret_cast<Rec4*>(kdt + (32 * kk + n) * PKE + tpos) = kd[kk][0];
+        *reinterpret_cast<Rec4*>(kdt + (32 * kk + 16 + n) * PKE + tpos) = kd[kk][1];
       }
     }
   }
 
   // Off-diagonal blocks (ti, jt), jt < ti: plain products; then this wave's
-  // rows of Tril(A_qk) packed (hi / lo) for the record.
+  // rows of Tril(A_qk) packed for the record.
   __device__ __forceinline__ void offdiag(const IntraScratch<T>& s) {
 #pragma unroll
     for (int jt = 0; jt < 3; ++jt) {
@@ -436,34 +419,29 @@ struct IntraCore {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         a[i] = (jt == ti) ? ((4 * g4 + i <= n) ? aqk_d[i] : 0.0f) : (jt < ti ? aqk[jt < 3 ? jt : 0][i] : 0.0f);
-      aqs[jt][0] = P4::pack(a);
-      if constexpr (AP::kHasLo) {
-        f32x4 lo;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lo[i] = a[i] - bf16_to_f32(f32_to_bf16(a[i]));
-        aqs[jt][1] = P4::pack(lo);
-      }
+      aqs[jt] = RO::pack4(a);
     }
   }
 
-  // Tril(A_qk) rows to the record, 8-byte stores.  The scan reads the upper
-  // blocks (0, 1) and (2, 3) as part of its K-steps: they are written as zeros.
-  __device__ __forceinline__ void store_aq(T* aqh, T* aql) const {
+  // Tril(A_qk) rows to the record: the column pairs p <= ti / 2 of this row
+  // tile, blocks 2 p and 2 p + 1 side by side (the upper blocks (0, 1) and
+  // (2, 3), which the scan multiplies as part of its K-steps, are zeros).
+  __device__ __forceinline__ void store_aq(RE* aq) const {
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      const bool lower = jt <= ti;
-      const bool zero_blk = (ti == 0 && jt == 1) || (ti == 2 && jt == 3);
-      if (UNITS ? lower : (lower || zero_blk)) {
-        if constexpr (UNITS) {  // hi then lo of one block row piece per 16-byte unit
-          T* dst = aqh + (16 / (int)sizeof(T)) * (64 * aq_block_index(ti, jt) + 16 * g4 + n);
-          if constexpr (AP::kHasLo)
-            sink.st16(dst, u32x4{aqs[jt][0].x, aqs[jt][0].y, aqs[jt][1].x, aqs[jt][1].y});
-          else
-            sink.st16(dst, __builtin_bit_cast(u32x4, aqs[jt][0]));
+    for (int p = 0; p < 2; ++p) {
+      if (p <= (ti >> 1)) {
+        if constexpr (UNITS) {
+          RE* dst = aq + 8 * (64 * aq_group(ti, p) + 16 * g4 + n);
+          if constexpr (sizeof(RE) == 2) {
+            sink.st16(dst, u32x4{aqs[2 * p].x, aqs[2 * p].y, aqs[2 * p + 1].x, aqs[2 * p + 1].y});
+          } else {
+            sink.st16(dst, __builtin_bit_cast(u32x4, aqs[2 * p]));
+            sink.st16(dst + 4, __builtin_bit_cast(u32x4, aqs[2 * p + 1]));
+          }
         } else {
-          const int off = r * PKE + 32 * (jt >> 1) + 8 * g4 + 4 * (jt & 1);
-          P4::store(aqh + off, aqs[jt][0]);
-          if constexpr (AP::kHasLo) P4::store(aql + off, aqs[jt][1]);
+          RE* dst = aq + r * PKE + 32 * p + 8 * g4;
+          *reinterpret_cast<Rec4*>(dst) = aqs[2 * p];
+          *reinterpret_cast<Rec4*>(dst + 4) = aqs[2 * p + 1];
         }
       }
     }
@@ -549,7 +527,7 @@ struct IntraCore {
       if constexpr (UNITS)
         sink_store8(*sink, tb + (rr < 32 ? 32 * rr : 1024 + 64 * (rr - 32)) + 8 * pg, x);
       else
-        store8<T>(tb + rr * PKE + 8 * pg, x);
+        rec_store8(tb + rr * PKE + 8 * pg, x);
     }
   }
 };

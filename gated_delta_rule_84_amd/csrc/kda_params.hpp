@@ -12,53 +12,58 @@ constexpr int kSub = 16;     // tokens per sub-tile
 
 // Per-chunk intermediates written by the intra-chunk kernel and read by the
 // state scan: one contiguous record per (b, h, chunk of the current segment),
-// record index ((b * H + h) * nc + c).  Element type T = the input type (bf16
-// bits or fp32).  What one record holds (D = head dim), as the arrays that
-// the LDS images of the scan and of the fused kernel keep (rows padded); in
-// the workspace the same values are stored in the unit layout of rec_units
-// below:
+// record index ((b * H + h) * nc + c).  Element type: fp16 for bf16 inputs,
+// fp32 for fp32 inputs (RecOps in kda_common.hpp, which also gives the
+// power-of-two factors the fp16 entries carry).  What one record holds
+// (D = head dim), as the arrays that the LDS images of the scan and of the
+// fused kernel keep (rows padded); in the workspace the same values are stored
+// in the unit layout of rec_units below:
 //   qg  [64][D]   q^ . Gamma, columns in slot order per 32-group
 //   kg  [64][D]   -(k^ . Gamma), columns in slot order (negated, so that the
 //                 scan forms V - (K . Gamma) S in one accumulator chain)
 //   kdt [D][64]   (k^ . Gamma_last / Gamma)^T, token columns in slot order
 //   tb  [64][64]  (I + Diag(beta) StrictTril(A_kk))^{-1} Diag(beta), slot order
-//   aqh [64][64]  Tril(A_qk): high bf16 part (bf16 path) or value (fp32 path)
-//   aql [64][64]  Tril(A_qk) - aqh (bf16 path only)
+//   aq  [64][64]  Tril(A_qk) (diagonal included), slot order
 //   gam [D]       Gamma_last, fp32
 __host__ __device__ constexpr int round256(int x) { return (x + 255) & ~255; }
 
 // Chunk record in the workspace: 16-byte units in the order the intra-chunk
 // kernel's lanes hold them, so that every store instruction of a wave writes
 // 1 KB of consecutive bytes, and only what the scan reads.  Offsets in units
-// (es = element size: 2 bf16, 4 fp32; a "piece" is 8 elements = es / 2 units):
+// (es = element size: 2 fp16, 4 fp32; a "piece" is 8 elements = es / 2 units):
 //   qg, kg  piece (ti, kk, lane) = (ti KS + kk) 64 + lane: row 16 ti + n,
 //           channels 32 kk + 8 g4 .. + 7 (n = lane % 16, g4 = lane / 16)
 //   kdt     the same pieces, each Kd^T rows 32 kk + n and 32 kk + 16 + n
 //           (4 elements each) at token slots 32 (ti / 2) + 8 g4 + 4 (ti % 2)
 //   tb      T Diag(beta) rows, slot order: slots 0..31 of rows 0..31, then
 //           slots 0..63 of rows 32..63 (the rest is never read)
-//   aq      the 10 blocks (ti, jt <= ti) of Tril(A_qk), block index
-//           ti (ti + 1) / 2 + jt: unit 64 block + lane = hi (4 elements) then,
-//           for bf16, lo (4 elements) of row 16 ti + n at slots
-//           32 (jt / 2) + 8 g4 + 4 (jt % 2).  The scan also multiplies the
-//           zero blocks (0, 1) and (2, 3): it keeps them zero in LDS.
+//   aq      pieces (group, lane) = group 64 + lane, six groups: the column
+//           pairs p of row tile ti that reach the diagonal, (ti, p) = (0, 0),
+//           (1, 0), (2, 0), (2, 1), (3, 0), (3, 1); a piece holds row
+//           16 ti + n at slots 32 p + 8 g4 .. + 7, i.e. blocks 2 p and
+//           2 p + 1 side by side.  The scan's K-steps also multiply the upper
+//           blocks (0, 1) and (2, 3): the record carries them as zeros.
 //   gam     Gamma_last, D fp32
 struct RecUnits {
   int qg, kg, kdt, tb, aq, gam, units, bytes;
 };
 __host__ __device__ constexpr RecUnits rec_units(int es, int D) {
   // qg, kg, kdt: 64 D es / 16 = 4 D es units each; tb: 32 rows x 32 slots +
-  // 32 rows x 64 slots = 192 es units; aq: 10 blocks x 64 lanes; gam: D / 4
+  // 32 rows x 64 slots = 192 es units; aq: 6 groups x 64 pieces x es / 2;
+  // gam: D / 4
   return RecUnits{0,
                   4 * D * es,
                   8 * D * es,
                   12 * D * es,
                   12 * D * es + 192 * es,
-                  12 * D * es + 192 * es + 640,
-                  12 * D * es + 192 * es + 640 + D / 4,
-                  round256(16 * (12 * D * es + 192 * es + 640 + D / 4))};
+                  12 * D * es + 384 * es,
+                  12 * D * es + 384 * es + D / 4,
+                  round256(16 * (12 * D * es + 384 * es + D / 4))};
 }
-__host__ __device__ constexpr int aq_block_index(int ti, int jt) { return ti * (ti + 1) / 2 + jt; }
+// aq group of the column pair p of row tile ti (p <= ti / 2), and back
+__host__ __device__ constexpr int aq_group(int ti, int p) { return ti < 2 ? ti : 2 * ti - 2 + p; }
+__host__ __device__ constexpr int aq_group_tile(int g) { return g < 2 ? g : 2 + (g - 2) / 2; }
+__host__ __device__ constexpr int aq_group_pair(int g) { return g < 2 ? 0 : (g - 2) % 2; }
 
 struct ChunkWs {
   char* base;       // record 0

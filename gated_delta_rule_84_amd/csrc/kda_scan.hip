@@ -23,10 +23,9 @@
 //     O      = (Q . Gamma) S + Tril(A_qk) U'
 //     S_next = Diag(Gamma_last) S + (K . Gamma_last / Gamma)^T U'
 // Section 2.3: y = Sigmoid(gate) . RMSNorm(o) over the d_v channels of a head.
-// Rounding plan (bf16 path): S, K . Gamma and Q . Gamma enter bf16 MFMAs with
-// fp32 accumulation; the residual V - (K . Gamma) S and U' are split into
-// hi/lo bf16 parts where they are multiplied (T R, Kd^T U'); Tril(A_qk) U'
-// uses hi/lo parts on both sides; S stays fp32.  The fp32 path uses fp32 MFMA.
+// Rounding plan (bf16 inputs): fp16 record entries, state and residual
+// operands with fp32 accumulation (RecOps, kda_scan_core.hpp); S stays fp32.
+// The fp32 path uses fp32 MFMA.
 #include "kda_scan_core.hpp"
 
 namespace kda {
@@ -36,17 +35,18 @@ namespace kda {
 // tile.
 template <typename T, int D>
 struct ScanLds {
-  static constexpr int ES = sizeof(T);
+  static constexpr int ES = sizeof(T);     // input element (V slab)
+  static constexpr int RS = sizeof(typename RecOps<T>::Elem);  // record element
+  static_assert(RS == ES, "one row pitch for the record and the V slab");
   static constexpr int NT = 4 * D;          // threads (D / 16 waves)
   static constexpr int PQ = D * ES + 16;    // row pitch of qg / kg / V slab
-  static constexpr int PK = 64 * ES + 16;   // row pitch of kdt / tb / aqh / aql
+  static constexpr int PK = 64 * RS + 16;   // row pitch of kdt / tb / aq
   static constexpr int QG = 0;
   static constexpr int KG = QG + 64 * PQ;
   static constexpr int KDT = KG + 64 * PQ;
   static constexpr int TB = KDT + D * PK;
-  static constexpr int AQH = TB + 64 * PK;
-  static constexpr int AQL = AQH + 64 * PK;
-  static constexpr int GAM = AQL + (ES == 2 ? 64 * PK : 0);
+  static constexpr int AQ = TB + 64 * PK;
+  static constexpr int GAM = AQ + 64 * PK;
   static constexpr int REC = GAM + 4 * D;   // end of the record image
   static constexpr int PO = D + 4;          // fp32 output tile [64][D + 4]
   static constexpr int LIMIT = 160 * 1024;
@@ -60,7 +60,7 @@ struct ScanLds {
   static constexpr int BYTES = O_ALIAS ? AFTER_V : AFTER_V + 64 * PO * 4;
   static_assert(BYTES <= LIMIT, "scan LDS image too large");
   static_assert(!O_ALIAS || 64 * PO * 4 <= KDT, "aliased output tile must fit in qg / kg");
-  static constexpr RecUnits RU = rec_units(ES, D);
+  static constexpr RecUnits RU = rec_units(RS, D);
   static constexpr int REC_UNITS = RU.units;   // 16-byte units
   static constexpr int V_UNITS = V_LDS ? 64 * D * ES / 16 : 0;
   static constexpr int UNITS = REC_UNITS + V_UNITS;
@@ -72,57 +72,39 @@ struct ScanLds {
 };
 
 // Record unit u (the workspace layout of rec_units) -> byte offset in the
-// padded LDS image.  A bf16 unit of Kd^T or of Tril(A_qk) carries two 8-byte
-// pieces: the offset is the first one's; the second goes kdt_second (16 rows
-// further down) or aq_second (the same place in the lo array) beyond it.
+// padded LDS image.  A 2-byte unit of Kd^T carries two 8-byte pieces: the
+// offset is the first one's; the second goes 16 rows further down (KDT_SECOND
+// beyond it).
 template <typename L, int D>
 __device__ __forceinline__ int lds_offset_of_unit(int u) {
   constexpr RecUnits RU = L::RU;
-  constexpr int KS = D / 32, UPP = L::ES / 2;  // units per 8-element piece
+  constexpr int KS = D / 32, UPP = L::RS / 2;  // units per 8-element piece
   if (u < RU.tb) {  // qg, kg, kdt: piece (ti, kk, lane), part h of it (fp32)
     const int region = u < RU.kg ? 0 : u < RU.kdt ? 1 : 2;
     const int v = u - (region == 0 ? RU.qg : region == 1 ? RU.kg : RU.kdt);
     const int pc = v / UPP, h = v % UPP;
     const int ti = pc / (64 * KS), kk = (pc / 64) % KS, lane = pc % 64;
     const int n = lane & 15, g4 = lane >> 4;
-    if (region < 2) return (region == 0 ? L::QG : L::KG) + (16 * ti + n) * L::PQ + (32 * kk + 8 * g4 + 4 * h) * L::ES;
+    if (region < 2) return (region == 0 ? L::QG : L::KG) + (16 * ti + n) * L::PQ + (32 * kk + 8 * g4 + 4 * h) * L::RS;
     const int tpos = 32 * (ti >> 1) + 8 * g4 + 4 * (ti & 1);
-    return L::KDT + (32 * kk + 16 * h + n) * L::PK + tpos * L::ES;
+    return L::KDT + (32 * kk + 16 * h + n) * L::PK + tpos * L::RS;
   }
   if (u < RU.aq) {  // T Diag(beta): 32 slots of rows 0..31, then 64 slots of rows 32..63
-    constexpr int W32 = 32 * L::ES / 16, W64 = 64 * L::ES / 16;
+    constexpr int W32 = 32 * L::RS / 16, W64 = 64 * L::RS / 16;
     const int v = u - RU.tb;
     const int rr = v < 32 * W32 ? v / W32 : 32 + (v - 32 * W32) / W64;
     const int w = v < 32 * W32 ? v % W32 : (v - 32 * W32) % W64;
     return L::TB + rr * L::PK + 16 * w;
   }
-  if (u < RU.gam) {  // Tril(A_qk) block (ti, jt <= ti), lane: hi at row 16 ti + n, its slot column
+  if (u < RU.gam) {  // Tril(A_qk): piece (group, lane), part h of it (fp32)
     const int v = u - RU.aq;
-    const int bi = v / 64, lane = v % 64;
-    const int ti = bi >= 6 ? 3 : bi >= 3 ? 2 : bi >= 1 ? 1 : 0;
-    const int jt = bi - ti * (ti + 1) / 2;
+    const int pc = v / UPP, h = v % UPP;
+    const int grp = pc / 64, lane = pc % 64;
+    const int ti = aq_group_tile(grp), pr = aq_group_pair(grp);
     const int n = lane & 15, g4 = lane >> 4;
-    return L::AQH + (16 * ti + n) * L::PK + (32 * (jt >> 1) + 8 * g4 + 4 * (jt & 1)) * L::ES;
+    return L::AQ + (16 * ti + n) * L::PK + (32 * pr + 8 * g4 + 4 * h) * L::RS;
   }
   return L::GAM + 16 * (u - RU.gam);
-}
-
-// The zero blocks (0, 1) and (2, 3) of Tril(A_qk) that the scan multiplies
-// are not in the record: zero their LDS places (hi and, for bf16, lo) once.
-// Thread t of nthreads; nothing else writes these bytes.
-template <typename L>
-__device__ __forceinline__ void zero_aq_blocks(char* lds, int t, int nthreads) {
-  constexpr int ARRAYS = L::ES == 2 ? 2 : 1;
-  constexpr int PIECES = 2 * 16 * 4 * ARRAYS;  // blocks x rows x 4-slot groups x arrays
-  for (int i = t; i < PIECES; i += nthreads) {
-    const int arr = i % ARRAYS, g4 = (i / ARRAYS) % 4, n = (i / (4 * ARRAYS)) % 16, blk = i / (64 * ARRAYS);
-    const int ti = blk == 0 ? 0 : 2, jt = ti + 1;
-    const int off = (arr == 0 ? L::AQH : L::AQL) + (16 * ti + n) * L::PK + (32 * (jt >> 1) + 8 * g4 + 4 * (jt & 1)) * L::ES;
-    if constexpr (L::ES == 2)
-      *reinterpret_cast<uint2*>(lds + off) = uint2{0u, 0u};
-    else
-      *reinterpret_cast<u32x4*>(lds + off) = u32x4{0u, 0u, 0u, 0u};
-  }
 }
 
 // 16 consecutive fp32 values -> 16 outputs (fp32 or bf16) at dst.
@@ -146,7 +128,7 @@ __device__ __forceinline__ void store16(void* dst, const float* x, int out_f32) 
 template <typename T, int D>
 __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanParams p) {
   using Ops = ScanOps<T>;
-  using V8 = typename Ops::V8;
+  using Opnd = typename Ops::Opnd;
   using L = ScanLds<T, D>;
   static_assert(sizeof(T) == 4, "one LDS place per record unit: fp32 records");
   constexpr int MT = D / 16;  // 16-row tiles of the state (key channels)
@@ -239,7 +221,6 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
       for (int i = 0; i < 4; ++i) S[mt][i] = s0[(16 * mt + 4 * g4 + i) * D + col];
   }
 
-  zero_aq_blocks<L>(lds, tid, NT);
   fetch(0);
   commit();
   __syncthreads();
@@ -248,8 +229,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
   const char* kg = lds + L::KG;
   const char* kdt = lds + L::KDT;
   const char* tb = lds + L::TB;
-  const char* aqh = lds + L::AQH;
-  const char* aql = lds + L::AQL;
+  const char* aq = lds + L::AQ;
   const float* gam = reinterpret_cast<const float*>(lds + L::GAM);
   float* otile = reinterpret_cast<float*>(lds + L::OT);
 
@@ -279,7 +259,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
     if (more) fetch(c + 1);
 
     // B operands from the state, K-slots in slot order
-    V8 Sb[KS];
+    Opnd Sb[KS];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) Sb[kk] = Ops::from_acc(S[2 * kk], S[2 * kk + 1]);
 
@@ -291,9 +271,9 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
       O[mt] = zero4();
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        const int off = (16 * mt + n) * L::PQ + (32 * kk + 8 * g4) * L::ES;
-        X[mt] = mma32(Ops::ld(kg + off), Sb[kk], X[mt]);
-        O[mt] = mma32(Ops::ld(qg + off), Sb[kk], O[mt]);
+        const int off = (16 * mt + n) * L::PQ + (32 * kk + 8 * g4) * L::RS;
+        X[mt] = Ops::mma(Ops::ld(kg + off), Sb[kk], X[mt]);
+        O[mt] = Ops::mma(Ops::ld(qg + off), Sb[kk], O[mt]);
       }
     }
 
@@ -311,9 +291,9 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
           vraw = vreg[4 * mt + i];
         R[mt][i] = (r < nvalid ? Ops::in_f32(vraw) : 0.f) + X[mt][i];
       }
-    typename Ops::Prec Rp[2];
-    Rp[0] = Ops::prec_from_acc(R[0], R[1]);
-    Rp[1] = Ops::prec_from_acc(R[2], R[3]);
+    Opnd Rp[2];
+    Rp[0] = Ops::from_acc(R[0], R[1]);
+    Rp[1] = Ops::from_acc(R[2], R[3]);
 
     // U' = (T Diag(beta)) R   (block lower triangular: tile mt needs steps <= mt/2)
     f32x4 U[4];
@@ -322,19 +302,19 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
       U[mt] = zero4();
 #pragma unroll
       for (int kk = 0; kk <= (mt >> 1); ++kk)
-        U[mt] = Ops::mma_split_b(Ops::ld(tb + (16 * mt + n) * L::PK + (32 * kk + 8 * g4) * L::ES), Rp[kk], U[mt]);
+        U[mt] = Ops::mma(Ops::ld(tb + (16 * mt + n) * L::PK + (32 * kk + 8 * g4) * L::RS), Rp[kk], U[mt]);
     }
-    typename Ops::Prec Up[2];
-    Up[0] = Ops::prec_from_acc(U[0], U[1]);
-    Up[1] = Ops::prec_from_acc(U[2], U[3]);
+    Opnd Up[2];
+    Up[0] = Ops::from_acc(U[0], U[1]);
+    Up[1] = Ops::from_acc(U[2], U[3]);
 
     // O += Tril(A_qk) U'
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int kk = 0; kk <= (mt >> 1); ++kk) {
-        const int off = (16 * mt + n) * L::PK + (32 * kk + 8 * g4) * L::ES;
-        O[mt] = Ops::mma_prec(Ops::ld(aqh + off), Ops::ld(aql + off), Up[kk], O[mt]);
+        const int off = (16 * mt + n) * L::PK + (32 * kk + 8 * g4) * L::RS;
+        O[mt] = Ops::mma(Ops::ld(aq + off), Up[kk], O[mt]);
       }
 
     // S <- Diag(Gamma_last) S + Kd^T U'
@@ -343,9 +323,9 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
       const f32x4 gm = *reinterpret_cast<const f32x4*>(gam + 16 * mt + 4 * g4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[mt][i] *= gm[i];
-      const int off = (16 * mt + n) * L::PK + 8 * g4 * L::ES;
-      S[mt] = Ops::mma_split_b(Ops::ld(kdt + off), Up[0], S[mt]);
-      S[mt] = Ops::mma_split_b(Ops::ld(kdt + off + 32 * L::ES), Up[1], S[mt]);
+      const int off = (16 * mt + n) * L::PK + 8 * g4 * L::RS;
+      S[mt] = Ops::mma(Ops::ld(kdt + off), Up[0], S[mt]);
+      S[mt] = Ops::mma(Ops::ld(kdt + off + 32 * L::RS), Up[1], S[mt]);
     }
 
     // prefix-cache snapshot of the state after this chunk
@@ -441,15 +421,16 @@ struct WsLds {
   static constexpr int NHW = NCW;              // helper waves
   static constexpr int NT = 64 * (NCW + NHW);  // threads
   static constexpr int NH = 64 * NHW;          // helper threads
+  static constexpr int RS = sizeof(typename RecOps<T>::Elem);  // record element
+  static_assert(RS == ES, "one row pitch for the record and the slabs");
   static constexpr int PQ = D * ES + 16;
-  static constexpr int PK = 64 * ES + 16;
+  static constexpr int PK = 64 * RS + 16;
   static constexpr int QG = 0;
   static constexpr int KG = QG + 64 * PQ;
   static constexpr int KDT = KG + 64 * PQ;
   static constexpr int TB = KDT + D * PK;
-  static constexpr int AQH = TB + 64 * PK;
-  static constexpr int AQL = AQH + 64 * PK;
-  static constexpr int GAM = AQL + (ES == 2 ? 64 * PK : 0);
+  static constexpr int AQ = TB + 64 * PK;
+  static constexpr int GAM = AQ + 64 * PK;
   static constexpr int REC = GAM + 4 * D;
   static constexpr int VS = REC;               // V slab   [64][PQ]
   static constexpr int GS = VS + 64 * PQ;      // gate slab [64][PQ]
@@ -457,18 +438,16 @@ struct WsLds {
   static constexpr int OT = GS + 64 * PQ;      // output tile [64][PO] fp32
   static constexpr int FLAG = OT + 64 * PO * 4;  // outcome of the record waits (int)
   static constexpr int BYTES = FLAG + 16;
-  static constexpr RecUnits RU = rec_units(ES, D);
+  static constexpr RecUnits RU = rec_units(RS, D);
   static constexpr int VPR = D * ES / 16;      // 16-byte units per slab row
   static constexpr int SLAB_UNITS = 64 * VPR;
   static constexpr int A_REC = RU.kdt;         // record units of part A (qg, kg)
   static constexpr int A_UNITS = A_REC + SLAB_UNITS;
   static constexpr int B_UNITS = RU.units - RU.kdt;
-  // part B (relative units): Kd^T (split, whole steps), T Diag(beta) (plain),
-  // Tril(A_qk) (split: hi | lo), Gamma_last (plain)
+  // part B (relative units): Kd^T (split, whole steps), then T Diag(beta),
+  // Tril(A_qk) and Gamma_last (plain)
   static constexpr int KDT_STEPS = (RU.tb - RU.kdt) / NH;
-  static constexpr int AQ_LO = RU.aq - RU.kdt, AQ_HI = RU.gam - RU.kdt;
   static constexpr int KDT_SECOND = 16 * PK;   // second piece of a Kd^T unit: 16 rows down
-  static constexpr int AQ_SECOND = AQL - AQH;  // second piece of an A_qk unit: the lo array
   static constexpr int PA = (A_UNITS + NH - 1) / NH;
   static constexpr int PB = (B_UNITS + NH - 1) / NH;
   static constexpr int PG = (SLAB_UNITS + NH - 1) / NH;
@@ -481,7 +460,7 @@ struct WsLds {
 template <typename T, int D, bool OUT_F32>
 __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const ScanParams p) {
   using L = WsLds<T, D>;
-  static_assert(sizeof(T) == 2, "the split commits of part B assume bf16 records");
+  static_assert(sizeof(typename RecOps<T>::Elem) == 2, "the split commits of part B assume 2-byte records");
   __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -598,18 +577,13 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
 #pragma unroll
         for (int i = 0; i < L::PB; ++i) stB[i] = u32x4{kPoison, kPoison, kPoison, kPoison};
     };
-    static_assert((L::RU.tb - L::RU.kdt) % NH == 0 && L::AQ_LO % 64 == 0,
-                  "Kd^T units fill whole steps; A_qk starts at a wave boundary");
+    static_assert((L::RU.tb - L::RU.kdt) % NH == 0, "Kd^T units fill whole steps");
     auto commit_B = [&]() {
 #pragma unroll
       for (int i = 0; i < L::PB; ++i) {
-        const int u = min(hid + NH * i, L::B_UNITS - 1);  // as loaded (clamped)
         if (i < L::KDT_STEPS) {  // Kd^T: two 8-byte pieces, 16 rows apart
           *reinterpret_cast<uint2*>(lds + lofB[i]) = uint2{stB[i][0], stB[i][1]};
           *reinterpret_cast<uint2*>(lds + lofB[i] + L::KDT_SECOND) = uint2{stB[i][2], stB[i][3]};
-        } else if (u >= L::AQ_LO && u < L::AQ_HI) {  // A_qk: hi and lo pieces (wave-uniform)
-          *reinterpret_cast<uint2*>(lds + lofB[i]) = uint2{stB[i][0], stB[i][1]};
-          *reinterpret_cast<uint2*>(lds + lofB[i] + L::AQ_SECOND) = uint2{stB[i][2], stB[i][3]};
         } else {
           *reinterpret_cast<u32x4*>(lds + lofB[i]) = stB[i];
         }
@@ -647,7 +621,6 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
     const int cl = p.nc - 1;
     // prologue: part A of chunk 0 into LDS; part B of chunk 0, part A of
     // chunk 1 and the gate logits of chunk 0 into registers
-    zero_aq_blocks<L>(lds, hid, NH);
     load_A(0);
     load_B(0);
     commit_A(0);

@@ -10,10 +10,11 @@
 //     O      = (Q . Gamma) S + Tril(A_qk) U'
 //     S_next = Diag(Gamma_last) S + (K . Gamma_last / Gamma)^T U'
 // Section 2.3: y = Sigmoid(gate) . RMSNorm(o) over the d_v channels of a head.
-// Rounding plan (bf16 path): S, K . Gamma and Q . Gamma enter bf16 MFMAs with
-// fp32 accumulation; the residual V - (K . Gamma) S and U' are split into
-// hi/lo bf16 parts where they are multiplied (T R, Kd^T U'); Tril(A_qk) U'
-// uses hi/lo parts on both sides; S stays fp32.  The fp32 path uses fp32 MFMA.
+// Rounding plan (bf16 inputs): every product takes fp16 operands -- the
+// record entries, the state (held as S * 2^-4, see RecOps), the residual
+// V - (K . Gamma) S and U' -- with fp32 accumulation; V enters the residual
+// through an exact bf16 selection product; S stays fp32.  The fp32 path uses
+// fp32 MFMA.
 #pragma once
 
 #include "kda_common.hpp"
@@ -23,54 +24,38 @@
 
 namespace kda {
 
+// Operand types of the scan's products: Opnd for the record entries and the
+// operands formed from accumulators (fp16 or fp32), In8 for the V slab (the
+// input type).
 template <typename T>
 struct ScanOps;
 
 template <>
 struct ScanOps<uint16_t> {
-  using V8 = bf16x8;
-  struct Prec {  // operand of a split product
-    bf16x8 hi, lo;
-  };
-  static __device__ __forceinline__ V8 ld(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
-  static __device__ __forceinline__ V8 from_acc(const f32x4& a, const f32x4& b) { return acc_pair_to_bf16(a, b); }
-  static __device__ __forceinline__ Prec prec_from_acc(const f32x4& a, const f32x4& b) {
-    Prec r;
-    acc_pair_split(a, b, r.hi, r.lo);
-    return r;
-  }
-  static __device__ __forceinline__ f32x4 mma_prec(const V8& ah, const V8& al, const Prec& b, f32x4 acc) {
-    return mma32_x3(ah, al, b.hi, b.lo, acc);
-  }
-  // a (bf16) times a split operand: a * hi + a * lo
-  static __device__ __forceinline__ f32x4 mma_split_b(const V8& a, const Prec& b, f32x4 acc) {
-    acc = mma32(a, b.lo, acc);
-    return mma32(a, b.hi, acc);
-  }
+  using RO = RecOps<uint16_t>;
+  using Opnd = f16x8;
+  using In8 = bf16x8;
+  static __device__ __forceinline__ Opnd ld(const char* p) { return *reinterpret_cast<const f16x8*>(p); }
+  static __device__ __forceinline__ In8 ld_in(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  static __device__ __forceinline__ Opnd from_acc(const f32x4& a, const f32x4& b) { return RO::plain_acc(a, b); }
+  static __device__ __forceinline__ f32x4 mma(const Opnd& a, const Opnd& b, f32x4 acc) { return mma32(a, b, acc); }
+  static __device__ __forceinline__ f32x4 mma_in(const In8& a, const In8& b, f32x4 acc) { return mma32(a, b, acc); }
   static __device__ __forceinline__ float in_f32(uint16_t x) { return bf16_to_f32(x); }
 };
 
 template <>
 struct ScanOps<float> {
-  using V8 = f32x8;
-  struct Prec {
-    f32x8 v;
-  };
-  static __device__ __forceinline__ V8 ld(const char* p) {
+  using Opnd = f32x8;
+  using In8 = f32x8;
+  static __device__ __forceinline__ Opnd ld(const char* p) {
     const float4 a = *reinterpret_cast<const float4*>(p);
     const float4 b = *reinterpret_cast<const float4*>(p + 16);
     return f32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   }
-  static __device__ __forceinline__ V8 from_acc(const f32x4& a, const f32x4& b) { return acc_pair_to_f32(a, b); }
-  static __device__ __forceinline__ Prec prec_from_acc(const f32x4& a, const f32x4& b) {
-    return Prec{acc_pair_to_f32(a, b)};
-  }
-  static __device__ __forceinline__ f32x4 mma_prec(const V8& ah, const V8&, const Prec& b, f32x4 acc) {
-    return mma32(ah, b.v, acc);
-  }
-  static __device__ __forceinline__ f32x4 mma_split_b(const V8& a, const Prec& b, f32x4 acc) {
-    return mma32(a, b.v, acc);
-  }
+  static __device__ __forceinline__ In8 ld_in(const char* p) { return ld(p); }
+  static __device__ __forceinline__ Opnd from_acc(const f32x4& a, const f32x4& b) { return acc_pair_to_f32(a, b); }
+  static __device__ __forceinline__ f32x4 mma(const Opnd& a, const Opnd& b, f32x4 acc) { return mma32(a, b, acc); }
+  static __device__ __forceinline__ f32x4 mma_in(const In8& a, const In8& b, f32x4 acc) { return mma32(a, b, acc); }
   static __device__ __forceinline__ float in_f32(float x) { return x; }
 };
 
@@ -87,8 +72,8 @@ __device__ __forceinline__ V8 v_select(int n, int g, int nt) {
 
 // Compute waves of a specialised workgroup: wave `wave` (0 .. D / 32 - 1)
 // owns value columns 32 wave .. 32 wave + 31 and keeps that d_k x 32 slice of
-// the fp32 state in accumulators for the whole sequence.  Per chunk step, with
-// the layout L of the LDS image:
+// the fp32 state in accumulators for the whole sequence (scaled by
+// RecOps<T>::kStateScale).  Per chunk step, with the layout L of the LDS image:
 //   first half  -- reads part A of the record (qg, kg) and the V slab;
 //   barrier M   -- part A consumed, part B (kdt, tb, aq, Gamma_last) staged;
 //   second half -- reads part B, writes the chunk's output tile;
@@ -98,7 +83,9 @@ __device__ __forceinline__ V8 v_select(int n, int g, int nt) {
 template <typename T, int D, typename L>
 __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* lds, int wave, int lane, int b, int h) {
   using Ops = ScanOps<T>;
-  using V8 = typename Ops::V8;
+  using Opnd = typename Ops::Opnd;
+  using In8 = typename Ops::In8;
+  constexpr float kScale = RecOps<T>::kStateScale, kUnscale = 1.0f / RecOps<T>::kStateScale;
   constexpr int MT = D / 16;
   constexpr int KS = D / 32;
   constexpr int NCT = 2;  // 16-column tiles per compute wave
@@ -118,15 +105,14 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
 #pragma unroll
       for (int nt = 0; nt < NCT; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[mt][nt][i] = s0[(16 * mt + 4 * g4 + i) * D + col0 + 16 * nt];
+        for (int i = 0; i < 4; ++i) S[mt][nt][i] = s0[(16 * mt + 4 * g4 + i) * D + col0 + 16 * nt] * kScale;
   }
-  const V8 vsel0 = v_select<V8>(n, g4, 0), vsel1 = v_select<V8>(n, g4, 1);
+  const In8 vsel0 = v_select<In8>(n, g4, 0), vsel1 = v_select<In8>(n, g4, 1);
   const char* qg = lds + L::QG;
   const char* kg = lds + L::KG;
   const char* kdt = lds + L::KDT;
   const char* tb = lds + L::TB;
-  const char* aqh = lds + L::AQH;
-  const char* aql = lds + L::AQL;
+  const char* aq = lds + L::AQ;
   const float* gam = reinterpret_cast<const float*>(lds + L::GAM);
   __syncthreads();  // part A of chunk 0 staged
 
@@ -146,14 +132,12 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
 
     // R = V - (K . Gamma) S (the record holds kg negated; V enters through a
     // 0/1 selection product, rows past the end are zero) and O = (Q . Gamma) S.
-    // S enters as hi/lo bf16 parts (two MFMAs per step): with little decay
-    // its rounding would otherwise accumulate from chunk to chunk.  The steps
-    // run K-step major, so only one K-step's parts of S are live at a time.
+    // The steps run K-step major, so only one K-step's operand of S is live.
     f32x4 R[4][NCT];
     {
-      V8 av[2];
+      In8 av[2];
       auto ldv = [&](int mt, int bf) {
-        av[bf] = Ops::ld(lds + L::VS + (16 * mt + n) * L::PQ + (32 * wave + 8 * g4) * L::ES);
+        av[bf] = Ops::ld_in(lds + L::VS + (16 * mt + n) * L::PQ + (32 * wave + 8 * g4) * L::ES);
       };
       ldv(0, 0);
 #pragma unroll
@@ -161,64 +145,60 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
         const int bf = mt & 1;
         if (mt + 1 < 4) ldv(mt + 1, bf ^ 1);
         __builtin_amdgcn_sched_barrier(0);
-        R[mt][0] = mma32(av[bf], vsel0, zero4());
-        R[mt][1] = mma32(av[bf], vsel1, zero4());
+        R[mt][0] = Ops::mma_in(av[bf], vsel0, zero4());
+        R[mt][1] = Ops::mma_in(av[bf], vsel1, zero4());
         O[mt][0] = O[mt][1] = zero4();
       }
       constexpr int G1 = 4 * KS;  // steps (kk, mt)
-      V8 ak[2], aq[2];
+      Opnd ak[2], aqv[2];
       auto ld1 = [&](int g, int bf) {
         const int kk = g / 4, mt = g % 4;
-        const int off = (16 * mt + n) * L::PQ + (32 * kk + 8 * g4) * L::ES;
+        const int off = (16 * mt + n) * L::PQ + (32 * kk + 8 * g4) * L::RS;
         ak[bf] = Ops::ld(kg + off);
-        aq[bf] = Ops::ld(qg + off);
+        aqv[bf] = Ops::ld(qg + off);
       };
       ld1(0, 0);
-      typename Ops::Prec Sp[NCT];
+      Opnd Sp[NCT];
 #pragma unroll
       for (int g = 0; g < G1; ++g) {
         const int bf = g & 1, kk = g / 4, mt = g % 4;
         if (g + 1 < G1) ld1(g + 1, bf ^ 1);
         if (mt == 0)
 #pragma unroll
-          for (int nt = 0; nt < NCT; ++nt) Sp[nt] = Ops::prec_from_acc(S[2 * kk][nt], S[2 * kk + 1][nt]);
+          for (int nt = 0; nt < NCT; ++nt) Sp[nt] = Ops::from_acc(S[2 * kk][nt], S[2 * kk + 1][nt]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int nt = 0; nt < NCT; ++nt) {
-          R[mt][nt] = Ops::mma_split_b(ak[bf], Sp[nt], R[mt][nt]);
-          O[mt][nt] = Ops::mma_split_b(aq[bf], Sp[nt], O[mt][nt]);
+          R[mt][nt] = Ops::mma(ak[bf], Sp[nt], R[mt][nt]);
+          O[mt][nt] = Ops::mma(aqv[bf], Sp[nt], O[mt][nt]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    typename Ops::Prec Rp[2][NCT];
+    Opnd Rp[2][NCT];
 #pragma unroll
     for (int nt = 0; nt < NCT; ++nt) {
-      Rp[0][nt] = Ops::prec_from_acc(R[0][nt], R[1][nt]);
-      Rp[1][nt] = Ops::prec_from_acc(R[2][nt], R[3][nt]);
+      Rp[0][nt] = Ops::from_acc(R[0][nt], R[1][nt]);
+      Rp[1][nt] = Ops::from_acc(R[2][nt], R[3][nt]);
     }
     __syncthreads();  // part A of chunk c consumed; part B of chunk c staged; tile c - 1 done
 
     // lower-triangular (token tile, K-step) blocks of T Diag(beta) and Tril(A_qk)
     constexpr int NB = 6;
     constexpr int BMT[NB] = {0, 1, 2, 2, 3, 3}, BKK[NB] = {0, 0, 0, 1, 0, 1};
-    V8 at[2], ah[2], al[2], k0[2], k1[2];
+    Opnd at[2], ah[2], k0[2], k1[2];
     f32x4 gm[2];
-    auto ld_t = [&](int i, int bf) { at[bf] = Ops::ld(tb + (16 * BMT[i] + n) * L::PK + (32 * BKK[i] + 8 * g4) * L::ES); };
-    auto ld_a = [&](int i, int bf) {
-      const int off = (16 * BMT[i] + n) * L::PK + (32 * BKK[i] + 8 * g4) * L::ES;
-      ah[bf] = Ops::ld(aqh + off);
-      al[bf] = Ops::ld(aql + off);
-    };
+    auto ld_t = [&](int i, int bf) { at[bf] = Ops::ld(tb + (16 * BMT[i] + n) * L::PK + (32 * BKK[i] + 8 * g4) * L::RS); };
+    auto ld_a = [&](int i, int bf) { ah[bf] = Ops::ld(aq + (16 * BMT[i] + n) * L::PK + (32 * BKK[i] + 8 * g4) * L::RS); };
     auto ld_s = [&](int mt, int bf) {
-      const int off = (16 * mt + n) * L::PK + 8 * g4 * L::ES;
+      const int off = (16 * mt + n) * L::PK + 8 * g4 * L::RS;
       k0[bf] = Ops::ld(kdt + off);
-      k1[bf] = Ops::ld(kdt + off + 32 * L::ES);
+      k1[bf] = Ops::ld(kdt + off + 32 * L::RS);
       gm[bf] = *reinterpret_cast<const f32x4*>(gam + 16 * mt + 4 * g4);
     };
 
     // U' = (T Diag(beta)) R
-    typename Ops::Prec Up[2][NCT];
+    Opnd Up[2][NCT];
     {
       f32x4 U[4][NCT];
       ld_t(0, 0);
@@ -231,14 +211,13 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
           ld_a(0, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int nt = 0; nt < NCT; ++nt)
-          U[mt][nt] = Ops::mma_split_b(at[bf], Rp[kk][nt], kk == 0 ? zero4() : U[mt][nt]);
+        for (int nt = 0; nt < NCT; ++nt) U[mt][nt] = Ops::mma(at[bf], Rp[kk][nt], kk == 0 ? zero4() : U[mt][nt]);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nt = 0; nt < NCT; ++nt) {
-        Up[0][nt] = Ops::prec_from_acc(U[0][nt], U[1][nt]);
-        Up[1][nt] = Ops::prec_from_acc(U[2][nt], U[3][nt]);
+        Up[0][nt] = Ops::from_acc(U[0][nt], U[1][nt]);
+        Up[1][nt] = Ops::from_acc(U[2][nt], U[3][nt]);
       }
     }
 
@@ -252,7 +231,7 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
         ld_s(0, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int nt = 0; nt < NCT; ++nt) O[mt][nt] = Ops::mma_prec(ah[bf], al[bf], Up[kk][nt], O[mt][nt]);
+      for (int nt = 0; nt < NCT; ++nt) O[mt][nt] = Ops::mma(ah[bf], Up[kk][nt], O[mt][nt]);
     }
 
     // S <- Diag(Gamma_last) S + Kd^T U'
@@ -265,8 +244,8 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
       for (int nt = 0; nt < NCT; ++nt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[mt][nt][i] *= gm[bf][i];
-        S[mt][nt] = Ops::mma_split_b(k0[bf], Up[0][nt], S[mt][nt]);
-        S[mt][nt] = Ops::mma_split_b(k1[bf], Up[1][nt], S[mt][nt]);
+        S[mt][nt] = Ops::mma(k0[bf], Up[0][nt], S[mt][nt]);
+        S[mt][nt] = Ops::mma(k1[bf], Up[1][nt], S[mt][nt]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -287,7 +266,7 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
 #pragma unroll
           for (int nt = 0; nt < NCT; ++nt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sn[(16 * mt + i) * D + 16 * nt] = S[mt][nt][i];
+            for (int i = 0; i < 4; ++i) sn[(16 * mt + i) * D + 16 * nt] = S[mt][nt][i] * kUnscale;
       }
     }
     __syncthreads();  // part B of chunk c consumed; tile c and part A of chunk c + 1 staged
@@ -300,7 +279,7 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
 #pragma unroll
     for (int nt = 0; nt < NCT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) so[(16 * mt + 4 * g4 + i) * D + col0 + 16 * nt] = S[mt][nt][i];
+      for (int i = 0; i < 4; ++i) so[(16 * mt + 4 * g4 + i) * D + col0 + 16 * nt] = S[mt][nt][i] * kUnscale;
 }
 
 // Gate epilogue over the output tile of one chunk (section 2.3): NH threads,
