@@ -174,7 +174,7 @@ def test_workspace_and_launch_queries():
     plans the one-stream segments; the size query still offers the pipelined
     schedule's workspace (every record) for bf16 inputs up to its cap."""
     L = kda.lib()
-    rec = 66048                                                   # bytes per chunk record at d = 128, bf16
+    rec = 61952                                                   # bytes per chunk record at d = 128, fp16 entries
     d = _desc(B=1, T=65536, H=96, fused=0)
     ws = L.kda_chunk_fwd_workspace_size(ctypes.byref(d))
     assert ws >= 96 * 1024 * rec and ws < 96 * 1024 * rec + (64 << 20)   # every record, plus state and counters
@@ -244,3 +244,4 @@ def test_kcp_host_errors():
 def test_decay_map_field():
     assert _desc().decay == 0                                        # K3 map by default
     assert _fwd(_desc(decay=2)) == 5                                 # unknown map
+
