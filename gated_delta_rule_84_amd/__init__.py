@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_launches.argtypes = [dp, sz, ctypes.POINTER(i32), i32, ctypes.POINTER(i32)]
         L.kda_chunk_fwd.restype = ctypes.c_int
         L.kda_chunk_fwd.argtypes = [dp] + [vp] * 13 + [sz, vp]
+        L.kda_chunk_fwd_noalloc.restype = ctypes.c_int
+        L.kda_chunk_fwd_noalloc.argtypes = [dp] + [vp] * 13
         L.kda_chunk_fwd_traced.restype = ctypes.c_int
         L.kda_chunk_fwd_traced.argtypes = [dp] + [vp] * 13 + [sz, vp, ctypes.POINTER(vp), i32]
         L.kda_recurrent_step.restype = ctypes.c_int
@@ -243,6 +245,34 @@ def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=
         rc = lib().kda_chunk_fwd_traced(*args, arr, len(events))
     if rc != 0:
         raise KdaError("kda_chunk_fwd", rc)
+    return res
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # KDA_NOALLOC_SCRATCH_BYTES
+
+
+def chunk_fwd_noalloc(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=None, want_o=True,
+                      want_y=None, want_state=True, out=None, **opts):
+    """kda_chunk_fwd_noalloc: the forward without a workspace (the library's
+    per-GPU scratch array, one-stream schedule).  Arguments and result as
+    chunk_fwd; only the outputs are allocated here, by the caller's side."""
+    B, T, H, D = q.shape
+    odt = q.dtype if out_dtype is None else out_dtype
+    desc = make_desc(B, T, H, D, _dt(q), _dt(torch.empty(0, dtype=odt)), **opts)
+    want_y = (gate is not None) if want_y is None else want_y
+    res = dict(out or {})
+    dev = q.device
+    if want_o and "o" not in res:
+        res["o"] = torch.empty((B, T, H, D), dtype=odt, device=dev)
+    if want_y and "y" not in res:
+        res["y"] = torch.empty((B, T, H, D), dtype=odt, device=dev)
+    if want_state and "S_T" not in res:
+        res["S_T"] = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    rc = lib().kda_chunk_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A),
+                                     _ptr(S0), _ptr(gate), _ptr(rms_w), _ptr(res.get("o")), _ptr(res.get("y")),
+                                     _ptr(res.get("S_T")), _stream(dev))
+    if rc != 0:
+        raise KdaError("kda_chunk_fwd_noalloc", rc)
     return res
 
 

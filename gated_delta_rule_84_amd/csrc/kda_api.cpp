@@ -757,6 +757,64 @@ kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const 
                         Tracer{nullptr, 0});
 }
 
+}  // extern "C"
+
+// ---- entry point for callers that cannot allocate ---------------------------
+// kda_chunk_fwd_noalloc keeps its chunk records and carried state in this
+// file-scope device array instead of a caller workspace.  In host code the
+// name is only a host-side stand-in: the array's device address, which differs
+// per GPU, is taken once per device with hipGetSymbolAddress and only that
+// address is handed to kernels.
+static constexpr size_t kNoAllocScratchBytes = KDA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (taken on the first call
+// on each device, with that device current).
+kda_status scratch_on_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return KDA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return KDA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd_noalloc(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
+                                 const void* z, const float* A, const float* S0, const void* gate,
+                                 const float* rms_w, void* o, void* y, float* S_T, void* stream) {
+  const kda_status st = validate_desc(d);
+  if (st != KDA_OK) return st;
+  // the one-stream schedule: no library streams or events, segments in turn
+  kda_desc one = *d;
+  one.overlap = 0;
+  one.fused = 0;
+  if (d->T > 0 && layout_for(&one, 1).total > kNoAllocScratchBytes) return KDA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (d->T > 0) {
+    const kda_status sst = scratch_on_current_device(&ws);
+    if (sst != KDA_OK) return sst;
+  }
+  return chunk_fwd_impl(&one, q, k, v, beta, z, A, S0, gate, rms_w, o, y, S_T, ws, d->T > 0 ? kNoAllocScratchBytes : 0,
+                        stream, Tracer{nullptr, 0});
+}
+
 kda_status kda_chunk_fwd_traced(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
                                 const void* z, const float* A, const float* S0, const void* gate,
                                 const float* rms_w, void* o, void* y, float* S_T, void* ws, size_t ws_bytes,

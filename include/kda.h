@@ -224,6 +224,32 @@ kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const 
                          const void* z, const float* A, const float* S0, const void* gate, const float* rms_w,
                          void* o, void* y, float* S_T, void* ws, size_t ws_bytes, void* stream);
 
+/* Size of the device scratch array kda_chunk_fwd_noalloc works in (per GPU). */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * kda_chunk_fwd without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, results and errors as kda_chunk_fwd, minus
+ * ws / ws_bytes.  It always takes the one-stream schedule (segments in turn
+ * on `stream`, so no library streams or events either) and keeps its chunk
+ * records and the carried state in a file-scope device array of
+ * KDA_NOALLOC_SCRATCH_BYTES bytes, which every GPU the library runs on holds
+ * until the process ends (its address is resolved on the first call on each
+ * device).  It calls no hipMalloc, hipFree or other allocating routine.
+ *  - The sequence is processed in segments of as many chunks as the array
+ *    holds; a call whose single chunk does not fit (B * H * (one chunk record
+ *    + one fp32 state) above the limit: B * H > ~1000 at d = 128) returns
+ *    KDA_ERR_WORKSPACE and enqueues nothing.
+ *  - Every call on one GPU shares that GPU's array: calls that can overlap in
+ *    time on one device (several streams, several host threads) race and
+ *    must be serialised by the caller.  Nothing in the array needs to start
+ *    zeroed; each call overwrites what it reads.
+ */
+kda_status kda_chunk_fwd_noalloc(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
+                                 const void* z, const float* A, const float* S0, const void* gate,
+                                 const float* rms_w, void* o, void* y, float* S_T, void* stream);
+
 /*
  * kda_chunk_fwd with per-kernel timing: identical work and results, and in
  * addition, for the i-th kernel launch of the call (the order that

@@ -245,3 +245,15 @@ def test_decay_map_field():
     assert _desc().decay == 0                                        # K3 map by default
     assert _fwd(_desc(decay=2)) == 5                                 # unknown map
 
+
+def test_noalloc_rejects_oversized_shapes_on_the_host():
+    """kda_chunk_fwd_noalloc: a shape whose single chunk of records and states
+    exceeds the per-GPU scratch array is refused before anything is enqueued
+    (no GPU needed); invalid descriptors are refused too."""
+    L = kda.lib()
+    d = kda.make_desc(16, 64, 128, 128, kda.KDA_BF16, kda.KDA_BF16)  # B * H = 2048
+    p = ctypes.c_void_p(256)
+    assert L.kda_chunk_fwd_noalloc(ctypes.byref(d), p, p, p, p, p, p, None, None, None, p, None, None, None) == 6
+    d.chunk = 32
+    assert L.kda_chunk_fwd_noalloc(ctypes.byref(d), p, p, p, p, p, p, None, None, None, p, None, None, None) == 5
+    assert kda.NOALLOC_SCRATCH_BYTES == 128 << 20
