@@ -9,19 +9,28 @@ pipelined two-kernel schedule for long sequences: every chunk record resident,
 one scan launch; two-segment records beyond the query's cap); --schedule
 forces one (the fused kernel measured slower at every size tried).
 --workload selects another configuration (long ones are generated slab by
-slab on the device).  Per-kernel durations come from HIP events recorded by
-the library around each of its launches on the launch stream
-(kda_chunk_fwd_traced, in the order kda_chunk_fwd_launches reports); the
-dominant kernel's roofline uses its algorithmic bytes:
-  fused       : q, k, z, v, gate logits (5 * 2d B) + beta (2 B) in, y out
-                (2d B) per token-head, + initial and final state
+slab on the device).  K timed steps follow W warm-up steps; the JSON line
+gives their mean (ms_per_step, and `value`), median and minimum.
+
+Roofline (`roofline`): the dominant kernel is the one with the longest
+average launch (the pipelined schedule's single scan launch, which spans the
+step); its achieved bandwidth is the path's algorithmic bytes of the
+token-heads one launch processes -- 1,538 B per token-head at d = 128: q, k, z,
+v, gate logits in and y out at 2d bytes each, beta 2 bytes -- plus the state,
+over the launch's average duration measured with HIP events that the library
+records around each of its launches on the launch stream
+(kda_chunk_fwd_traced, in the order kda_chunk_fwd_launches reports).
+`kernel_share` gives the same kernel's own inputs and outputs instead:
   intra-chunk : q, k, z (3 * 2d B) + beta (2 B) per token-head
   state scan  : v, gate logits in, y out (3 * 2d B) per token-head + final state
-i.e. the path's 1,538 B per token-head (2d = 256 B at d = 128).
+After the timed loop (outside it) the timed outputs are checked: finite, the
+library's status word clear (kda_chunk_fwd_status), and, in the CPU-baseline
+leg, y of the first and last sampled head against the fp64 oracle (<= 3e-3).
 Side measurements (skipped with their --no-* flags): the same forward
 without the output gate (o and S_T out, 1,282 B per token-head; sequences up
-to 65,536 tokens), the input steps, the decode step and the state export.
-The CPU baseline is the fp64 C oracle timed on a bounded sample of heads.
+to 65,536 tokens), the prefill workload (B4 T4096 H32), the input steps, the
+decode step and the state export.  The CPU baseline is the fp64 C oracle on
+every host core the process may use, over a bounded sample of heads.
 """
 from __future__ import annotations
 
@@ -30,6 +39,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -116,23 +127,106 @@ def profiled_counters(workload: str):
     return out
 
 
+def path_bytes_per_token_head(d: int) -> int:
+    # q, k, z, v, gate logits in and y out (bf16, 2d bytes each) + beta (2 bytes): 1,538 B at d = 128
+    return 6 * 2 * d + 2
+
+
 def path_flops_per_token_head(d: int, C: int = 64) -> float:
     # 6 d^2 (state products) + 5 (C + 16) d (sub-tile products) + C^2 / 3 (UT inverse)
     return 6 * d * d + 5 * (C + 16) * d + C * C / 3
 
 
-def cpu_baseline(wl, heads: int, threads: int) -> dict:
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, heads: int, y_gpu=None) -> dict:
+    """The fp64 C oracle (sequential recurrence + gate, OpenMP over heads) on
+    every host core the process may use, over heads 0 .. heads - 1 of the
+    workload; with y_gpu (the GPU's y of those heads from the timed loop) the
+    oracle's y also spot-checks it (relative L2 on the first and last sampled
+    head)."""
     import oracle
     from synth.workloads import gen_inputs
 
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     x = gen_inputs(wl, heads=(0, heads))
     t0 = time.perf_counter()
-    oracle.forward_c(x["q"], x["k"], x["v"], x["beta"], x["z"], x["A"], gate=x["gate"], nthreads=threads)
+    ref = oracle.forward_c(x["q"], x["k"], x["v"], x["beta"], x["z"], x["A"], gate=x["gate"], nthreads=threads,
+                           want_o=False)
     dt = time.perf_counter() - t0
     th = wl.B * wl.T * heads
-    return {"value": th / dt, "unit": "tokens·heads/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 C oracle (sequential recurrence + gate, OpenMP over heads) on heads 0..{heads - 1} "
-                      f"of the {wl.name} workload, all {wl.T} tokens ({th} token-heads, {dt:.1f} s)"}
+    res = {"value": th / dt, "unit": "tokens·heads/s", "cores": threads, "kind": "oracle",
+           "nproc": os.cpu_count(), "cpu_model": cpu_model(),
+           "sample": f"fp64 C oracle (sequential recurrence + gate, OpenMP over heads) on heads 0..{heads - 1} "
+                     f"of the {wl.name} workload, all {wl.T} tokens ({th} token-heads, {dt:.1f} s, "
+                     f"{threads} threads)"}
+    if y_gpu is not None:
+        errs = {}
+        for hh in sorted({0, heads - 1}):
+            a = y_gpu[:, :, hh].astype(np.float64)
+            r = ref["y"][:, :, hh]
+            errs[f"head_{hh}"] = float(np.linalg.norm(a - r) / np.linalg.norm(r))
+        res["parity_y_rel_l2"] = errs
+        res["parity_ok"] = all(e <= 3e-3 for e in errs.values())
+    return res
+
+
+def time_calls(fn, steps: int, warmup: int):
+    """Mean, median and minimum milliseconds of `steps` calls of fn (events on
+    the current stream between the calls)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record()
+    for k in range(steps):
+        fn()
+        marks[k + 1].record()
+    torch.cuda.synchronize()
+    per = [marks[k].elapsed_time(marks[k + 1]) for k in range(steps)]
+    return marks[0].elapsed_time(marks[-1]) / steps, float(np.median(per)), float(np.min(per))
+
+
+def time_prefill(kda, wl, steps: int, warmup: int) -> dict:
+    """The prefill workload (B4 T4096 H32 d128, bf16, gate; y and S_T out) with
+    the library's own schedule for the workspace its size query offers."""
+    import torch
+    from synth.workloads import gen_inputs
+
+    x = gen_inputs(wl)
+    t = {k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16) if v.dtype == np.uint16 else v).cuda()
+         for k, v in x.items()}
+    for k, v in x.items():
+        if v.dtype == np.uint16:
+            t[k] = t[k].view(torch.bfloat16)
+    del x
+    B, T, H, D = wl.B, wl.T, wl.H, wl.D
+    desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16)
+    ws = torch.empty(kda.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    out = {"y": torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda"),
+           "S_T": torch.empty((B, H, D, D), device="cuda")}
+
+    def call():
+        kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], gate=t["gate"], want_o=False, out=out,
+                      workspace=ws)
+
+    ms, med, mn = time_calls(call, steps, warmup)
+    th = B * T * H
+    nbytes = th * path_bytes_per_token_head(D) + 2 * B * H * D * D * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": wl.name, "B": B, "T": T, "H": H, "d": D, "schedule": kda.schedule(desc, ws.numel())[1],
+            "ms": ms, "ms_median": med, "ms_min": mn, "token_heads_per_s": th / (ms * 1e-3),
+            "algorithmic_bytes": nbytes, "achieved_GBs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+            "outputs_finite": bool(torch.isfinite(out["y"]).all().item())}
 
 
 def time_input_prep(kda, t, B, T, H, D, steps, warmup, workload, W=4):
@@ -222,7 +316,7 @@ def time_decode(kda, H, D, steps, warmup, n=256):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="k3_layer")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-baseline sample (0: all heads)")
@@ -235,6 +329,8 @@ def main() -> int:
     ap.add_argument("--decay", choices=("k3", "softplus"), default="k3",
                     help="decay map: K3's bounded map (the method), or Kimi Linear's softplus map (ablation)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step side measurement")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill workload's side measurement (B4 T4096 H32)")
     ap.add_argument("--no-o-only", action="store_true", help="skip the side measurement without the output gate")
     ap.add_argument("--no-input-prep", action="store_true",
                     help="skip timing the input steps (ShortConv + Swish, Sigmoid) on the workload's shapes")
@@ -340,16 +436,21 @@ def main() -> int:
             e.record()
     torch.cuda.synchronize()
     handles = [[e.cuda_event for e in row] for row in ev]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # step boundaries on the caller's stream (each call joins the library's streams back into it)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
 
     torch.cuda.synchronize()
-    start.record()
+    marks[0].record()
     for k in range(args.steps):
         step(events=handles[k])
-    stop.record()
+        marks[k + 1].record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
+    total_ms = marks[0].elapsed_time(marks[-1])
     ms = total_ms / args.steps
+    step_ms = [marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps)]
+    # the timed outputs are checked outside the timed region
+    status_ok = kda.call_status(desc, ws) == 0
+    finite = bool(torch.isfinite(out["y"]).all().item()) and bool(torch.isfinite(out["S_T"]).all().item())
 
     per = {n: [] for n in set(names)}
     for row in ev:
@@ -361,11 +462,16 @@ def main() -> int:
     kern_ms = {n: float(np.mean(v)) for n, v in per.items()}  # per step, summed over its launches
     launches = {n: names.count(n) for n in per}
     dom = max(kern_ms, key=lambda n: kern_ms[n] / launches[n])  # longest average launch
-    # algorithmic bytes of all of the kernel's launches in a step over their summed duration
-    # (= bytes per launch / average launch duration for equal segments)
-    dom_bytes = kernel_bytes(dom, token_heads, D, B * H, T)
-    achieved = dom_bytes / (kern_ms[dom] * 1e-3) / 1e9
-    path_bytes = token_heads * (1538 if D == 128 else (6 * D + 2 + 4 * D)) + 2 * B * H * D * D * 4
+    avg_launch_ms = kern_ms[dom] / launches[dom]
+    path_bytes = token_heads * path_bytes_per_token_head(D) + 2 * B * H * D * D * 4
+    # headline roofline: the path's algorithmic bytes of the token-heads one launch of
+    # the dominant kernel processes (all of them for the pipelined schedule's single
+    # scan launch) over that launch's average duration
+    dom_path_bytes = path_bytes / launches[dom]
+    achieved = dom_path_bytes / (avg_launch_ms * 1e-3) / 1e9
+    # secondary: the kernel's own share of the path's bytes (its inputs and outputs)
+    share_bytes = kernel_bytes(dom, token_heads, D, B * H, T)
+    share_gbs = share_bytes / (kern_ms[dom] * 1e-3) / 1e9
     path_gbs = path_bytes / (ms * 1e-3) / 1e9
     path_tflops = token_heads * path_flops_per_token_head(D) / (ms * 1e-3) / 1e12
 
@@ -377,6 +483,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_median": float(np.median(step_ms)),
+        "ms_min": float(np.min(step_ms)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -388,13 +496,16 @@ def main() -> int:
                    "schedule": sched, "segment_tokens": seg, "decay": args.decay},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(dom, wl.name),
-                     "algorithmic_bytes_per_launch": dom_bytes / launches[dom],
-                     "launches_per_step": launches[dom], "avg_launch_ms": kern_ms[dom] / launches[dom]},
+                     "algorithmic_bytes_per_launch": dom_path_bytes,
+                     "launches_per_step": launches[dom], "avg_launch_ms": avg_launch_ms,
+                     "kernel_share": {"algorithmic_bytes_per_launch": share_bytes / launches[dom],
+                                      "achieved_GBs": share_gbs, "frac": share_gbs / HBM_PEAK_GBS}},
         "path_roofline": {"achieved_GBs": path_gbs, "frac_hbm": path_gbs / HBM_PEAK_GBS,
                           "achieved_TFLOPs": path_tflops, "frac_bf16_mfma": path_tflops / BF16_PEAK_TFLOPS,
                           "algorithmic_bytes": path_bytes},
         "counters": profiled_counters(wl.name),
         "kernel_ms": kern_ms,
+        "checks": {"outputs_finite": finite, "library_status_ok": status_ok},
         "input_setup_s": t_gen,
     }
     if not args.no_o_only and T <= 65536:
@@ -406,17 +517,10 @@ def main() -> int:
             kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t.get("S0"), out=out_o,
                           workspace=ws, segment_tokens=seg_arg, overlap=overlap, fused=fused, decay=args.decay)
 
-        for _ in range(args.warmup):
-            step_o()
-        torch.cuda.synchronize()
-        start.record()
-        for _ in range(args.steps):
-            step_o()
-        stop.record()
-        torch.cuda.synchronize()
-        ms_o = start.elapsed_time(stop) / args.steps
+        ms_o, med_o, min_o = time_calls(step_o, args.steps, args.warmup)
         o_bytes = token_heads * (5 * 2 * D + 2) + 2 * B * H * D * D * 4  # q, k, z, v, beta in; o out; S0, S_T
-        result["o_only"] = {"ms": ms_o, "token_heads_per_s": token_heads / (ms_o * 1e-3),
+        result["o_only"] = {"ms": ms_o, "ms_median": med_o, "ms_min": min_o,
+                            "token_heads_per_s": token_heads / (ms_o * 1e-3),
                             "algorithmic_bytes": o_bytes, "achieved_GBs": o_bytes / (ms_o * 1e-3) / 1e9,
                             "frac_hbm": o_bytes / (ms_o * 1e-3) / 1e9 / HBM_PEAK_GBS}
         del out_o
@@ -424,11 +528,17 @@ def main() -> int:
         result["input_prep"] = time_input_prep(kda, t, B, T, H, D, args.steps, args.warmup, wl.name)
     if not args.no_decode:
         result["decode"] = time_decode(kda, H, D, args.steps, args.warmup)
+    if not args.no_prefill and wl.name != "prefill":
+        result["prefill"] = time_prefill(kda, WORKLOADS["prefill"], args.steps, args.warmup)
     if not args.no_cpu_baseline:
-        threads = min(16, os.cpu_count() or 1)
         heads = args.cpu_heads or H
-        result["cpu_baseline"] = cpu_baseline(wl, min(heads, H), threads)
+        y_host = out["y"][:, :, :min(heads, H)].float().cpu().numpy()  # the last timed step's output
+        result["cpu_baseline"] = cpu_baseline(wl, min(heads, H), y_host)
     print(json.dumps(result), flush=True)
+    valid = finite and status_ok and result.get("cpu_baseline", {}).get("parity_ok", True)
+    if not valid:
+        print("bench: the timed outputs failed their checks (see 'checks' / 'cpu_baseline')", file=sys.stderr)
+        return 3
     return 0
 
 

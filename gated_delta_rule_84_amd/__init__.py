@@ -21,7 +21,8 @@ KDA_F32, KDA_BF16 = 0, 1
 STATE_ZERO, STATE_IMPORT, STATE_EXPORT = 0, 1, 2
 LAYOUT_KV, LAYOUT_VK = 0, 1
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL_ARG", 2: "KDA_ERR_BAD_SHAPE", 3: "KDA_ERR_BAD_DTYPE",
-          4: "KDA_ERR_MISALIGNED", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_HIP"}
+          4: "KDA_ERR_MISALIGNED", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_HIP",
+          8: "KDA_ERR_TIMEOUT"}
 
 
 class KdaDesc(ctypes.Structure):
@@ -83,14 +84,16 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_launches.argtypes = [dp, sz, ctypes.POINTER(i32), i32, ctypes.POINTER(i32)]
         L.kda_chunk_fwd.restype = ctypes.c_int
         L.kda_chunk_fwd.argtypes = [dp] + [vp] * 13 + [sz, vp]
+        L.kda_chunk_fwd_status.restype = ctypes.c_int
+        L.kda_chunk_fwd_status.argtypes = [dp, vp, sz, vp]
         L.kda_chunk_fwd_noalloc.restype = ctypes.c_int
         L.kda_chunk_fwd_noalloc.argtypes = [dp] + [vp] * 13
         L.kda_chunk_fwd_traced.restype = ctypes.c_int
         L.kda_chunk_fwd_traced.argtypes = [dp] + [vp] * 13 + [sz, vp, ctypes.POINTER(vp), i32]
         L.kda_recurrent_step.restype = ctypes.c_int
-        L.kda_recurrent_step.argtypes = [dp] + [vp] * 12
+        L.kda_recurrent_step.argtypes = [dp] + [vp] * 7 + [i32] + [vp] * 7
         L.kda_state_io.restype = ctypes.c_int
-        L.kda_state_io.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.c_int, vp, vp, vp, vp]
+        L.kda_state_io.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.c_int, vp, i32, vp, vp, vp, vp]
         L.kda_prepass.restype = ctypes.c_int
         L.kda_prepass.argtypes = [dp] + [vp] * 7 + [vp]
         _lib = L
@@ -151,6 +154,14 @@ def release_resources() -> None:
 
 SCHEDULES = {0: "segments", 1: "overlapped", 2: "fused", 3: "pipelined"}
 LAUNCH_KINDS = {0: "intra", 1: "scan", 2: "fused"}
+
+
+def call_status(desc: KdaDesc, workspace) -> int:
+    """kda_chunk_fwd_status: waits for the current stream, then 0 (KDA_OK) or
+    8 (KDA_ERR_TIMEOUT: the last call through `workspace` had an in-kernel
+    wait for chunk records give up, so its outputs are invalid)."""
+    return int(lib().kda_chunk_fwd_status(ctypes.byref(desc), _ptr(workspace), workspace.numel(),
+                                          _stream(workspace.device)))
 
 
 def schedule(desc: KdaDesc, ws_bytes: int) -> tuple[int, str]:
@@ -301,10 +312,11 @@ def input_prep(xq, xk, xv, wq, wk, wv, beta_logits=None, state_in=None, state_ou
 
 
 def recurrent_step(q, k, v, beta, z, A, S_pool, slot=None, gate=None, rms_w=None, *, out_dtype=None,
-                   want_o=True, want_y=None, out=None, **opts):
+                   want_o=True, want_y=None, out=None, status=None, **opts):
     """One decode token for n sequences.  q, k, v, z (and gate): [n, H, D];
     beta [n, H]; S_pool [n_slots, H, D, D] fp32 updated in place; slot: int32
-    [n] or None."""
+    [n] or None.  status: a device uint32 tensor that collects
+    KDA_FLAG_BAD_SLOT for slots outside [0, n_slots) (those are skipped)."""
     n, H, D = q.shape
     odt = q.dtype if out_dtype is None else out_dtype
     desc = make_desc(n, 1, H, D, _dt(q), _dt(torch.empty(0, dtype=odt)), **opts)
@@ -315,20 +327,25 @@ def recurrent_step(q, k, v, beta, z, A, S_pool, slot=None, gate=None, rms_w=None
     if want_y and "y" not in res:
         res["y"] = torch.empty((n, H, D), dtype=odt, device=q.device)
     rc = lib().kda_recurrent_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A),
-                                  _ptr(S_pool), _ptr(slot), _ptr(gate), _ptr(rms_w), _ptr(res.get("o")),
-                                  _ptr(res.get("y")), _stream(q.device))
+                                  _ptr(S_pool), int(S_pool.shape[0]), _ptr(slot), _ptr(gate), _ptr(rms_w),
+                                  _ptr(res.get("o")), _ptr(res.get("y")), _ptr(status), _stream(q.device))
     if rc != 0:
         raise KdaError("kda_recurrent_step", rc)
     return res
 
 
-def state_io(op: int, pool, user=None, slot=None, n=None, layout: int = LAYOUT_KV):
+FLAG_BAD_SLOT = 1  # KDA_FLAG_BAD_SLOT
+
+
+def state_io(op: int, pool, user=None, slot=None, n=None, layout: int = LAYOUT_KV, status=None):
     """ZERO / IMPORT / EXPORT states between ``pool`` [n_slots, H, D, D] and
-    ``user`` [n, H, D, D] (layout KV) or its transpose (layout VK)."""
-    _, H, Dk, Dv = pool.shape
+    ``user`` [n, H, D, D] (layout KV) or its transpose (layout VK).  status:
+    as for recurrent_step."""
+    n_slots, H, Dk, Dv = pool.shape
     if n is None:
         n = user.shape[0] if user is not None else (slot.numel() if slot is not None else pool.shape[0])
-    rc = lib().kda_state_io(op, n, H, Dk, Dv, layout, _ptr(pool), _ptr(slot), _ptr(user), _stream(pool.device))
+    rc = lib().kda_state_io(op, n, H, Dk, Dv, layout, _ptr(pool), int(n_slots), _ptr(slot), _ptr(user), _ptr(status),
+                            _stream(pool.device))
     if rc != 0:
         raise KdaError("kda_state_io", rc)
 

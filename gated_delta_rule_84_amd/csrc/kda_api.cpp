@@ -24,6 +24,17 @@ constexpr int32_t kDefaultSegmentTokens = 65536;  // one-stream schedule
 constexpr int32_t kDefaultPipeTokens = 8192;      // overlapped schedule
 constexpr int32_t kDefaultPipelinedTokens = 4096; // pipelined schedule's steady segments
 
+// Test hook (failure handling): KDA_TEST_PRODUCED_SEGMENTS=n makes the
+// pipelined schedule launch only the first n of its intra-chunk segments, so
+// that the scan's bounded wait for the next one runs out and the status word
+// is raised while every kernel still exits normally.  Unset: all segments.
+int withheld_segments(int n_seg) {
+  const char* e = std::getenv("KDA_TEST_PRODUCED_SEGMENTS");
+  if (e == nullptr || e[0] == 0) return n_seg;
+  const int n = std::atoi(e);
+  return n < 0 ? n_seg : std::min(n, n_seg);
+}
+
 bool debug_sync() {
   const char* e = std::getenv("KDA_DEBUG");
   return e != nullptr && e[0] == '1';
@@ -77,6 +88,7 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 struct WsLayout {
   size_t off_rec, rec_bytes, off_carry, off_done, total;
 };
+constexpr int kStatusWords = 64;  // status block ahead of the record counters
 
 // Workspace for a segment of seg_nc chunks: one record per (b, h, chunk), the
 // fp32 state carried between segments and one record counter per (segment,
@@ -96,7 +108,8 @@ WsLayout layout_for(const kda_desc* d, int64_t seg_nc) {
   L.rec_bytes = (size_t)kda::rec_units(es, (int)D).bytes;
   L.off_rec = take(R * L.rec_bytes);
   L.off_carry = take((size_t)d->B * d->H * D * D * 4);
-  L.off_done = take((size_t)(((int64_t)d->T + kChunk - 1) / kChunk + 1) * d->B * d->H * 4);
+  // a 256-byte status block (word 0: kda::kStatus* bits), then the counters
+  L.off_done = take(kStatusWords * 4 + (size_t)(((int64_t)d->T + kChunk - 1) / kChunk + 1) * d->B * d->H * 4);
   L.total = o;
   return L;
 }
@@ -177,10 +190,17 @@ int segment_table(const kda_desc* d, int32_t* ends) {
   return n;
 }
 
-// ---- per-device streams and events of the overlapped schedule --------------
+// ---- per-device streams and events of the two-stream schedules --------------
+// At most one pair of library streams per device (the intra-chunk stream and
+// the scan stream, each restricted to its own compute units) plus five
+// events.  The pair is made for the scan's unit count of the call at hand;
+// a call with another count first waits for the old pair's work and destroys
+// it, so a process that alternates B * H between calls pays that wait (the
+// library's own streams only) at each change.  Streams are only created by
+// the forward calls, never by the query entry points.
 struct StreamPair {
-  int n_scan;
-  hipStream_t intra, scan;
+  int n_scan = 0;
+  hipStream_t intra = nullptr, scan = nullptr;
 };
 struct DeviceCtx {
   std::mutex mu;
@@ -188,7 +208,7 @@ struct DeviceCtx {
   int cus = 0;
   hipEvent_t fork = nullptr, join_intra = nullptr, join_scan = nullptr;
   hipEvent_t scan_done[2] = {nullptr, nullptr};
-  std::vector<StreamPair> pairs;
+  StreamPair pair;
 };
 constexpr int kMaxDevices = 64;
 DeviceCtx g_dev[kMaxDevices];
@@ -210,27 +230,37 @@ bool ctx_ready(DeviceCtx& c, int dev) {
   return true;
 }
 
-// Streams for a scan of n_scan workgroups: the scan stream may use the first
-// n_scan compute units of the mask, the intra stream the others (the runtime
-// spreads consecutive mask bits over the device's XCDs).  Called with c.mu held.
+// Waits for and destroys the device's stream pair.  Called with c.mu held.
+bool drop_pair(DeviceCtx& c) {
+  bool ok = true;
+  for (hipStream_t q : {c.pair.intra, c.pair.scan})
+    if (q != nullptr && (hipStreamSynchronize(q) != hipSuccess || hipStreamDestroy(q) != hipSuccess)) ok = false;
+  (void)hipGetLastError();
+  c.pair = StreamPair{};
+  return ok;
+}
+
+// The device's stream pair for a scan of n_scan workgroups: the scan stream
+// may use the first n_scan compute units of the mask, the intra stream the
+// others (consecutive mask bits are spread evenly over the XCDs, measured).
+// Called with c.mu held.
 bool stream_pair(DeviceCtx& c, int n_scan, hipStream_t* si, hipStream_t* ss) {
-  for (const StreamPair& p : c.pairs)
-    if (p.n_scan == n_scan) {
-      *si = p.intra;
-      *ss = p.scan;
-      return true;
+  if (c.pair.scan == nullptr || c.pair.n_scan != n_scan) {
+    if (c.pair.scan != nullptr && !drop_pair(c)) return false;
+    std::vector<uint32_t> ms((c.cus + 31) / 32, 0u), mi((c.cus + 31) / 32, 0u);
+    for (int i = 0; i < c.cus; ++i) (i < n_scan ? ms : mi)[i / 32] |= 1u << (i % 32);
+    StreamPair p{n_scan, nullptr, nullptr};
+    if (hipExtStreamCreateWithCUMask(&p.scan, (uint32_t)ms.size(), ms.data()) != hipSuccess ||
+        hipExtStreamCreateWithCUMask(&p.intra, (uint32_t)mi.size(), mi.data()) != hipSuccess) {
+      (void)hipGetLastError();
+      if (p.scan != nullptr) (void)hipStreamDestroy(p.scan);
+      (void)hipGetLastError();
+      return false;
     }
-  std::vector<uint32_t> ms((c.cus + 31) / 32, 0u), mi((c.cus + 31) / 32, 0u);
-  for (int i = 0; i < c.cus; ++i) (i < n_scan ? ms : mi)[i / 32] |= 1u << (i % 32);
-  StreamPair p{n_scan, nullptr, nullptr};
-  if (hipExtStreamCreateWithCUMask(&p.scan, (uint32_t)ms.size(), ms.data()) != hipSuccess ||
-      hipExtStreamCreateWithCUMask(&p.intra, (uint32_t)mi.size(), mi.data()) != hipSuccess) {
-    (void)hipGetLastError();
-    return false;
+    c.pair = p;
   }
-  c.pairs.push_back(p);
-  *si = p.intra;
-  *ss = p.scan;
+  *si = c.pair.intra;
+  *ss = c.pair.scan;
   return true;
 }
 
@@ -247,8 +277,9 @@ struct Plan {
   int32_t seg_end[kda::kMaxSegs];
 };
 
-// The two library streams can be used for B * H scan workgroups on the
-// current device (B * H at most 5/8 of its compute units).
+// The two library streams can serve B * H scan workgroups on the current
+// device (B * H at most 5/8 of its compute units); the streams themselves
+// are made at launch time (stream_pair).
 bool two_streams(const kda_desc* d, int* dev_out, int* n_scan_out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
@@ -258,15 +289,16 @@ bool two_streams(const kda_desc* d, int* dev_out, int* n_scan_out) {
   DeviceCtx& c = g_dev[dev];
   std::lock_guard<std::mutex> lock(c.mu);
   const int64_t bh = (int64_t)d->B * d->H;
-  const int n_scan = (int)((bh + 7) / 8 * 8);
-  hipStream_t si = nullptr, ss = nullptr;
-  if (!(ctx_ready(c, dev) && bh * 8 <= (int64_t)c.cus * 5 && stream_pair(c, n_scan, &si, &ss))) return false;
+  if (!(ctx_ready(c, dev) && bh * 8 <= (int64_t)c.cus * 5)) return false;
   *dev_out = dev;
-  *n_scan_out = n_scan;
+  *n_scan_out = (int)((bh + 7) / 8 * 8);
   return true;
 }
 
-Plan make_plan(const kda_desc* d, size_t ws_bytes) {
+// one_stream: the call's stream is being captured into a graph; the
+// two-stream schedules then stay out (their scan waits inside the kernel for
+// producers that a graph would be free to run after it).
+Plan make_plan(const kda_desc* d, size_t ws_bytes, bool one_stream = false) {
   Plan p{};
   p.seg_nc = 1;
   const int64_t nc_total = num_chunks(d);
@@ -276,7 +308,8 @@ Plan make_plan(const kda_desc* d, size_t ws_bytes) {
     return p;
   }
   int dev = 0, n_scan = 0;
-  if (pipelined_eligible(d) && ws_bytes >= layout_for(d, nc_total).total && two_streams(d, &dev, &n_scan)) {
+  if (!one_stream && pipelined_eligible(d) && ws_bytes >= layout_for(d, nc_total).total &&
+      two_streams(d, &dev, &n_scan)) {
     p.pipelined = true;
     p.dev = dev;
     p.n_scan = n_scan;
@@ -285,7 +318,8 @@ Plan make_plan(const kda_desc* d, size_t ws_bytes) {
       p.seg_nc = std::max<int64_t>(p.seg_nc, p.seg_end[s] - (s > 0 ? p.seg_end[s - 1] : 0));
     return p;
   }
-  if (pipe_wanted(d) && ws_bytes >= layout_for(d, 2 * pipe_chunks(d)).total && two_streams(d, &dev, &n_scan)) {
+  if (!one_stream && pipe_wanted(d) && ws_bytes >= layout_for(d, 2 * pipe_chunks(d)).total &&
+      two_streams(d, &dev, &n_scan)) {
     p.seg_nc = pipe_chunks(d);
     p.overlapped = true;
     p.dev = dev;
@@ -316,9 +350,8 @@ int32_t plan_launches(const kda_desc* d, const Plan& p, int32_t* kinds, int32_t 
   if (p.fused) {
     put(KDA_LAUNCH_FUSED);
   } else if (p.pipelined) {
-    put(KDA_LAUNCH_INTRA);
+    for (int s = 0; s < p.n_seg; ++s) put(KDA_LAUNCH_INTRA);
     put(KDA_LAUNCH_SCAN);
-    for (int s = 1; s < p.n_seg; ++s) put(KDA_LAUNCH_INTRA);
   } else {
     const int64_t nc_total = num_chunks(d);
     for (int64_t c0 = 0; c0 < nc_total; c0 += p.seg_nc) {
@@ -342,16 +375,13 @@ kda_status kda_release_resources(void) {
   for (int dev = 0; dev < kMaxDevices; ++dev) {
     DeviceCtx& c = g_dev[dev];
     std::lock_guard<std::mutex> lock(c.mu);
-    if (!c.ready && c.pairs.empty()) continue;
+    if (!c.ready && c.pair.scan == nullptr) continue;
     if (hipSetDevice(dev) != hipSuccess) {
       (void)hipGetLastError();
       st = KDA_ERR_HIP;
       continue;
     }
-    for (StreamPair& p : c.pairs)
-      for (hipStream_t q : {p.intra, p.scan})
-        if (hipStreamSynchronize(q) != hipSuccess || hipStreamDestroy(q) != hipSuccess) st = KDA_ERR_HIP;
-    c.pairs.clear();
+    if (!drop_pair(c)) st = KDA_ERR_HIP;
     for (hipEvent_t* e : {&c.fork, &c.join_intra, &c.join_scan, &c.scan_done[0],
                           &c.scan_done[1]}) {
       if (*e != nullptr && hipEventDestroy(*e) != hipSuccess) st = KDA_ERR_HIP;
@@ -379,6 +409,27 @@ kda_status kda_chunk_fwd_schedule(const kda_desc* d, size_t ws_bytes, int32_t* s
   return KDA_OK;
 }
 
+kda_status kda_chunk_fwd_status(const kda_desc* d, const void* ws, size_t ws_bytes, void* stream) {
+  const kda_status st = validate_desc(d);
+  if (st != KDA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) {
+    (void)hipGetLastError();
+    return KDA_ERR_HIP;
+  }
+  if (ws == nullptr || fused_wanted(d) || ws_bytes < layout_for(d, 1).total || d->T == 0) return KDA_OK;
+  const Plan p = make_plan(d, ws_bytes);
+  if (!p.pipelined && !p.overlapped) return KDA_OK;  // nothing waits in the one-stream schedule
+  const WsLayout L = layout_for(d, p.pipelined ? num_chunks(d) : 2 * pipe_chunks(d));
+  uint32_t word = 0;
+  if (hipMemcpy(&word, static_cast<const char*>(ws) + L.off_done, sizeof(word), hipMemcpyDeviceToHost) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return KDA_ERR_HIP;
+  }
+  return (word & kda::kStatusWaitGaveUp) ? KDA_ERR_TIMEOUT : KDA_OK;
+}
+
 kda_status kda_chunk_fwd_launches(const kda_desc* d, size_t ws_bytes, int32_t* kinds, int32_t max_kinds,
                                   int32_t* n_launches) {
   const kda_status st = validate_desc(d);
@@ -399,6 +450,7 @@ const char* kda_status_str(kda_status s) {
     case KDA_ERR_UNSUPPORTED: return "unsupported configuration";
     case KDA_ERR_WORKSPACE: return "workspace missing or too small";
     case KDA_ERR_HIP: return "HIP launch failure";
+    case KDA_ERR_TIMEOUT: return "an in-kernel wait for chunk records gave up: outputs invalid";
   }
   return "unknown status";
 }
@@ -549,7 +601,8 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     return r;
   };
   auto launch_scan = [&](int64_t c0, int nc, const kda::ChunkWs& recs, const float* S_in, float* S_out,
-                         hipStream_t st_, const uint32_t* done = nullptr, const Plan* segs = nullptr) {
+                         hipStream_t st_, const uint32_t* done = nullptr, const Plan* segs = nullptr,
+                         uint32_t* status = nullptr) {
     kda::ScanParams sp{};
     sp.v = v;
     sp.gate = y ? gate : nullptr;
@@ -567,6 +620,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     sp.nc = nc;
     sp.ws = recs;
     sp.done = done;
+    sp.status = status;
     sp.snaps = snap.n > 0 ? snap.ptr : nullptr;
     sp.snap_every = snap.every;
     sp.n_snap = snap.n;
@@ -580,7 +634,12 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     return r;
   };
 
-  const Plan plan = make_plan(d, ws_bytes);
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &capture) != hipSuccess) {
+    (void)hipGetLastError();
+    capture = hipStreamCaptureStatusNone;
+  }
+  const Plan plan = make_plan(d, ws_bytes, capture != hipStreamCaptureStatusNone);
 
   // ---- fused schedule: one launch, records in LDS
   if (plan.fused) {
@@ -635,32 +694,37 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     DeviceCtx& c = g_dev[plan.dev];
     std::lock_guard<std::mutex> lock(c.mu);
     hipStream_t si = nullptr, ss = nullptr;
-    if (!stream_pair(c, plan.n_scan, &si, &ss)) return KDA_ERR_HIP;  // make_plan created the pair
+    if (!stream_pair(c, plan.n_scan, &si, &ss)) return KDA_ERR_HIP;
     kda::ChunkWs recs{};
     recs.base = base + L.off_rec;
     recs.rec_bytes = (int64_t)L.rec_bytes;
-    uint32_t* done = reinterpret_cast<uint32_t*>(base + L.off_done);
+    uint32_t* status = reinterpret_cast<uint32_t*>(base + L.off_done);
+    uint32_t* done = status + kStatusWords;
     auto ok = [](hipError_t e) {
       if (e == hipSuccess) return true;
       (void)hipGetLastError();
       return false;
     };
     const int64_t bh_n = (int64_t)d->B * d->H;
-    st = check_launch(kda::launch_copy_state(nullptr, reinterpret_cast<float*>(done), plan.n_seg * bh_n, s), s);
+    st = check_launch(
+        kda::launch_copy_state(nullptr, reinterpret_cast<float*>(status), kStatusWords + plan.n_seg * bh_n, s), s);
     if (st != KDA_OK) return st;
     if (!ok(hipEventRecord(c.fork, s)) || !ok(hipStreamWaitEvent(si, c.fork, 0)) ||
         !ok(hipStreamWaitEvent(ss, c.fork, 0)))
       return KDA_ERR_HIP;
     float* S_out = S_T ? S_T : reinterpret_cast<float*>(base + L.off_carry);
-    for (int sg = 0; sg < plan.n_seg; ++sg) {
+    // Every intra-chunk launch is enqueued before the scan: should the two
+    // library streams share a hardware queue (their work then runs in
+    // enqueue order), the scan still finds every record written instead of
+    // waiting for producers queued behind it.
+    const int produced = withheld_segments(plan.n_seg);
+    for (int sg = 0; sg < produced; ++sg) {
       const int c0 = sg == 0 ? 0 : plan.seg_end[sg - 1];
       st = launch_intra(c0, plan.seg_end[sg] - c0, recs, si, done + sg * bh_n, (int)nc_total, c0);
       if (st != KDA_OK) return st;
-      if (sg == 0) {
-        st = launch_scan(0, (int)nc_total, recs, S0, S_out, ss, done, &plan);
-        if (st != KDA_OK) return st;
-      }
     }
+    st = launch_scan(0, (int)nc_total, recs, S0, S_out, ss, done, &plan, status);
+    if (st != KDA_OK) return st;
     if (!ok(hipEventRecord(c.join_intra, si)) || !ok(hipEventRecord(c.join_scan, ss)) ||
         !ok(hipStreamWaitEvent(s, c.join_intra, 0)) || !ok(hipStreamWaitEvent(s, c.join_scan, 0)))
       return KDA_ERR_HIP;
@@ -690,7 +754,8 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
       }
       float* carry = reinterpret_cast<float*>(base + L.off_carry);
       float* S_run = S_T ? S_T : carry;
-      uint32_t* done = reinterpret_cast<uint32_t*>(base + L.off_done);
+      uint32_t* status = reinterpret_cast<uint32_t*>(base + L.off_done);
+      uint32_t* done = status + kStatusWords;
       auto ok = [](hipError_t e) {
         if (e == hipSuccess) return true;
         (void)hipGetLastError();
@@ -699,7 +764,8 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
       const int64_t n_seg = (nc_total + seg_nc - 1) / seg_nc;
       // zero bits: the fp32 fill of a state copy from nothing
       const int64_t bh_n = (int64_t)d->B * d->H;
-      st = check_launch(kda::launch_copy_state(nullptr, reinterpret_cast<float*>(done), n_seg * bh_n, s), s);
+      st = check_launch(
+          kda::launch_copy_state(nullptr, reinterpret_cast<float*>(status), kStatusWords + n_seg * bh_n, s), s);
       if (st != KDA_OK) return st;
       if (!ok(hipEventRecord(c.fork, s)) || !ok(hipStreamWaitEvent(si, c.fork, 0)) ||
           !ok(hipStreamWaitEvent(ss, c.fork, 0)))
@@ -713,7 +779,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
         if (seg >= 2 && !ok(hipStreamWaitEvent(si, c.scan_done[j], 0))) return KDA_ERR_HIP;
         st = launch_intra(c0, nc, bufs[j], si, done + seg * bh_n);
         if (st != KDA_OK) return st;
-        st = launch_scan(c0, nc, bufs[j], S_in, S_run, ss, done + seg * bh_n);
+        st = launch_scan(c0, nc, bufs[j], S_in, S_run, ss, done + seg * bh_n, nullptr, status);
         if (st != KDA_OK) return st;
         if (!ok(hipEventRecord(c.scan_done[j], ss))) return KDA_ERR_HIP;
         S_in = S_run;
@@ -988,11 +1054,12 @@ int32_t kda_snapshot_count(const kda_desc* d, int32_t every_chunks) {
 }
 
 kda_status kda_recurrent_step(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
-                              const void* z, const float* A, float* S_pool, const int32_t* slot,
-                              const void* gate, const float* rms_w, void* o, void* y, void* stream) {
+                              const void* z, const float* A, float* S_pool, int32_t n_slots, const int32_t* slot,
+                              const void* gate, const float* rms_w, void* o, void* y, uint32_t* status,
+                              void* stream) {
   kda_status st = validate_desc(d);
   if (st != KDA_OK) return st;
-  if (d->T != 1) return KDA_ERR_BAD_SHAPE;
+  if (d->T != 1 || n_slots < 1 || (slot == nullptr && d->B > n_slots)) return KDA_ERR_BAD_SHAPE;
   if (!q || !k || !v || !beta || !z || !A || !S_pool) return KDA_ERR_NULL_ARG;
   if (!o && !y) return KDA_ERR_NULL_ARG;
   if (y && !gate) return KDA_ERR_NULL_ARG;
@@ -1000,10 +1067,12 @@ kda_status kda_recurrent_step(const kda_desc* d, const void* q, const void* k, c
   for (const void* p : {q, k, v, z, (const void*)o, (const void*)y, gate})
     if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
   if (!aligned(beta, es) || !aligned(A, 4) || !aligned(S_pool, 4) || (slot && !aligned(slot, 4)) ||
-      (rms_w && !aligned(rms_w, 4)))
+      (rms_w && !aligned(rms_w, 4)) || (status && !aligned(status, 4)))
     return KDA_ERR_MISALIGNED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   kda::DecodeParams p{};
+  p.n_slots = n_slots;
+  p.status = status;
   p.q = q;
   p.k = k;
   p.v = v;
@@ -1029,17 +1098,22 @@ kda_status kda_recurrent_step(const kda_desc* d, const void* q, const void* k, c
 }
 
 kda_status kda_state_io(kda_state_op op, int32_t n, int32_t H, int32_t d_k, int32_t d_v, kda_state_layout layout,
-                        float* pool, const int32_t* slot, float* user, void* stream) {
+                        float* pool, int32_t n_slots, const int32_t* slot, float* user, uint32_t* status,
+                        void* stream) {
   if (op != KDA_STATE_ZERO && op != KDA_STATE_IMPORT && op != KDA_STATE_EXPORT) return KDA_ERR_UNSUPPORTED;
   if (layout != KDA_LAYOUT_KV && layout != KDA_LAYOUT_VK) return KDA_ERR_UNSUPPORTED;
-  if (n < 0 || H < 1 || d_k < 1 || d_v < 1) return KDA_ERR_BAD_SHAPE;
+  if (n < 0 || H < 1 || d_k < 1 || d_v < 1 || n_slots < 1 || (slot == nullptr && n > n_slots))
+    return KDA_ERR_BAD_SHAPE;
   if (d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_ERR_UNSUPPORTED;
   if (!pool) return KDA_ERR_NULL_ARG;
   if (op != KDA_STATE_ZERO && !user) return KDA_ERR_NULL_ARG;
-  if (!aligned(pool, 4) || (user && !aligned(user, 4)) || (slot && !aligned(slot, 4))) return KDA_ERR_MISALIGNED;
+  if (!aligned(pool, 4) || (user && !aligned(user, 4)) || (slot && !aligned(slot, 4)) || (status && !aligned(status, 4)))
+    return KDA_ERR_MISALIGNED;
   if (n == 0) return KDA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   kda::StateIoParams p{};
+  p.n_slots = n_slots;
+  p.status = status;
   p.op = static_cast<int>(op);
   p.transpose = layout == KDA_LAYOUT_VK;
   p.n = n;

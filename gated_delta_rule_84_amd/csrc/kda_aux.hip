@@ -14,6 +14,10 @@ __global__ __launch_bounds__(256) void kda_state_io_kernel(const StateIoParams p
   const int h = blockIdx.x, n = blockIdx.y;
   const int tid = threadIdx.x;
   const int64_t slot = (p.slot != nullptr) ? (int64_t)p.slot[n] : (int64_t)n;
+  if (slot < 0 || slot >= p.n_slots) {  // uniform over the workgroup: nothing is touched
+    if (tid == 0) raise_status(p.status, kFlagBadSlot);
+    return;
+  }
   float* pool = p.pool + (slot * p.H + h) * D * D;
   float* user = (p.user != nullptr) ? p.user + ((int64_t)n * p.H + h) * D * D : nullptr;
   // Same layout: a copy of the head's D x D floats in 16-byte vectors (each

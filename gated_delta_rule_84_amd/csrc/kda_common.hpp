@@ -232,4 +232,9 @@ __device__ __forceinline__ bool wait_records(const uint32_t* done, uint32_t targ
   return ok;
 }
 
+// OR a status bit into a device-wide status word (a device-scope atomic).
+__device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bit) {
+  if (status != nullptr) __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace kda

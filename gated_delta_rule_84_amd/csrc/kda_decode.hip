@@ -30,6 +30,11 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const DecodeParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = tid % D, rg = tid / D;
   const int64_t row = (int64_t)n * p.H + h;  // [n, H] token row
+  const int64_t slot = (p.slot != nullptr) ? (int64_t)p.slot[n] : (int64_t)n;
+  if (slot < 0 || slot >= p.n_slots) {  // uniform over the workgroup: no state, o or y is touched
+    if (tid == 0) raise_status(p.status, kFlagBadSlot);
+    return;
+  }
   const T* q = static_cast<const T*>(p.q) + row * D;
   const T* k = static_cast<const T*>(p.k) + row * D;
   const T* z = static_cast<const T*>(p.z) + row * D;
@@ -68,7 +73,6 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const DecodeParams p) {
   }
   __syncthreads();
 
-  const int64_t slot = (p.slot != nullptr) ? (int64_t)p.slot[n] : (int64_t)n;
   float* S = p.S_pool + (slot * p.H + h) * D * D;
   float s[RPT];
   float w = 0.f;

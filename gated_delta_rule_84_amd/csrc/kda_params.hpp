@@ -89,6 +89,11 @@ struct IntraParams {
   int rec_stride, rec_c0;
 };
 
+// Status bits a kernel ORs into the workspace's status word (read by
+// kda_chunk_fwd_status).
+constexpr uint32_t kStatusWaitGaveUp = 1u;  // a bounded wait for records ran out: outputs are invalid
+constexpr uint32_t kFlagBadSlot = 1u;       // a state-pool slot was outside [0, n_slots): that sequence skipped
+
 // Segment table of a scan launch that covers several intra-chunk launches
 // (the pipelined schedule): segment s holds the launch's chunks
 // [seg_end[s - 1], seg_end[s]) (seg_end[-1] = 0), and its records are
@@ -109,6 +114,7 @@ struct ScanParams {
   int t0, nc;           // first token and number of chunks of the segment
   ChunkWs ws;
   const uint32_t* done;  // [B * H]: wait until done[b H + h] >= nc before reading records, or nullptr
+  uint32_t* status;     // word OR-ed with kStatusWaitGaveUp when such a wait gives up, or nullptr
   float* snaps;         // [B, n_snap, H, D, D] states at every snap_every-th chunk boundary, or nullptr
   int snap_every;       // chunks between snapshots (snapshot j: state after chunk (j + 1) * snap_every - 1)
   int n_snap;
@@ -134,8 +140,10 @@ struct DecodeParams {
   const void* beta;
   const void* z;
   const float* A;
-  float* S_pool;          // [*, H, D, D]
-  const int32_t* slot;    // [n] or nullptr
+  float* S_pool;          // [n_slots, H, D, D]
+  int n_slots;
+  const int32_t* slot;    // [n] or nullptr; a slot outside [0, n_slots) is skipped and flagged
+  uint32_t* status;       // OR-ed with kFlagBadSlot for such a slot, or nullptr
   const void* gate;       // [n, H, D] or nullptr
   const float* rms_w;     // [H, D] or nullptr
   void* o;                // [n, H, D] or nullptr
@@ -151,8 +159,10 @@ struct StateIoParams {
   int op;          // 0 zero, 1 import (user -> pool), 2 export (pool -> user)
   int transpose;   // user layout [D_v][D_k] when 1
   int n, H;
-  float* pool;
-  const int32_t* slot;
+  float* pool;            // [n_slots, H, D, D]
+  int n_slots;
+  const int32_t* slot;    // [n] or nullptr; a slot outside [0, n_slots) is skipped and flagged
+  uint32_t* status;       // OR-ed with kFlagBadSlot for such a slot, or nullptr
   float* user;
   int vec16;       // pool and user (if any) 16-byte aligned: copy in 16-byte vectors
 };

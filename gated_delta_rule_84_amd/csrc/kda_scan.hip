@@ -168,6 +168,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
     if (wave == 0) {
       const bool ok = wait_records(p.done + bh, (uint32_t)p.nc);
       if (lane == 0) gave_up = ok ? 0 : 1;
+      if (!ok && lane == 0) raise_status(p.status, kStatusWaitGaveUp);
     }
     __syncthreads();
     poison = gave_up != 0;
@@ -496,6 +497,7 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
         for (int s = 0; s < wseg && ok; ++s) ok = wait_records(seg_done(s), (uint32_t)(p.seg_end[s] - seg_start(s)));
       }
       if (lane == 0) *gave_up = ok ? 0 : 1;
+      if (!ok && lane == 0) raise_status(p.status, kStatusWaitGaveUp);
     }
     __syncthreads();
     poison = *gave_up != 0;
@@ -637,6 +639,7 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
       if (opens && wave == L::NCW && !poison) {
         const bool ok = wait_records(seg_done(wseg), (uint32_t)(p.seg_end[wseg] - seg_start(wseg)));
         if (lane == 0) *gave_up = ok ? 0 : 1;
+        if (!ok && lane == 0) raise_status(p.status, kStatusWaitGaveUp);
       }
       __syncthreads();
       if (opens) {

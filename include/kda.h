@@ -11,8 +11,18 @@
  *
  * Conventions shared by every entry point
  *  - Tensors are dense, row-major, caller-owned DEVICE pointers (HIP device
- *    memory).  The library never allocates or frees device memory and keeps no
- *    global state; it is safe to call from several host threads.
+ *    memory).  The library never allocates or frees device memory (apart from
+ *    kda_chunk_fwd_noalloc's file-scope scratch array, see there).  Its only
+ *    global state is per device: for the two-stream schedules of
+ *    kda_chunk_fwd, one pair of library streams (default priority, each
+ *    restricted to its own compute units; made by the first such call,
+ *    rebuilt -- after waiting for them -- when a call needs a different
+ *    split, released by kda_release_resources) and five events, guarded by a
+ *    per-device lock.  It is safe to call from several host threads.
+ *  - Hardware queues: the two-stream schedules use two queues of their own
+ *    beside the caller's.  They do not depend on running concurrently for
+ *    correctness (every producer launch is enqueued before the consumer that
+ *    waits for it), only for speed.
  *  - Layouts: q, k, z: [B, T, H, d_k]; v, o, gate, y: [B, T, H, d_v];
  *    beta: [B, T, H]; A: [H] fp32; states S0, S_T, S_pool: [.., H, d_k, d_v]
  *    fp32 with the key channel as row index (o = S^T q).
@@ -41,7 +51,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 typedef enum {
   KDA_OK = 0,
@@ -51,7 +61,9 @@ typedef enum {
   KDA_ERR_MISALIGNED = 4,   /* a pointer breaks the alignment rules above          */
   KDA_ERR_UNSUPPORTED = 5,  /* valid request outside what the kernels implement    */
   KDA_ERR_WORKSPACE = 6,    /* workspace missing or smaller than one chunk needs   */
-  KDA_ERR_HIP = 7           /* a kernel launch failed (HIP error read and cleared)  */
+  KDA_ERR_HIP = 7,          /* a kernel launch failed (HIP error read and cleared)  */
+  KDA_ERR_TIMEOUT = 8       /* reported by kda_chunk_fwd_status: an in-kernel wait
+                               for chunk records gave up (outputs are invalid)     */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -159,6 +171,19 @@ kda_status kda_release_resources(void);
 kda_status kda_chunk_fwd_schedule(const kda_desc* d, size_t ws_bytes, int32_t* segment_tokens,
                                   int32_t* schedule);
 
+/*
+ * Outcome of the most recent kda_chunk_fwd / kda_chunk_fwd_traced call that
+ * used workspace ws (ws_bytes bytes) with this descriptor: waits for `stream`
+ * (a host synchronisation, unlike every other entry point), then returns
+ * KDA_OK, or KDA_ERR_TIMEOUT when that call took a two-stream schedule and
+ * one of the scan's bounded in-kernel waits for chunk records gave up -- its
+ * producers never ran beside it (e.g. another process held the device's
+ * compute units for about a second); the call's outputs are then invalid
+ * (NaN).  Calls that took the one-stream or fused schedule always report
+ * KDA_OK here.
+ */
+kda_status kda_chunk_fwd_status(const kda_desc* d, const void* ws, size_t ws_bytes, void* stream);
+
 /* The kernel launches, in order, that kda_chunk_fwd_traced brackets with
  * events for this descriptor and workspace size on the current device:
  * *n_launches receives their number and kinds[i] (i < max_kinds) the
@@ -216,9 +241,16 @@ kda_status kda_chunk_fwd_launches(const kda_desc* d, size_t ws_bytes, int32_t* k
  * d->segment_tokens each, 4096 by default) and a single
  * scan launch over the whole sequence runs on the other, waiting inside the
  * kernel for each segment's records (device-scope record stores, one counter
- * per segment and (b, h); bounded waits, so a producer that never runs shows
- * as NaN output, not a hang).  Results are bit-identical to the other
- * two-kernel schedules.
+ * per segment and (b, h)).  Every intra-chunk launch is enqueued before the
+ * scan, so the call completes correctly even when the two library streams
+ * end up sharing a hardware queue (their work then runs one after the
+ * other).  The waits are bounded (about a second): a producer kept from
+ * running that long shows as NaN output, not a hang, and
+ * kda_chunk_fwd_status reports KDA_ERR_TIMEOUT for the call.  Results are
+ * bit-identical to the other two-kernel schedules.
+ *
+ * When `stream` is being captured into a HIP graph, the one-stream schedule
+ * is taken (its launches have no in-kernel waits on other nodes).
  */
 kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
                          const void* z, const float* A, const float* S0, const void* gate, const float* rms_w,
@@ -347,30 +379,46 @@ kda_status kda_input_prep(const kda_desc* d, int32_t conv_width, const void* xq,
                           const float* state_in, float* state_out, void* q, void* k, void* v, void* beta,
                           void* stream);
 
+/* Bit that kda_recurrent_step / kda_state_io OR into *status for a slot
+ * outside [0, n_slots) (that sequence / state is skipped, nothing of it is
+ * read or written). */
+#define KDA_FLAG_BAD_SLOT 1u
+
 /*
  * One decode step (single token) for d->B sequences: the same recurrence,
  * section 2.1, applied to one token.  d->T must be 1.  Each sequence n reads
  * and updates its state in place at S_pool[slot[n]] (slot == NULL: slot n):
  *  q, k, v, z, gate, o, y  are [B, 1, H, d], beta is [B, 1, H];
  *  S_pool  [n_slots, H, d_k, d_v] fp32 state pool, updated in place;
- *  slot    [B] int32 device array of distinct pool rows, or NULL;
- *  o, y    outputs as in kda_chunk_fwd (y requires gate).
+ *  slot    [B] int32 device array of distinct pool rows, or NULL (then
+ *          B <= n_slots, else KDA_ERR_BAD_SHAPE);
+ *  o, y    outputs as in kda_chunk_fwd (y requires gate);
+ *  status  device uint32 or NULL: a sequence whose slot lies outside
+ *          [0, n_slots) is skipped (its state row, o and y are not touched)
+ *          and KDA_FLAG_BAD_SLOT is OR-ed into *status (which the caller
+ *          clears).  The slots live in device memory, so this check runs in
+ *          the kernel, not on the host.
  * Slots must be distinct within one call (two sequences writing one slot race).
  */
 kda_status kda_recurrent_step(const kda_desc* d, const void* q, const void* k, const void* v, const void* beta,
-                              const void* z, const float* A, float* S_pool, const int32_t* slot,
-                              const void* gate, const float* rms_w, void* o, void* y, void* stream);
+                              const void* z, const float* A, float* S_pool, int32_t n_slots, const int32_t* slot,
+                              const void* gate, const float* rms_w, void* o, void* y, uint32_t* status,
+                              void* stream);
 
 /*
  * State hand-off between a state pool and caller buffers (prefill -> decode,
  * prefix-cache snapshots): ZERO clears pool rows, IMPORT copies user -> pool,
  * EXPORT copies pool -> user.
- *  n      number of states moved; slot [n] int32 device array or NULL (0..n-1);
+ *  n      number of states moved; slot [n] int32 device array or NULL (0..n-1,
+ *         then n <= n_slots);
  *  pool   [n_slots, H, d_k, d_v] fp32;  user [n, H, ...] fp32 in `layout`
  *         (NULL for ZERO).  d_k == d_v in {64, 128}.
+ *  status device uint32 or NULL: a slot outside [0, n_slots) is skipped and
+ *         KDA_FLAG_BAD_SLOT is OR-ed into *status, as for kda_recurrent_step.
  */
 kda_status kda_state_io(kda_state_op op, int32_t n, int32_t H, int32_t d_k, int32_t d_v, kda_state_layout layout,
-                        float* pool, const int32_t* slot, float* user, void* stream);
+                        float* pool, int32_t n_slots, const int32_t* slot, float* user, uint32_t* status,
+                        void* stream);
 
 /*
  * Pre-pass diagnostic (the first step of kda_chunk_fwd, exposed for tests):

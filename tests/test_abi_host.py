@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert {"kda_chunk_fwd", "kda_recurrent_step", "kda_state_io"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kda_abi_version() == 4
+    assert L.kda_abi_version() == 5
     assert L.kda_status_str(6) == b"workspace missing or too small"
 
 
@@ -104,16 +104,23 @@ def test_decode_and_state_io_host_errors():
     L = kda.lib()
     d = _desc()
     args = [FAKE] * 6
-    assert L.kda_recurrent_step(ctypes.byref(d), *args, FAKE, None, None, None, FAKE, None, None) == 2  # T != 1
+    assert L.kda_recurrent_step(ctypes.byref(d), *args, FAKE, 64, None, None, None, FAKE, None, None, None) == 2  # T != 1
     d.T = 1
-    assert L.kda_recurrent_step(ctypes.byref(d), *args, None, None, None, None, FAKE, None, None) == 1  # no pool
-    assert L.kda_recurrent_step(ctypes.byref(d), *args, FAKE, None, None, None, None, FAKE, None) == 1  # y, no gate
-    assert L.kda_recurrent_step(ctypes.byref(d), *args, FAKE, FAKE + 2, None, None, FAKE, None, None) == 4
-    assert L.kda_state_io(9, 1, 1, 128, 128, 0, FAKE, None, FAKE, None) == 5
-    assert L.kda_state_io(1, 1, 1, 128, 64, 0, FAKE, None, FAKE, None) == 5
-    assert L.kda_state_io(1, 1, 1, 128, 128, 0, FAKE, None, None, None) == 1
-    assert L.kda_state_io(0, -1, 1, 128, 128, 0, FAKE, None, None, None) == 2
-    assert L.kda_state_io(1, 0, 1, 128, 128, 0, FAKE, None, FAKE, None) == 0  # nothing to do
+    assert L.kda_recurrent_step(ctypes.byref(d), *args, None, 64, None, None, None, FAKE, None, None, None) == 1  # no pool
+    assert L.kda_recurrent_step(ctypes.byref(d), *args, FAKE, 64, None, None, None, None, FAKE, None, None) == 1  # y, no gate
+    # pool rows: at least one, and B of them for the identity mapping
+    assert L.kda_recurrent_step(ctypes.byref(d), *args, FAKE, 0, None, None, None, FAKE, None, None, None) == 2
+    assert L.kda_recurrent_step(ctypes.byref(d), *args, FAKE, d.B - 1, None, None, None, FAKE, None, None, None) == 2
+    assert L.kda_recurrent_step(ctypes.byref(d), *args, FAKE, 64, FAKE + 2, None, None, FAKE, None, None, None) == 4
+    assert L.kda_state_io(9, 1, 1, 128, 128, 0, FAKE, 1, None, FAKE, None, None) == 5
+    assert L.kda_state_io(1, 1, 1, 128, 64, 0, FAKE, 1, None, FAKE, None, None) == 5
+    assert L.kda_state_io(1, 1, 1, 128, 128, 0, FAKE, 1, None, None, None, None) == 1
+    assert L.kda_state_io(0, -1, 1, 128, 128, 0, FAKE, 1, None, None, None, None) == 2
+    # pool row counts: at least one, and enough rows for the identity mapping
+    assert L.kda_state_io(0, 2, 1, 128, 128, 0, FAKE, 0, None, None, None, None) == 2
+    assert L.kda_state_io(0, 3, 1, 128, 128, 0, FAKE, 2, None, None, None, None) == 2
+    assert L.kda_state_io(1, 1, 1, 128, 128, 0, FAKE, 1, None, FAKE, FAKE + 2, None) == 4  # status alignment
+    assert L.kda_state_io(1, 0, 1, 128, 128, 0, FAKE, 1, None, FAKE, None, None) == 0  # nothing to do
 
 
 def test_no_cpu_fallback(monkeypatch, tmp_path):

@@ -53,3 +53,15 @@ def test_profile_figures_follow_the_source_hash(tmp_path, monkeypatch):
     _write_profile(tmp_path, "hbm_traffic_w.txt", "0" * 64, ["scan_hbm_bytes_per_launch: 1234"])
     (tmp_path / "profiles" / "counters_w.txt").write_text("# source_sha256: " + "0" * 64 + "\nscan_mfma_tflops: 1\n")
     assert bench.profiled_traffic("scan", "w") is None and bench.profiled_counters("w") is None
+
+
+def test_path_bytes_and_headline_roofline_definition():
+    """The headline roofline credits the dominant launch with the path's
+    algorithmic bytes of every token-head it processes: 1,538 B per token-head
+    at d = 128 (q, k, z, v, gate in and y out at 2 d bytes, beta 2 bytes)."""
+    assert bench.path_bytes_per_token_head(128) == 1538
+    assert bench.path_bytes_per_token_head(64) == 6 * 128 + 2
+
+
+def test_cpu_model_is_a_string():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()

@@ -193,14 +193,17 @@ def test_pipelined_schedule_matches_one_stream(kda, B, T, H, D, seg, opts):
     intra-chunk kernel launched per segment on one library stream beside ONE
     scan launch over the sequence that waits inside the kernel for each
     segment's record counters) gives bit-identical results to the one-stream
-    schedule; the launch-order query matches what the call does."""
+    schedule; the launch-order query matches what the call does (every
+    intra-chunk launch, then the scan: should the library's two streams
+    share a hardware queue, the scan then finds every record written)."""
     wl = _custom(B, T, H, D, "bf16", seed=B * 1000 + T)
     x = gen_inputs(wl)
     desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg, overlap=True, fused=False)
     nbytes = kda.workspace_size(desc)
     assert kda.schedule(desc, nbytes)[1] == "pipelined"
     order = kda.launches(desc, nbytes)
-    assert order[:2] == ["intra", "scan"] and order.count("scan") == 1 and len(order) >= 3
+    # every intra-chunk launch first, then the one scan launch
+    assert order[-1] == "scan" and order.count("scan") == 1 and len(order) >= 3
     log(f"[pipelined] B={B} T={T} H={H} D={D} segment={seg} launches={len(order)}")
     one = _run(kda, x, overlap=False, fused=False, **opts)
     pip = _run(kda, x, overlap=True, segment_tokens=seg, fused=False, **opts)
@@ -238,7 +241,7 @@ def test_pipelined_schedule_reuses_workspace_and_traces(kda):
     ws = torch.empty(kda.workspace_size(desc), dtype=torch.uint8, device="cuda")
     assert kda.schedule(desc, ws.numel())[1] == "pipelined"
     order = kda.launches(desc, ws.numel())
-    assert order == ["intra", "scan"] + ["intra"] * 31
+    assert order == ["intra"] * 32 + ["scan"]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(order))]
     for e in ev:
         e.record()
@@ -254,7 +257,7 @@ def test_pipelined_schedule_reuses_workspace_and_traces(kda):
         outs.append((x, r))
     torch.cuda.synchronize()
     ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(len(order))]
-    assert all(m >= 0.0 for m in ms) and ms[1] > 0.0
+    assert all(m >= 0.0 for m in ms) and ms[-1] > 0.0
     for x, r in outs:
         one = _run(kda, x, overlap=False, fused=False)
         for key in ("o", "y", "S_T"):
