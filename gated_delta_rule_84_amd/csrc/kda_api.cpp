@@ -350,7 +350,7 @@ int32_t plan_launches(const kda_desc* d, const Plan& p, int32_t* kinds, int32_t 
   if (p.fused) {
     put(KDA_LAUNCH_FUSED);
   } else if (p.pipelined) {
-    for (int s = 0; s < p.n_seg; ++s) put(KDA_LAUNCH_INTRA);
+    put(KDA_LAUNCH_INTRA);
     put(KDA_LAUNCH_SCAN);
   } else {
     const int64_t nc_total = num_chunks(d);
@@ -573,8 +573,10 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   char* base = static_cast<char*>(ws);
 
   // one segment: records of chunks [c0, c0 + nc) in `recs`; state S_in -> S_out
+  // segs: the pipelined schedule's segment table (the record counters of one
+  // launch over several segments)
   auto launch_intra = [&](int64_t c0, int nc, const kda::ChunkWs& recs, hipStream_t st_, uint32_t* done = nullptr,
-                          int rec_stride = 0, int rec_c0 = 0) {
+                          int rec_stride = 0, int rec_c0 = 0, const Plan* segs = nullptr) {
     kda::IntraParams ip{};
     ip.q = q;
     ip.k = k;
@@ -593,6 +595,10 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     ip.decay = d->decay;
     ip.ws = recs;
     ip.done = done;
+    if (segs != nullptr) {
+      ip.n_seg = segs->n_seg;
+      for (int i = 0; i < segs->n_seg; ++i) ip.seg_end[i] = segs->seg_end[i];
+    }
     ip.rec_stride = rec_stride;
     ip.rec_c0 = rec_c0;
     tr.before(st_);
@@ -684,11 +690,11 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   }
 
   // ---- pipelined schedule (see pipelined_eligible): every record in the
-  // workspace, [B H][nc_total]; intra-chunk launches per segment on one
-  // library stream, one scan launch over the sequence on the other, which
-  // waits inside the kernel for each segment's record counters (zeroed on the
-  // caller's stream first).  Launch order: intra(0), scan, intra(1), ... so
-  // that the scan is queued before the later segments' producers.
+  // workspace, [B H][nc_total]; one intra-chunk launch over the sequence on
+  // one library stream (records in chunk order, each counted in its
+  // segment's counter), one scan launch over the sequence on the other,
+  // which waits inside the kernel for each segment's record counters (zeroed
+  // on the caller's stream first).
   if (plan.pipelined) {
     const WsLayout L = layout_for(d, nc_total);
     DeviceCtx& c = g_dev[plan.dev];
@@ -713,14 +719,13 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
         !ok(hipStreamWaitEvent(ss, c.fork, 0)))
       return KDA_ERR_HIP;
     float* S_out = S_T ? S_T : reinterpret_cast<float*>(base + L.off_carry);
-    // Every intra-chunk launch is enqueued before the scan: should the two
+    // The intra-chunk launch is enqueued before the scan: should the two
     // library streams share a hardware queue (their work then runs in
     // enqueue order), the scan still finds every record written instead of
     // waiting for producers queued behind it.
     const int produced = withheld_segments(plan.n_seg);
-    for (int sg = 0; sg < produced; ++sg) {
-      const int c0 = sg == 0 ? 0 : plan.seg_end[sg - 1];
-      st = launch_intra(c0, plan.seg_end[sg] - c0, recs, si, done + sg * bh_n, (int)nc_total, c0);
+    if (produced > 0) {
+      st = launch_intra(0, plan.seg_end[produced - 1], recs, si, done, (int)nc_total, 0, &plan);
       if (st != KDA_OK) return st;
     }
     st = launch_scan(0, (int)nc_total, recs, S0, S_out, ss, done, &plan, status);

@@ -1,6 +1,6 @@
-// Intra-chunk kernel: one workgroup (4 waves) per (chunk, head, batch) runs
-// the intra-chunk steps of kda_intra_core.hpp and writes the chunk's record
-// to the workspace for the state scan.
+// Intra-chunk kernel: workgroups of 4 waves run the intra-chunk steps of
+// kda_intra_core.hpp for the launch's (chunk, batch, head) records and write
+// each record to the workspace for the state scan.
 //
 // Source: "Kimi K3: KDA, Attention Residuals and Stable LatentMoE"
 // (hs-black.github.io/posts/kimi-k3), sections 2.1 and 2.2 (see
@@ -28,6 +28,11 @@ struct IntraLds {
   static constexpr int BYTES = TM + 64 * LP * 4;
 };
 
+// One workgroup (4 waves) per record of the launch, in chunk-major order:
+// workgroup item = c B H + b H + h, so that the records of a chunk come out
+// together for every head, as the state scan consumes them, and the rows of
+// a chunk's q, k, z are read for all heads at once.
+//
 // SP: the unbounded softplus decay (pairwise diagonal blocks, more registers:
 // two workgroups per CU).
 template <typename T, int D, bool SP>
@@ -41,12 +46,15 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
                           reinterpret_cast<float*>(lds + L::EL),   reinterpret_cast<float*>(lds + L::BETA),
                           reinterpret_cast<T*>(lds + L::KC),       reinterpret_cast<float*>(lds + L::TM)};
 
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
+  const int bh_n = p.B * p.H;
+  const int item = blockIdx.x;
+  const int c = item / bh_n, bh = item % bh_n;
+  const int b = bh / p.H, h = bh % p.H;
   const int tok0 = p.t0 + c * kChunk;
   const int nvalid = min(kChunk, p.T - tok0);
   const int64_t stride = p.rec_stride > 0 ? p.rec_stride : p.nc;
-  const int64_t rec = ((int64_t)b * p.H + h) * stride + p.rec_c0 + c;
+  const int64_t rec = (int64_t)bh * stride + p.rec_c0 + c;
   constexpr RecUnits RU = rec_units((int)sizeof(T), D);
   char* recp = p.ws.base + rec * p.ws.rec_bytes;
 
@@ -71,12 +79,25 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
     __syncthreads();
   }
   Core::template tb_pass<256>(tid, s, reinterpret_cast<T*>(recp + 16 * RU.tb), &ic.sink);
-  if (p.done != nullptr) count_record(p.done + (int64_t)b * p.H + h);
+  if (p.done != nullptr) {
+    // the record's counter: its segment of seg_end (binary search; one segment if n_seg = 0)
+    int seg = 0;
+    if (p.n_seg > 0) {
+      int lo = 0, hi = p.n_seg - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (c < p.seg_end[mid]) hi = mid;
+        else lo = mid + 1;
+      }
+      seg = lo;
+    }
+    count_record(p.done + (int64_t)seg * bh_n + bh);
+  }
 }
 
 template <bool SP>
 static void launch_intra_t(const IntraParams& p, int D, int in_f32, hipStream_t s) {
-  const dim3 grid(p.nc, p.H, p.B), block(256);
+  const dim3 grid((unsigned)(p.nc * p.B * p.H)), block(256);
   if (in_f32) {
     if (D == 64) hipLaunchKernelGGL((kda_intra_kernel<float, 64, SP>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((kda_intra_kernel<float, 128, SP>), grid, block, 0, s, p);
@@ -87,6 +108,7 @@ static void launch_intra_t(const IntraParams& p, int D, int in_f32, hipStream_t 
 }
 
 hipError_t launch_intra(const IntraParams& p, int D, int in_f32, hipStream_t s) {
+  if (p.nc <= 0) return hipSuccess;
   if (p.decay) launch_intra_t<true>(p, D, in_f32, s);
   else launch_intra_t<false>(p, D, in_f32, s);
   return hipGetLastError();

@@ -226,11 +226,12 @@ struct IntraCore {
       Bv[i] = SP ? off[i] : off[i] + s.loc7[i * D + ch];
       Ev[i] = SP ? (i < 3 ? off[i + 1] : glast) : Bv[i];
     }
+    // 15 items per channel, item % TPC == part for this thread; every index
+    // is a compile-time constant and `part` is uniform over a wave (D >= 64)
 #pragma unroll
-    for (int it = 0; it < (15 + TPC - 1) / TPC; ++it) {
-      const int item = part + TPC * it;
-      if (item >= 15) {
-      } else if (item < 4) {
+    for (int item = 0; item < 15; ++item) {
+      if (item % TPC != part) continue;
+      if (item < 4) {
         s.eB[item * D + ch] = hw_exp2(Bv[item] + RO::kLog2Up);  // the record's factor on q^ . Gamma, k^ . Gamma
       } else if (item < 8) {
         s.eL[(item - 4) * D + ch] = hw_exp2(glast - Ev[item - 4] - RO::kLog2Up);  // and its inverse on Kd

@@ -70,6 +70,10 @@ struct ChunkWs {
   int64_t rec_bytes;
 };
 
+// Segment table of the pipelined schedule: segment s holds the chunks
+// [seg_end[s - 1], seg_end[s]) (seg_end[-1] = 0) of the launch.
+constexpr int kMaxSegs = 128;
+
 struct IntraParams {
   const void* q;
   const void* k;
@@ -83,9 +87,13 @@ struct IntraParams {
   int l2norm;
   int decay;       // 0: K3 bounded map; 1: Kimi Linear softplus map (pairwise diagonal blocks)
   ChunkWs ws;
-  uint32_t* done;  // [B * H] finished records of each (b, h) in the segment (count_record), or nullptr
-  // Record of chunk c of the segment: ((b H + h) rec_stride + rec_c0 + c).
-  // rec_stride = 0 means nc (records of this segment only, rec_c0 = 0).
+  // Finished records (count_record), or nullptr: chunk c's record counts in
+  // done[s B H + b H + h], s its segment in seg_end (n_seg = 0: s = 0).
+  uint32_t* done;
+  int n_seg;
+  int32_t seg_end[kMaxSegs];
+  // Record of chunk c of the launch: ((b H + h) rec_stride + rec_c0 + c).
+  // rec_stride = 0 means nc (records of this launch only, rec_c0 = 0).
   int rec_stride, rec_c0;
 };
 
@@ -94,11 +102,9 @@ struct IntraParams {
 constexpr uint32_t kStatusWaitGaveUp = 1u;  // a bounded wait for records ran out: outputs are invalid
 constexpr uint32_t kFlagBadSlot = 1u;       // a state-pool slot was outside [0, n_slots): that sequence skipped
 
-// Segment table of a scan launch that covers several intra-chunk launches
-// (the pipelined schedule): segment s holds the launch's chunks
-// [seg_end[s - 1], seg_end[s]) (seg_end[-1] = 0), and its records are
-// complete once done[s B H + b H + h] reaches seg_end[s] - seg_end[s - 1].
-constexpr int kMaxSegs = 128;
+// The scan launch of the pipelined schedule covers every segment of the
+// table; segment s's records are complete once done[s B H + b H + h]
+// reaches seg_end[s] - seg_end[s - 1].
 
 struct ScanParams {
   const void* v;        // [B, T, H, D], or nullptr for V = 0 (the transfer of a segment, see kda_chunk_fwd_kcp)

@@ -82,8 +82,8 @@ typedef enum {
   KDA_SCHEDULE_SEGMENTS = 0,   /* intra-chunk kernel, then scan, segment after segment */
   KDA_SCHEDULE_OVERLAPPED = 1, /* the two kernels of consecutive segments overlapped   */
   KDA_SCHEDULE_FUSED = 2,      /* one fused kernel, chunk records kept in LDS          */
-  KDA_SCHEDULE_PIPELINED = 3   /* every record in the workspace: intra-chunk launches
-                                  per segment beside one scan launch over the sequence */
+  KDA_SCHEDULE_PIPELINED = 3   /* every record in the workspace: one intra-chunk launch
+                                  beside one scan launch over the sequence            */
 } kda_schedule;
 
 /* Kernel launches that kda_chunk_fwd_traced times (kda_chunk_fwd_launches). */
@@ -137,8 +137,8 @@ kda_status kda_desc_init(kda_desc* d, int32_t B, int32_t T, int32_t H, int32_t h
  * The fused schedule needs none (256 is reported; ws may also be NULL then).
  * With d->overlap, bf16 inputs and a sequence longer than one segment
  * (d->segment_tokens, default 8192) this holds every
- * chunk record of the call (the pipelined schedule: 66,048 bytes per chunk and
- * (b, h) at d = 128, e.g. 6.5 GB for B 1, T 65,536, H 96) as long as that is at
+ * chunk record of the call (the pipelined schedule: 61,952 bytes per chunk and
+ * (b, h) at d = 128, e.g. 6.1 GB for B 1, T 65,536, H 96) as long as that is at
  * most 8 GiB; otherwise, with d->overlap and a sequence longer than one
  * segment, it holds two segments of chunk records (the overlapped schedule),
  * and else the whole sequence (at most 65536 tokens per segment).  A smaller
@@ -188,9 +188,8 @@ kda_status kda_chunk_fwd_status(const kda_desc* d, const void* ws, size_t ws_byt
  * events for this descriptor and workspace size on the current device:
  * *n_launches receives their number and kinds[i] (i < max_kinds) the
  * kda_launch_kind of the i-th.  Segments and overlapped: per segment the
- * intra-chunk kernel, then the scan; pipelined: intra-chunk kernel of segment
- * 0, the scan (one launch), then the intra-chunk kernels of segments 1, 2, ...;
- * fused: one launch.  kinds may be NULL when max_kinds is 0. */
+ * intra-chunk kernel, then the scan; pipelined: the intra-chunk kernel (one
+ * launch), then the scan (one launch); fused: one launch.  kinds may be NULL when max_kinds is 0. */
 kda_status kda_chunk_fwd_launches(const kda_desc* d, size_t ws_bytes, int32_t* kinds, int32_t max_kinds,
                                   int32_t* n_launches);
 
@@ -235,14 +234,15 @@ kda_status kda_chunk_fwd_launches(const kda_desc* d, size_t ws_bytes, int32_t* k
  * their enqueue (a per-device lock); they must not share a workspace.
  *
  * Pipelined schedule (the same conditions, bf16 inputs, and a workspace that
- * holds every chunk record of the call): the intra-chunk
- * kernel runs segment by segment on one library stream (segments of 16, 16,
- * 24, 32, 48, 64 and 96 chunks, each at most the steady length, then
- * d->segment_tokens each, 4096 by default) and a single
- * scan launch over the whole sequence runs on the other, waiting inside the
- * kernel for each segment's records (device-scope record stores, one counter
- * per segment and (b, h)).  Every intra-chunk launch is enqueued before the
- * scan, so the call completes correctly even when the two library streams
+ * holds every chunk record of the call): one intra-chunk launch over the
+ * whole sequence runs on one library stream, producing the records chunk by
+ * chunk (every head's record of chunk c before any of chunk c + 1), and a
+ * single scan launch over the whole sequence runs on the other, waiting
+ * inside the kernel for each segment's records (device-scope record stores,
+ * one counter per segment and (b, h); segments of 16, 16, 24, 32, 48, 64 and
+ * 96 chunks, each at most the steady length, then d->segment_tokens each,
+ * 4096 by default).  The intra-chunk launch is enqueued before the scan, so
+ * the call completes correctly even when the two library streams
  * end up sharing a hardware queue (their work then runs one after the
  * other).  The waits are bounded (about a second): a producer kept from
  * running that long shows as NaN output, not a hang, and

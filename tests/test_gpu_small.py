@@ -202,8 +202,8 @@ def test_pipelined_schedule_matches_one_stream(kda, B, T, H, D, seg, opts):
     nbytes = kda.workspace_size(desc)
     assert kda.schedule(desc, nbytes)[1] == "pipelined"
     order = kda.launches(desc, nbytes)
-    # every intra-chunk launch first, then the one scan launch
-    assert order[-1] == "scan" and order.count("scan") == 1 and len(order) >= 3
+    # the one intra-chunk launch first, then the one scan launch
+    assert order == ["intra", "scan"]
     log(f"[pipelined] B={B} T={T} H={H} D={D} segment={seg} launches={len(order)}")
     one = _run(kda, x, overlap=False, fused=False, **opts)
     pip = _run(kda, x, overlap=True, segment_tokens=seg, fused=False, **opts)
@@ -215,15 +215,16 @@ def test_pipelined_schedule_matches_one_stream(kda, B, T, H, D, seg, opts):
 
 def test_pipelined_segment_table_overflow(kda):
     """More segments than the scan's 128-entry table: 201 chunks (ragged) in
-    one-chunk segments become 7 ramp segments of one chunk and 97 of two, and
-    the results still equal the one-stream schedule bit for bit."""
+    one-chunk segments become 7 ramp segments of one chunk and 97 of two
+    (counted by the one intra-chunk launch), and the results still equal the
+    one-stream schedule bit for bit."""
     B, T, H, D, seg = 1, 64 * 201 - 30, 2, 64, 64
     x = gen_inputs(_custom(B, T, H, D, "bf16", seed=4201))
     desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg, overlap=True, fused=False)
     nbytes = kda.workspace_size(desc)
     assert kda.schedule(desc, nbytes) == (128, "pipelined")
     order = kda.launches(desc, nbytes)
-    assert order.count("scan") == 1 and order.count("intra") == 7 + 97, len(order)
+    assert kda.schedule(desc, nbytes) == (128, "pipelined") and order == ["intra", "scan"], order
     log(f"[pipelined overflow] T={T} launches={len(order)}")
     one = _run(kda, x, overlap=False, fused=False)
     pip = _run(kda, x, overlap=True, segment_tokens=seg, fused=False)
@@ -241,7 +242,7 @@ def test_pipelined_schedule_reuses_workspace_and_traces(kda):
     ws = torch.empty(kda.workspace_size(desc), dtype=torch.uint8, device="cuda")
     assert kda.schedule(desc, ws.numel())[1] == "pipelined"
     order = kda.launches(desc, ws.numel())
-    assert order == ["intra"] * 32 + ["scan"]
+    assert order == ["intra", "scan"]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(order))]
     for e in ev:
         e.record()
