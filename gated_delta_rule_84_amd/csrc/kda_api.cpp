@@ -22,7 +22,7 @@ using kda::kChunk;
 
 constexpr int32_t kDefaultSegmentTokens = 65536;  // one-stream schedule
 constexpr int32_t kDefaultPipeTokens = 8192;      // overlapped schedule
-constexpr int32_t kDefaultPipelinedTokens = 4096; // pipelined schedule's steady segments
+constexpr int32_t kDefaultPipelinedTokens = 512;  // pipelined schedule's record-counting segments
 
 // Test hook (failure handling): KDA_TEST_PRODUCED_SEGMENTS=n makes the
 // pipelined schedule launch only the first n of its intra-chunk segments, so
@@ -160,10 +160,13 @@ bool pipelined_eligible(const kda_desc* d) {
   return d->overlap != 0 && d->in_dtype == KDA_BF16 && !fused_wanted(d) && pipe_wanted(d);
 }
 
-// Steady segment length of the pipelined schedule in chunks: 4,096 tokens by
-// default (K3 layer, B 1 T 65,536 H 96: 5.37 ms against 5.40 at 3,072, 5.52
-// at 6,144, 5.65 at 8,192 and 7.0 at 1,024 tokens, where the intra-chunk
-// launches become too short).
+// Steady segment length of the pipelined schedule in chunks (the unit in
+// which the scan waits for records; the producer's pacing lead is the
+// longest segment plus four chunks): 512 tokens by default.  Short segments
+// keep the records the scan reads within a few chunk steps of their writing,
+// while they are still in the memory-side cache (K3 layer, B 1 T 65,536
+// H 96: 4.78 ms at 512 tokens against 5.02 at 4,096, 5.07 unpaced; 256
+// tokens, beyond the 128-entry table, measured 4.74).
 int64_t pipelined_chunks(const kda_desc* d) {
   const int64_t toks = d->segment_tokens > 0 ? d->segment_tokens : kDefaultPipelinedTokens;
   return (toks + kChunk - 1) / kChunk;
@@ -576,7 +579,8 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   // segs: the pipelined schedule's segment table (the record counters of one
   // launch over several segments)
   auto launch_intra = [&](int64_t c0, int nc, const kda::ChunkWs& recs, hipStream_t st_, uint32_t* done = nullptr,
-                          int rec_stride = 0, int rec_c0 = 0, const Plan* segs = nullptr) {
+                          int rec_stride = 0, int rec_c0 = 0, const Plan* segs = nullptr,
+                          const uint32_t* progress = nullptr, uint32_t* pacing_off = nullptr, int lead = 0) {
     kda::IntraParams ip{};
     ip.q = q;
     ip.k = k;
@@ -601,6 +605,9 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     }
     ip.rec_stride = rec_stride;
     ip.rec_c0 = rec_c0;
+    ip.progress = progress;
+    ip.pacing_off = pacing_off;
+    ip.lead = lead;
     tr.before(st_);
     const kda_status r = check_launch(kda::launch_intra(ip, D, in_f32, st_), st_);
     tr.after(st_);
@@ -608,7 +615,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   };
   auto launch_scan = [&](int64_t c0, int nc, const kda::ChunkWs& recs, const float* S_in, float* S_out,
                          hipStream_t st_, const uint32_t* done = nullptr, const Plan* segs = nullptr,
-                         uint32_t* status = nullptr) {
+                         uint32_t* status = nullptr, uint32_t* progress = nullptr) {
     kda::ScanParams sp{};
     sp.v = v;
     sp.gate = y ? gate : nullptr;
@@ -634,6 +641,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
       sp.n_seg = segs->n_seg;
       for (int i = 0; i < segs->n_seg; ++i) sp.seg_end[i] = segs->seg_end[i];
     }
+    sp.progress = progress;
     tr.before(st_);
     const kda_status r = check_launch(kda::launch_scan(sp, D, in_f32, st_), st_);
     tr.after(st_);
@@ -712,23 +720,34 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
       return false;
     };
     const int64_t bh_n = (int64_t)d->B * d->H;
-    st = check_launch(
-        kda::launch_copy_state(nullptr, reinterpret_cast<float*>(status), kStatusWords + plan.n_seg * bh_n, s), s);
+    // status words (word 1: pacing off), the segment counters, then the
+    // scan's progress per (b, h), all zeroed on the caller's stream first
+    uint32_t* progress = done + plan.n_seg * bh_n;
+    st = check_launch(kda::launch_copy_state(nullptr, reinterpret_cast<float*>(status),
+                                             kStatusWords + (plan.n_seg + 1) * bh_n, s),
+                      s);
     if (st != KDA_OK) return st;
     if (!ok(hipEventRecord(c.fork, s)) || !ok(hipStreamWaitEvent(si, c.fork, 0)) ||
         !ok(hipStreamWaitEvent(ss, c.fork, 0)))
       return KDA_ERR_HIP;
     float* S_out = S_T ? S_T : reinterpret_cast<float*>(base + L.off_carry);
+    // pacing lead: the longest segment and four chunks (a producer waiting
+    // for the scan never holds back a record the scan is waiting for)
+    int lead = 0;
+    for (int sg = 0; sg < plan.n_seg; ++sg)
+      lead = std::max(lead, plan.seg_end[sg] - (sg > 0 ? plan.seg_end[sg - 1] : 0));
+    lead += 4;
     // The intra-chunk launch is enqueued before the scan: should the two
     // library streams share a hardware queue (their work then runs in
     // enqueue order), the scan still finds every record written instead of
     // waiting for producers queued behind it.
     const int produced = withheld_segments(plan.n_seg);
     if (produced > 0) {
-      st = launch_intra(0, plan.seg_end[produced - 1], recs, si, done, (int)nc_total, 0, &plan);
+      st = launch_intra(0, plan.seg_end[produced - 1], recs, si, done, (int)nc_total, 0, &plan, progress, status + 1,
+                        lead);
       if (st != KDA_OK) return st;
     }
-    st = launch_scan(0, (int)nc_total, recs, S0, S_out, ss, done, &plan, status);
+    st = launch_scan(0, (int)nc_total, recs, S0, S_out, ss, done, &plan, status, progress);
     if (st != KDA_OK) return st;
     if (!ok(hipEventRecord(c.join_intra, si)) || !ok(hipEventRecord(c.join_scan, ss)) ||
         !ok(hipStreamWaitEvent(s, c.join_intra, 0)) || !ok(hipStreamWaitEvent(s, c.join_scan, 0)))

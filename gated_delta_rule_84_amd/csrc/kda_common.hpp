@@ -232,6 +232,25 @@ __device__ __forceinline__ bool wait_records(const uint32_t* done, uint32_t targ
   return ok;
 }
 
+// Producer pacing (one thread per workgroup): wait until *progress >= target,
+// unless pacing is off.  Performance only, never needed for correctness: the
+// wait is bounded (about 200 µs), and the first wait that runs out turns
+// pacing off for the whole launch (*off = 1), e.g. when the consumer is not
+// running at the same time.
+constexpr int kPaceSpinLimit = 128;
+__device__ __forceinline__ void pace(const uint32_t* progress, uint32_t target, uint32_t* off) {
+  uint32_t* pr = const_cast<uint32_t*>(progress);
+  if (__hip_atomic_load(pr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return;
+  if (__hip_atomic_load(off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return;
+  for (int spin = 0; __hip_atomic_load(pr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++spin) {
+    if (spin >= kPaceSpinLimit) {
+      __hip_atomic_store(off, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(32);
+  }
+}
+
 // OR a status bit into a device-wide status word (a device-scope atomic).
 __device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bit) {
   if (status != nullptr) __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -31,7 +31,8 @@ struct IntraLds {
 // One workgroup (4 waves) per record of the launch, in chunk-major order:
 // workgroup item = c B H + b H + h, so that the records of a chunk come out
 // together for every head, as the state scan consumes them, and the rows of
-// a chunk's q, k, z are read for all heads at once.
+// a chunk's q, k, z are read for all heads at once.  In the pipelined
+// schedule the launch is paced by the scan's progress (IntraParams::progress).
 //
 // SP: the unbounded softplus decay (pairwise diagonal blocks, more registers:
 // two workgroups per CU).
@@ -58,6 +59,10 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
   constexpr RecUnits RU = rec_units((int)sizeof(T), D);
   char* recp = p.ws.base + rec * p.ws.rec_bytes;
 
+  if (p.progress != nullptr && (c & 3) == 0 && c > p.lead) {  // uniform: pacing (see IntraParams)
+    if (tid == 0) pace(p.progress + bh, (uint32_t)(c - p.lead), p.pacing_off);
+    __syncthreads();
+  }
   Core ic;
   ic.init(tid >> 6, tid & 63);
   ic.sink = rec_sink(recp, (int)p.ws.rec_bytes);

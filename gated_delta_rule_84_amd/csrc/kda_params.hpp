@@ -95,6 +95,15 @@ struct IntraParams {
   // Record of chunk c of the launch: ((b H + h) rec_stride + rec_c0 + c).
   // rec_stride = 0 means nc (records of this launch only, rec_c0 = 0).
   int rec_stride, rec_c0;
+  // Pacing (pipelined schedule), or progress = nullptr: a workgroup of a
+  // chunk c with c % 4 == 0 first waits until the scan of its (b, h) has
+  // reached chunk c - lead (progress[b H + h]), so that a record is read a
+  // few chunk steps after it is written, while it is still in the memory-side
+  // cache.  Performance only: the wait is bounded, and the first one that
+  // runs out sets *pacing_off, which ends pacing for the launch.
+  const uint32_t* progress;
+  uint32_t* pacing_off;
+  int lead;
 };
 
 // Status bits a kernel ORs into the workspace's status word (read by
@@ -125,11 +134,14 @@ struct ScanParams {
   int snap_every;       // chunks between snapshots (snapshot j: state after chunk (j + 1) * snap_every - 1)
   int n_snap;
   // Pipelined schedule (specialised scan kernel only): n_seg > 0 segments of
-  // records produced by intra-chunk launches running beside this one; done
+  // records produced by an intra-chunk launch running beside this one; done
   // then holds one counter per (segment, b, h) (see kMaxSegs).  n_seg = 0:
   // all records exist, or done (if not nullptr) is one counter per (b, h).
   int n_seg;
   int seg_end[kMaxSegs];
+  // [B * H]: the chunk each (b, h) has reached, published every chunk step
+  // for the producer's pacing (see IntraParams::progress), or nullptr
+  uint32_t* progress;
 };
 
 // Whether the state after chunk `cg` (global index) is snapshot j, and which.

@@ -630,14 +630,29 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
     if (gated) load_G(0);
     __syncthreads();
     for (int c = 0; c < p.nc; ++c) {
+      // pipelined schedule: chunk c + 2 (loaded in the second half) opens a
+      // segment.  Its counter is read at the start of the half, so that the
+      // read's latency overlaps the half's work; only a segment not yet
+      // complete then needs the bounded wait.  The step also publishes this
+      // head's progress for the producer's pacing.
+      const bool opens = wseg < p.n_seg && c + 2 <= cl && c + 2 == seg_start(wseg);
+      uint32_t probe = 0;
+      if (wave == L::NCW) {
+        if (p.progress != nullptr && lane == 0)
+          __hip_atomic_store(p.progress + bh, (uint32_t)(p.t0 / kChunk + c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (opens && !poison) probe = __hip_atomic_load(const_cast<uint32_t*>(seg_done(wseg)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       // first half of step c: the compute waves read part A of chunk c
       commit_B();                                        // part B of chunk c
       load_B(min(c + 1, cl));
       if (c > 0) epilogue(c - 1, std::false_type{});     // tile and gate logits of chunk c - 1
-      // pipelined schedule: chunk c + 2 (loaded in the second half) opens a segment
-      const bool opens = wseg < p.n_seg && c + 2 <= cl && c + 2 == seg_start(wseg);
       if (opens && wave == L::NCW && !poison) {
-        const bool ok = wait_records(seg_done(wseg), (uint32_t)(p.seg_end[wseg] - seg_start(wseg)));
+        const uint32_t need = (uint32_t)(p.seg_end[wseg] - seg_start(wseg));
+        bool ok = true;
+        if (__builtin_amdgcn_readfirstlane(probe) >= need)
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        else
+          ok = wait_records(seg_done(wseg), need);
         if (lane == 0) *gave_up = ok ? 0 : 1;
         if (!ok && lane == 0) raise_status(p.status, kStatusWaitGaveUp);
       }

@@ -108,7 +108,7 @@ typedef struct {
   kda_dtype out_dtype;   /* o, y                                                   */
   int32_t segment_tokens; /* tokens per internal segment of the overlapped
                              and pipelined schedules; 0: library default
-                             (8192 overlapped, 4096 pipelined)               */
+                             (8192 overlapped, 512 pipelined)                */
   int32_t overlap;       /* 1: run the intra-chunk kernel of the next segment
                             concurrently with the scan of the current one
                             (library-owned streams, see kda_chunk_fwd); 0: one
@@ -241,7 +241,12 @@ kda_status kda_chunk_fwd_launches(const kda_desc* d, size_t ws_bytes, int32_t* k
  * inside the kernel for each segment's records (device-scope record stores,
  * one counter per segment and (b, h); segments of 16, 16, 24, 32, 48, 64 and
  * 96 chunks, each at most the steady length, then d->segment_tokens each,
- * 4096 by default).  The intra-chunk launch is enqueued before the scan, so
+ * 512 by default).  The scan publishes each (b, h)'s chunk every step, and
+ * every fourth chunk's producers wait until their scan is within the longest
+ * segment plus four chunks, so that records are read back from the
+ * memory-side cache; this pacing is a bounded wait that switches itself off
+ * for the call when it runs out, and never affects results.  The
+ * intra-chunk launch is enqueued before the scan, so
  * the call completes correctly even when the two library streams
  * end up sharing a hardware queue (their work then runs one after the
  * other).  The waits are bounded (about a second): a producer kept from
