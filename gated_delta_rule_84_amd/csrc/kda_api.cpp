@@ -59,18 +59,31 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t elem_size(kda_dtype t) { return t == KDA_F32 ? 4 : 2; }
 
+// The integer an enum-typed field or argument of the C ABI holds, read as an
+// int: a C caller may store any int there, and in C++ reading a value outside
+// the enum's range through the enum type is undefined.  Every enum is checked
+// this way before it is used as its type.
+template <typename E>
+int enum_int(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "int-sized enums");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 kda_status validate_desc(const kda_desc* d) {
   if (d == nullptr) return KDA_ERR_NULL_ARG;
   if (d->B < 1 || d->H < 1 || d->T < 0 || d->d_k < 1 || d->d_v < 1 || d->chunk < 1) return KDA_ERR_BAD_SHAPE;
-  if ((d->in_dtype != KDA_F32 && d->in_dtype != KDA_BF16) || (d->out_dtype != KDA_F32 && d->out_dtype != KDA_BF16))
-    return KDA_ERR_BAD_DTYPE;
+  const int in_dt = enum_int(d->in_dtype), out_dt = enum_int(d->out_dtype);
+  if ((in_dt != KDA_F32 && in_dt != KDA_BF16) || (out_dt != KDA_F32 && out_dt != KDA_BF16)) return KDA_ERR_BAD_DTYPE;
   if (d->d_k != d->d_v || (d->d_k != 64 && d->d_k != 128)) return KDA_ERR_UNSUPPORTED;
   if (d->chunk != kChunk) return KDA_ERR_UNSUPPORTED;
   if (!(d->g_min < 0.0f) || d->g_min < -5.5f) return KDA_ERR_UNSUPPORTED;
   if (!(d->l2_eps >= 0.0f) || !(d->rms_eps >= 0.0f)) return KDA_ERR_UNSUPPORTED;
   if (d->segment_tokens < 0 || (d->overlap != 0 && d->overlap != 1) || d->fused < 0 || d->fused > 2)
     return KDA_ERR_BAD_SHAPE;
-  if (d->decay != KDA_DECAY_K3 && d->decay != KDA_DECAY_SOFTPLUS) return KDA_ERR_UNSUPPORTED;
+  const int decay = enum_int(d->decay);
+  if (decay != KDA_DECAY_K3 && decay != KDA_DECAY_SOFTPLUS) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
 }
 
@@ -1124,8 +1137,9 @@ kda_status kda_recurrent_step(const kda_desc* d, const void* q, const void* k, c
 kda_status kda_state_io(kda_state_op op, int32_t n, int32_t H, int32_t d_k, int32_t d_v, kda_state_layout layout,
                         float* pool, int32_t n_slots, const int32_t* slot, float* user, uint32_t* status,
                         void* stream) {
-  if (op != KDA_STATE_ZERO && op != KDA_STATE_IMPORT && op != KDA_STATE_EXPORT) return KDA_ERR_UNSUPPORTED;
-  if (layout != KDA_LAYOUT_KV && layout != KDA_LAYOUT_VK) return KDA_ERR_UNSUPPORTED;
+  const int op_i = enum_int(op), layout_i = enum_int(layout);
+  if (op_i != KDA_STATE_ZERO && op_i != KDA_STATE_IMPORT && op_i != KDA_STATE_EXPORT) return KDA_ERR_UNSUPPORTED;
+  if (layout_i != KDA_LAYOUT_KV && layout_i != KDA_LAYOUT_VK) return KDA_ERR_UNSUPPORTED;
   if (n < 0 || H < 1 || d_k < 1 || d_v < 1 || n_slots < 1 || (slot == nullptr && n > n_slots))
     return KDA_ERR_BAD_SHAPE;
   if (d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_ERR_UNSUPPORTED;
