@@ -175,7 +175,7 @@ bool pipelined_eligible(const kda_desc* d) {
 
 // Steady segment length of the pipelined schedule in chunks (the unit in
 // which the scan waits for records; the producer's pacing lead is the
-// longest segment plus four chunks): 512 tokens by default.  Short segments
+// longest segment plus eight chunks): 512 tokens by default.  Short segments
 // keep the records the scan reads within a few chunk steps of their writing,
 // while they are still in the memory-side cache (K3 layer, B 1 T 65,536
 // H 96: 4.78 ms at 512 tokens against 5.02 at 4,096, 5.07 unpaced; 256
@@ -744,12 +744,15 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
         !ok(hipStreamWaitEvent(ss, c.fork, 0)))
       return KDA_ERR_HIP;
     float* S_out = S_T ? S_T : reinterpret_cast<float*>(base + L.off_carry);
-    // pacing lead: the longest segment and four chunks (a producer waiting
+    // pacing lead: the longest segment and eight chunks (a producer waiting
     // for the scan never holds back a record the scan is waiting for)
     int lead = 0;
     for (int sg = 0; sg < plan.n_seg; ++sg)
       lead = std::max(lead, plan.seg_end[sg] - (sg > 0 ? plan.seg_end[sg - 1] : 0));
-    lead += 4;
+    // (K3 layer: with four chunks the scan found 9,000 of its 12,200
+    // segments incomplete when it reached them, with eight 5,500-7,800, with
+    // twenty 1,400, but records then leave the cache: 4.71 / 4.65 / 4.79 ms)
+    lead += 8;
     // The intra-chunk launch is enqueued before the scan: should the two
     // library streams share a hardware queue (their work then runs in
     // enqueue order), the scan still finds every record written instead of

@@ -187,7 +187,7 @@ __device__ __forceinline__ float sigmoid_fast(float x) { return hw_rcp(1.0f + hw
 // which plain loads see the records.  No cache-wide write-back per record.
 constexpr int kDeviceScope = 16;            // buffer-op cache policy: sc1
 constexpr uint32_t kPoison = 0x7FC07FC0u;  // a NaN as fp32 and as both bf16 halves
-constexpr int kCountSpinLimit = 1 << 18;   // polls (about a second) before giving up
+constexpr int kCountSpinLimit = 1 << 20;   // polls (about a second) before giving up
 
 struct RecSink {
   __amdgpu_buffer_rsrc_t rsrc;  // the record (uniform)
@@ -213,7 +213,7 @@ __device__ __forceinline__ void count_record(uint32_t* done) {
 }
 
 // Consumer side (one wave per workgroup: every poll is a load of the same
-// word, so few pollers, ≈3 µs apart): wait until *done >= target, then
+// word, so few pollers, ≈0.2 µs plus a load's latency apart): wait until *done >= target, then
 // acquire; the caller's workgroup barrier orders the other waves' loads after
 // it.  Returns false when the bounded wait gave up (the caller then poisons
 // what it stages, so that a producer that never ran shows as NaN, not a hang).
@@ -226,7 +226,7 @@ __device__ __forceinline__ bool wait_records(const uint32_t* done, uint32_t targ
       ok = false;
       break;
     }
-    __builtin_amdgcn_s_sleep(127);
+    __builtin_amdgcn_s_sleep(8);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return ok;

@@ -243,7 +243,7 @@ kda_status kda_chunk_fwd_launches(const kda_desc* d, size_t ws_bytes, int32_t* k
  * 96 chunks, each at most the steady length, then d->segment_tokens each,
  * 512 by default).  The scan publishes each (b, h)'s chunk every step, and
  * every fourth chunk's producers wait until their scan is within the longest
- * segment plus four chunks, so that records are read back from the
+ * segment plus eight chunks, so that records are read back from the
  * memory-side cache; this pacing is a bounded wait that switches itself off
  * for the call when it runs out, and never affects results.  The
  * intra-chunk launch is enqueued before the scan, so
