@@ -22,7 +22,7 @@ using kda::kChunk;
 
 constexpr int32_t kDefaultSegmentTokens = 65536;  // one-stream schedule
 constexpr int32_t kDefaultPipeTokens = 8192;      // overlapped schedule
-constexpr int32_t kDefaultPipelinedTokens = 512;  // pipelined schedule's record-counting segments
+constexpr int32_t kDefaultPipelinedTokens = 128;  // pipelined schedule's record-counting segments
 
 // Test hook (failure handling): KDA_TEST_PRODUCED_SEGMENTS=n makes the
 // pipelined schedule launch only the first n of its intra-chunk segments, so
@@ -151,18 +151,16 @@ bool fused_wanted(const kda_desc* d) {
 constexpr size_t kFusedWorkspace = 256;  // what the size query reports for it (nothing is used)
 
 // Pipelined schedule: every record of the sequence stays in the workspace.
-// The intra-chunk kernel runs segment by segment on one library stream while
-// one scan launch over the whole sequence runs on the other and waits inside
-// the kernel for each segment's records.  Segments grow from 16 chunks to the
-// steady length (d->segment_tokens), so the scan of every head starts after
-// the first 1,024 tokens' records instead of after a whole segment, and the
-// scan has no per-segment restart (state reload, pipeline fill and drain,
-// launch gap).  No record buffer is reused, so no intra-chunk launch ever
-// waits for the scan.  It needs the specialised scan workgroup (bf16 inputs)
-// and a workspace that holds every record; the size query offers that
-// workspace up to kPipelinedWorkspaceCap.
-constexpr int64_t kRamp[] = {16, 16, 24, 32, 48, 64, 96};
-constexpr int kRampLen = sizeof(kRamp) / sizeof(kRamp[0]);
+// One intra-chunk launch over the whole sequence runs on one library stream,
+// producing the records in chunk order, while one scan launch over the
+// whole sequence runs on the other and waits inside the kernel for each
+// segment's records (short uniform segments, counted per (b, h)).  The scan
+// has no per-segment restart (state reload, pipeline fill and drain, launch
+// gap), and no record buffer is reused, so correctness never needs a
+// producer to wait for the scan (the pacing waits are bounded and for speed
+// only).  It needs the specialised scan workgroup (bf16 inputs) and a
+// workspace that holds every record; the size query offers that workspace
+// up to kPipelinedWorkspaceCap.
 constexpr size_t kPipelinedWorkspaceCap = size_t(8) << 30;
 
 // Like the overlapped schedule, only for sequences longer than one segment:
@@ -173,37 +171,24 @@ bool pipelined_eligible(const kda_desc* d) {
   return d->overlap != 0 && d->in_dtype == KDA_BF16 && !fused_wanted(d) && pipe_wanted(d);
 }
 
-// Steady segment length of the pipelined schedule in chunks (the unit in
-// which the scan waits for records; the producer's pacing lead is the
-// longest segment plus eight chunks): 512 tokens by default.  Short segments
-// keep the records the scan reads within a few chunk steps of their writing,
-// while they are still in the memory-side cache (K3 layer, B 1 T 65,536
-// H 96: 4.78 ms at 512 tokens against 5.02 at 4,096, 5.07 unpaced; 256
-// tokens, beyond the 128-entry table, measured 4.74).
+// Segment length of the pipelined schedule in chunks (the unit in which the
+// scan waits for records): 128 tokens by default.  The producers run at most
+// a pacing lead of kPipelinedSlack chunks past the segment ahead of their
+// scan, so that a record is read a few chunk steps after it was written,
+// while it is still in the memory-side cache, and a short segment lets that
+// lead stay short without the scan finding its next segment incomplete.
+// Measured on the K3 layer (B 1, T 65,536, H 96; step ms, one box):
+// segments of 128 tokens with a lead of 8 chunks 4.29; 192 / 8: 4.31;
+// 256 / 8: 4.42-4.60; 512 / 16: 4.70; 64 / 8: 4.57 (an acquire per chunk);
+// 128 / 7: 4.81 (the scan waits); 128 / 12: 4.52 (records leave the cache).
 int64_t pipelined_chunks(const kda_desc* d) {
   const int64_t toks = d->segment_tokens > 0 ? d->segment_tokens : kDefaultPipelinedTokens;
   return (toks + kChunk - 1) / kChunk;
 }
+constexpr int kPipelinedSlack = 6;
 
-// Cumulative chunk ends of the pipelined schedule's segments (at most
-// kda::kMaxSegs, each at least one chunk); returns their number.
-int segment_table(const kda_desc* d, int32_t* ends) {
-  const int64_t nc = num_chunks(d), steady = pipelined_chunks(d);
-  int n = 0;
-  int64_t at = 0;
-  for (int i = 0; i < kRampLen && at < nc; ++i) {
-    at = std::min(nc, at + std::min(kRamp[i], steady));
-    ends[n++] = (int32_t)at;
-  }
-  if (at < nc) {  // steady segments, lengthened when needed to stay within the table
-    const int64_t slots = kda::kMaxSegs - n;
-    const int64_t len = std::max(steady, (nc - at + slots - 1) / slots);
-    while (at < nc) {
-      at = std::min(nc, at + len);
-      ends[n++] = (int32_t)at;
-    }
-  }
-  return n;
+int pipelined_segments(const kda_desc* d, int64_t seg_nc) {
+  return kda::num_segments((int)num_chunks(d), (int)seg_nc);
 }
 
 // ---- per-device streams and events of the two-stream schedules --------------
@@ -289,8 +274,6 @@ struct Plan {
   int n_scan;
   bool fused;
   bool pipelined;
-  int n_seg;                      // pipelined: segments and their chunk ends
-  int32_t seg_end[kda::kMaxSegs];
 };
 
 // The two library streams can serve B * H scan workgroups on the current
@@ -329,9 +312,7 @@ Plan make_plan(const kda_desc* d, size_t ws_bytes, bool one_stream = false) {
     p.pipelined = true;
     p.dev = dev;
     p.n_scan = n_scan;
-    p.n_seg = segment_table(d, p.seg_end);
-    for (int s = 0; s < p.n_seg; ++s)  // reported: the longest segment (steady ones may be lengthened)
-      p.seg_nc = std::max<int64_t>(p.seg_nc, p.seg_end[s] - (s > 0 ? p.seg_end[s - 1] : 0));
+    p.seg_nc = pipelined_chunks(d);
     return p;
   }
   if (!one_stream && pipe_wanted(d) && ws_bytes >= layout_for(d, 2 * pipe_chunks(d)).total &&
@@ -589,10 +570,10 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   char* base = static_cast<char*>(ws);
 
   // one segment: records of chunks [c0, c0 + nc) in `recs`; state S_in -> S_out
-  // segs: the pipelined schedule's segment table (the record counters of one
-  // launch over several segments)
+  // seg_len: the pipelined schedule's counting segments (the record counters
+  // of one launch over several segments), 0 for one counter per (b, h)
   auto launch_intra = [&](int64_t c0, int nc, const kda::ChunkWs& recs, hipStream_t st_, uint32_t* done = nullptr,
-                          int rec_stride = 0, int rec_c0 = 0, const Plan* segs = nullptr,
+                          int rec_stride = 0, int rec_c0 = 0, int seg_len = 0,
                           const uint32_t* progress = nullptr, uint32_t* pacing_off = nullptr, int lead = 0) {
     kda::IntraParams ip{};
     ip.q = q;
@@ -612,10 +593,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     ip.decay = d->decay;
     ip.ws = recs;
     ip.done = done;
-    if (segs != nullptr) {
-      ip.n_seg = segs->n_seg;
-      for (int i = 0; i < segs->n_seg; ++i) ip.seg_end[i] = segs->seg_end[i];
-    }
+    ip.seg_len = seg_len;
     ip.rec_stride = rec_stride;
     ip.rec_c0 = rec_c0;
     ip.progress = progress;
@@ -627,7 +605,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     return r;
   };
   auto launch_scan = [&](int64_t c0, int nc, const kda::ChunkWs& recs, const float* S_in, float* S_out,
-                         hipStream_t st_, const uint32_t* done = nullptr, const Plan* segs = nullptr,
+                         hipStream_t st_, const uint32_t* done = nullptr, int seg_len = 0,
                          uint32_t* status = nullptr, uint32_t* progress = nullptr) {
     kda::ScanParams sp{};
     sp.v = v;
@@ -650,10 +628,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     sp.snaps = snap.n > 0 ? snap.ptr : nullptr;
     sp.snap_every = snap.every;
     sp.n_snap = snap.n;
-    if (segs != nullptr) {
-      sp.n_seg = segs->n_seg;
-      for (int i = 0; i < segs->n_seg; ++i) sp.seg_end[i] = segs->seg_end[i];
-    }
+    sp.seg_len = seg_len;
     sp.progress = progress;
     tr.before(st_);
     const kda_status r = check_launch(kda::launch_scan(sp, D, in_f32, st_), st_);
@@ -733,37 +708,33 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
       return false;
     };
     const int64_t bh_n = (int64_t)d->B * d->H;
+    const int seg_len = (int)plan.seg_nc;
+    const int n_seg = pipelined_segments(d, plan.seg_nc);
     // status words (word 1: pacing off), the segment counters, then the
     // scan's progress per (b, h), all zeroed on the caller's stream first
-    uint32_t* progress = done + plan.n_seg * bh_n;
+    uint32_t* progress = done + n_seg * bh_n;
     st = check_launch(kda::launch_copy_state(nullptr, reinterpret_cast<float*>(status),
-                                             kStatusWords + (plan.n_seg + 1) * bh_n, s),
+                                             kStatusWords + (n_seg + 1) * bh_n, s),
                       s);
     if (st != KDA_OK) return st;
     if (!ok(hipEventRecord(c.fork, s)) || !ok(hipStreamWaitEvent(si, c.fork, 0)) ||
         !ok(hipStreamWaitEvent(ss, c.fork, 0)))
       return KDA_ERR_HIP;
     float* S_out = S_T ? S_T : reinterpret_cast<float*>(base + L.off_carry);
-    // pacing lead: the longest segment and eight chunks (a producer waiting
+    // pacing lead: a segment and kPipelinedSlack chunks (a producer waiting
     // for the scan never holds back a record the scan is waiting for)
-    int lead = 0;
-    for (int sg = 0; sg < plan.n_seg; ++sg)
-      lead = std::max(lead, plan.seg_end[sg] - (sg > 0 ? plan.seg_end[sg - 1] : 0));
-    // (K3 layer: with four chunks the scan found 9,000 of its 12,200
-    // segments incomplete when it reached them, with eight 5,500-7,800, with
-    // twenty 1,400, but records then leave the cache: 4.71 / 4.65 / 4.79 ms)
-    lead += 8;
+    const int lead = seg_len + kPipelinedSlack;
     // The intra-chunk launch is enqueued before the scan: should the two
     // library streams share a hardware queue (their work then runs in
     // enqueue order), the scan still finds every record written instead of
     // waiting for producers queued behind it.
-    const int produced = withheld_segments(plan.n_seg);
+    const int produced = withheld_segments(n_seg);
     if (produced > 0) {
-      st = launch_intra(0, plan.seg_end[produced - 1], recs, si, done, (int)nc_total, 0, &plan, progress, status + 1,
-                        lead);
+      const int nc_prod = (int)std::min<int64_t>(nc_total, (int64_t)produced * seg_len);
+      st = launch_intra(0, nc_prod, recs, si, done, (int)nc_total, 0, seg_len, progress, status + 1, lead);
       if (st != KDA_OK) return st;
     }
-    st = launch_scan(0, (int)nc_total, recs, S0, S_out, ss, done, &plan, status, progress);
+    st = launch_scan(0, (int)nc_total, recs, S0, S_out, ss, done, seg_len, status, progress);
     if (st != KDA_OK) return st;
     if (!ok(hipEventRecord(c.join_intra, si)) || !ok(hipEventRecord(c.join_scan, ss)) ||
         !ok(hipStreamWaitEvent(s, c.join_intra, 0)) || !ok(hipStreamWaitEvent(s, c.join_scan, 0)))
@@ -819,7 +790,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
         if (seg >= 2 && !ok(hipStreamWaitEvent(si, c.scan_done[j], 0))) return KDA_ERR_HIP;
         st = launch_intra(c0, nc, bufs[j], si, done + seg * bh_n);
         if (st != KDA_OK) return st;
-        st = launch_scan(c0, nc, bufs[j], S_in, S_run, ss, done + seg * bh_n, nullptr, status);
+        st = launch_scan(c0, nc, bufs[j], S_in, S_run, ss, done + seg * bh_n, 0, status);
         if (st != KDA_OK) return st;
         if (!ok(hipEventRecord(c.scan_done[j], ss))) return KDA_ERR_HIP;
         S_in = S_run;

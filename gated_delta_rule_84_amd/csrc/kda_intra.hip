@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
   constexpr RecUnits RU = rec_units((int)sizeof(T), D);
   char* recp = p.ws.base + rec * p.ws.rec_bytes;
 
-  if (p.progress != nullptr && (c & 3) == 0 && c > p.lead) {  // uniform: pacing (see IntraParams)
+  if (p.progress != nullptr && c % kPaceEvery == 0 && c > p.lead) {  // uniform: pacing (see IntraParams)
     if (tid == 0) pace(p.progress + bh, (uint32_t)(c - p.lead), p.pacing_off);
     __syncthreads();
   }
@@ -85,17 +85,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
   }
   Core::template tb_pass<256>(tid, s, reinterpret_cast<T*>(recp + 16 * RU.tb), &ic.sink);
   if (p.done != nullptr) {
-    // the record's counter: its segment of seg_end (binary search; one segment if n_seg = 0)
-    int seg = 0;
-    if (p.n_seg > 0) {
-      int lo = 0, hi = p.n_seg - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (c < p.seg_end[mid]) hi = mid;
-        else lo = mid + 1;
-      }
-      seg = lo;
-    }
+    // the record's counter: that of its segment (one segment if seg_len = 0)
+    const int seg = p.seg_len > 0 ? c / p.seg_len : 0;
     count_record(p.done + (int64_t)seg * bh_n + bh);
   }
 }

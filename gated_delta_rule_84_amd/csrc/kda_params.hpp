@@ -70,9 +70,12 @@ struct ChunkWs {
   int64_t rec_bytes;
 };
 
-// Segment table of the pipelined schedule: segment s holds the chunks
-// [seg_end[s - 1], seg_end[s]) (seg_end[-1] = 0) of the launch.
-constexpr int kMaxSegs = 128;
+// Pipelined schedule: the records of a launch are counted in segments of
+// seg_len chunks (segment s holds chunks [s seg_len, (s + 1) seg_len) of the
+// launch, the last one possibly shorter), and producers of every
+// kPaceEvery-th chunk wait for the scan's progress (IntraParams::progress).
+constexpr int kPaceEvery = 2;
+__host__ __device__ constexpr int num_segments(int nc, int seg_len) { return (nc + seg_len - 1) / seg_len; }
 
 struct IntraParams {
   const void* q;
@@ -88,15 +91,14 @@ struct IntraParams {
   int decay;       // 0: K3 bounded map; 1: Kimi Linear softplus map (pairwise diagonal blocks)
   ChunkWs ws;
   // Finished records (count_record), or nullptr: chunk c's record counts in
-  // done[s B H + b H + h], s its segment in seg_end (n_seg = 0: s = 0).
+  // done[s B H + b H + h], s = c / seg_len its segment (seg_len = 0: s = 0).
   uint32_t* done;
-  int n_seg;
-  int32_t seg_end[kMaxSegs];
+  int seg_len;
   // Record of chunk c of the launch: ((b H + h) rec_stride + rec_c0 + c).
   // rec_stride = 0 means nc (records of this launch only, rec_c0 = 0).
   int rec_stride, rec_c0;
   // Pacing (pipelined schedule), or progress = nullptr: a workgroup of a
-  // chunk c with c % 4 == 0 first waits until the scan of its (b, h) has
+  // chunk c with c % kPaceEvery == 0 first waits until the scan of its (b, h) has
   // reached chunk c - lead (progress[b H + h]), so that a record is read a
   // few chunk steps after it is written, while it is still in the memory-side
   // cache.  Performance only: the wait is bounded, and the first one that
@@ -111,9 +113,9 @@ struct IntraParams {
 constexpr uint32_t kStatusWaitGaveUp = 1u;  // a bounded wait for records ran out: outputs are invalid
 constexpr uint32_t kFlagBadSlot = 1u;       // a state-pool slot was outside [0, n_slots): that sequence skipped
 
-// The scan launch of the pipelined schedule covers every segment of the
-// table; segment s's records are complete once done[s B H + b H + h]
-// reaches seg_end[s] - seg_end[s - 1].
+// The scan launch of the pipelined schedule covers every segment; segment
+// s's records are complete once done[s B H + b H + h] reaches its number of
+// chunks.
 
 struct ScanParams {
   const void* v;        // [B, T, H, D], or nullptr for V = 0 (the transfer of a segment, see kda_chunk_fwd_kcp)
@@ -133,12 +135,12 @@ struct ScanParams {
   float* snaps;         // [B, n_snap, H, D, D] states at every snap_every-th chunk boundary, or nullptr
   int snap_every;       // chunks between snapshots (snapshot j: state after chunk (j + 1) * snap_every - 1)
   int n_snap;
-  // Pipelined schedule (specialised scan kernel only): n_seg > 0 segments of
-  // records produced by an intra-chunk launch running beside this one; done
-  // then holds one counter per (segment, b, h) (see kMaxSegs).  n_seg = 0:
-  // all records exist, or done (if not nullptr) is one counter per (b, h).
-  int n_seg;
-  int seg_end[kMaxSegs];
+  // Pipelined schedule (specialised scan kernel only): seg_len > 0, records
+  // produced by an intra-chunk launch running beside this one and counted in
+  // segments of seg_len chunks; done then holds one counter per (segment, b,
+  // h) (see num_segments).  seg_len = 0: all records exist, or done (if not
+  // nullptr) is one counter per (b, h).
+  int seg_len;
   // [B * H]: the chunk each (b, h) has reached, published every chunk step
   // for the producer's pacing (see IntraParams::progress), or nullptr
   uint32_t* progress;

@@ -479,22 +479,24 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
   // later segment two chunk steps before its first record is loaded.  The
   // outcome goes through an LDS word; a wait that gave up poisons what the
   // helpers stage from then on (and no later wait is made).
-  auto seg_start = [&](int s) { return s == 0 ? 0 : p.seg_end[s - 1]; };
+  const int n_seg = p.seg_len > 0 ? num_segments(p.nc, p.seg_len) : 0;
+  auto seg_start = [&](int s) { return s * p.seg_len; };
+  auto seg_size = [&](int s) { return (uint32_t)(min((s + 1) * p.seg_len, p.nc) - s * p.seg_len); };
   auto seg_done = [&](int s) { return p.done + ((int64_t)s * p.B * p.H + bh); };
   int* gave_up = reinterpret_cast<int*>(lds + L::FLAG);
   int wseg = 0;  // segments waited for (pipelined schedule); uniform
-  if (p.n_seg > 0) {
+  if (n_seg > 0) {
     const int first = min(1, p.nc - 1);
-    while (wseg < p.n_seg && seg_start(wseg) <= first) ++wseg;
+    while (wseg < n_seg && seg_start(wseg) <= first) ++wseg;
   }
   bool poison = false;
   if (p.done != nullptr) {
     if (wave == L::NCW) {
       bool ok = true;
-      if (p.n_seg == 0) {
+      if (n_seg == 0) {
         ok = wait_records(p.done + bh, (uint32_t)p.nc);
       } else {
-        for (int s = 0; s < wseg && ok; ++s) ok = wait_records(seg_done(s), (uint32_t)(p.seg_end[s] - seg_start(s)));
+        for (int s = 0; s < wseg && ok; ++s) ok = wait_records(seg_done(s), seg_size(s));
       }
       if (lane == 0) *gave_up = ok ? 0 : 1;
       if (!ok && lane == 0) raise_status(p.status, kStatusWaitGaveUp);
@@ -635,7 +637,7 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
       // read's latency overlaps the half's work; only a segment not yet
       // complete then needs the bounded wait.  The step also publishes this
       // head's progress for the producer's pacing.
-      const bool opens = wseg < p.n_seg && c + 2 <= cl && c + 2 == seg_start(wseg);
+      const bool opens = wseg < n_seg && c + 2 <= cl && c + 2 == seg_start(wseg);
       uint32_t probe = 0;
       if (wave == L::NCW) {
         if (p.progress != nullptr && lane == 0)
@@ -647,7 +649,7 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
       load_B(min(c + 1, cl));
       if (c > 0) epilogue(c - 1, std::false_type{});     // tile and gate logits of chunk c - 1
       if (opens && wave == L::NCW && !poison) {
-        const uint32_t need = (uint32_t)(p.seg_end[wseg] - seg_start(wseg));
+        const uint32_t need = seg_size(wseg);
         bool ok = true;
         if (__builtin_amdgcn_readfirstlane(probe) >= need)
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");

@@ -108,7 +108,7 @@ typedef struct {
   kda_dtype out_dtype;   /* o, y                                                   */
   int32_t segment_tokens; /* tokens per internal segment of the overlapped
                              and pipelined schedules; 0: library default
-                             (8192 overlapped, 512 pipelined)                */
+                             (8192 overlapped, 128 pipelined)                */
   int32_t overlap;       /* 1: run the intra-chunk kernel of the next segment
                             concurrently with the scan of the current one
                             (library-owned streams, see kda_chunk_fwd); 0: one
@@ -164,7 +164,7 @@ kda_status kda_release_resources(void);
  * The schedule kda_chunk_fwd takes on the current device for this descriptor
  * and a workspace of ws_bytes bytes: *segment_tokens receives the tokens per
  * segment (a multiple of the chunk; the whole sequence for the fused
- * schedule, the longest segment for the pipelined one), *schedule a
+ * schedule, the record-counting segment for the pipelined one), *schedule a
  * kda_schedule value.  KDA_ERR_WORKSPACE if a
  * two-kernel schedule is taken and the workspace is too small for one chunk.
  */
@@ -239,12 +239,10 @@ kda_status kda_chunk_fwd_launches(const kda_desc* d, size_t ws_bytes, int32_t* k
  * chunk (every head's record of chunk c before any of chunk c + 1), and a
  * single scan launch over the whole sequence runs on the other, waiting
  * inside the kernel for each segment's records (device-scope record stores,
- * one counter per segment and (b, h); segments of 16, 16, 24, 32, 48, 64 and
- * 96 chunks, each at most the steady length, then d->segment_tokens each,
- * 512 by default).  The scan publishes each (b, h)'s chunk every step, and
- * every fourth chunk's producers wait until their scan is within the longest
- * segment plus eight chunks, so that records are read back from the
- * memory-side cache; this pacing is a bounded wait that switches itself off
+ * one counter per segment and (b, h); segments of d->segment_tokens tokens,
+ * 128 by default).  The scan publishes each (b, h)'s chunk every step, and
+ * every second chunk's producers wait until their scan is within a segment
+ * plus six chunks, so that records are read back from the memory-side cache; this pacing is a bounded wait that switches itself off
  * for the call when it runs out, and never affects results.  The
  * intra-chunk launch is enqueued before the scan, so
  * the call completes correctly even when the two library streams

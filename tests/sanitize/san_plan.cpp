@@ -1,6 +1,6 @@
 // Driver for the AddressSanitizer / UndefinedBehaviorSanitizer build of the
 // library's host layer: it includes kda_api.cpp itself, so that the internal
-// planning steps (descriptor validation, segment_table, layout_for,
+// planning steps (descriptor validation, pipelined_segments, layout_for,
 // make_plan, plan_launches) can be called directly and their invariants
 // checked over a sweep of shapes, and then drives the C ABI's queries and
 // argument checks (every call here returns before any GPU work; no GPU is
@@ -29,16 +29,13 @@ static kda_desc make(int B, int T, int H, int D, kda_dtype dt, int seg, int over
 }
 
 static void check_segments(const kda_desc* d) {
-  int32_t ends[kda::kMaxSegs + 1];
-  const int n = segment_table(d, ends);
   const int64_t nc = num_chunks(d);
-  EXPECT(n >= (nc > 0 ? 1 : 0) && n <= kda::kMaxSegs);  // no segment for an empty sequence
-  int32_t prev = 0;
-  for (int s = 0; s < n; ++s) {
-    EXPECT(ends[s] > prev);  // every segment holds at least one chunk
-    prev = ends[s];
-  }
-  EXPECT(prev == nc);
+  const int64_t len = pipelined_chunks(d);
+  EXPECT(len >= 1);
+  const int n = pipelined_segments(d, len);
+  // no segment for an empty sequence; at most one per chunk (the counters the layout holds)
+  EXPECT(n >= (nc > 0 ? 1 : 0) && n <= nc);
+  if (n > 0) EXPECT((int64_t)(n - 1) * len < nc && (int64_t)n * len >= nc);  // they cover the chunks exactly
 }
 
 static void check_layout(const kda_desc* d, int64_t seg_nc) {

@@ -181,7 +181,7 @@ def test_overlapped_schedule_reuses_workspace(kda):
 
 
 @pytest.mark.parametrize("B,T,H,D,seg,opts", [
-    (1, 9000, 4, 128, 0, {}),                                   # default: segments of 16, 16, 24, 32, 48, 5 chunks
+    (1, 9000, 4, 128, 0, {}),                                   # default: 71 segments of 2 chunks (the last 1)
     (2, 3000, 3, 128, 256, {}),                                 # ragged last chunk, 4-chunk steady segments
     (1, 2065, 2, 64, 64, {"out_dtype": torch.float32}),         # d = 64, 33 one-chunk segments, fp32 outputs
     (3, 1100, 2, 128, 128, {"gate": False}),                    # o only; 18 chunks in 2-chunk segments
@@ -189,13 +189,14 @@ def test_overlapped_schedule_reuses_workspace(kda):
     (1, 2000, 2, 128, 128, {"want_state": False}),              # no S_T: the scan ends in the workspace
 ])
 def test_pipelined_schedule_matches_one_stream(kda, B, T, H, D, seg, opts):
-    """The pipelined schedule (every chunk record in the workspace, the
-    intra-chunk kernel launched per segment on one library stream beside ONE
-    scan launch over the sequence that waits inside the kernel for each
-    segment's record counters) gives bit-identical results to the one-stream
-    schedule; the launch-order query matches what the call does (every
-    intra-chunk launch, then the scan: should the library's two streams
-    share a hardware queue, the scan then finds every record written)."""
+    """The pipelined schedule (every chunk record in the workspace, ONE
+    intra-chunk launch on one library stream beside ONE scan launch over the
+    sequence that waits inside the kernel for each segment's record counters,
+    producers paced by the scan's progress) gives bit-identical results to
+    the one-stream schedule; the launch-order query matches what the call
+    does (the intra-chunk launch, then the scan: should the library's two
+    streams share a hardware queue, the scan then finds every record
+    written)."""
     wl = _custom(B, T, H, D, "bf16", seed=B * 1000 + T)
     x = gen_inputs(wl)
     desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg, overlap=True, fused=False)
@@ -213,19 +214,17 @@ def test_pipelined_schedule_matches_one_stream(kda, B, T, H, D, seg, opts):
         assert _bit_equal(one[key], pip[key]), key
 
 
-def test_pipelined_segment_table_overflow(kda):
-    """More segments than the scan's 128-entry table: 201 chunks (ragged) in
-    one-chunk segments become 7 ramp segments of one chunk and 97 of two
-    (counted by the one intra-chunk launch), and the results still equal the
-    one-stream schedule bit for bit."""
+def test_pipelined_one_chunk_segments(kda):
+    """201 chunks (ragged) counted in 201 one-chunk segments (a record wait
+    at every chunk step, pacing lead of 7 chunks) by the one intra-chunk
+    launch: the results still equal the one-stream schedule bit for bit."""
     B, T, H, D, seg = 1, 64 * 201 - 30, 2, 64, 64
     x = gen_inputs(_custom(B, T, H, D, "bf16", seed=4201))
     desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg, overlap=True, fused=False)
     nbytes = kda.workspace_size(desc)
-    assert kda.schedule(desc, nbytes) == (128, "pipelined")
     order = kda.launches(desc, nbytes)
-    assert kda.schedule(desc, nbytes) == (128, "pipelined") and order == ["intra", "scan"], order
-    log(f"[pipelined overflow] T={T} launches={len(order)}")
+    assert kda.schedule(desc, nbytes) == (64, "pipelined") and order == ["intra", "scan"], order
+    log(f"[pipelined one-chunk segments] T={T} launches={len(order)}")
     one = _run(kda, x, overlap=False, fused=False)
     pip = _run(kda, x, overlap=True, segment_tokens=seg, fused=False)
     for key in ("o", "y", "S_T"):

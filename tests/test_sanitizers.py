@@ -7,7 +7,7 @@ run on the CPU:
 * the library's host layer (gated_delta_rule_84_amd/csrc/kda_api.cpp), built
   with hipcc with the sanitizers on its host compilation only and driven by
   tests/sanitize/san_plan.cpp, which includes it to call the planning steps
-  (descriptor validation, segment_table, layout_for, make_plan,
+  (descriptor validation, pipelined_segments, layout_for, make_plan,
   plan_launches) over a sweep of shapes and the C ABI's queries and argument
   checks, none of which needs a GPU.
 
