@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -33,6 +34,13 @@ int withheld_segments(int n_seg) {
   if (e == nullptr || e[0] == 0) return n_seg;
   const int n = std::atoi(e);
   return n < 0 ? n_seg : std::min(n, n_seg);
+}
+
+// Test hook: KDA_TEST_NO_SPLIT=1 keeps one-stream launches on the unsplit
+// scan workgroup, so that tests can compare the two bit for bit.
+bool split_disabled() {
+  const char* e = std::getenv("KDA_TEST_NO_SPLIT");
+  return e != nullptr && e[0] == '1';
 }
 
 bool debug_sync() {
@@ -99,14 +107,15 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 struct WsLayout {
-  size_t off_rec, rec_bytes, off_carry, off_done, total;
+  size_t off_rec, rec_bytes, off_carry, off_done, off_xchg, total;
 };
 constexpr int kStatusWords = 64;  // status block ahead of the record counters
 
 // Workspace for a segment of seg_nc chunks: one record per (b, h, chunk), the
-// fp32 state carried between segments and one record counter per (segment,
-// b, h) of the sequence (the overlapped schedule's hand-over; at most one
-// segment per chunk).
+// fp32 state carried between segments, one record counter per (segment,
+// b, h) of the sequence (the two-stream schedules' hand-over; at most one
+// segment per chunk) and the split scan's RMSNorm exchange ring (4 KB per
+// head).
 WsLayout layout_for(const kda_desc* d, int64_t seg_nc) {
   const int es = (int)elem_size(d->in_dtype);
   const int64_t D = d->d_k;
@@ -123,6 +132,8 @@ WsLayout layout_for(const kda_desc* d, int64_t seg_nc) {
   L.off_carry = take((size_t)d->B * d->H * D * D * 4);
   // a 256-byte status block (word 0: kda::kStatus* bits), then the counters
   L.off_done = take(kStatusWords * 4 + (size_t)(((int64_t)d->T + kChunk - 1) / kChunk + 1) * d->B * d->H * 4);
+  // the split scan's RMSNorm exchange ring (kda::ScanParams::xchg)
+  L.off_xchg = take((size_t)d->B * d->H * kda::kXchgWordsPerHead * 8);
   L.total = o;
   return L;
 }
@@ -213,6 +224,25 @@ struct DeviceCtx {
 };
 constexpr int kMaxDevices = 64;
 DeviceCtx g_dev[kMaxDevices];
+
+// Compute units of the current device (0 if unknown), cached per device.
+int device_cus() {
+  static std::atomic<int> cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // Called with c.mu held.
 bool ctx_ready(DeviceCtx& c, int dev) {
@@ -574,7 +604,8 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   // of one launch over several segments), 0 for one counter per (b, h)
   auto launch_intra = [&](int64_t c0, int nc, const kda::ChunkWs& recs, hipStream_t st_, uint32_t* done = nullptr,
                           int rec_stride = 0, int rec_c0 = 0, int seg_len = 0,
-                          const uint32_t* progress = nullptr, uint32_t* pacing_off = nullptr, int lead = 0) {
+                          const uint32_t* progress = nullptr, uint32_t* pacing_off = nullptr, int lead = 0,
+                          uint64_t* clear = nullptr, int64_t clear_words = 0) {
     kda::IntraParams ip{};
     ip.q = q;
     ip.k = k;
@@ -599,6 +630,8 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     ip.progress = progress;
     ip.pacing_off = pacing_off;
     ip.lead = lead;
+    ip.clear = clear;
+    ip.clear_words = clear_words;
     tr.before(st_);
     const kda_status r = check_launch(kda::launch_intra(ip, D, in_f32, st_), st_);
     tr.after(st_);
@@ -606,7 +639,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   };
   auto launch_scan = [&](int64_t c0, int nc, const kda::ChunkWs& recs, const float* S_in, float* S_out,
                          hipStream_t st_, const uint32_t* done = nullptr, int seg_len = 0,
-                         uint32_t* status = nullptr, uint32_t* progress = nullptr) {
+                         uint32_t* status = nullptr, uint32_t* progress = nullptr, uint64_t* xchg = nullptr) {
     kda::ScanParams sp{};
     sp.v = v;
     sp.gate = y ? gate : nullptr;
@@ -630,6 +663,8 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     sp.n_snap = snap.n;
     sp.seg_len = seg_len;
     sp.progress = progress;
+    sp.nsplit = xchg != nullptr ? 2 : 1;
+    sp.xchg = xchg;
     tr.before(st_);
     const kda_status r = check_launch(kda::launch_scan(sp, D, in_f32, st_), st_);
     tr.after(st_);
@@ -803,7 +838,10 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     return KDA_ERR_HIP;  // unreachable: make_plan created the pair
   }
 
-  // ---- one stream: segments in turn
+  // ---- one stream: segments in turn.  With the device's compute units to
+  // spare (2 B H of them), each head's scan is split between two workgroups
+  // by value columns (kda_scan.hip); the first intra-chunk launch clears the
+  // split's exchange ring.
   const int64_t seg_nc = plan.seg_nc;
   const WsLayout L = layout_for(d, seg_nc);
   kda::ChunkWs cw{};
@@ -812,11 +850,17 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   float* carry = reinterpret_cast<float*>(base + L.off_carry);
   float* S_run = S_T ? S_T : carry;
   const float* S_in = S0;
+  const int64_t bh_n = (int64_t)d->B * d->H;
+  uint64_t* xchg = nullptr;
+  if (kda::split_supported((int)elem_size(d->in_dtype), D) && 2 * bh_n <= device_cus() && !split_disabled())
+    xchg = reinterpret_cast<uint64_t*>(base + L.off_xchg);
   for (int64_t c0 = 0; c0 < nc_total; c0 += seg_nc) {
     const int nc = (int)((nc_total - c0) < seg_nc ? (nc_total - c0) : seg_nc);
-    st = launch_intra(c0, nc, cw, s);
+    const bool clear = xchg != nullptr && y != nullptr && c0 == 0;
+    st = launch_intra(c0, nc, cw, s, nullptr, 0, 0, 0, nullptr, nullptr, 0, clear ? xchg : nullptr,
+                      clear ? bh_n * kda::kXchgWordsPerHead : 0);
     if (st != KDA_OK) return st;
-    st = launch_scan(c0, nc, cw, S_in, S_run, s);
+    st = launch_scan(c0, nc, cw, S_in, S_run, s, nullptr, 0, nullptr, nullptr, xchg);
     if (st != KDA_OK) return st;
     S_in = S_run;
   }

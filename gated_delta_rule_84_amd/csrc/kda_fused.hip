@@ -46,6 +46,9 @@ struct FusedLds {
   static constexpr int RS = sizeof(typename RecOps<T>::Elem);  // record element
   static_assert(RS == ES, "one row pitch for the record and the V slab");
   static constexpr int PQ = D * ES + 16;       // row pitch of qg / kg / V slab (bytes)
+  static constexpr int PV = PQ;                // of the V slab, as the scan's compute waves read it
+  static constexpr int NCT = 2;                // 16-column tiles per compute wave
+  static constexpr int NOT = 1;                // output tiles
   static constexpr int PK = 64 * RS + 16;      // row pitch of kdt / tb / aq (bytes)
   static constexpr int PO = D + 4;             // output tile row pitch (floats)
   // record image read by the compute waves

@@ -59,6 +59,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
   constexpr RecUnits RU = rec_units((int)sizeof(T), D);
   char* recp = p.ws.base + rec * p.ws.rec_bytes;
 
+  if (p.clear != nullptr)
+    for (int64_t w = (int64_t)item * 256 + tid; w < p.clear_words; w += (int64_t)gridDim.x * 256) p.clear[w] = 0;
   if (p.progress != nullptr && c % kPaceEvery == 0 && c > p.lead) {  // uniform: pacing (see IntraParams)
     if (tid == 0) pace(p.progress + bh, (uint32_t)(c - p.lead), p.pacing_off);
     __syncthreads();

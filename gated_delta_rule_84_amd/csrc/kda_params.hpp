@@ -106,6 +106,11 @@ struct IntraParams {
   const uint32_t* progress;
   uint32_t* pacing_off;
   int lead;
+  // clear_words 8-byte words at clear set to zero (grid-strided), or nullptr:
+  // the split scan's exchange ring, cleared by the intra-chunk launch that
+  // precedes that scan on the same stream
+  uint64_t* clear;
+  int64_t clear_words;
 };
 
 // Status bits a kernel ORs into the workspace's status word (read by
@@ -144,7 +149,17 @@ struct ScanParams {
   // [B * H]: the chunk each (b, h) has reached, published every chunk step
   // for the producer's pacing (see IntraParams::progress), or nullptr
   uint32_t* progress;
+  // 2: each head's value columns split between two workgroups (see
+  // split_supported); xchg then holds their RMSNorm row sums, [B H][2][4][64]
+  // 8-byte words zeroed before the launch (needed when y is written)
+  int nsplit;
+  uint64_t* xchg;
 };
+
+// The specialised scan workgroup can split a head's value columns between
+// two workgroups for 2-byte inputs at d = 128.
+__host__ __device__ constexpr bool split_supported(int in_bytes, int D) { return in_bytes == 2 && D == 128; }
+constexpr int kXchgWordsPerHead = 2 * 4 * 64;
 
 // Whether the state after chunk `cg` (global index) is snapshot j, and which.
 __device__ __forceinline__ int snapshot_index(const ScanParams& p, int cg) {

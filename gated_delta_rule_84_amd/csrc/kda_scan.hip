@@ -407,6 +407,26 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
 // the gate-logit slab of the previous chunk, the previous chunk's fp32 output
 // tile.  NCW compute waves (32 columns each) and as many helper waves.
 //
+// NS = 2 splits a head's value columns between two workgroups (half s owns
+// columns s D / 2 .. (s + 1) D / 2 - 1; grid mapping in the kernel): every product
+// of the chunk form is separable in the value columns, so each keeps half of
+// the state and reads the whole record but only its half of V, the gate and
+// y; its compute waves own 16 columns each, which halves their product chain.
+// RMSNorm needs the whole row: each workgroup publishes the sum of squares
+// of its half of every row of chunk c - 1 during step c and reads the other
+// half's during step c + 1 (so the exchange's latency is hidden), then
+// writes y of chunk c - 1; the output tiles and gate slabs are therefore
+// double-buffered.  The sums go through a ring of four chunks per
+// workgroup in the workspace as 8-byte (value, chunk + 1) words written and
+// read with device-scope atomics, so a word is never seen half written and a
+// stale one never matches; one workgroup can run at most two chunk steps
+// ahead of the other, so four slots are never overwritten before they are
+// read.  Both workgroups of a pair must be resident together: the host uses
+// the split only for one-stream launches with 2 B H within the device's
+// compute units, and the wait is bounded (status bit, NaN y).  The sums of
+// squares are formed in the same order as the unsplit epilogue's, so results
+// are bit-identical.
+//
 // The staging is split in two parts so that it never stalls the compute waves:
 // part A (qg, kg of the record and the V slab) is read in the first half of a
 // chunk step, part B (kdt, tb, aq, Gamma_last) in the second half.  Helpers
@@ -415,9 +435,11 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
 // loaded into registers one step before it is committed.  The helpers turn
 // chunk c - 1's output tile into o / y during the first half of step c, while
 // the compute waves run the long independent product chains of chunk c.
-template <typename T, int D>
+template <typename T, int D, int NS = 1>
 struct WsLds {
   static constexpr int ES = sizeof(T);
+  static constexpr int DV = D / NS;            // value columns of the workgroup
+  static constexpr int NCT = 2 / NS;           // 16-column tiles per compute wave
   static constexpr int NCW = D / 32;           // compute waves
   static constexpr int NHW = NCW;              // helper waves
   static constexpr int NT = 64 * (NCW + NHW);  // threads
@@ -433,14 +455,16 @@ struct WsLds {
   static constexpr int AQ = TB + 64 * PK;
   static constexpr int GAM = AQ + 64 * PK;
   static constexpr int REC = GAM + 4 * D;
-  static constexpr int VS = REC;               // V slab   [64][PQ]
-  static constexpr int GS = VS + 64 * PQ;      // gate slab [64][PQ]
-  static constexpr int PO = D + 4;
-  static constexpr int OT = GS + 64 * PQ;      // output tile [64][PO] fp32
-  static constexpr int FLAG = OT + 64 * PO * 4;  // outcome of the record waits (int)
+  static constexpr int PV = DV * ES + 16;      // row pitch of the V and gate slabs
+  static constexpr int NOT = NS;               // gate slabs and output tiles (double-buffered when split)
+  static constexpr int VS = REC;               // V slab   [64][PV]
+  static constexpr int GS = VS + 64 * PV;      // gate slabs [NOT][64][PV]
+  static constexpr int PO = DV + 4;
+  static constexpr int OT = GS + NOT * 64 * PV;  // output tiles [NOT][64][PO] fp32
+  static constexpr int FLAG = OT + NOT * 64 * PO * 4;  // outcome of the record waits (int)
   static constexpr int BYTES = FLAG + 16;
   static constexpr RecUnits RU = rec_units(RS, D);
-  static constexpr int VPR = D * ES / 16;      // 16-byte units per slab row
+  static constexpr int VPR = DV * ES / 16;     // 16-byte units per slab row
   static constexpr int SLAB_UNITS = 64 * VPR;
   static constexpr int A_REC = RU.kdt;         // record units of part A (qg, kg)
   static constexpr int A_UNITS = A_REC + SLAB_UNITS;
@@ -453,20 +477,33 @@ struct WsLds {
   static constexpr int PB = (B_UNITS + NH - 1) / NH;
   static constexpr int PG = (SLAB_UNITS + NH - 1) / NH;
   static constexpr int TPR = NH / 64;          // helper threads per output row
-  static constexpr int EC = D / TPR;           // columns per helper thread
+  static constexpr int EC = DV / TPR;          // columns per helper thread
   // used when the image fits in LDS and a helper's staging registers stay modest
   static constexpr bool FITS = BYTES <= 160 * 1024 && PA + PB + PG <= 40;
 };
 
-template <typename T, int D, bool OUT_F32>
-__global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const ScanParams p) {
-  using L = WsLds<T, D>;
+template <typename T, int D, bool OUT_F32, int NS>
+__global__ __launch_bounds__((WsLds<T, D, NS>::NT), 1) void kda_scan_ws_kernel(const ScanParams p) {
+  using L = WsLds<T, D, NS>;
   static_assert(sizeof(typename RecOps<T>::Elem) == 2, "the split commits of part B assume 2-byte records");
   __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.x, b = blockIdx.y;
+  // NS = 2: a 1-D grid of groups of 16 workgroups, 8 heads each: workgroup
+  // 16 g + 8 s + r takes half s of head (b, h) = pair 8 g + r, so that the two
+  // halves of a head, which read the same chunk records, are dispatched to the
+  // same XCD (workgroups go to the XCDs in turn) and share its L2.  Workgroups
+  // past the last pair return at once.
+  int h = blockIdx.x, b = blockIdx.y, half = 0;
+  if constexpr (NS == 2) {
+    const int pair = 8 * ((int)blockIdx.x / 16) + (int)blockIdx.x % 8;
+    if (pair >= p.B * p.H) return;
+    half = ((int)blockIdx.x / 8) & 1;
+    b = pair / p.H;
+    h = pair % p.H;
+  }
+  const int cb = half * L::DV;            // first column of the workgroup's half
   const int64_t bh = (int64_t)b * p.H + h;
   const int64_t tok_stride = (int64_t)p.H * D;
   const int64_t head_base = ((int64_t)b * p.T * p.H + h) * D;
@@ -506,7 +543,7 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
   }
 
   if (wave < L::NCW) {
-    scan_compute_waves<T, D, L>(p, lds, wave, lane, b, h);
+    scan_compute_waves<T, D, L>(p, lds, wave, lane, b, h, cb);
   } else {
     // ======================= helper waves =======================
     constexpr int NH = L::NH, VPR = L::VPR;
@@ -526,14 +563,14 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
     for (int i = 0; i < L::PA; ++i) {
       const int u = hid + NH * i;
       lofA[i] = (i < AR) ? lds_offset_of_unit<L, D>(u)
-                         : L::VS + ((u - L::A_REC) / VPR) * L::PQ + ((u - L::A_REC) % VPR) * 16;
+                         : L::VS + ((u - L::A_REC) / VPR) * L::PV + ((u - L::A_REC) % VPR) * 16;
     }
 #pragma unroll
     for (int i = 0; i < L::PB; ++i) lofB[i] = lds_offset_of_unit<L, D>(L::A_REC + min(hid + NH * i, L::B_UNITS - 1));
 #pragma unroll
     for (int i = 0; i < L::PG; ++i) {
       const int u = hid + NH * i;
-      lofG[i] = L::GS + (u / VPR) * L::PQ + (u % VPR) * 16;
+      lofG[i] = L::GS + (u / VPR) * L::PV + (u % VPR) * 16;  // + the slab of the chunk (split)
     }
     u32x4 stA[L::PA], stB[L::PB], stG[L::PG];
     auto rec_ptr = [&](int c) { return p.ws.base + (bh * p.nc + c) * p.ws.rec_bytes; };
@@ -542,7 +579,7 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
     // part A of chunk c: qg, kg and the V slab (rows past the end are clamped)
     auto load_A = [&](int c) {
       const u32x4* rp = reinterpret_cast<const u32x4*>(rec_ptr(c));
-      const T* v0 = vin + head_base + (int64_t)(p.t0 + c * kChunk) * tok_stride;
+      const T* v0 = vin + head_base + cb + (int64_t)(p.t0 + c * kChunk) * tok_stride;
       const int last = last_row(c);
 #pragma unroll
       for (int i = 0; i < L::PA; ++i) {
@@ -594,7 +631,7 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
       }
     };
     auto load_G = [&](int c) {
-      const T* g0 = gin + head_base + (int64_t)(p.t0 + c * kChunk) * tok_stride;
+      const T* g0 = gin + head_base + cb + (int64_t)(p.t0 + c * kChunk) * tok_stride;
       const int last = last_row(c);
 #pragma unroll
       for (int i = 0; i < L::PG; ++i) {
@@ -602,22 +639,71 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
         stG[i] = reinterpret_cast<const u32x4*>(g0 + min(u / VPR, last) * tok_stride)[u % VPR];
       }
     };
-    auto commit_G = [&]() {
+    constexpr int GSLAB = 64 * L::PV;  // bytes of one gate slab
+    auto commit_G = [&](int c) {      // gate logits of chunk c into its slab
 #pragma unroll
-      for (int i = 0; i < L::PG; ++i) *reinterpret_cast<u32x4*>(lds + lofG[i]) = stG[i];
+      for (int i = 0; i < L::PG; ++i) *reinterpret_cast<u32x4*>(lds + lofG[i] + (c % L::NOT) * GSLAB) = stG[i];
     };
 
-    // epilogue role: row er, columns ec .. ec + EC - 1; gate logits from the slab
-    using Epi = GateEpilogue<T, D, OUT_F32, NH, false>;
+    // epilogue role: row er, columns ec .. ec + EC - 1 of the workgroup's;
+    // gate logits from the slab of the chunk
+    using Epi = GateEpilogue<T, D, OUT_F32, NH, false, L::DV>;
     static_assert(Epi::TPR == L::TPR && Epi::EC == L::EC, "epilogue mapping");
     Epi epi;
-    epi.init(p, h, hid);
-    const float* otile = reinterpret_cast<const float*>(lds + L::OT);
-    auto getg = [&](int q) {
-      return *reinterpret_cast<const u32x4*>(lds + L::GS + epi.er * L::PQ + epi.ec * L::ES + 16 * q);
+    epi.init(p, h, hid, cb);
+    auto tile_of = [&](int c) {
+      return reinterpret_cast<const float*>(lds + L::OT) + (c % L::NOT) * (64 * L::PO);
+    };
+    auto getg_of = [&](int c) {
+      const char* gs = lds + L::GS + (c % L::NOT) * GSLAB + epi.er * L::PV + epi.ec * L::ES;
+      return [gs](int q) { return *reinterpret_cast<const u32x4*>(gs + 16 * q); };
     };
     auto epilogue = [&](int c, auto check_rows) {
-      epi.template run<decltype(check_rows)::value, L::PO>(p, h, head_base, p.t0 + c * kChunk, otile, getg);
+      epi.template run<decltype(check_rows)::value, L::PO>(p, h, head_base, p.t0 + c * kChunk, tile_of(c), getg_of(c));
+    };
+    // NS = 2: the row sums of squares of chunk c go through the ring
+    // xchg[((b H + h) 2 + half) 4 + c % 4][64] of 8-byte (value, tag) words
+    const bool row_lead = (hid % L::TPR) == 0;  // one thread per row publishes
+    auto xslot = [&](int hf, int c) {
+      return p.xchg + (((bh * 2 + hf) * 4 + (c & 3)) * 64 + epi.er);
+    };
+    // tag: the chunk's index in the sequence plus one (segments of one call
+    // share the ring; the launch before the call's first scan zeroes it)
+    auto tag_of = [&](int c) { return (uint32_t)(p.t0 / kChunk + c + 1); };
+    auto publish_ss = [&](int c, float ss) {
+      if (row_lead)
+        __hip_atomic_store(xslot(half, c), (uint64_t)__float_as_uint(ss) | ((uint64_t)tag_of(c) << 32),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto peek_ss = [&](int c) {
+      return __hip_atomic_load(xslot(half ^ 1, c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // the other half's sum of squares of chunk c (its word already read once
+    // into w); bounded wait, NaN when it never arrives
+    auto other_ss = [&](int c, uint64_t w) {
+      for (int spin = 0; (uint32_t)(w >> 32) != tag_of(c); ++spin) {
+        if (spin >= kCountSpinLimit) {
+          raise_status(p.status, kStatusWaitGaveUp);
+          return __uint_as_float(kPoison);
+        }
+        __builtin_amdgcn_s_sleep(2);
+        w = peek_ss(c);
+      }
+      return __uint_as_float((uint32_t)w);
+    };
+    float ss_last = 0.f, ss_prev = 0.f;  // own half sums of the last two chunks split_first saw
+    auto split_first = [&](int c, auto check_rows) {  // o and the half sums of chunk c
+      const float ss = epi.template half_ss<decltype(check_rows)::value, L::PO>(p, head_base, p.t0 + c * kChunk,
+                                                                             tile_of(c));
+      ss_prev = ss_last;
+      ss_last = ss;
+      if (gated) publish_ss(c, ss);
+    };
+    // y of chunk c from the own half `mine` and the other half's word w
+    auto split_second = [&](int c, float mine, uint64_t w, auto check_rows) {
+      if (decltype(check_rows)::value && epi.er >= p.T - (p.t0 + c * kChunk)) return;
+      const float ss = mine + other_ss(c, w);
+      epi.template split_y<false, L::PO>(p, h, head_base, p.t0 + c * kChunk, tile_of(c), getg_of(c), ss);
     };
 
     // Loads past the last chunk are clamped to it (their commits land where
@@ -644,10 +730,18 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
           __hip_atomic_store(p.progress + bh, (uint32_t)(p.t0 / kChunk + c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (opens && !poison) probe = __hip_atomic_load(const_cast<uint32_t*>(seg_done(wseg)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      // split: the other half's sums of chunk c - 2, read early
+      uint64_t wprev = 0;
+      if (NS == 2 && gated && c > 1) wprev = peek_ss(c - 2);
       // first half of step c: the compute waves read part A of chunk c
       commit_B();                                        // part B of chunk c
       load_B(min(c + 1, cl));
-      if (c > 0) epilogue(c - 1, std::false_type{});     // tile and gate logits of chunk c - 1
+      if constexpr (NS == 1) {
+        if (c > 0) epilogue(c - 1, std::false_type{});   // tile and gate logits of chunk c - 1
+      } else {
+        if (c > 0) split_first(c - 1, std::false_type{});                       // o and half sums of chunk c - 1
+        if (gated && c > 1) split_second(c - 2, ss_prev, wprev, std::false_type{});  // y of chunk c - 2
+      }
       if (opens && wave == L::NCW && !poison) {
         const uint32_t need = seg_size(wseg);
         bool ok = true;
@@ -665,12 +759,20 @@ __global__ __launch_bounds__((WsLds<T, D>::NT), 1) void kda_scan_ws_kernel(const
       }
       // second half: the compute waves read part B of chunk c and write tile c
       commit_A(min(c + 1, cl));
-      if (gated) commit_G();                             // gate logits of chunk c
+      if (gated) commit_G(c);                            // gate logits of chunk c
       load_A(min(c + 2, cl));
       if (gated) load_G(min(c + 1, cl));
       __syncthreads();
     }
-    epilogue(cl, std::true_type{});
+    if constexpr (NS == 1) {
+      epilogue(cl, std::true_type{});
+    } else {
+      split_first(cl, std::true_type{});
+      if (gated) {
+        if (cl > 0) split_second(cl - 1, ss_prev, peek_ss(cl - 1), std::false_type{});
+        split_second(cl, ss_last, peek_ss(cl), std::true_type{});
+      }
+    }
   }
 }
 
@@ -678,10 +780,22 @@ template <typename T, int D>
 static void launch_scan_t(const ScanParams& p, hipStream_t s) {
   using W = WsLds<T, D>;
   if constexpr (W::FITS) {
+    if constexpr (split_supported(sizeof(T), D)) {
+      using W2 = WsLds<T, D, 2>;
+      static_assert(W2::FITS, "the split workgroup fits");
+      if (p.nsplit == 2) {
+        const dim3 grid((unsigned)(16 * ((p.B * p.H + 7) / 8)));
+        if (p.out_f32)
+          hipLaunchKernelGGL((kda_scan_ws_kernel<T, D, true, 2>), grid, dim3(W2::NT), 0, s, p);
+        else
+          hipLaunchKernelGGL((kda_scan_ws_kernel<T, D, false, 2>), grid, dim3(W2::NT), 0, s, p);
+        return;
+      }
+    }
     if (p.out_f32)
-      hipLaunchKernelGGL((kda_scan_ws_kernel<T, D, true>), dim3(p.H, p.B), dim3(W::NT), 0, s, p);
+      hipLaunchKernelGGL((kda_scan_ws_kernel<T, D, true, 1>), dim3(p.H, p.B), dim3(W::NT), 0, s, p);
     else
-      hipLaunchKernelGGL((kda_scan_ws_kernel<T, D, false>), dim3(p.H, p.B), dim3(W::NT), 0, s, p);
+      hipLaunchKernelGGL((kda_scan_ws_kernel<T, D, false, 1>), dim3(p.H, p.B), dim3(W::NT), 0, s, p);
   } else {
     hipLaunchKernelGGL((kda_scan_serial_kernel<T, D>), dim3(p.H, p.B), dim3(4 * D), 0, s, p);
   }

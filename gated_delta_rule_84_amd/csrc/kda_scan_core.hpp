@@ -71,9 +71,12 @@ __device__ __forceinline__ V8 v_select(int n, int g, int nt) {
 }
 
 // Compute waves of a specialised workgroup: wave `wave` (0 .. D / 32 - 1)
-// owns value columns 32 wave .. 32 wave + 31 and keeps that d_k x 32 slice of
-// the fp32 state in accumulators for the whole sequence (scaled by
-// RecOps<T>::kStateScale).  Per chunk step, with the layout L of the LDS image:
+// owns the L::NCT 16-column tiles of value columns cb + 16 NCT wave + 0 ..
+// 16 NCT - 1 (32 columns, or 16 when a head's columns are split between two
+// workgroups, each with column base cb) and keeps that d_k-row slice of the
+// fp32 state in accumulators for the whole sequence (scaled by
+// RecOps<T>::kStateScale).  The LDS slabs (V, output tile) hold the
+// workgroup's own columns.  Per chunk step, with the layout L of the LDS image:
 //   first half  -- reads part A of the record (qg, kg) and the V slab;
 //   barrier M   -- part A consumed, part B (kdt, tb, aq, Gamma_last) staged;
 //   second half -- reads part B, writes the chunk's output tile;
@@ -81,18 +84,22 @@ __device__ __forceinline__ V8 v_select(int n, int g, int nt) {
 // One barrier before the first step (part A of chunk 0 staged).  Writes the
 // final state, and the prefix-cache snapshots when asked for.
 template <typename T, int D, typename L>
-__device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* lds, int wave, int lane, int b, int h) {
+__device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* lds, int wave, int lane, int b, int h,
+                                                   int cb = 0) {
   using Ops = ScanOps<T>;
   using Opnd = typename Ops::Opnd;
   using In8 = typename Ops::In8;
   constexpr float kScale = RecOps<T>::kStateScale, kUnscale = 1.0f / RecOps<T>::kStateScale;
   constexpr int MT = D / 16;
   constexpr int KS = D / 32;
-  constexpr int NCT = 2;  // 16-column tiles per compute wave
+  constexpr int NCT = L::NCT;  // 16-column tiles per compute wave
   const int n = lane & 15, g4 = lane >> 4;
   const int64_t bh = (int64_t)b * p.H + h;
-  float* otile = reinterpret_cast<float*>(lds + L::OT);
-  const int col0 = 32 * wave + n;  // column of tile nt: col0 + 16 nt
+  const int lc0 = 16 * NCT * wave + n;  // column of tile nt in the workgroup's slabs: lc0 + 16 nt
+  const int col0 = cb + lc0;            // and in the head's state
+  // V enters through a 32-wide K-step over the slab columns that hold this
+  // wave's tiles: window w32, tile nt at selection position vpos + nt
+  const int w32 = (16 * NCT * wave) / 32 * 32, vpos = (NCT * wave) & 1;
   f32x4 S[MT][NCT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -107,7 +114,9 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[mt][nt][i] = s0[(16 * mt + 4 * g4 + i) * D + col0 + 16 * nt] * kScale;
   }
-  const In8 vsel0 = v_select<In8>(n, g4, 0), vsel1 = v_select<In8>(n, g4, 1);
+  In8 vsel[NCT];
+#pragma unroll
+  for (int nt = 0; nt < NCT; ++nt) vsel[nt] = v_select<In8>(n, g4, vpos + nt);
   const char* qg = lds + L::QG;
   const char* kg = lds + L::KG;
   const char* kdt = lds + L::KDT;
@@ -117,13 +126,14 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
   __syncthreads();  // part A of chunk 0 staged
 
   f32x4 O[4][NCT];  // outputs of the chunk
-  auto write_tile = [&]() {
+  auto write_tile = [&](int c) {  // into the tile buffer of chunk c (L::NOT buffers)
+    float* otile = reinterpret_cast<float*>(lds + L::OT) + (c % L::NOT) * (64 * L::PO);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NCT; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) otile[(16 * mt + 4 * g4 + i) * L::PO + col0 + 16 * nt] = O[mt][nt][i];
+        for (int i = 0; i < 4; ++i) otile[(16 * mt + 4 * g4 + i) * L::PO + lc0 + 16 * nt] = O[mt][nt][i];
   };
   for (int c = 0; c < p.nc; ++c) {
     // Every product step below issues the LDS reads of the next step's
@@ -137,7 +147,7 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
     {
       In8 av[2];
       auto ldv = [&](int mt, int bf) {
-        av[bf] = Ops::ld_in(lds + L::VS + (16 * mt + n) * L::PQ + (32 * wave + 8 * g4) * L::ES);
+        av[bf] = Ops::ld_in(lds + L::VS + (16 * mt + n) * L::PV + (w32 + 8 * g4) * L::ES);
       };
       ldv(0, 0);
 #pragma unroll
@@ -145,9 +155,11 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
         const int bf = mt & 1;
         if (mt + 1 < 4) ldv(mt + 1, bf ^ 1);
         __builtin_amdgcn_sched_barrier(0);
-        R[mt][0] = Ops::mma_in(av[bf], vsel0, zero4());
-        R[mt][1] = Ops::mma_in(av[bf], vsel1, zero4());
-        O[mt][0] = O[mt][1] = zero4();
+#pragma unroll
+        for (int nt = 0; nt < NCT; ++nt) {
+          R[mt][nt] = Ops::mma_in(av[bf], vsel[nt], zero4());
+          O[mt][nt] = zero4();
+        }
       }
       constexpr int G1 = 4 * KS;  // steps (kk, mt)
       Opnd ak[2], aqv[2];
@@ -250,7 +262,7 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    write_tile();     // the helpers finished tile c - 1 before the barrier above
+    write_tile(c);    // the helpers are done with this buffer's previous tile (barrier above)
     {
       // prefix-cache snapshot of the state after this chunk
       const int j = snapshot_index(p, p.t0 / kChunk + c);
@@ -259,8 +271,8 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
         // id, so that they are not computed ahead and held across the loop
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        float* sn = p.snaps + (((int64_t)b * p.n_snap + j) * p.H + h) * D * D + 4 * (ln >> 4) * D + 32 * wave +
-                    (ln & 15);
+        float* sn = p.snaps + (((int64_t)b * p.n_snap + j) * p.H + h) * D * D + 4 * (ln >> 4) * D + cb +
+                    16 * NCT * wave + (ln & 15);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -283,32 +295,53 @@ __device__ __forceinline__ void scan_compute_waves(const ScanParams& p, char* ld
 }
 
 // Gate epilogue over the output tile of one chunk (section 2.3): NH threads,
-// TPR per token row, each with EC consecutive columns; the row's RMS comes
-// from a shuffle reduction over its TPR threads.  o is stored when asked for;
-// y = Sigmoid(gate) . o / rms(o) . w when the gate is given.  LIGHT: two
-// passes over the tile (sum of squares, then y in groups of 8 columns) and
-// the RMSNorm weight read when used, for callers short of registers;
-// otherwise one pass with the row segment and the weights in registers.  Both
-// forms round identically.
-template <typename T, int D, bool OUT_F32, int NH, bool LIGHT>
+// TPR per token row, each with EC consecutive columns of the DV columns the
+// workgroup owns (DV = D, or D / 2 when a head's columns are split between
+// two workgroups; cb is the first of them); the row's RMS comes from a
+// shuffle reduction over its TPR threads (and, split, the other workgroup's
+// half).  o is stored when asked for; y = Sigmoid(gate) . o / rms(o) . w
+// when the gate is given.  LIGHT: two passes over the tile (sum of squares,
+// then y in groups of 8 columns) and the RMSNorm weight read when used, for
+// callers short of registers; otherwise one pass with the row segment and
+// the weights in registers.  Every form sums the squares in the same order --
+// sequential sums over 16-column blocks, added block by block, then the
+// shuffle tree over the threads of the row -- so the split halves, the
+// one-pass and the two-pass forms all round identically.
+template <typename T, int D, bool OUT_F32, int NH, bool LIGHT, int DV = D>
 struct GateEpilogue {
   using OutT = typename std::conditional<OUT_F32, float, uint16_t>::type;
   static constexpr int ES = sizeof(T);
   static constexpr int TPR = NH / 64;      // threads per output row
-  static constexpr int EC = D / TPR;       // columns per thread
+  static constexpr int EC = DV / TPR;      // columns per thread
   static constexpr int NG = EC * ES / 16;  // 16-byte vectors of gate logits per thread
   static constexpr int PER = 16 / ES;      // gate logits per 16-byte vector
-  static_assert(EC % 8 == 0, "groups of 8 columns");
-  int er, ec;                              // row and first column of this thread
+  static_assert(EC % 16 == 0, "blocks of 16 columns");
+  int er, ec;                              // row and first column (within the DV) of this thread
+  int cb;                                  // first column of the workgroup's DV
   float wv[LIGHT ? 1 : EC];                // RMSNorm weight of those columns (one-pass form)
 
-  __device__ __forceinline__ void init(const ScanParams& p, int h, int hid) {
+  __device__ __forceinline__ void init(const ScanParams& p, int h, int hid, int col_base = 0) {
     er = hid / TPR;
     ec = (hid % TPR) * EC;
+    cb = col_base;
     if constexpr (!LIGHT) {
 #pragma unroll
-      for (int j = 0; j < EC; ++j) wv[j] = (p.rms_w != nullptr) ? p.rms_w[h * D + ec + j] : 1.0f;
+      for (int j = 0; j < EC; ++j) wv[j] = (p.rms_w != nullptr) ? p.rms_w[h * D + cb + ec + j] : 1.0f;
     }
+  }
+
+  // sum of squares of a 16-column block, sequentially
+  static __device__ __forceinline__ float sumsq16(const float* x) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s = __builtin_fmaf(x[j], x[j], s);
+    return s;
+  }
+  // over the threads of a row
+  static __device__ __forceinline__ float row_reduce(float ss) {
+#pragma unroll
+    for (int m = 1; m < TPR; m <<= 1) ss += __shfl_xor(ss, m);
+    return ss;
   }
 
   // 8 values to 8 output elements (16 or 32 bytes)
@@ -338,9 +371,53 @@ struct GateEpilogue {
     const int64_t tok_stride = (int64_t)p.H * D;
     const int row = min(er, p.T - tok0 - 1);
     const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const T*>(p.gate) + head_base +
-                                                      (int64_t)(tok0 + row) * tok_stride + ec);
+                                                      (int64_t)(tok0 + row) * tok_stride + cb + ec);
 #pragma unroll
     for (int q = 0; q < NG; ++q) g[q] = src[q];
+  }
+
+  // this thread's 16-column block q16 of its row of the tile
+  __device__ __forceinline__ void read16(const float* trow, int q16, float (&x)[16]) const {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(trow + 16 * q16 + 4 * k);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[4 * k + j] = t[j];
+    }
+  }
+
+  // y of this thread's row segment from the row's full sum of squares
+  template <int PO, typename GetG>
+  __device__ __forceinline__ void emit_y(const ScanParams& p, int h, int64_t orow, const float* trow, GetG getg,
+                                         float ss) const {
+    const float rinv = hw_rsqrt(ss / D + p.rms_eps);
+#pragma unroll
+    for (int q = 0; q < EC / 8; ++q) {
+      float yv[8];
+      const f32x4 t0 = *reinterpret_cast<const f32x4*>(trow + 8 * q);
+      const f32x4 t1 = *reinterpret_cast<const f32x4*>(trow + 8 * q + 4);
+      f32x4 w0 = {1.f, 1.f, 1.f, 1.f}, w1 = w0;
+      if constexpr (LIGHT) {
+        if (p.rms_w != nullptr) {
+          w0 = *reinterpret_cast<const f32x4*>(p.rms_w + h * D + cb + ec + 8 * q);
+          w1 = *reinterpret_cast<const f32x4*>(p.rms_w + h * D + cb + ec + 8 * q + 4);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          w0[j] = wv[8 * q + j];
+          w1[j] = wv[8 * q + 4 + j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = 8 * q + j;  // column within the segment
+        const float ov = j < 4 ? t0[j] : t1[j - 4];
+        const float w = j < 4 ? w0[j] : w1[j - 4];
+        yv[j] = sigmoid_fast(logit(getg(e / PER), e % PER)) * ov * (rinv * w);
+      }
+      store8(static_cast<OutT*>(p.y) + orow + 8 * q, yv);
+    }
   }
 
   // o / y of the chunk at token tok0 of head h from the tile (row pitch PO
@@ -349,73 +426,55 @@ struct GateEpilogue {
   template <bool CHECK_ROWS, int PO, typename GetG>
   __device__ __forceinline__ void run(const ScanParams& p, int h, int64_t head_base, int tok0, const float* otile,
                                       GetG getg) const {
+    static_assert(DV == D, "a split row needs half_ss / emit_y");
     if (CHECK_ROWS && er >= p.T - tok0) return;
     const int64_t tok_stride = (int64_t)p.H * D;
-    const int64_t orow = head_base + (tok0 + er) * tok_stride + ec;
+    const int64_t orow = head_base + (tok0 + er) * tok_stride + cb + ec;
     const float* trow = otile + er * PO + ec;
-    if constexpr (!LIGHT) {
-      float ov[EC];
+    float ss = 0.f;
 #pragma unroll
-      for (int q = 0; q < EC / 4; ++q) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(trow + 4 * q);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ov[4 * q + j] = t[j];
-      }
+    for (int q16 = 0; q16 < EC / 16; ++q16) {
+      float x[16];
+      read16(trow, q16, x);
+      const float s16 = sumsq16(x);
+      ss = q16 == 0 ? s16 : ss + s16;
       if (p.o != nullptr)
 #pragma unroll
-        for (int q = 0; q < EC / 8; ++q) store8(static_cast<OutT*>(p.o) + orow + 8 * q, ov + 8 * q);
-      if (p.y == nullptr) return;
-      float ss = 0.f;
-#pragma unroll
-      for (int j = 0; j < EC; ++j) ss += ov[j] * ov[j];
-#pragma unroll
-      for (int m = 1; m < TPR; m <<= 1) ss += __shfl_xor(ss, m);
-      const float rinv = hw_rsqrt(ss / D + p.rms_eps);
-      float yv[EC];
-#pragma unroll
-      for (int e = 0; e < EC; ++e) yv[e] = sigmoid_fast(logit(getg(e / PER), e % PER)) * ov[e] * (rinv * wv[e]);
-#pragma unroll
-      for (int q = 0; q < EC / 8; ++q) store8(static_cast<OutT*>(p.y) + orow + 8 * q, yv + 8 * q);
-    } else {
-      float ss = 0.f;
-#pragma unroll
-      for (int q = 0; q < EC / 8; ++q) {
-        float x[8];
-        const f32x4 t0 = *reinterpret_cast<const f32x4*>(trow + 8 * q);
-        const f32x4 t1 = *reinterpret_cast<const f32x4*>(trow + 8 * q + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          x[j] = t0[j];
-          x[4 + j] = t1[j];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
-        if (p.o != nullptr) store8(static_cast<OutT*>(p.o) + orow + 8 * q, x);
-      }
-      if (p.y == nullptr) return;
-#pragma unroll
-      for (int m = 1; m < TPR; m <<= 1) ss += __shfl_xor(ss, m);
-      const float rinv = hw_rsqrt(ss / D + p.rms_eps);
-#pragma unroll
-      for (int q = 0; q < EC / 8; ++q) {
-        float yv[8];
-        const f32x4 t0 = *reinterpret_cast<const f32x4*>(trow + 8 * q);
-        const f32x4 t1 = *reinterpret_cast<const f32x4*>(trow + 8 * q + 4);
-        f32x4 w0 = {1.f, 1.f, 1.f, 1.f}, w1 = w0;
-        if (p.rms_w != nullptr) {
-          w0 = *reinterpret_cast<const f32x4*>(p.rms_w + h * D + ec + 8 * q);
-          w1 = *reinterpret_cast<const f32x4*>(p.rms_w + h * D + ec + 8 * q + 4);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int e = 8 * q + j;  // column within the segment
-          const float ov = j < 4 ? t0[j] : t1[j - 4];
-          const float w = j < 4 ? w0[j] : w1[j - 4];
-          yv[j] = sigmoid_fast(logit(getg(e / PER), e % PER)) * ov * (rinv * w);
-        }
-        store8(static_cast<OutT*>(p.y) + orow + 8 * q, yv);
-      }
+        for (int k = 0; k < 2; ++k) store8(static_cast<OutT*>(p.o) + orow + 16 * q16 + 8 * k, x + 8 * k);
     }
+    if (p.y == nullptr) return;
+    emit_y<PO>(p, h, orow, trow, getg, row_reduce(ss));
+  }
+
+  // Split row, first half: o of this thread's segment (when asked for) and
+  // the sum of squares over the workgroup's DV columns of the row.
+  template <bool CHECK_ROWS, int PO>
+  __device__ __forceinline__ float half_ss(const ScanParams& p, int64_t head_base, int tok0, const float* otile) const {
+    if (CHECK_ROWS && er >= p.T - tok0) return 0.f;
+    const int64_t tok_stride = (int64_t)p.H * D;
+    const int64_t orow = head_base + (tok0 + er) * tok_stride + cb + ec;
+    const float* trow = otile + er * PO + ec;
+    float ss = 0.f;
+#pragma unroll
+    for (int q16 = 0; q16 < EC / 16; ++q16) {
+      float x[16];
+      read16(trow, q16, x);
+      const float s16 = sumsq16(x);
+      ss = q16 == 0 ? s16 : ss + s16;
+      if (p.o != nullptr)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) store8(static_cast<OutT*>(p.o) + orow + 16 * q16 + 8 * k, x + 8 * k);
+    }
+    return row_reduce(ss);
+  }
+
+  // Split row, second half: y from the tile and the row's full sum of squares.
+  template <bool CHECK_ROWS, int PO, typename GetG>
+  __device__ __forceinline__ void split_y(const ScanParams& p, int h, int64_t head_base, int tok0, const float* otile,
+                                          GetG getg, float ss) const {
+    if (CHECK_ROWS && er >= p.T - tok0) return;
+    const int64_t tok_stride = (int64_t)p.H * D;
+    emit_y<PO>(p, h, head_base + (tok0 + er) * tok_stride + cb + ec, otile + er * PO + ec, getg, ss);
   }
 };
 

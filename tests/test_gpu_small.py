@@ -429,3 +429,43 @@ def test_fused_with_heads_filling_the_device(kda):
     ref = _run(kda, x, fused=False, overlap=False)
     for key in ("o", "y", "S_T"):
         assert _bit_equal(auto[key], ref[key]), key
+
+
+@pytest.mark.parametrize("B,T,H,opts", [
+    (4, 4096, 32, {}),                                           # the prefill workload's shape: 256 workgroups
+    (1, 1000, 3, {}),                                            # ragged last chunk, 6 workgroups (a partial group of 16)
+    (2, 700, 5, {"out_dtype": torch.float32, "rms_w": True}),    # fp32 outputs, RMSNorm weight
+    (1, 640, 2, {"gate": False}),                                # o and S_T only: no row-sum exchange
+    (3, 512, 2, {"S0": False, "want_o": False}),                 # zero initial state, y and S_T only
+    (1, 2048, 4, {"snapshot_chunks": 8}),                        # prefix-cache snapshots from both halves
+])
+def test_split_scan_matches_unsplit(kda, monkeypatch, B, T, H, opts):
+    """One-stream calls with 2 B H within the device's compute units split
+    each head's value columns between two scan workgroups that exchange their
+    RMSNorm row sums; the result equals the unsplit scan workgroup's bit for
+    bit (o, y, S_T, snapshots) and the fp64 oracle within 3e-3."""
+    D = 128
+    x = gen_inputs(_custom(B, T, H, D, "bf16", seed=5000 + B * T + H))
+    opts = dict(opts)
+    kw = {"overlap": False, "fused": False}
+    if opts.pop("rms_w", False):
+        w = torch.from_numpy(np.random.default_rng(7).uniform(0.5, 1.5, (H, D)).astype(np.float32)).cuda()
+        kw["rms_w"] = w
+    for k_ in ("out_dtype", "want_o", "snapshot_chunks"):
+        if k_ in opts:
+            kw[k_] = opts.pop(k_)
+    log(f"[split] B={B} T={T} H={H} {sorted(kw)}")
+    split = _run(kda, x, **opts, **kw)
+    monkeypatch.setenv("KDA_TEST_NO_SPLIT", "1")
+    whole = _run(kda, x, **opts, **kw)
+    monkeypatch.delenv("KDA_TEST_NO_SPLIT")
+    keys = [k_ for k_ in ("o", "y", "S_T", "snapshots") if k_ in whole]
+    assert keys and all(k_ in split for k_ in keys)
+    for key in keys:
+        assert _bit_equal(split[key], whole[key]), key
+    if "rms_w" not in kw and kw.get("snapshot_chunks", 0) == 0:
+        ref = _oracle(x, gate=opts.get("gate", True), S0=opts.get("S0", True))
+        for key in keys:
+            e = rel_l2(host64(split[key]), ref[key])
+            log(f"[split] {key} rel_l2={e:.3e}")
+            assert e <= TOL_BF16, key
