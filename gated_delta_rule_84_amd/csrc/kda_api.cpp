@@ -226,6 +226,17 @@ constexpr int kMaxDevices = 64;
 DeviceCtx g_dev[kMaxDevices];
 
 // Compute units of the current device (0 if unknown), cached per device.
+int device_cus();
+
+// Whether a one-stream call splits each head's scan between two workgroups
+// (kda_scan.hip): bf16 inputs at d = 128 and 2 B H workgroups within the
+// device's compute units.
+bool split_taken(const kda_desc* d) {
+  return kda::split_supported((int)elem_size(d->in_dtype), d->d_k) &&
+         2 * (int64_t)d->B * d->H <= device_cus() && !split_disabled();
+}
+
+// Compute units of the current device (0 if unknown), cached per device.
 int device_cus() {
   static std::atomic<int> cached[kMaxDevices] = {};
   int dev = 0;
@@ -304,7 +315,29 @@ struct Plan {
   int n_scan;
   bool fused;
   bool pipelined;
+  int64_t window;  // pipelined: chunks per window (a multiple of seg_nc, or the whole sequence)
 };
+
+// Chunks per window of the pipelined schedule for a workspace of ws_bytes
+// bytes: the whole sequence when every record fits, else the largest
+// multiple of the segment length whose records fit, or 0 when that is below
+// kMinPipelinedWindow chunks (the double-buffered overlapped schedule is then
+// at least as fast: with one window of 512 chunks the pipelined windows run
+// about as fast as the overlapped schedule's 128-chunk segments).
+constexpr int64_t kMinPipelinedWindow = 512;
+int64_t pipelined_window(const kda_desc* d, size_t ws_bytes) {
+  const int64_t nc = num_chunks(d), seg = pipelined_chunks(d);
+  if (ws_bytes >= layout_for(d, nc).total) return nc;
+  int64_t lo = 0, hi = nc / seg;  // in segments
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo + 1) / 2;
+    if (layout_for(d, mid * seg).total <= ws_bytes)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo * seg >= kMinPipelinedWindow ? lo * seg : 0;
+}
 
 // The two library streams can serve B * H scan workgroups on the current
 // device (B * H at most 5/8 of its compute units); the streams themselves
@@ -337,12 +370,13 @@ Plan make_plan(const kda_desc* d, size_t ws_bytes, bool one_stream = false) {
     return p;
   }
   int dev = 0, n_scan = 0;
-  if (!one_stream && pipelined_eligible(d) && ws_bytes >= layout_for(d, nc_total).total &&
-      two_streams(d, &dev, &n_scan)) {
+  const int64_t window = (!one_stream && pipelined_eligible(d)) ? pipelined_window(d, ws_bytes) : 0;
+  if (window > 0 && two_streams(d, &dev, &n_scan)) {
     p.pipelined = true;
     p.dev = dev;
     p.n_scan = n_scan;
     p.seg_nc = pipelined_chunks(d);
+    p.window = window;
     return p;
   }
   if (!one_stream && pipe_wanted(d) && ws_bytes >= layout_for(d, 2 * pipe_chunks(d)).total &&
@@ -377,8 +411,10 @@ int32_t plan_launches(const kda_desc* d, const Plan& p, int32_t* kinds, int32_t 
   if (p.fused) {
     put(KDA_LAUNCH_FUSED);
   } else if (p.pipelined) {
-    put(KDA_LAUNCH_INTRA);
-    put(KDA_LAUNCH_SCAN);
+    for (int64_t c0 = 0; c0 < num_chunks(d); c0 += p.window) {
+      put(KDA_LAUNCH_INTRA);
+      put(KDA_LAUNCH_SCAN);
+    }
   } else {
     const int64_t nc_total = num_chunks(d);
     for (int64_t c0 = 0; c0 < nc_total; c0 += p.seg_nc) {
@@ -446,8 +482,9 @@ kda_status kda_chunk_fwd_status(const kda_desc* d, const void* ws, size_t ws_byt
   }
   if (ws == nullptr || fused_wanted(d) || ws_bytes < layout_for(d, 1).total || d->T == 0) return KDA_OK;
   const Plan p = make_plan(d, ws_bytes);
-  if (!p.pipelined && !p.overlapped) return KDA_OK;  // nothing waits in the one-stream schedule
-  const WsLayout L = layout_for(d, p.pipelined ? num_chunks(d) : 2 * pipe_chunks(d));
+  // in the one-stream schedule only the split scan waits (for its other half)
+  if (!p.pipelined && !p.overlapped && !split_taken(d)) return KDA_OK;
+  const WsLayout L = layout_for(d, p.pipelined ? p.window : p.overlapped ? 2 * pipe_chunks(d) : p.seg_nc);
   uint32_t word = 0;
   if (hipMemcpy(&word, static_cast<const char*>(ws) + L.off_done, sizeof(word), hipMemcpyDeviceToHost) !=
       hipSuccess) {
@@ -516,8 +553,12 @@ size_t kda_chunk_fwd_workspace_size(const kda_desc* d) {
   if (validate_desc(d) != KDA_OK) return 0;
   if (fused_wanted(d)) return kFusedWorkspace;
   if (pipelined_eligible(d)) {
+    // every record when that fits the cap, else the largest window of the
+    // pipelined schedule that does
     const size_t all = layout_for(d, num_chunks(d)).total;
     if (all <= kPipelinedWorkspaceCap) return all;
+    const int64_t w = pipelined_window(d, kPipelinedWorkspaceCap);
+    if (w > 0) return layout_for(d, w).total;
   }
   if (pipe_wanted(d)) return layout_for(d, 2 * pipe_chunks(d)).total;
   const int32_t toks = d->T < kDefaultSegmentTokens ? (d->T > 0 ? d->T : 1) : kDefaultSegmentTokens;
@@ -605,7 +646,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   auto launch_intra = [&](int64_t c0, int nc, const kda::ChunkWs& recs, hipStream_t st_, uint32_t* done = nullptr,
                           int rec_stride = 0, int rec_c0 = 0, int seg_len = 0,
                           const uint32_t* progress = nullptr, uint32_t* pacing_off = nullptr, int lead = 0,
-                          uint64_t* clear = nullptr, int64_t clear_words = 0) {
+                          uint64_t* clear = nullptr, int64_t clear_words = 0, uint32_t* clear_status = nullptr) {
     kda::IntraParams ip{};
     ip.q = q;
     ip.k = k;
@@ -632,6 +673,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     ip.lead = lead;
     ip.clear = clear;
     ip.clear_words = clear_words;
+    ip.clear_status = clear_status;
     tr.before(st_);
     const kda_status r = check_launch(kda::launch_intra(ip, D, in_f32, st_), st_);
     tr.after(st_);
@@ -727,7 +769,8 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   // which waits inside the kernel for each segment's record counters (zeroed
   // on the caller's stream first).
   if (plan.pipelined) {
-    const WsLayout L = layout_for(d, nc_total);
+    const int64_t window = plan.window;
+    const WsLayout L = layout_for(d, window);
     DeviceCtx& c = g_dev[plan.dev];
     std::lock_guard<std::mutex> lock(c.mu);
     hipStream_t si = nullptr, ss = nullptr;
@@ -755,22 +798,34 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     if (!ok(hipEventRecord(c.fork, s)) || !ok(hipStreamWaitEvent(si, c.fork, 0)) ||
         !ok(hipStreamWaitEvent(ss, c.fork, 0)))
       return KDA_ERR_HIP;
-    float* S_out = S_T ? S_T : reinterpret_cast<float*>(base + L.off_carry);
+    float* S_run = S_T ? S_T : reinterpret_cast<float*>(base + L.off_carry);
+    const float* S_in = S0;
     // pacing lead: a segment and kPipelinedSlack chunks (a producer waiting
     // for the scan never holds back a record the scan is waiting for)
     const int lead = seg_len + kPipelinedSlack;
-    // The intra-chunk launch is enqueued before the scan: should the two
-    // library streams share a hardware queue (their work then runs in
-    // enqueue order), the scan still finds every record written instead of
-    // waiting for producers queued behind it.
-    const int produced = withheld_segments(n_seg);
-    if (produced > 0) {
-      const int nc_prod = (int)std::min<int64_t>(nc_total, (int64_t)produced * seg_len);
-      st = launch_intra(0, nc_prod, recs, si, done, (int)nc_total, 0, seg_len, progress, status + 1, lead);
+    // Windows of `window` chunks (one window when every record fits): per
+    // window one intra-chunk launch and one scan launch, the state carried
+    // from window to window.  The records of a window reuse the workspace,
+    // so a window's intra-chunk launch first waits, through an event, for
+    // the previous window's scan.  Each intra-chunk launch is enqueued
+    // before its scan: should the two library streams share a hardware queue
+    // (their work then runs in enqueue order), every scan still finds its
+    // records written instead of waiting for producers queued behind it.
+    const int64_t produced = (int64_t)withheld_segments(n_seg) * seg_len;  // chunks the producers cover
+    int w = 0;
+    for (int64_t c0 = 0; c0 < nc_total; c0 += window, ++w) {
+      const int nw = (int)std::min<int64_t>(window, nc_total - c0);
+      if (w > 0 && !ok(hipStreamWaitEvent(si, c.scan_done[(w - 1) & 1], 0))) return KDA_ERR_HIP;
+      const int nc_prod = (int)std::max<int64_t>(0, std::min<int64_t>(nw, produced - c0));
+      if (nc_prod > 0) {
+        st = launch_intra(c0, nc_prod, recs, si, done, nw, 0, seg_len, progress, status + 1, lead);
+        if (st != KDA_OK) return st;
+      }
+      st = launch_scan(c0, nw, recs, S_in, S_run, ss, done, seg_len, status, progress);
       if (st != KDA_OK) return st;
+      S_in = S_run;
+      if (c0 + window < nc_total && !ok(hipEventRecord(c.scan_done[w & 1], ss))) return KDA_ERR_HIP;
     }
-    st = launch_scan(0, (int)nc_total, recs, S0, S_out, ss, done, seg_len, status, progress);
-    if (st != KDA_OK) return st;
     if (!ok(hipEventRecord(c.join_intra, si)) || !ok(hipEventRecord(c.join_scan, ss)) ||
         !ok(hipStreamWaitEvent(s, c.join_intra, 0)) || !ok(hipStreamWaitEvent(s, c.join_scan, 0)))
       return KDA_ERR_HIP;
@@ -851,16 +906,22 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   float* S_run = S_T ? S_T : carry;
   const float* S_in = S0;
   const int64_t bh_n = (int64_t)d->B * d->H;
+  // the split's bounded wait for the other half reports through the status
+  // word, cleared by the first intra-chunk launch with the exchange ring
   uint64_t* xchg = nullptr;
-  if (kda::split_supported((int)elem_size(d->in_dtype), D) && 2 * bh_n <= device_cus() && !split_disabled())
+  uint32_t* status = nullptr;
+  if (split_taken(d)) {
     xchg = reinterpret_cast<uint64_t*>(base + L.off_xchg);
+    status = reinterpret_cast<uint32_t*>(base + L.off_done);
+  }
   for (int64_t c0 = 0; c0 < nc_total; c0 += seg_nc) {
     const int nc = (int)((nc_total - c0) < seg_nc ? (nc_total - c0) : seg_nc);
-    const bool clear = xchg != nullptr && y != nullptr && c0 == 0;
+    const bool first = xchg != nullptr && c0 == 0;
+    const bool clear = first && y != nullptr;
     st = launch_intra(c0, nc, cw, s, nullptr, 0, 0, 0, nullptr, nullptr, 0, clear ? xchg : nullptr,
-                      clear ? bh_n * kda::kXchgWordsPerHead : 0);
+                      clear ? bh_n * kda::kXchgWordsPerHead : 0, first ? status : nullptr);
     if (st != KDA_OK) return st;
-    st = launch_scan(c0, nc, cw, S_in, S_run, s, nullptr, 0, nullptr, nullptr, xchg);
+    st = launch_scan(c0, nc, cw, S_in, S_run, s, nullptr, 0, status, nullptr, xchg);
     if (st != KDA_OK) return st;
     S_in = S_run;
   }

@@ -61,8 +61,10 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
 
   if (p.clear != nullptr)
     for (int64_t w = (int64_t)item * 256 + tid; w < p.clear_words; w += (int64_t)gridDim.x * 256) p.clear[w] = 0;
-  if (p.progress != nullptr && c % kPaceEvery == 0 && c > p.lead) {  // uniform: pacing (see IntraParams)
-    if (tid == 0) pace(p.progress + bh, (uint32_t)(c - p.lead), p.pacing_off);
+  if (p.clear_status != nullptr && item == 0 && tid == 0) *p.clear_status = 0;
+  const int cg = p.t0 / kChunk + c;  // chunk index in the sequence
+  if (p.progress != nullptr && cg % kPaceEvery == 0 && cg > p.lead) {  // uniform: pacing (see IntraParams)
+    if (tid == 0) pace(p.progress + bh, (uint32_t)(cg - p.lead), p.pacing_off);
     __syncthreads();
   }
   Core ic;
@@ -87,8 +89,9 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
   }
   Core::template tb_pass<256>(tid, s, reinterpret_cast<T*>(recp + 16 * RU.tb), &ic.sink);
   if (p.done != nullptr) {
-    // the record's counter: that of its segment (one segment if seg_len = 0)
-    const int seg = p.seg_len > 0 ? c / p.seg_len : 0;
+    // the record's counter: that of its segment of the sequence (one
+    // segment if seg_len = 0)
+    const int seg = p.seg_len > 0 ? cg / p.seg_len : 0;
     count_record(p.done + (int64_t)seg * bh_n + bh);
   }
 }

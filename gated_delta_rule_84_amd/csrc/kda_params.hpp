@@ -91,15 +91,17 @@ struct IntraParams {
   int decay;       // 0: K3 bounded map; 1: Kimi Linear softplus map (pairwise diagonal blocks)
   ChunkWs ws;
   // Finished records (count_record), or nullptr: chunk c's record counts in
-  // done[s B H + b H + h], s = c / seg_len its segment (seg_len = 0: s = 0).
+  // done[s B H + b H + h], s = (t0 / 64 + c) / seg_len its segment of the
+  // sequence (seg_len = 0: s = 0); t0 / 64 is then a multiple of seg_len.
   uint32_t* done;
   int seg_len;
   // Record of chunk c of the launch: ((b H + h) rec_stride + rec_c0 + c).
   // rec_stride = 0 means nc (records of this launch only, rec_c0 = 0).
   int rec_stride, rec_c0;
   // Pacing (pipelined schedule), or progress = nullptr: a workgroup of a
-  // chunk c with c % kPaceEvery == 0 first waits until the scan of its (b, h) has
-  // reached chunk c - lead (progress[b H + h]), so that a record is read a
+  // chunk c (index in the sequence) with c % kPaceEvery == 0 first waits until
+  // the scan of its (b, h) has reached chunk c - lead (progress[b H + h]),
+  // so that a record is read a
   // few chunk steps after it is written, while it is still in the memory-side
   // cache.  Performance only: the wait is bounded, and the first one that
   // runs out sets *pacing_off, which ends pacing for the launch.
@@ -111,6 +113,7 @@ struct IntraParams {
   // precedes that scan on the same stream
   uint64_t* clear;
   int64_t clear_words;
+  uint32_t* clear_status;  // a status word set to zero as well, or nullptr
 };
 
 // Status bits a kernel ORs into the workspace's status word (read by
@@ -142,9 +145,10 @@ struct ScanParams {
   int n_snap;
   // Pipelined schedule (specialised scan kernel only): seg_len > 0, records
   // produced by an intra-chunk launch running beside this one and counted in
-  // segments of seg_len chunks; done then holds one counter per (segment, b,
-  // h) (see num_segments).  seg_len = 0: all records exist, or done (if not
-  // nullptr) is one counter per (b, h).
+  // segments of seg_len chunks of the sequence; done then holds one counter
+  // per (segment, b, h), the launch's first at segment t0 / 64 / seg_len.
+  // seg_len = 0: all records exist, or done (if not nullptr) is one counter
+  // per (b, h).
   int seg_len;
   // [B * H]: the chunk each (b, h) has reached, published every chunk step
   // for the producer's pacing (see IntraParams::progress), or nullptr

@@ -525,7 +525,10 @@ __global__ __launch_bounds__((WsLds<T, D, NS>::NT), 1) void kda_scan_ws_kernel(c
   const int n_seg = p.seg_len > 0 ? num_segments(p.nc, p.seg_len) : 0;
   auto seg_start = [&](int s) { return s * p.seg_len; };
   auto seg_size = [&](int s) { return (uint32_t)(min((s + 1) * p.seg_len, p.nc) - s * p.seg_len); };
-  auto seg_done = [&](int s) { return p.done + ((int64_t)s * p.B * p.H + bh); };
+  // counters are indexed by the segment of the sequence (launches start on
+  // a segment boundary: a window of the pipelined schedule)
+  const int seg0 = p.seg_len > 0 ? p.t0 / kChunk / p.seg_len : 0;
+  auto seg_done = [&](int s) { return p.done + ((int64_t)(seg0 + s) * p.B * p.H + bh); };
   int* gave_up = reinterpret_cast<int*>(lds + L::FLAG);
   int wseg = 0;  // segments waited for (pipelined schedule); uniform
   if (n_seg > 0) {

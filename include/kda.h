@@ -135,16 +135,17 @@ kda_status kda_desc_init(kda_desc* d, int32_t B, int32_t T, int32_t H, int32_t h
 
 /* Workspace bytes for kda_chunk_fwd's preferred schedule; 0 if *d is invalid.
  * The fused schedule needs none (256 is reported; ws may also be NULL then).
- * With d->overlap, bf16 inputs and a sequence longer than one segment
- * (d->segment_tokens, default 8192) this holds every
- * chunk record of the call (the pipelined schedule: 61,952 bytes per chunk and
- * (b, h) at d = 128, e.g. 6.1 GB for B 1, T 65,536, H 96) as long as that is at
- * most 8 GiB; otherwise, with d->overlap and a sequence longer than one
- * segment, it holds two segments of chunk records (the overlapped schedule),
- * and else the whole sequence (at most 65536 tokens per segment).  A smaller
- * workspace also works as long as it holds one chunk: the library then takes
- * the overlapped schedule if two segments fit, else it processes the sequence
- * in shorter segments, one after the other. */
+ * With d->overlap, bf16 inputs and a sequence longer than 8,192 tokens this
+ * holds every chunk record of the call (the pipelined schedule: 61,952 bytes
+ * per chunk and (b, h) at d = 128, e.g. 6.1 GB for B 1, T 65,536, H 96) as
+ * long as that is at most 8 GiB, and otherwise the largest window of the
+ * pipelined schedule within 8 GiB (e.g. 1,444 chunks = 92,416 tokens for
+ * H 96); else the whole sequence (at most 65536 tokens per segment).  A
+ * smaller workspace also works as long as it holds one chunk: the library
+ * takes the pipelined schedule in windows if at least 512 chunks of records
+ * fit, else the overlapped schedule if two segments of d->segment_tokens
+ * (default 8192) fit, else it processes the sequence in shorter segments,
+ * one after the other. */
 size_t kda_chunk_fwd_workspace_size(const kda_desc* d);
 
 /* Bytes needed for one segment of `segment_tokens` tokens (rounded up to whole
@@ -176,10 +177,12 @@ kda_status kda_chunk_fwd_schedule(const kda_desc* d, size_t ws_bytes, int32_t* s
  * used workspace ws (ws_bytes bytes) with this descriptor: waits for `stream`
  * (a host synchronisation, unlike every other entry point), then returns
  * KDA_OK, or KDA_ERR_TIMEOUT when that call took a two-stream schedule and
- * one of the scan's bounded in-kernel waits for chunk records gave up -- its
- * producers never ran beside it (e.g. another process held the device's
- * compute units for about a second); the call's outputs are then invalid
- * (NaN).  Calls that took the one-stream or fused schedule always report
+ * one of the scan's bounded in-kernel waits gave up -- for chunk records
+ * whose producers never ran beside it, or, in the one-stream schedule with
+ * a head's scan split between two workgroups, for the other workgroup (e.g.
+ * another process held the device's compute units for about a second); the
+ * call's outputs are then invalid (NaN).  Calls that took the fused
+ * schedule, or the one-stream schedule without the split, always report
  * KDA_OK here.
  */
 kda_status kda_chunk_fwd_status(const kda_desc* d, const void* ws, size_t ws_bytes, void* stream);
@@ -234,10 +237,13 @@ kda_status kda_chunk_fwd_launches(const kda_desc* d, size_t ws_bytes, int32_t* k
  * their enqueue (a per-device lock); they must not share a workspace.
  *
  * Pipelined schedule (the same conditions, bf16 inputs, and a workspace that
- * holds every chunk record of the call): one intra-chunk launch over the
- * whole sequence runs on one library stream, producing the records chunk by
- * chunk (every head's record of chunk c before any of chunk c + 1), and a
- * single scan launch over the whole sequence runs on the other, waiting
+ * holds every chunk record of the call, or at least 512 chunks of them: the
+ * sequence is then processed in windows of as many whole segments as fit,
+ * the state carried from window to window and each window's producers
+ * waiting for the previous window's scan through an event): per window one
+ * intra-chunk launch runs on one library stream, producing the records chunk
+ * by chunk (every head's record of chunk c before any of chunk c + 1), and a
+ * single scan launch over the window runs on the other, waiting
  * inside the kernel for each segment's records (device-scope record stores,
  * one counter per segment and (b, h); segments of d->segment_tokens tokens,
  * 128 by default).  The scan publishes each (b, h)'s chunk every step, and

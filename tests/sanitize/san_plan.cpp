@@ -48,11 +48,27 @@ static void check_layout(const kda_desc* d, int64_t seg_nc) {
   EXPECT(L.rec_bytes == (size_t)kda::rec_units((int)elem_size(d->in_dtype), d->d_k).bytes);
 }
 
+// the pipelined schedule's window for a workspace: none, the whole sequence,
+// or the largest run of whole segments (at least kMinPipelinedWindow chunks)
+// whose records fit
+static void check_window(const kda_desc* d, size_t ws) {
+  const int64_t nc = num_chunks(d), seg = pipelined_chunks(d);
+  const int64_t w = pipelined_window(d, ws);
+  EXPECT(w == 0 || w == nc || (w % seg == 0 && w >= kMinPipelinedWindow && w < nc));
+  if (w > 0) EXPECT(layout_for(d, w).total <= ws);
+  if (w > 0 && w < nc) EXPECT(layout_for(d, w + seg).total > ws);
+}
+
 static void check_plan(const kda_desc* d, size_t ws_bytes) {
   const Plan p = make_plan(d, ws_bytes);
   const int64_t nc = num_chunks(d);
   EXPECT(p.seg_nc >= 1);
   EXPECT(!(p.fused && p.pipelined) && !(p.overlapped && p.pipelined));
+  if (p.pipelined) {  // windows: the whole sequence or whole segments that fit
+    EXPECT(p.window >= 1 && p.window <= (nc < 1 ? 1 : nc));
+    EXPECT(p.window == nc || (p.window % p.seg_nc == 0 && p.window >= kMinPipelinedWindow));
+    EXPECT(layout_for(d, p.window).total <= ws_bytes);
+  }
   if (!p.fused && !p.pipelined && !p.overlapped && ws_bytes >= layout_for(d, 1).total) {
     EXPECT(layout_for(d, p.seg_nc).total <= ws_bytes);  // the chosen segment fits
     EXPECT(p.seg_nc <= (nc < 1 ? 1 : nc));
@@ -81,8 +97,12 @@ int main() {
             for (int64_t sn : {int64_t(1), int64_t(7), num_chunks(&d) < 1 ? int64_t(1) : num_chunks(&d)})
               check_layout(&d, sn);
             for (size_t ws : {size_t(0), layout_for(&d, 1).total, layout_for(&d, 3).total - 1,
+                              layout_for(&d, 700).total, layout_for(&d, 2049).total + 100,
                               kda_chunk_fwd_workspace_size(&d), size_t(1) << 40})
+            {
               check_plan(&d, ws);
+              check_window(&d, ws);
+            }
           }
   // the fused schedule on request (bf16, K3 decay): one launch, no workspace
   for (int T : Ts) {

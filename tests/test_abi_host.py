@@ -179,15 +179,17 @@ def _launches(d, ws):
 def test_workspace_and_launch_queries():
     """Without a GPU the two-stream schedules are unavailable, so the library
     plans the one-stream segments; the size query still offers the pipelined
-    schedule's workspace (every record) for bf16 inputs up to its cap."""
+    schedule's workspace for bf16 inputs: every record up to its cap, beyond
+    it the largest window that fits the cap."""
     L = kda.lib()
     rec = 61952                                                   # bytes per chunk record at d = 128, fp16 entries
     d = _desc(B=1, T=65536, H=96, fused=0)
     ws = L.kda_chunk_fwd_workspace_size(ctypes.byref(d))
     assert ws >= 96 * 1024 * rec and ws < 96 * 1024 * rec + (64 << 20)   # every record, plus state and counters
-    big = _desc(B=1, T=1 << 20, H=96, fused=0)                    # every record would be 104 GB: two segments
+    big = _desc(B=1, T=1 << 20, H=96, fused=0)                    # every record would be 97 GB: windows
     ws_big = L.kda_chunk_fwd_workspace_size(ctypes.byref(big))
-    assert 2 * 96 * 128 * rec <= ws_big < 2 * 96 * 128 * rec + (64 << 20)
+    cap = 8 << 30                                                 # the largest window of the pipelined schedule
+    assert cap - 96 * 2 * rec - (64 << 20) <= ws_big <= cap       # within the cap, less than a segment short of it
     f32 = _desc(B=1, T=65536, H=96, fused=0, in_dtype=kda.KDA_F32)  # fp32: no pipelined schedule
     assert L.kda_chunk_fwd_workspace_size(ctypes.byref(f32)) < 96 * 1024 * rec
     # launch order of the one-stream plan: (intra, scan) per segment

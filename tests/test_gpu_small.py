@@ -469,3 +469,32 @@ def test_split_scan_matches_unsplit(kda, monkeypatch, B, T, H, opts):
             e = rel_l2(host64(split[key]), ref[key])
             log(f"[split] {key} rel_l2={e:.3e}")
             assert e <= TOL_BF16, key
+
+
+@pytest.mark.parametrize("B,T,H,D,windows", [
+    (1, 625 * 64 - 20, 3, 128, 2),        # 512 + 113 chunks, the last window short and ragged
+    (1, 4 * 512 * 64 + 1000, 1, 64, 5),   # four full windows and one of 16 chunks, d = 64
+])
+def test_pipelined_windows_match_one_stream(kda, B, T, H, D, windows):
+    """A workspace that holds 512 chunks of records but not all of them: the
+    pipelined schedule runs in windows of 512 chunks (per window one
+    intra-chunk launch and one scan launch, the state carried across, a
+    window's producers waiting for the previous window's scan), bit-identical
+    to the one-stream schedule and within 3e-3 of the oracle."""
+    x = gen_inputs(_custom(B, T, H, D, "bf16", seed=7000 + T + H))
+    desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, overlap=True, fused=False)
+    nbytes = kda.workspace_size(desc, 512 * 64)
+    assert kda.schedule(desc, nbytes)[1] == "pipelined"
+    assert kda.launches(desc, nbytes) == ["intra", "scan"] * windows
+    log(f"[pipelined windows] B={B} T={T} H={H} D={D} windows={windows}")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    pip = _run(kda, x, overlap=True, fused=False, workspace=ws)
+    assert kda.call_status(desc, ws) == 0
+    one = _run(kda, x, overlap=False, fused=False)
+    for key in ("o", "y", "S_T"):
+        assert _bit_equal(one[key], pip[key]), key
+    ref = _oracle(x)
+    for key in ("o", "y", "S_T"):
+        e = rel_l2(host64(pip[key]), ref[key])
+        log(f"[pipelined windows] {key} rel_l2={e:.3e}")
+        assert e <= TOL_BF16, key
