@@ -67,7 +67,7 @@ __device__ __forceinline__ void store8<uint16_t>(uint16_t* p, const float* x) {
   u32x4 w;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    w[i] = static_cast<uint32_t>(f32_to_bf16(x[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * i + 1])) << 16);
+    w[i] = pack2_bf16(x[2 * i], x[2 * i + 1]);
   *reinterpret_cast<u32x4*>(p) = w;
 }
 template <>
@@ -82,8 +82,8 @@ __device__ __forceinline__ void store4(T* p, const f32x4& x);
 template <>
 __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const f32x4& x) {
   uint2 w;
-  w.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
-  w.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+  w.x = pack2_bf16(x[0], x[1]);
+  w.y = pack2_bf16(x[2], x[3]);
   *reinterpret_cast<uint2*>(p) = w;
 }
 template <>

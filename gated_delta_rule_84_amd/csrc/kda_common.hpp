@@ -46,6 +46,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   __bf16 h = static_cast<__bf16>(f);  // v_cvt_pk_bf16_f32: round to nearest even
   return __builtin_bit_cast(uint16_t, h);
 }
+// Two fp32 values as packed bf16 (a in the low half), one v_cvt_pk_bf16_f32
+// with both sources (the same rounding as f32_to_bf16; converting element
+// by element instead packs each value alone and merges them with two more
+// instructions).
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
 
 // ---- element types of the two precision policies -------------------------
 // bf16 path: bf16 inputs, bf16 MFMA operands, hi/lo split where needed.
@@ -64,10 +73,8 @@ template <> struct Elem<float> {
 
 // 8 fp32 -> packed operand of the given element type.
 __device__ __forceinline__ bf16x8 pack8_bf16(const float* x) {
-  bf16x8 r;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = static_cast<__bf16>(x[j]);
-  return r;
+  const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, bf16x8);  // four paired conversions
 }
 // ---- one K=32 step: acc += A(16x32) * B(32x16) ---------------------------
 __device__ __forceinline__ f32x4 mma32(const bf16x8& a, const bf16x8& b, f32x4 acc) {

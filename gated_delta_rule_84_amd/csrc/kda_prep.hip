@@ -40,7 +40,7 @@ struct Vec8<uint16_t> {
     u32x4 w;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      w[i] = static_cast<uint32_t>(f32_to_bf16(x[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * i + 1])) << 16);
+      w[i] = pack2_bf16(x[2 * i], x[2 * i + 1]);
     *reinterpret_cast<u32x4*>(p) = w;
   }
 };

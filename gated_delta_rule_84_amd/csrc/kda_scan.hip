@@ -117,8 +117,7 @@ __device__ __forceinline__ void store16(void* dst, const float* x, int out_f32) 
     u32x4 w[2];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      w[q >> 2][q & 3] = static_cast<uint32_t>(f32_to_bf16(x[2 * q])) |
-                         (static_cast<uint32_t>(f32_to_bf16(x[2 * q + 1])) << 16);
+      w[q >> 2][q & 3] = pack2_bf16(x[2 * q], x[2 * q + 1]);
     u32x4* d = static_cast<u32x4*>(dst);
     d[0] = w[0];
     d[1] = w[1];

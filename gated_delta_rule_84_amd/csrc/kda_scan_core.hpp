@@ -353,7 +353,7 @@ struct GateEpilogue {
       u32x4 w;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        w[k] = static_cast<uint32_t>(f32_to_bf16(x[2 * k])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * k + 1])) << 16);
+        w[k] = pack2_bf16(x[2 * k], x[2 * k + 1]);
       *reinterpret_cast<u32x4*>(dst) = w;
     }
   }
