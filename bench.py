@@ -6,7 +6,7 @@ outputs), inputs already resident in HBM.  Prints ONE JSON line.
 
 The library picks the schedule for the workspace the size query offers (the
 pipelined two-kernel schedule for long sequences: every chunk record resident,
-one scan launch; two-segment records beyond the query's cap); --schedule
+one scan launch, or windows of records beyond the query's cap); --schedule
 forces one (the fused kernel measured slower at every size tried).
 --workload selects another configuration (long ones are generated slab by
 slab on the device).  K timed steps follow W warm-up steps; the JSON line
