@@ -146,7 +146,7 @@ def workspace_size(desc: KdaDesc, segment_tokens: int | None = None) -> int:
 
 def release_resources() -> None:
     """Synchronise and destroy the library's own streams and events (the
-    overlapped schedule creates them again when needed).  Registered to run at
+    two-stream schedules create them again when needed).  Registered to run at
     interpreter exit, while the HIP runtime is still up."""
     if _lib is not None:
         _lib.kda_release_resources()
@@ -199,9 +199,11 @@ def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=
     (raw hipEvent_t handles) selects the traced entry point.  With
     ``fused`` True (bf16 inputs) one fused kernel runs the whole forward (None:
     the library's choice, currently the two-kernel schedules); otherwise, with
-    ``overlap`` the library may run the overlapped schedule in segments of
-    ``segment_tokens`` tokens; without it, ``segment_tokens`` sizes the
-    segments processed in turn (default: the whole sequence).  With
+    ``overlap`` the library may run the pipelined schedule (records counted in
+    segments of ``segment_tokens`` tokens, default 128) or the overlapped one
+    (segments of ``segment_tokens``, default 8192), as the workspace allows;
+    without it, ``segment_tokens`` sizes the segments processed in turn on
+    one stream (default: as many as the workspace holds).  With
     ``snapshot_chunks`` = N > 0 the result also holds 'snapshots'
     [B, n, H, D, D]: the state after every N-th chunk (prefix-cache resume
     points, n = T // (64 N)).  With ``kcp_parts`` = P > 1 the sequence runs as P

@@ -153,7 +153,7 @@ size_t kda_chunk_fwd_workspace_size(const kda_desc* d);
 size_t kda_chunk_fwd_workspace_size_for(const kda_desc* d, int32_t segment_tokens);
 
 /*
- * Waits for and destroys the streams and events the overlapped schedule
+ * Waits for and destroys the streams and events the two-stream schedules
  * created (on every device); later calls create them again.  Optional: call
  * before the process or the HIP runtime shuts down when tools that track
  * queues (profilers) are attached.  Not thread-safe against concurrent calls
