@@ -480,7 +480,8 @@ def test_pipelined_windows_match_one_stream(kda, B, T, H, D, windows):
     pipelined schedule runs in windows of 512 chunks (per window one
     intra-chunk launch and one scan launch, the state carried across, a
     window's producers waiting for the previous window's scan), bit-identical
-    to the one-stream schedule and within 3e-3 of the oracle."""
+    to the one-stream schedule (outputs and prefix-cache snapshots) and within
+    3e-3 of the oracle."""
     x = gen_inputs(_custom(B, T, H, D, "bf16", seed=7000 + T + H))
     desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, overlap=True, fused=False)
     nbytes = kda.workspace_size(desc, 512 * 64)
@@ -488,10 +489,10 @@ def test_pipelined_windows_match_one_stream(kda, B, T, H, D, windows):
     assert kda.launches(desc, nbytes) == ["intra", "scan"] * windows
     log(f"[pipelined windows] B={B} T={T} H={H} D={D} windows={windows}")
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    pip = _run(kda, x, overlap=True, fused=False, workspace=ws)
+    pip = _run(kda, x, overlap=True, fused=False, workspace=ws, snapshot_chunks=100)
     assert kda.call_status(desc, ws) == 0
-    one = _run(kda, x, overlap=False, fused=False)
-    for key in ("o", "y", "S_T"):
+    one = _run(kda, x, overlap=False, fused=False, snapshot_chunks=100)
+    for key in ("o", "y", "S_T", "snapshots"):  # snapshots every 100 chunks, across the windows
         assert _bit_equal(one[key], pip[key]), key
     ref = _oracle(x)
     for key in ("o", "y", "S_T"):
