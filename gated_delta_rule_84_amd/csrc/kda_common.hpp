@@ -184,6 +184,17 @@ __device__ __forceinline__ float softplus_log2(float x) {
 // Logistic function: 1 / (1 + e^{-x}); saturates to 0 and 1 at the extremes.
 __device__ __forceinline__ float sigmoid_fast(float x) { return hw_rcp(1.0f + hw_exp2(-x * kLog2e)); }
 
+// 16 bytes read once (STREAM: a non-temporal load, so that data nobody reads
+// again does not displace what the caches still hold for other waves, such as
+// chunk records written a few scan steps earlier).
+template <bool STREAM>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+  if constexpr (STREAM)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
 // ---- hand-over of chunk records between two kernels that run at once -------
 // The producer stores the record with device-scope buffer stores (the sc1
 // cache-policy bit: written through to memory, so a load from another

@@ -581,6 +581,12 @@ __global__ __launch_bounds__((WsLds<T, D, NS>::NT), 1) void kda_scan_ws_kernel(c
       lofG[i] = L::GS + (u / VPR) * L::PV + (u % VPR) * 16;  // + the slab of the chunk (split)
     }
     u32x4 stA[L::PA], stB[L::PB], stG[L::PG];
+    // Every byte staged here is read once.  Loads are non-temporal, except
+    // the records of the split workgroup, whose other half reads the same
+    // record through the shared L2 (measured, K3 layer on the pipelined
+    // schedule: 4.57 -> 4.31 ms; with non-temporal stores of y as well it
+    // slows to 4.94).
+    constexpr bool kStreamRec = NS == 1;
     auto rec_ptr = [&](int c) { return p.ws.base + (bh * p.nc + c) * p.ws.rec_bytes; };
     // `poison`: the records never became complete (staged values become NaN)
     auto last_row = [&](int c) { return min(kChunk, p.T - (p.t0 + c * kChunk)) - 1; };
@@ -593,10 +599,10 @@ __global__ __launch_bounds__((WsLds<T, D, NS>::NT), 1) void kda_scan_ws_kernel(c
       for (int i = 0; i < L::PA; ++i) {
         const int u = hid + NH * i;
         if (i < AR) {
-          stA[i] = rp[u];
+          stA[i] = load16<kStreamRec>(rp + u);
         } else if (vin != nullptr) {
           const int vu = u - L::A_REC;
-          stA[i] = reinterpret_cast<const u32x4*>(v0 + min(vu / VPR, last) * tok_stride)[vu % VPR];
+          stA[i] = load16<true>(reinterpret_cast<const u32x4*>(v0 + min(vu / VPR, last) * tok_stride) + vu % VPR);
         } else {  // no V: V = 0
           stA[i] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -621,7 +627,7 @@ __global__ __launch_bounds__((WsLds<T, D, NS>::NT), 1) void kda_scan_ws_kernel(c
     auto load_B = [&](int c) {
       const u32x4* rp = reinterpret_cast<const u32x4*>(rec_ptr(c)) + L::A_REC;
 #pragma unroll
-      for (int i = 0; i < L::PB; ++i) stB[i] = rp[min(hid + NH * i, L::B_UNITS - 1)];
+      for (int i = 0; i < L::PB; ++i) stB[i] = load16<kStreamRec>(rp + min(hid + NH * i, L::B_UNITS - 1));
       if (poison)
 #pragma unroll
         for (int i = 0; i < L::PB; ++i) stB[i] = u32x4{kPoison, kPoison, kPoison, kPoison};
@@ -644,7 +650,7 @@ __global__ __launch_bounds__((WsLds<T, D, NS>::NT), 1) void kda_scan_ws_kernel(c
 #pragma unroll
       for (int i = 0; i < L::PG; ++i) {
         const int u = hid + NH * i;
-        stG[i] = reinterpret_cast<const u32x4*>(g0 + min(u / VPR, last) * tok_stride)[u % VPR];
+        stG[i] = load16<true>(reinterpret_cast<const u32x4*>(g0 + min(u / VPR, last) * tok_stride) + u % VPR);
       }
     };
     constexpr int GSLAB = 64 * L::PV;  // bytes of one gate slab
