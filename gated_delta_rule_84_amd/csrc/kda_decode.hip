@@ -73,13 +73,16 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const DecodeParams p) {
   }
   __syncthreads();
 
+  // The state is read once and written once: both non-temporally (so that
+  // neither displaces the other in the caches; measured on 256 x 96 states:
+  // 0.58 -> 0.55 ms, while either alone changes little).
   float* S = p.S_pool + (slot * p.H + h) * D * D;
   float s[RPT];
   float w = 0.f;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rg * RPT + i;
-    s[i] = S[r * D + col] * as[r];
+    s[i] = __builtin_nontemporal_load(S + r * D + col) * as[r];
     w += s[i] * ks[r];
   }
   part[rg][col] = w;
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const DecodeParams p) {
     const int r = rg * RPT + i;
     s[i] += ks[r] * u;
     ov += s[i] * qs[r];
-    S[r * D + col] = s[i];
+    __builtin_nontemporal_store(s[i], S + r * D + col);
   }
   __syncthreads();  // everyone has read part[] for w
   part[rg][col] = ov;
