@@ -31,7 +31,8 @@ struct IntraLds {
 // One workgroup (4 waves) per record of the launch, in chunk-major order:
 // workgroup item = c B H + b H + h, so that the records of a chunk come out
 // together for every head, as the state scan consumes them, and the rows of
-// a chunk's q, k, z are read for all heads at once.  In the pipelined
+// a chunk's q, k, z are read for all heads at once (c counted from the last
+// chunk when IntraParams::reverse is set).  In the pipelined
 // schedule the launch is paced by the scan's progress (IntraParams::progress).
 //
 // SP: the unbounded softplus decay (pairwise diagonal blocks, more registers:
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && !SP ? 3 : 2)) void kda_intr
   const int tid = threadIdx.x;
   const int bh_n = p.B * p.H;
   const int item = blockIdx.x;
-  const int c = item / bh_n, bh = item % bh_n;
+  const int c = p.reverse ? p.nc - 1 - item / bh_n : item / bh_n, bh = item % bh_n;
   const int b = bh / p.H, h = bh % p.H;
   const int tok0 = p.t0 + c * kChunk;
   const int nvalid = min(kChunk, p.T - tok0);

@@ -95,6 +95,12 @@ struct IntraParams {
   // sequence (seg_len = 0: s = 0); t0 / 64 is then a multiple of seg_len.
   uint32_t* done;
   int seg_len;
+  // Chunk order of the workgroups: 0 first chunk first (what a consumer
+  // running at the same time needs), 1 last chunk first (a launch whose
+  // records are read only after it ends: the records of the first chunks,
+  // which the scan reads first, are then the most recently written and the
+  // likeliest still to be in the memory-side cache).
+  int reverse;
   // Record of chunk c of the launch: ((b H + h) rec_stride + rec_c0 + c).
   // rec_stride = 0 means nc (records of this launch only, rec_c0 = 0).
   int rec_stride, rec_c0;
