@@ -29,8 +29,11 @@ leg, y of the first and last sampled head against the fp64 oracle (<= 3e-3).
 Side measurements (skipped with their --no-* flags): the same forward
 without the output gate (o and S_T out, 1,282 B per token-head; sequences up
 to 65,536 tokens), the prefill workload (B4 T4096 H32), the input steps, the
-decode step and the state export.  The CPU baseline is the fp64 C oracle on
-every host core the process may use, over a bounded sample of heads.
+decode step and the state export, and the long-context workload (B1
+T1,048,576 H96, the workspace the size query offers; up to 5 timed calls
+after its inputs are generated, which takes about a minute).  The CPU
+baseline is the fp64 C oracle on every host core the process may use, over
+a bounded sample of heads.
 """
 from __future__ import annotations
 
@@ -242,6 +245,76 @@ def time_prefill(kda, wl, steps: int, warmup: int) -> dict:
             "outputs_finite": all_finite(out["y"])}
 
 
+def load_inputs(wl, dev) -> dict:
+    """The workload's seeded inputs as device tensors (bf16 as torch.bfloat16).
+    Long sequences are generated slab by slab straight into the device
+    tensors (the whole host copy would be ~150 GB at 1M tokens)."""
+    import torch
+    from synth.workloads import gen_inputs
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    slab = 65536
+    if wl.T > slab and wl.T % slab == 0:
+        t = {}
+        for t0 in range(0, wl.T, slab):
+            x = gen_inputs(wl, time=(t0, slab))
+            for k, v in x.items():
+                if k in ("A", "S0"):
+                    t.setdefault(k, to_dev(v))
+                    continue
+                if k not in t:
+                    t[k] = torch.empty((wl.B, wl.T) + v.shape[2:],
+                                       dtype=torch.bfloat16 if v.dtype == np.uint16 else torch.float32, device=dev)
+                t[k][:, t0:t0 + slab].copy_(to_dev(v))
+            del x
+            print(f"inputs {wl.name}: tokens {t0 + slab}/{wl.T}", file=sys.stderr, flush=True)
+        return t
+    x = gen_inputs(wl)
+    return {k: to_dev(v) for k, v in x.items()}
+
+
+def time_long_context(kda, wl, steps: int, warmup: int) -> dict:
+    """The long-context workload (B1 T1,048,576 H96 d128, bf16, gate; y and
+    S_T out) with the workspace the size query offers (the pipelined
+    schedule over windows of records within its cap)."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    t = load_inputs(wl, dev)
+    t_gen = time.perf_counter() - t_gen
+    B, T, H, D = wl.B, wl.T, wl.H, wl.D
+    desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16)
+    ws_bytes = kda.workspace_size(desc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = {"y": torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev),
+           "S_T": torch.empty((B, H, D, D), device=dev)}
+
+    def call():
+        kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t.get("S0"), gate=t["gate"],
+                      want_o=False, out=out, workspace=ws)
+
+    ms, med, mn = time_calls(call, steps, warmup)
+    th = B * T * H
+    nbytes = th * path_bytes_per_token_head(D) + 2 * B * H * D * D * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"workload": wl.name, "B": B, "T": T, "H": H, "d": D, "schedule": kda.schedule(desc, ws_bytes)[1],
+           "workspace_bytes": ws_bytes, "launches": len(kda.launches(desc, ws_bytes)),
+           "ms": ms, "ms_median": med, "ms_min": mn, "steps": steps, "warmup": warmup,
+           "token_heads_per_s": th / (ms * 1e-3), "algorithmic_bytes": nbytes, "achieved_GBs": gbs,
+           "frac_hbm": gbs / HBM_PEAK_GBS, "input_setup_s": t_gen,
+           "outputs_finite": all_finite(out["y"]) and all_finite(out["S_T"]),
+           "library_status_ok": kda.call_status(desc, ws) == 0}
+    del t, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_input_prep(kda, t, B, T, H, D, steps, warmup, workload, W=4):
     """The input steps before the core (q, k, v = Swish(ShortConv(x)), beta =
     Sigmoid(logit)) at the workload's shapes: the workload's q, k, v, beta
@@ -345,6 +418,9 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill workload's side measurement (B4 T4096 H32)")
     ap.add_argument("--no-o-only", action="store_true", help="skip the side measurement without the output gate")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-context workload's side measurement (B1 T1,048,576 H96, about a minute "
+                         "of input generation)")
     ap.add_argument("--no-input-prep", action="store_true",
                     help="skip timing the input steps (ShortConv + Swish, Sigmoid) on the workload's shapes")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -361,7 +437,7 @@ def main() -> int:
     import torch
 
     import gated_delta_rule_84_amd as kda
-    from synth.workloads import WORKLOADS, gen_inputs
+    from synth.workloads import WORKLOADS
 
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -379,34 +455,7 @@ def main() -> int:
     kda.lib()
 
     t_gen = time.perf_counter()
-
-    def to_dev(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(a).to(dev)
-
-    slab = 65536
-    if wl.T > slab and wl.T % slab == 0:
-        # long sequences: the same seeded values, generated slab by slab straight
-        # into the device tensors (the whole host copy would be ~150 GB at 1M tokens)
-        t = {}
-        for t0 in range(0, wl.T, slab):
-            x = gen_inputs(wl, time=(t0, slab))
-            for k, v in x.items():
-                if k in ("A", "S0"):
-                    t.setdefault(k, to_dev(v))
-                    continue
-                if k not in t:
-                    t[k] = torch.empty((wl.B, wl.T) + v.shape[2:],
-                                       dtype=torch.bfloat16 if v.dtype == np.uint16 else torch.float32, device=dev)
-                t[k][:, t0:t0 + slab].copy_(to_dev(v))
-            del x
-            print(f"inputs: tokens {t0 + slab}/{wl.T}", file=sys.stderr, flush=True)
-    else:
-        x = gen_inputs(wl)
-        t = {k: to_dev(v) for k, v in x.items()}
-        del x
+    t = load_inputs(wl, dev)
     t_gen = time.perf_counter() - t_gen
     B, T, H, D = wl.B, wl.T, wl.H, wl.D
     token_heads = B * T * H
@@ -547,6 +596,11 @@ def main() -> int:
         heads = args.cpu_heads or H
         y_host = out["y"][:, :, :min(heads, H)].float().cpu().numpy()  # the last timed step's output
         result["cpu_baseline"] = cpu_baseline(wl, min(heads, H), y_host)
+    if not args.no_long and wl.name != "long_context":
+        del t, out
+        torch.cuda.empty_cache()
+        result["long_context"] = time_long_context(kda, WORKLOADS["long_context"], min(args.steps, 5),
+                                                   min(args.warmup, 2))
     print(json.dumps(result), flush=True)
     valid = finite and status_ok and result.get("cpu_baseline", {}).get("parity_ok", True)
     if not valid:
