@@ -315,6 +315,37 @@ def time_long_context(kda, wl, steps: int, warmup: int) -> dict:
     return res
 
 
+def measure_peaks(kda) -> dict:
+    """What this GPU achieves against the published peaks (8 TB/s HBM, 2.5
+    PFLOP/s dense bf16 MFMA, 157.3 TFLOP/s fp32): the library's state copy
+    (kda_state_io export, non-temporal 16-byte loads and stores) over a pool
+    of 1,536 x 96 states (2 x 9.7 GB moved per call), a torch device copy of
+    4 GiB, and square GEMMs of torch (hipBLASLt) at n = 8,192."""
+    import torch
+
+    res = {"hbm_peak_GBs": HBM_PEAK_GBS, "bf16_mfma_peak_TFLOPs": BF16_PEAK_TFLOPS, "fp32_peak_TFLOPs": 157.3}
+    pool = torch.zeros((1536, 96, 128, 128), device="cuda")
+    user = torch.empty_like(pool)
+    ms, med, _ = time_calls(lambda: kda.state_io(kda.STATE_EXPORT, pool, user), 10, 2)
+    nbytes = 2 * pool.numel() * 4
+    res["state_copy"] = {"bytes": nbytes, "ms_median": med, "GBs": nbytes / (med * 1e-3) / 1e9}
+    del pool, user
+    a = torch.empty(1 << 30, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    ms, med, _ = time_calls(lambda: b.copy_(a), 10, 2)
+    res["torch_copy"] = {"bytes": 2 * a.numel() * 4, "ms_median": med, "GBs": 2 * a.numel() * 4 / (med * 1e-3) / 1e9}
+    del a, b
+    n = 8192
+    for dt, name in ((torch.bfloat16, "gemm_bf16"), (torch.float32, "gemm_fp32")):
+        x = torch.randn((n, n), device="cuda").to(dt)
+        y = torch.randn((n, n), device="cuda").to(dt)
+        ms, med, _ = time_calls(lambda: torch.mm(x, y), 10, 3)
+        res[name] = {"n": n, "ms_median": med, "TFLOPs": 2 * n ** 3 / (med * 1e-3) / 1e12}
+        del x, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_input_prep(kda, t, B, T, H, D, steps, warmup, workload, W=4):
     """The input steps before the core (q, k, v = Swish(ShortConv(x)), beta =
     Sigmoid(logit)) at the workload's shapes: the workload's q, k, v, beta
@@ -425,6 +456,9 @@ def main() -> int:
                     help="skip timing the input steps (ShortConv + Swish, Sigmoid) on the workload's shapes")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of GIB GiB (reference for HBM byte counters)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure what this GPU achieves against its published peaks: the library's state "
+                         "copy over 24 GB, a plain torch device copy, and bf16 / fp32 GEMMs of torch (hipBLASLt)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -451,6 +485,9 @@ def main() -> int:
             b_.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": nbytes, "reads_per_copy": nbytes, "writes_per_copy": nbytes}))
+        return 0
+    if args.peaks:
+        print(json.dumps(measure_peaks(kda)), flush=True)
         return 0
     kda.lib()
 
