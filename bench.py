@@ -29,7 +29,9 @@ leg, y of the first and last sampled head against the fp64 oracle (<= 3e-3).
 Side measurements (skipped with their --no-* flags): the same forward
 without the output gate (o and S_T out, 1,282 B per token-head; sequences up
 to 65,536 tokens), the prefill workload (B4 T4096 H32), the input steps, the
-decode step and the state export, and the long-context workload (B1
+decode step and the state export, the same K3-layer forward with the
+tensors head first ([B, H, T, d]: y checked bit for bit against the
+headline call's), and the long-context workload (B1
 T1,048,576 H96, the workspace the size query offers; up to 5 timed calls
 after its inputs are generated, which takes about a minute).  The CPU
 baseline is the fp64 C oracle on every host core the process may use, over
@@ -346,6 +348,35 @@ def measure_peaks(kda) -> dict:
     return res
 
 
+def time_head_first(kda, t, out, ws, B, T, H, D, steps: int, warmup: int) -> dict:
+    """The same forward with the per-token tensors head first ([B, H, T, d],
+    beta [B, H, T]; kda_desc.tokens = KDA_TOKENS_BHTD), as a caller whose
+    projections write each head's tokens in one block would pass them; y is
+    compared bit for bit with the token-major call's (its last timed step)."""
+    import torch
+
+    hf = {n: t[n].permute(0, 2, 1, 3).contiguous() for n in ("q", "k", "v", "z", "gate")}
+    hf["beta"] = t["beta"].permute(0, 2, 1).contiguous()
+    y_hf = torch.empty((B, H, T, D), dtype=out["y"].dtype, device=out["y"].device)
+    st_hf = torch.empty_like(out["S_T"])
+
+    def call():
+        kda.chunk_fwd(hf["q"], hf["k"], hf["v"], hf["beta"], hf["z"], t["A"], S0=t.get("S0"), gate=hf["gate"],
+                      want_o=False, out={"y": y_hf, "S_T": st_hf}, workspace=ws, head_first=True)
+
+    ms, med, mn = time_calls(call, steps, warmup)
+    same = all(torch.equal(y_hf[:, h].view(torch.int16), out["y"][:, :, h].view(torch.int16)) for h in range(H))
+    same = same and torch.equal(st_hf, out["S_T"])
+    th = B * T * H
+    nbytes = th * path_bytes_per_token_head(D) + 2 * B * H * D * D * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del hf, y_hf, st_hf
+    torch.cuda.empty_cache()
+    return {"layout": "[B, H, T, d]", "ms": ms, "ms_median": med, "ms_min": mn, "token_heads_per_s": th / (ms * 1e-3),
+            "algorithmic_bytes": nbytes, "achieved_GBs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+            "bit_identical_to_token_major": bool(same)}
+
+
 def time_input_prep(kda, t, B, T, H, D, steps, warmup, workload, W=4):
     """The input steps before the core (q, k, v = Swish(ShortConv(x)), beta =
     Sigmoid(logit)) at the workload's shapes: the workload's q, k, v, beta
@@ -449,6 +480,8 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill workload's side measurement (B4 T4096 H32)")
     ap.add_argument("--no-o-only", action="store_true", help="skip the side measurement without the output gate")
+    ap.add_argument("--no-head-first", action="store_true",
+                    help="skip the side measurement with the inputs and outputs head first ([B, H, T, d])")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the long-context workload's side measurement (B1 T1,048,576 H96, about a minute "
                          "of input generation)")
@@ -623,6 +656,8 @@ def main() -> int:
                             "algorithmic_bytes": o_bytes, "achieved_GBs": o_bytes / (ms_o * 1e-3) / 1e9,
                             "frac_hbm": o_bytes / (ms_o * 1e-3) / 1e9 / HBM_PEAK_GBS}
         del out_o
+    if not args.no_head_first and args.schedule == "auto" and wl.name == "k3_layer":
+        result["head_first"] = time_head_first(kda, t, out, ws, B, T, H, D, args.steps, args.warmup)
     if not args.no_input_prep:
         result["input_prep"] = time_input_prep(kda, t, B, T, H, D, args.steps, args.warmup, wl.name)
     if not args.no_decode:

@@ -32,7 +32,10 @@ class KdaDesc(ctypes.Structure):
                 ("rms_eps", ctypes.c_float), ("qk_l2norm", ctypes.c_int32),
                 ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
                 ("segment_tokens", ctypes.c_int32), ("overlap", ctypes.c_int32), ("fused", ctypes.c_int32),
-                ("decay", ctypes.c_int)]
+                ("decay", ctypes.c_int), ("tokens", ctypes.c_int)]
+
+
+ABI_VERSION = 6  # KDA_ABI_VERSION of include/kda.h that KdaDesc mirrors
 
 
 DECAYS = {"k3": 0, "softplus": 1}
@@ -58,6 +61,9 @@ def lib() -> ctypes.CDLL:
         vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
         dp = ctypes.POINTER(KdaDesc)
         L.kda_abi_version.restype = ctypes.c_int
+        if L.kda_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.kda_abi_version()}, this binding expects "
+                               f"{ABI_VERSION}: rebuild it with `python __graft_entry__.py`")
         L.kda_status_str.restype = ctypes.c_char_p
         L.kda_status_str.argtypes = [ctypes.c_int]
         L.kda_desc_init.restype = ctypes.c_int
@@ -124,7 +130,7 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 def make_desc(B, T, H, D, in_dtype, out_dtype, g_min=-5.0, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6,
-              qk_l2norm=True, segment_tokens=0, overlap=True, fused=None, decay="k3") -> KdaDesc:
+              qk_l2norm=True, segment_tokens=0, overlap=True, fused=None, decay="k3", head_first=False) -> KdaDesc:
     d = KdaDesc()
     rc = lib().kda_desc_init(ctypes.byref(d), B, T, H, D, in_dtype, out_dtype)
     if rc != 0:
@@ -133,6 +139,7 @@ def make_desc(B, T, H, D, in_dtype, out_dtype, g_min=-5.0, q_scale=1.0, l2_eps=1
     d.segment_tokens, d.overlap = int(segment_tokens or 0), int(bool(overlap))
     d.fused = 1 if fused is None else (2 if fused else 0)  # None: the library decides
     d.decay = DECAYS[decay]
+    d.tokens = 1 if head_first else 0  # KDA_TOKENS_BHTD / KDA_TOKENS_BTHD
     return d
 
 
@@ -191,7 +198,7 @@ def launches(desc: KdaDesc, ws_bytes: int) -> list[str]:
 
 def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=None, want_o=True,
               want_y=None, want_state=True, workspace=None, segment_tokens=None, overlap=True, fused=None,
-              out=None, events=None, snapshot_chunks=0, kcp_parts=0, **opts):
+              out=None, events=None, snapshot_chunks=0, kcp_parts=0, head_first=False, **opts):
     """KDA forward over whole sequences.  q, k, z: [B, T, H, D]; v (and gate):
     [B, T, H, D]; beta: [B, T, H]; A: [H] fp32; S0: [B, H, D, D] fp32 or None.
     Returns a dict with 'o' / 'y' (out_dtype, default the input dtype) and
@@ -207,19 +214,26 @@ def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=
     ``snapshot_chunks`` = N > 0 the result also holds 'snapshots'
     [B, n, H, D, D]: the state after every N-th chunk (prefix-cache resume
     points, n = T // (64 N)).  With ``kcp_parts`` = P > 1 the sequence runs as P
-    parallel segments folded through their (M, S~) pairs (kda_chunk_fwd_kcp)."""
-    B, T, H, D = q.shape
+    parallel segments folded through their (M, S~) pairs (kda_chunk_fwd_kcp).
+    With ``head_first`` the per-token tensors are [B, H, T, D] (beta
+    [B, H, T]) and o, y come out the same way."""
+    if head_first:
+        B, H, T, D = q.shape
+    else:
+        B, T, H, D = q.shape
+    tok_shape = (B, H, T, D) if head_first else (B, T, H, D)
     in_dt = _dt(q)
     odt = q.dtype if out_dtype is None else out_dtype
     desc = make_desc(B, T, H, D, in_dt, _dt(torch.empty(0, dtype=odt)),
-                     segment_tokens=(segment_tokens or 0) if overlap else 0, overlap=overlap, fused=fused, **opts)
+                     segment_tokens=(segment_tokens or 0) if overlap else 0, overlap=overlap, fused=fused,
+                     head_first=head_first, **opts)
     want_y = (gate is not None) if want_y is None else want_y
     res = dict(out or {})
     dev = q.device
     if want_o and "o" not in res:
-        res["o"] = torch.empty((B, T, H, D), dtype=odt, device=dev)
+        res["o"] = torch.empty(tok_shape, dtype=odt, device=dev)
     if want_y and "y" not in res:
-        res["y"] = torch.empty((B, T, H, D), dtype=odt, device=dev)
+        res["y"] = torch.empty(tok_shape, dtype=odt, device=dev)
     if want_state and "S_T" not in res:
         res["S_T"] = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
     if workspace is None:
@@ -265,20 +279,24 @@ NOALLOC_SCRATCH_BYTES = 128 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 
 
 def chunk_fwd_noalloc(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=None, want_o=True,
-                      want_y=None, want_state=True, out=None, **opts):
+                      want_y=None, want_state=True, out=None, head_first=False, **opts):
     """kda_chunk_fwd_noalloc: the forward without a workspace (the library's
     per-GPU scratch array, one-stream schedule).  Arguments and result as
     chunk_fwd; only the outputs are allocated here, by the caller's side."""
-    B, T, H, D = q.shape
+    if head_first:
+        B, H, T, D = q.shape
+    else:
+        B, T, H, D = q.shape
+    tok_shape = (B, H, T, D) if head_first else (B, T, H, D)
     odt = q.dtype if out_dtype is None else out_dtype
-    desc = make_desc(B, T, H, D, _dt(q), _dt(torch.empty(0, dtype=odt)), **opts)
+    desc = make_desc(B, T, H, D, _dt(q), _dt(torch.empty(0, dtype=odt)), head_first=head_first, **opts)
     want_y = (gate is not None) if want_y is None else want_y
     res = dict(out or {})
     dev = q.device
     if want_o and "o" not in res:
-        res["o"] = torch.empty((B, T, H, D), dtype=odt, device=dev)
+        res["o"] = torch.empty(tok_shape, dtype=odt, device=dev)
     if want_y and "y" not in res:
-        res["y"] = torch.empty((B, T, H, D), dtype=odt, device=dev)
+        res["y"] = torch.empty(tok_shape, dtype=odt, device=dev)
     if want_state and "S_T" not in res:
         res["S_T"] = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
     rc = lib().kda_chunk_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(z), _ptr(A),

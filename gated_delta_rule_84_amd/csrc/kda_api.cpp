@@ -92,8 +92,13 @@ kda_status validate_desc(const kda_desc* d) {
     return KDA_ERR_BAD_SHAPE;
   const int decay = enum_int(d->decay);
   if (decay != KDA_DECAY_K3 && decay != KDA_DECAY_SOFTPLUS) return KDA_ERR_UNSUPPORTED;
+  const int tokens = enum_int(d->tokens);
+  if (tokens != KDA_TOKENS_BTHD && tokens != KDA_TOKENS_BHTD) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
 }
+
+// q, k, z, v, gate, o, y and beta head first (kda_desc.tokens)
+int head_first(const kda_desc* d) { return enum_int(d->tokens) == KDA_TOKENS_BHTD ? 1 : 0; }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -540,6 +545,7 @@ kda_status kda_desc_init(kda_desc* d, int32_t B, int32_t T, int32_t H, int32_t h
   d->overlap = 1;
   d->fused = 1;
   d->decay = KDA_DECAY_K3;
+  d->tokens = KDA_TOKENS_BTHD;
   return validate_desc(d);
 }
 
@@ -648,6 +654,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
                           const uint32_t* progress = nullptr, uint32_t* pacing_off = nullptr, int lead = 0,
                           uint64_t* clear = nullptr, int64_t clear_words = 0, uint32_t* clear_status = nullptr) {
     kda::IntraParams ip{};
+    ip.head_first = head_first(d);
     ip.q = q;
     ip.k = k;
     ip.z = z;
@@ -687,6 +694,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
                          hipStream_t st_, const uint32_t* done = nullptr, int seg_len = 0,
                          uint32_t* status = nullptr, uint32_t* progress = nullptr, uint64_t* xchg = nullptr) {
     kda::ScanParams sp{};
+    sp.head_first = head_first(d);
     sp.v = v;
     sp.gate = y ? gate : nullptr;
     sp.rms_w = rms_w;
@@ -727,6 +735,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
   // ---- fused schedule: one launch, records in LDS
   if (plan.fused) {
     kda::IntraParams ip{};
+    ip.head_first = head_first(d);
     ip.q = q;
     ip.k = k;
     ip.z = z;
@@ -743,6 +752,7 @@ kda_status chunk_fwd_impl(const kda_desc* d, const void* q, const void* k, const
     ip.l2norm = d->qk_l2norm;
     ip.decay = d->decay;
     kda::ScanParams sp{};
+    sp.head_first = head_first(d);
     sp.v = v;
     sp.gate = y ? gate : nullptr;
     sp.rms_w = rms_w;
@@ -1034,7 +1044,7 @@ kda_status kda_input_prep(const kda_desc* d, int32_t conv_width, const void* xq,
                           void* stream) {
   const kda_status st = validate_desc(d);
   if (st != KDA_OK) return st;
-  if (conv_width < 1 || conv_width > 4) return KDA_ERR_UNSUPPORTED;
+  if (conv_width < 1 || conv_width > 4 || head_first(d)) return KDA_ERR_UNSUPPORTED;
   if ((beta_logits == nullptr) != (beta == nullptr)) return KDA_ERR_NULL_ARG;
   const size_t es = elem_size(d->in_dtype);
   for (const float* p : {state_in, (const float*)state_out})
@@ -1110,7 +1120,7 @@ size_t kda_chunk_fwd_kcp_workspace_size(const kda_desc* d, int32_t n_parts) {
   if (validate_desc(d) != KDA_OK) return 0;
   if (n_parts == 1 || d->T == 0) return kda_chunk_fwd_workspace_size(d);
   kda_desc inner;
-  if (!kcp_shape(d, n_parts, &inner)) return 0;
+  if (head_first(d) || !kcp_shape(d, n_parts, &inner)) return 0;
   return 3 * kcp_state_bytes(d, n_parts) + kda_chunk_fwd_workspace_size(&inner);
 }
 
@@ -1125,7 +1135,9 @@ kda_status kda_chunk_fwd_kcp(const kda_desc* d, int32_t n_parts, const void* q, 
     return chunk_fwd_impl(d, q, k, v, beta, z, A, S0, gate, rms_w, o, y, S_T, ws, ws_bytes, stream,
                           Tracer{nullptr, 0});
   kda_desc inner;
-  if (!kcp_shape(d, n_parts, &inner)) return KDA_ERR_UNSUPPORTED;
+  // the segments are read as B * n_parts shorter sequences, which only the
+  // token-major order lays out that way
+  if (head_first(d) || !kcp_shape(d, n_parts, &inner)) return KDA_ERR_UNSUPPORTED;
   if (!o && !y && !S_T) return KDA_ERR_NULL_ARG;
   if (!q || !k || !v || !beta || !z || !A) return KDA_ERR_NULL_ARG;
   if (y && !gate) return KDA_ERR_NULL_ARG;
@@ -1250,6 +1262,7 @@ kda_status kda_prepass(const kda_desc* d, const void* q, const void* k, const vo
                        float* rq, float* rk, void* stream) {
   kda_status st = validate_desc(d);
   if (st != KDA_OK) return st;
+  if (head_first(d)) return KDA_ERR_UNSUPPORTED;  // token major only
   if (!q || !k || !z || !A || !G || !rq || !rk) return KDA_ERR_NULL_ARG;
   for (const void* p : {q, k, z})
     if (!aligned(p, 16)) return KDA_ERR_MISALIGNED;

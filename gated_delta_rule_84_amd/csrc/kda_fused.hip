@@ -147,8 +147,8 @@ __global__ __launch_bounds__((FusedLds<T, D>::NT), 1) void kda_fused_kernel(cons
   float* gam = reinterpret_cast<float*>(lds + L::GAM);
   float* gams = reinterpret_cast<float*>(lds + L::GAMS);
   const float* otile = reinterpret_cast<const float*>(lds + L::OT);
-  const int64_t tok_stride = (int64_t)p.H * D;
-  const int64_t head_base = ((int64_t)b * p.T * p.H + h) * D;
+  const int64_t tok_stride = token_stride(p.head_first, p.H, D);
+  const int64_t head_base = token_base(p.head_first, b, h, p.T, p.H, D);
   const int nc = p.nc;
   auto nvalid_of = [&](int c) { return min(kChunk, p.T - c * kChunk); };
 

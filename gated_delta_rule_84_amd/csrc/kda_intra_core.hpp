@@ -175,8 +175,8 @@ struct IntraCore {
   // This wave's sub-tile rows of q, k, z (operand layout) and beta.  Rows past
   // the end of the sequence re-read the last row and are masked later.
   __device__ __forceinline__ void load(const IntraParams& p, int b, int h, int tok0, int nvalid) {
-    const int64_t tok_stride = (int64_t)p.H * D;
-    const int64_t row0 = ((int64_t)b * p.T + tok0) * p.H * D + (int64_t)h * D;
+    const int64_t tok_stride = token_stride(p.head_first, p.H, D);
+    const int64_t row0 = token_base(p.head_first, b, h, p.T, p.H, D) + tok0 * tok_stride;
     rvalid = r < nvalid;
     const int64_t rowp = row0 + min(r, nvalid - 1) * tok_stride;
 #pragma unroll
@@ -185,7 +185,8 @@ struct IntraCore {
       kraw[kk] = R8::load(static_cast<const T*>(p.k) + rowp, kk, g4);
       zraw[kk] = R8::load(static_cast<const T*>(p.z) + rowp, kk, g4);
     }
-    beta_r = rvalid ? Elem<T>::to_f32(static_cast<const T*>(p.beta)[((int64_t)b * p.T + tok0 + r) * p.H + h]) : 0.0f;
+    const int64_t bi = token_base(p.head_first, b, h, p.T, p.H, 1) + (tok0 + r) * token_stride(p.head_first, p.H, 1);
+    beta_r = rvalid ? Elem<T>::to_f32(static_cast<const T*>(p.beta)[bi]) : 0.0f;
   }
 
   // Decay prefix within the sub-tile (base 2); anchor rows and totals to LDS;

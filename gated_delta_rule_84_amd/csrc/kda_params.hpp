@@ -77,6 +77,16 @@ struct ChunkWs {
 constexpr int kPaceEvery = 2;
 __host__ __device__ constexpr int num_segments(int nc, int seg_len) { return (nc + seg_len - 1) / seg_len; }
 
+// Per-token tensors [B, T, H, d] (token major) or [B, H, T, d] (head first,
+// kda_desc.tokens): element offset of token 0 of (b, h), and the distance
+// between consecutive tokens of one head (d = 1 for beta).
+__host__ __device__ inline int64_t token_base(int head_first, int b, int h, int T, int H, int d) {
+  return head_first ? ((int64_t)b * H + h) * T * d : ((int64_t)b * T * H + h) * d;
+}
+__host__ __device__ inline int64_t token_stride(int head_first, int H, int d) {
+  return head_first ? (int64_t)d : (int64_t)H * d;
+}
+
 struct IntraParams {
   const void* q;
   const void* k;
@@ -84,6 +94,7 @@ struct IntraParams {
   const void* beta;
   const float* A;
   int B, T, H;
+  int head_first;  // q, k, z, beta head first ([B, H, T, ..]) instead of token major
   int t0;          // first token of the segment
   int nc;          // chunks in the segment
   float g_min, q_scale, l2_eps;
@@ -142,6 +153,7 @@ struct ScanParams {
   int out_f32;          // element type of o and y: 1 fp32, 0 bf16
   float rms_eps;
   int B, T, H;
+  int head_first;       // v, gate, o, y head first ([B, H, T, D]) instead of token major
   int t0, nc;           // first token and number of chunks of the segment
   ChunkWs ws;
   const uint32_t* done;  // [B * H]: wait until done[b H + h] >= nc before reading records, or nullptr

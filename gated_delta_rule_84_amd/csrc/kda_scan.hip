@@ -140,8 +140,8 @@ __global__ __launch_bounds__(4 * D, 1) void kda_scan_serial_kernel(const ScanPar
   const int h = blockIdx.x, b = blockIdx.y;
   const int col = 16 * wave + n;
   const int64_t bh = (int64_t)b * p.H + h;
-  const int64_t tok_stride = (int64_t)p.H * D;  // elements between tokens of one head
-  const int64_t head_base = ((int64_t)b * p.T * p.H + h) * D;
+  const int64_t tok_stride = token_stride(p.head_first, p.H, D);  // elements between tokens of one head
+  const int64_t head_base = token_base(p.head_first, b, h, p.T, p.H, D);
 
   // ---- per-thread copy units: record units, then V-slab units -------------
   constexpr int VPR = D * L::ES / 16;  // 16-byte units per V row
@@ -510,8 +510,8 @@ __global__ __launch_bounds__((WsLds<T, D, NS>::NT), 1) void kda_scan_ws_kernel(c
   }
   const int cb = half * L::DV;            // first column of the workgroup's half
   const int64_t bh = (int64_t)b * p.H + h;
-  const int64_t tok_stride = (int64_t)p.H * D;
-  const int64_t head_base = ((int64_t)b * p.T * p.H + h) * D;
+  const int64_t tok_stride = token_stride(p.head_first, p.H, D);
+  const int64_t head_base = token_base(p.head_first, b, h, p.T, p.H, D);
 
   // Records of a producer running at the same time: the first helper wave
   // waits until they are written, and a workgroup barrier orders every

@@ -368,7 +368,7 @@ struct GateEpilogue {
   // Gate logits of this thread's row segment of the chunk at token tok0 from
   // HBM (rows past the end re-read the last row; they are never stored).
   __device__ __forceinline__ void load_gate(const ScanParams& p, int64_t head_base, int tok0, u32x4 (&g)[NG]) const {
-    const int64_t tok_stride = (int64_t)p.H * D;
+    const int64_t tok_stride = token_stride(p.head_first, p.H, D);
     const int row = min(er, p.T - tok0 - 1);
     const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const T*>(p.gate) + head_base +
                                                       (int64_t)(tok0 + row) * tok_stride + cb + ec);
@@ -428,7 +428,7 @@ struct GateEpilogue {
                                       GetG getg) const {
     static_assert(DV == D, "a split row needs half_ss / emit_y");
     if (CHECK_ROWS && er >= p.T - tok0) return;
-    const int64_t tok_stride = (int64_t)p.H * D;
+    const int64_t tok_stride = token_stride(p.head_first, p.H, D);
     const int64_t orow = head_base + (tok0 + er) * tok_stride + cb + ec;
     const float* trow = otile + er * PO + ec;
     float ss = 0.f;
@@ -451,7 +451,7 @@ struct GateEpilogue {
   template <bool CHECK_ROWS, int PO>
   __device__ __forceinline__ float half_ss(const ScanParams& p, int64_t head_base, int tok0, const float* otile) const {
     if (CHECK_ROWS && er >= p.T - tok0) return 0.f;
-    const int64_t tok_stride = (int64_t)p.H * D;
+    const int64_t tok_stride = token_stride(p.head_first, p.H, D);
     const int64_t orow = head_base + (tok0 + er) * tok_stride + cb + ec;
     const float* trow = otile + er * PO + ec;
     float ss = 0.f;
@@ -473,7 +473,7 @@ struct GateEpilogue {
   __device__ __forceinline__ void split_y(const ScanParams& p, int h, int64_t head_base, int tok0, const float* otile,
                                           GetG getg, float ss) const {
     if (CHECK_ROWS && er >= p.T - tok0) return;
-    const int64_t tok_stride = (int64_t)p.H * D;
+    const int64_t tok_stride = token_stride(p.head_first, p.H, D);
     emit_y<PO>(p, h, head_base + (tok0 + er) * tok_stride + cb + ec, otile + er * PO + ec, getg, ss);
   }
 };

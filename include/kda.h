@@ -24,8 +24,9 @@
  *    correctness (every producer launch is enqueued before the consumer that
  *    waits for it), only for speed.
  *  - Layouts: q, k, z: [B, T, H, d_k]; v, o, gate, y: [B, T, H, d_v];
- *    beta: [B, T, H]; A: [H] fp32; states S0, S_T, S_pool: [.., H, d_k, d_v]
- *    fp32 with the key channel as row index (o = S^T q).
+ *    beta: [B, T, H] (or head first, [B, H, T, ..], see kda_token_layout);
+ *    A: [H] fp32; states S0, S_T, S_pool: [.., H, d_k, d_v] fp32 with the key
+ *    channel as row index (o = S^T q).
  *  - Element types: q, k, v, beta, z and gate are all `in_dtype`; o and y are
  *    `out_dtype`; A, states and rms_w are fp32.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 typedef enum {
   KDA_OK = 0,
@@ -89,6 +90,17 @@ typedef enum {
 /* Kernel launches that kda_chunk_fwd_traced times (kda_chunk_fwd_launches). */
 typedef enum { KDA_LAUNCH_INTRA = 0, KDA_LAUNCH_SCAN = 1, KDA_LAUNCH_FUSED = 2 } kda_launch_kind;
 
+/* Order of the per-token tensors of kda_chunk_fwd* (q, k, z, v, gate, o, y:
+ * [B, T, H, d] or [B, H, T, d]; beta: [B, T, H] or [B, H, T]); the innermost
+ * d elements are contiguous either way.  kda_prepass and kda_input_prep take
+ * token major only (KDA_ERR_UNSUPPORTED for KDA_TOKENS_BHTD).  Token
+ * major is what a projection of the hidden state writes directly; head
+ * first puts each head's tokens in one block, so that the 64 rows of a
+ * chunk are one contiguous 16 KB (bf16, d = 128) instead of 64 rows a token
+ * stride apart, which the state scan reads and writes faster beside the
+ * intra-chunk kernel. */
+typedef enum { KDA_TOKENS_BTHD = 0, KDA_TOKENS_BHTD = 1 } kda_token_layout;
+
 typedef enum {
   KDA_LAYOUT_KV = 0, /* user state is [d_k][d_v], same as the pool               */
   KDA_LAYOUT_VK = 1  /* user state is [d_v][d_k] (transposed)                      */
@@ -121,6 +133,9 @@ typedef struct {
                             KDA_DECAY_SOFTPLUS ablation; used by
                             kda_chunk_fwd*, kda_recurrent_step, kda_prepass;
                             g_min applies to the K3 map only                  */
+  kda_token_layout tokens; /* order of the per-token tensors (above):
+                            KDA_TOKENS_BTHD (default) or KDA_TOKENS_BHTD;
+                            kda_recurrent_step (one token) ignores it        */
 } kda_desc;
 
 /* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
@@ -340,7 +355,8 @@ int32_t kda_snapshot_count(const kda_desc* d, int32_t every_chunks);
  * state after the last segment.  Arguments as kda_chunk_fwd; ws of
  * kda_chunk_fwd_kcp_workspace_size(d, n_parts) bytes (three fp32 state sets
  * of B * n_parts * H * d_k * d_v plus the segments' own workspace).
- * T must be a multiple of 64 * n_parts (KDA_ERR_UNSUPPORTED otherwise);
+ * T must be a multiple of 64 * n_parts and the tensors token major
+ * (KDA_ERR_UNSUPPORTED otherwise);
  * n_parts == 1 is kda_chunk_fwd.  Outputs equal kda_chunk_fwd's up to fp32
  * rounding of the folded entry states.  The work is about three forward
  * passes: this is the one-GPU share of sequence parallelism across GPUs, not
@@ -352,7 +368,7 @@ kda_status kda_chunk_fwd_kcp(const kda_desc* d, int32_t n_parts, const void* q, 
                              void* stream);
 
 /* Workspace bytes for kda_chunk_fwd_kcp (0 if *d is invalid or T is not a
- * multiple of 64 * n_parts). */
+ * multiple of 64 * n_parts, or the tensors are head first). */
 size_t kda_chunk_fwd_kcp_workspace_size(const kda_desc* d, int32_t n_parts);
 
 /*

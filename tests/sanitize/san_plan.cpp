@@ -135,6 +135,12 @@ int main() {
   bad = d;
   bad.fused = 3;
   EXPECT(validate_desc(&bad) == KDA_ERR_BAD_SHAPE);
+  bad = d;
+  std::memcpy(&bad.tokens, &seven, sizeof seven);
+  EXPECT(validate_desc(&bad) == KDA_ERR_UNSUPPORTED);
+  bad = d;
+  bad.tokens = KDA_TOKENS_BHTD;
+  EXPECT(validate_desc(&bad) == KDA_OK && head_first(&bad) == 1 && head_first(&d) == 0);
   EXPECT(kda_desc_init(nullptr, 1, 1, 1, 128, KDA_BF16, KDA_BF16) == KDA_ERR_NULL_ARG);
 
   // C ABI queries and argument checks (all return before any GPU work)

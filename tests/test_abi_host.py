@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert {"kda_chunk_fwd", "kda_recurrent_step", "kda_state_io"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kda_abi_version() == 5
+    assert L.kda_abi_version() == kda.ABI_VERSION == int(re.search(r"#define KDA_ABI_VERSION (\d+)", open(kda.HEADER_PATH).read()).group(1))
     assert L.kda_status_str(6) == b"workspace missing or too small"
 
 
@@ -248,6 +248,25 @@ def test_kcp_host_errors():
     one = L.kda_chunk_fwd_kcp_workspace_size(ctypes.byref(d2), 1)
     four = L.kda_chunk_fwd_kcp_workspace_size(ctypes.byref(d2), 4)
     assert one == L.kda_chunk_fwd_workspace_size(ctypes.byref(d2)) and four >= 3 * 2 * 4 * 3 * 128 * 128 * 4
+
+
+def test_token_layout_field():
+    """kda_desc.tokens: token major by default; head first is accepted by the
+    forward, rejected (KDA_ERR_UNSUPPORTED, before any GPU work) by the
+    entry points that take token-major tensors only; other values are
+    rejected."""
+    L = kda.lib()
+    assert _desc().tokens == 0
+    assert kda.make_desc(1, 64, 2, 128, kda.KDA_BF16, kda.KDA_BF16, head_first=True).tokens == 1
+    assert _fwd(_desc(tokens=2)) == 5
+    hf = _desc(T=1024, tokens=1)
+    assert L.kda_chunk_fwd_workspace_size(ctypes.byref(hf)) == L.kda_chunk_fwd_workspace_size(ctypes.byref(_desc(T=1024)))
+    assert L.kda_chunk_fwd_kcp_workspace_size(ctypes.byref(hf), 2) == 0
+    assert L.kda_chunk_fwd_kcp(ctypes.byref(hf), 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None,
+                               None, FAKE, 1 << 40, None) == 5
+    assert L.kda_prepass(ctypes.byref(hf), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 5
+    assert L.kda_input_prep(ctypes.byref(hf), 4, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None,
+                            FAKE, FAKE, FAKE, None, None) == 5
 
 
 def test_decay_map_field():
