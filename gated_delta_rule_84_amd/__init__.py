@@ -129,6 +129,41 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _check_forward_args(q, k, v, beta, z, A, S0, gate, rms_w, out, head_first):
+    """Shapes and element types of a forward call's tensors (the C ABI sees
+    only pointers, so a mismatch here would make the kernels read or write
+    past a tensor).  Returns (B, T, H, D)."""
+    if q.dim() != 4:
+        raise ValueError(f"q must be 4-D ({'[B, H, T, D]' if head_first else '[B, T, H, D]'}), got {tuple(q.shape)}")
+    if head_first:
+        B, H, T, D = q.shape
+        tok, per_tok = (B, H, T, D), (B, H, T)
+    else:
+        B, T, H, D = q.shape
+        tok, per_tok = (B, T, H, D), (B, T, H)
+
+    def expect(name, t, shape, dtype):
+        if t is None:
+            return
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+    for name, t in (("k", k), ("v", v), ("z", z), ("gate", gate)):
+        expect(name, t, tok, q.dtype)
+    expect("beta", beta, per_tok, q.dtype)
+    expect("A", A, (H,), torch.float32)
+    expect("S0", S0, (B, H, D, D), torch.float32)
+    expect("rms_w", rms_w, (H, D), torch.float32)
+    for name in ("o", "y"):
+        if out and out.get(name) is not None and tuple(out[name].shape) != tok:
+            raise ValueError(f"out['{name}'] has shape {tuple(out[name].shape)}, expected {tok}")
+    if out and out.get("S_T") is not None:
+        expect("out['S_T']", out["S_T"], (B, H, D, D), torch.float32)
+    return B, T, H, D
+
+
 def make_desc(B, T, H, D, in_dtype, out_dtype, g_min=-5.0, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6,
               qk_l2norm=True, segment_tokens=0, overlap=True, fused=None, decay="k3", head_first=False) -> KdaDesc:
     d = KdaDesc()
@@ -217,10 +252,7 @@ def chunk_fwd(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, out_dtype=
     parallel segments folded through their (M, S~) pairs (kda_chunk_fwd_kcp).
     With ``head_first`` the per-token tensors are [B, H, T, D] (beta
     [B, H, T]) and o, y come out the same way."""
-    if head_first:
-        B, H, T, D = q.shape
-    else:
-        B, T, H, D = q.shape
+    B, T, H, D = _check_forward_args(q, k, v, beta, z, A, S0, gate, rms_w, out, head_first)
     tok_shape = (B, H, T, D) if head_first else (B, T, H, D)
     in_dt = _dt(q)
     odt = q.dtype if out_dtype is None else out_dtype
@@ -283,10 +315,7 @@ def chunk_fwd_noalloc(q, k, v, beta, z, A, S0=None, gate=None, rms_w=None, *, ou
     """kda_chunk_fwd_noalloc: the forward without a workspace (the library's
     per-GPU scratch array, one-stream schedule).  Arguments and result as
     chunk_fwd; only the outputs are allocated here, by the caller's side."""
-    if head_first:
-        B, H, T, D = q.shape
-    else:
-        B, T, H, D = q.shape
+    B, T, H, D = _check_forward_args(q, k, v, beta, z, A, S0, gate, rms_w, out, head_first)
     tok_shape = (B, H, T, D) if head_first else (B, T, H, D)
     odt = q.dtype if out_dtype is None else out_dtype
     desc = make_desc(B, T, H, D, _dt(q), _dt(torch.empty(0, dtype=odt)), head_first=head_first, **opts)
