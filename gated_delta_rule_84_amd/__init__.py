@@ -129,6 +129,16 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _expect(name, t, shape, dtype=None):
+    """A tensor argument's shape (and element type); None passes."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
 def _check_forward_args(q, k, v, beta, z, A, S0, gate, rms_w, out, head_first):
     """Shapes and element types of a forward call's tensors (the C ABI sees
     only pointers, so a mismatch here would make the kernels read or write
@@ -142,13 +152,7 @@ def _check_forward_args(q, k, v, beta, z, A, S0, gate, rms_w, out, head_first):
         B, T, H, D = q.shape
         tok, per_tok = (B, T, H, D), (B, T, H)
 
-    def expect(name, t, shape, dtype):
-        if t is None:
-            return
-        if tuple(t.shape) != tuple(shape):
-            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
-        if t.dtype != dtype:
-            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    expect = _expect
 
     for name, t in (("k", k), ("v", v), ("z", z), ("gate", gate)):
         expect(name, t, tok, q.dtype)
@@ -343,8 +347,20 @@ def input_prep(xq, xk, xv, wq, wk, wv, beta_logits=None, state_in=None, state_ou
     state_out: [B, 3, W - 1, H * D] fp32 conv windows (None: zeros / not
     written; they may be the same tensor).  Returns a dict with q, k, v (and
     beta)."""
+    if xq.dim() != 4 or wq.dim() != 2:
+        raise ValueError("xq must be [B, T, H, D] and wq [H * D, W]")
     B, T, H, D = xq.shape
     W = wq.shape[1]
+    for name, t in (("xk", xk), ("xv", xv)):
+        _expect(name, t, xq.shape, xq.dtype)
+    _expect("beta_logits", beta_logits, (B, T, H), xq.dtype)
+    for name, t in (("wq", wq), ("wk", wk), ("wv", wv)):
+        _expect(name, t, (H * D, W), torch.float32)
+    for name, t in (("state_in", state_in), ("state_out", state_out)):
+        _expect(name, t, (B, 3, W - 1, H * D), torch.float32)
+    for name in ("q", "k", "v"):
+        _expect(f"out['{name}']", (out or {}).get(name), (B, T, H, D), xq.dtype)
+    _expect("out['beta']", (out or {}).get("beta"), (B, T, H), xq.dtype)
     desc = make_desc(B, T, H, D, _dt(xq), _dt(xq))
     res = dict(out or {})
     for n in ("q", "k", "v"):
@@ -366,7 +382,18 @@ def recurrent_step(q, k, v, beta, z, A, S_pool, slot=None, gate=None, rms_w=None
     beta [n, H]; S_pool [n_slots, H, D, D] fp32 updated in place; slot: int32
     [n] or None.  status: a device uint32 tensor that collects
     KDA_FLAG_BAD_SLOT for slots outside [0, n_slots) (those are skipped)."""
+    if q.dim() != 3 or S_pool.dim() != 4:
+        raise ValueError("q must be [n, H, D] and S_pool [n_slots, H, D, D]")
     n, H, D = q.shape
+    for name, t in (("k", k), ("v", v), ("z", z), ("gate", gate)):
+        _expect(name, t, (n, H, D), q.dtype)
+    _expect("beta", beta, (n, H), q.dtype)
+    _expect("A", A, (H,), torch.float32)
+    _expect("S_pool", S_pool, (S_pool.shape[0], H, D, D), torch.float32)
+    _expect("slot", slot, (n,), torch.int32)
+    _expect("rms_w", rms_w, (H, D), torch.float32)
+    for name in ("o", "y"):
+        _expect(f"out['{name}']", (out or {}).get(name), (n, H, D))
     odt = q.dtype if out_dtype is None else out_dtype
     desc = make_desc(n, 1, H, D, _dt(q), _dt(torch.empty(0, dtype=odt)), **opts)
     want_y = (gate is not None) if want_y is None else want_y
@@ -390,9 +417,14 @@ def state_io(op: int, pool, user=None, slot=None, n=None, layout: int = LAYOUT_K
     """ZERO / IMPORT / EXPORT states between ``pool`` [n_slots, H, D, D] and
     ``user`` [n, H, D, D] (layout KV) or its transpose (layout VK).  status:
     as for recurrent_step."""
+    if pool.dim() != 4:
+        raise ValueError("pool must be [n_slots, H, D, D]")
     n_slots, H, Dk, Dv = pool.shape
+    _expect("pool", pool, pool.shape, torch.float32)
     if n is None:
         n = user.shape[0] if user is not None else (slot.numel() if slot is not None else pool.shape[0])
+    _expect("user", user, (n, H, Dk, Dv) if layout == LAYOUT_KV else (n, H, Dv, Dk), torch.float32)
+    _expect("slot", slot, (n,), torch.int32)
     rc = lib().kda_state_io(op, n, H, Dk, Dv, layout, _ptr(pool), int(n_slots), _ptr(slot), _ptr(user), _ptr(status),
                             _stream(pool.device))
     if rc != 0:
@@ -402,7 +434,12 @@ def state_io(op: int, pool, user=None, slot=None, n=None, layout: int = LAYOUT_K
 def prepass(q, k, z, A, **opts):
     """Chunk-local cumulative log-decay G [B, T, H, D] and inverse norms rq, rk
     [B, T, H] (diagnostic view of the first step of chunk_fwd)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, D]")
     B, T, H, D = q.shape
+    for name, t in (("k", k), ("z", z)):
+        _expect(name, t, q.shape, q.dtype)
+    _expect("A", A, (H,), torch.float32)
     desc = make_desc(B, T, H, D, _dt(q), KDA_F32, **opts)
     G = torch.empty((B, T, H, D), dtype=torch.float32, device=q.device)
     rq = torch.empty((B, T, H), dtype=torch.float32, device=q.device)

@@ -47,3 +47,31 @@ def test_forward_refuses_mismatched_tensors(fn, head_first):
     # consistent CPU tensors pass the shape checks and stop at the device check
     with pytest.raises(ValueError, match="GPU"):
         _call(_tensors(head_first=head_first), fn, head_first=head_first)
+
+
+def test_decode_state_io_prep_prepass_refuse_mismatched_tensors():
+    bf = torch.bfloat16
+    n, H, D = 3, 2, 64
+    q = torch.zeros((n, H, D), dtype=bf)
+    pool = torch.zeros((5, H, D, D))
+    A = torch.zeros((H,))
+    with pytest.raises(ValueError, match="beta"):
+        kda.recurrent_step(q, q, q, torch.zeros((n, H + 1), dtype=bf), q, A, pool)
+    with pytest.raises(ValueError, match="slot"):
+        kda.recurrent_step(q, q, q, torch.zeros((n, H), dtype=bf), q, A, pool, slot=torch.zeros((n,), dtype=torch.int64))
+    with pytest.raises(ValueError, match="S_pool"):
+        kda.recurrent_step(q, q, q, torch.zeros((n, H), dtype=bf), q, A, torch.zeros((5, H, D, D), dtype=torch.float64))
+    with pytest.raises(ValueError, match="user"):
+        kda.state_io(kda.STATE_EXPORT, pool, torch.zeros((n, H, D, D // 2)))
+    with pytest.raises(ValueError, match="slot"):
+        kda.state_io(kda.STATE_EXPORT, pool, torch.zeros((n, H, D, D)), slot=torch.zeros((n + 1,), dtype=torch.int32))
+    x = torch.zeros((1, 10, H, D), dtype=bf)
+    w = torch.zeros((H * D, 4))
+    with pytest.raises(ValueError, match="xv"):
+        kda.input_prep(x, x, torch.zeros((1, 11, H, D), dtype=bf), w, w, w)
+    with pytest.raises(ValueError, match="state_in"):
+        kda.input_prep(x, x, x, w, w, w, state_in=torch.zeros((1, 3, 4, H * D)))
+    with pytest.raises(ValueError, match="wk"):
+        kda.input_prep(x, x, x, w, torch.zeros((H * D, 3)), w)
+    with pytest.raises(ValueError, match="z"):
+        kda.prepass(x, x, torch.zeros((1, 10, H, D)), A)
