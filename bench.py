@@ -465,7 +465,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="k3_layer")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-baseline sample (0: all heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
