@@ -7,7 +7,6 @@ kernel, prefix-cache snapshots, the no-alloc entry point) and for fp32
 inputs.  The token-major path itself is checked against the fp64 oracle by
 the other GPU tests; a second, oracle-checked case here covers a head-first
 call directly."""
-import numpy as np
 import pytest
 import torch
 
@@ -108,3 +107,24 @@ def test_head_first_pipelined_vs_oracle(kda):
             "S_T": rel_l2(host64(r["S_T"]), ref["S_T"])}
     log(f"[layout] head first vs oracle: " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()))
     assert all(v <= 3e-3 for v in errs.values()), errs
+
+
+def test_head_first_pipelined_windows(kda):
+    """Head first on the pipelined schedule in windows (a workspace of 512
+    chunks of records: two windows, the second short and ragged, each
+    starting at a token offset): bit-identical to the token-major call with
+    the same workspace, snapshots across the windows included."""
+    B, T, H, D = 1, 625 * 64 - 20, 3, 128
+    t, _ = _inputs(B, T, H, D, "bf16", seed=55)
+    desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, head_first=True)
+    nbytes = kda.workspace_size(desc, 512 * 64)
+    assert kda.schedule(desc, nbytes)[1] == "pipelined"
+    assert kda.launches(desc, nbytes) == ["intra", "scan"] * 2
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    log(f"[layout] pipelined windows head first: B={B} T={T} H={H}")
+    ref = _call(kda, t, fused=False, workspace=ws, snapshot_chunks=100)
+    hf = _call(kda, _head_first(t), head_first=True, fused=False, workspace=ws, snapshot_chunks=100)
+    assert kda.call_status(desc, ws) == 0
+    for key in ("o", "y", "S_T", "snapshots"):
+        got = hf[key].permute(0, 2, 1, 3) if key in ("o", "y") else hf[key]
+        assert _bit_equal(got.contiguous(), ref[key]), key
