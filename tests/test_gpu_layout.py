@@ -65,6 +65,9 @@ CASES = [
     ("fp32 inputs, d = 64", 1, 333, 2, 64, "f32", "segments", {"overlap": False, "fused": False}),
     ("snapshots", 1, 700, 2, 128, "bf16", None, {"overlap": False, "fused": False, "snapshot_chunks": 3}),
     ("no-alloc entry point", 2, 150, 3, 128, "bf16", None, {"noalloc": True}),
+    ("one token", 2, 1, 3, 128, "bf16", None, {"fused": False}),
+    ("no tokens (state copied)", 2, 0, 3, 128, "bf16", None, {"fused": False}),
+    ("o only, ragged, d = 64", 1, 65, 2, 64, "bf16", None, {"fused": False, "want_y": False}),
 ]
 
 
@@ -85,7 +88,7 @@ def test_head_first_matches_token_major(kda, name, B, T, H, D, dtype, sched, opt
     log(f"[layout] {name}: B={B} T={T} H={H} D={D} {dtype}")
     ref = _call(kda, t, **opts, **extra)
     hf = _call(kda, _head_first(t), head_first=True, **opts, **extra)
-    keys = [k for k in ("o", "y", "S_T", "snapshots") if k in ref]
+    keys = [k for k in ("o", "y", "S_T", "snapshots") if ref.get(k) is not None]
     assert {"o", "S_T"} <= set(keys) and all(k in hf for k in keys)
     for key in keys:
         got = hf[key].permute(0, 2, 1, 3) if key in ("o", "y") else hf[key]
