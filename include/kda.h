@@ -216,6 +216,8 @@ kda_status kda_chunk_fwd_launches(const kda_desc* d, size_t ws_bytes, int32_t* k
  * section 2.1's chunk form with section 2.2's 16-token dense sub-tiles.
  *
  *  q, k, v, beta, z, A   inputs (see layouts above); beta in (0, 1).
+ *         The shapes here are token major; with d->tokens ==
+ *         KDA_TOKENS_BHTD every [B, T, H, ..] below is [B, H, T, ..].
  *  S0     [B, H, d_k, d_v] fp32 initial state, or NULL for zero.
  *  gate   [B, T, H, d_v] gate logits W_g x, or NULL (no gate).
  *  rms_w  [H, d_v] fp32 RMSNorm weight, or NULL (weight 1).
