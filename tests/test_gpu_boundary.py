@@ -112,15 +112,23 @@ def test_status_word_reports_a_withheld_producer(kda):
         assert torch.equal(_bits(again[key]), _bits(good[key])), key
 
 
-@pytest.mark.parametrize("sched", ["pipelined", "overlapped", "segments"])
-def test_guard_bands_around_workspace_and_outputs(kda, sched):
+@pytest.mark.parametrize("sched,head_first", [("pipelined", False), ("overlapped", False), ("segments", False),
+                                              ("pipelined", True), ("segments", True)])
+def test_guard_bands_around_workspace_and_outputs(kda, sched, head_first):
     """Workspace, o, y and S_T carved out of one buffer with 64 KiB guard bands
-    of a fixed pattern between them; after the call every guard is intact."""
+    of a fixed pattern between them; after the call every guard is intact
+    (token major, and head first)."""
     B, T, H, D = 1, 1536, 3, 128
     t = _inputs(B, T, H, D, seed=3)
+    tok = (B, T, H, D)
+    if head_first:
+        for n in ("q", "k", "v", "z", "gate"):
+            t[n] = t[n].permute(0, 2, 1, 3).contiguous()
+        t["beta"] = t["beta"].permute(0, 2, 1).contiguous()
+        tok = (B, H, T, D)
     seg = 128
     desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, segment_tokens=seg if sched != "segments" else 0,
-                         overlap=sched != "segments")
+                         overlap=sched != "segments", head_first=head_first)
     if sched == "pipelined":
         ws_bytes = kda.workspace_size(desc)
     elif sched == "overlapped":
@@ -138,12 +146,12 @@ def test_guard_bands_around_workspace_and_outputs(kda, sched):
     pattern = torch.arange(at, device="cuda", dtype=torch.int64).remainder(251).to(torch.uint8)
     buf.copy_(pattern)
     ws = buf[offs[0]:offs[0] + ws_bytes]
-    out = {"o": buf[offs[1]:offs[1] + sizes[1]].view(torch.bfloat16).view(B, T, H, D),
-           "y": buf[offs[2]:offs[2] + sizes[2]].view(torch.bfloat16).view(B, T, H, D),
+    out = {"o": buf[offs[1]:offs[1] + sizes[1]].view(torch.bfloat16).view(tok),
+           "y": buf[offs[2]:offs[2] + sizes[2]].view(torch.bfloat16).view(tok),
            "S_T": buf[offs[3]:offs[3] + sizes[3]].view(torch.float32).view(B, H, D, D)}
     r = kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t["S0"], gate=t["gate"], out=out,
                       workspace=ws, segment_tokens=seg if sched != "segments" else 256,
-                      overlap=sched != "segments")
+                      overlap=sched != "segments", head_first=head_first)
     torch.cuda.synchronize()
     assert kda.call_status(desc, ws) == 0
     used = torch.zeros(at, dtype=torch.bool, device="cuda")
@@ -151,25 +159,33 @@ def test_guard_bands_around_workspace_and_outputs(kda, sched):
         used[o_:o_ + sz] = True
     assert torch.equal(buf[~used], pattern[~used]), "a guard band was written"
     ref = kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t["S0"], gate=t["gate"],
-                        overlap=False)
+                        overlap=False, head_first=head_first)
     for key in ("o", "y", "S_T"):
         assert torch.equal(_bits(r[key]), _bits(ref[key])), key
 
 
-def test_forward_captured_in_a_graph(kda):
+@pytest.mark.parametrize("head_first", [False, True])
+def test_forward_captured_in_a_graph(kda, head_first):
     """A call whose stream is being captured takes the one-stream schedule (no
     in-kernel waits for producers a graph may order after the scan); the graph
     replays, with eager work and synchronisations in between, give the eager
-    result bit for bit every time."""
+    result bit for bit every time (token major, and head first)."""
     B, T, H, D = 1, 2048, 2, 128
     t = _inputs(B, T, H, D, seed=4)
-    desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16)
+    tok = (B, T, H, D)
+    if head_first:
+        for n in ("q", "k", "v", "z", "gate"):
+            t[n] = t[n].permute(0, 2, 1, 3).contiguous()
+        t["beta"] = t["beta"].permute(0, 2, 1).contiguous()
+        tok = (B, H, T, D)
+    desc = kda.make_desc(B, T, H, D, kda.KDA_BF16, kda.KDA_BF16, head_first=head_first)
     ws = torch.empty(kda.workspace_size(desc), dtype=torch.uint8, device="cuda")
-    out = {"o": torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda"),
-           "y": torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda"),
+    out = {"o": torch.empty(tok, dtype=torch.bfloat16, device="cuda"),
+           "y": torch.empty(tok, dtype=torch.bfloat16, device="cuda"),
            "S_T": torch.empty((B, H, D, D), device="cuda")}
     eager = {k: v.clone() for k, v in kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t["S0"],
-                                                     gate=t["gate"], out=out, workspace=ws).items()}
+                                                     gate=t["gate"], out=out, workspace=ws,
+                                                     head_first=head_first).items()}
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
@@ -177,7 +193,7 @@ def test_forward_captured_in_a_graph(kda):
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
             kda.chunk_fwd(t["q"], t["k"], t["v"], t["beta"], t["z"], t["A"], S0=t["S0"], gate=t["gate"], out=out,
-                          workspace=ws)
+                          workspace=ws, head_first=head_first)
     torch.cuda.current_stream().wait_stream(s)
     for rep in range(3):
         for v_ in out.values():
