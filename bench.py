@@ -624,7 +624,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded; K3 layer shapes, no trained weights)",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "d_k": D, "d_v": D, "chunk": 64,
-                   "inputs": "bf16", "state": "fp32", "outputs": "y (bf16) + S_T (fp32)", "gate": True,
+                   "inputs": "bf16", "layout": "[B, T, H, d] (token major)", "state": "fp32",
+                   "outputs": "y (bf16) + S_T (fp32)", "gate": True,
                    "schedule": sched, "segment_tokens": seg, "decay": args.decay},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(dom, wl.name),
